@@ -1,0 +1,188 @@
+"""CPU oracle for the Q4_K x Q8 products -- TEST INFRASTRUCTURE ONLY.
+
+Thin numpy/ctypes wrapper over `q4k_oracle.c` (plain single-threaded C, fp64
+products, bit-exact fp32 activation quantizer).  Only the tests, the smoke check
+and the benchmark's CPU-baseline leg may import this package; the GPU product
+path neither imports it nor shares any code with it.
+
+`build()` compiles the C file with gcc (no fast-math, no FMA contraction) into
+`liboracle.so` next to it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4k_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+QK, SB_BYTES, QB = 256, 144, 32
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc.  Returns the library path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-ffp-contract=off", "-fno-fast-math",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        sig = {
+            "oracle_unpack_q4k": [_P, _P, _P, _P, _P, _P],
+            "oracle_dequant_row": [_P, _I, _P],
+            "oracle_quantize_act": [_P, _I, _I, _P, _P, _P],
+            "oracle_swiglu": [_P, _P, _I, _P],
+            "oracle_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
+            "oracle_subblock_dots": [_P, _I, _P, _I, _P, _I, _P],
+            "oracle_matvec_intform": [_P, _I, _P, _P, _P, _I, _P, _I, _P],
+            "oracle_moe_matvec": [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P,
+                                  ctypes.c_int, _P],
+            "oracle_moe_layer": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+                                 _P, _P, _P, _P, _P, _P, _P, _P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def unpack_q4k(sb: np.ndarray):
+    """Fields of one 144-byte super-block: (d, dmin, sc[8], mn[8], q[256])."""
+    sb = _c(sb, np.uint8).reshape(SB_BYTES)
+    d, dmin = ctypes.c_double(), ctypes.c_double()
+    sc = np.zeros(8, np.int32)
+    mn = np.zeros(8, np.int32)
+    q = np.zeros(QK, np.int32)
+    _load().oracle_unpack_q4k(_ptr(sb), ctypes.addressof(d), ctypes.addressof(dmin),
+                              _ptr(sc), _ptr(mn), _ptr(q))
+    return d.value, dmin.value, sc, mn, q
+
+
+def dequant(w: np.ndarray, K: int) -> np.ndarray:
+    """fp64 [N, K] dequantized weights of packed Q4_K rows."""
+    w = _c(w, np.uint8)
+    N = w.size // (K // QK * SB_BYTES)
+    w = w.reshape(N, -1)
+    out = np.zeros((N, K), np.float64)
+    for n in range(N):
+        _load().oracle_dequant_row(_ptr(w[n]), K, _ptr(out[n]))
+    return out
+
+
+def quantize_act(x: np.ndarray):
+    """Q8 of fp32 [M, K]: (codes int8 [M, K], scales fp32 [M, K/32], sums int32 [M, K/32])."""
+    x = _c(x, np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    M, K = x.shape
+    codes = np.zeros((M, K), np.int8)
+    scales = np.zeros((M, K // QB), np.float32)
+    sums = np.zeros((M, K // QB), np.int32)
+    _load().oracle_quantize_act(_ptr(x), M, K, _ptr(codes), _ptr(scales), _ptr(sums))
+    return codes, scales, sums
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g, u = _c(g, np.float32), _c(u, np.float32)
+    h = np.zeros_like(g)
+    _load().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def _rows(rows, N):
+    if rows is None:
+        return np.arange(N, dtype=np.int64)
+    return _c(rows, np.int64)
+
+
+def matvec(w, N, K, codes, scales, rows=None) -> np.ndarray:
+    """fp64 [M, len(rows)]: y[m, r] = sum_k w[rows[r], k] * xhat[m, k]."""
+    codes, scales = _c(codes, np.int8), _c(scales, np.float32)
+    M = codes.size // K
+    r = _rows(rows, N)
+    y = np.zeros((M, r.size), np.float64)
+    _load().oracle_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
+                          _ptr(r), r.size, _ptr(y))
+    return y
+
+
+def matvec_intform(w, N, K, codes, scales, sums, rows=None) -> np.ndarray:
+    codes, scales, sums = _c(codes, np.int8), _c(scales, np.float32), _c(sums, np.int32)
+    M = codes.size // K
+    r = _rows(rows, N)
+    y = np.zeros((M, r.size), np.float64)
+    _load().oracle_matvec_intform(_ptr(_c(w, np.uint8)), K, _ptr(codes), _ptr(scales),
+                                  _ptr(sums), M, _ptr(r), r.size, _ptr(y))
+    return y
+
+
+def subblock_dots(w, N, K, codes, rows=None) -> np.ndarray:
+    """int32 [M, len(rows), K/32] sub-block dots D = sum q*c."""
+    codes = _c(codes, np.int8)
+    M = codes.size // K
+    r = _rows(rows, N)
+    D = np.zeros((M, r.size, K // QB), np.int32)
+    _load().oracle_subblock_dots(_ptr(_c(w, np.uint8)), K, _ptr(codes), M, _ptr(r),
+                                 r.size, _ptr(D))
+    return D
+
+
+def moe_matvec(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales,
+               act_per_slot: bool) -> np.ndarray:
+    ids = _c(ids, np.int32)
+    T, topk = ids.shape
+    rw = None if route_w is None else _c(route_w, np.float32)
+    codes, scales = _c(codes, np.int8), _c(scales, np.float32)
+    y = np.zeros((T if rw is not None else T * topk, N), np.float64)
+    _load().oracle_moe_matvec(_ptr(_c(w, np.uint8)), n_experts, expert_stride, N, K,
+                              _ptr(ids), _ptr(rw), T, topk, _ptr(codes), _ptr(scales),
+                              int(act_per_slot), _ptr(y))
+    return y
+
+
+def moe_layer(w_gate, w_up, w_down, n_experts, H, F, ids, route_w, x):
+    """Whole routed-expert FFN layer.  Returns dict with y (fp64 [T, H]) and the
+    intermediates g, u, h (fp32 [T*topk, F]) and hc/hs/hsum (Q8 of h)."""
+    ids, rw, x = _c(ids, np.int32), _c(route_w, np.float32), _c(x, np.float32)
+    T, topk = ids.shape
+    P = T * topk
+    stride_gu = F * (H // QK) * SB_BYTES
+    stride_dn = H * (F // QK) * SB_BYTES
+    out = dict(g=np.zeros((P, F), np.float32), u=np.zeros((P, F), np.float32),
+               h=np.zeros((P, F), np.float32), hc=np.zeros((P, F), np.int8),
+               hs=np.zeros((P, F // QB), np.float32), hsum=np.zeros((P, F // QB), np.int32),
+               y=np.zeros((T, H), np.float64))
+    _load().oracle_moe_layer(_ptr(_c(w_gate, np.uint8)), _ptr(_c(w_up, np.uint8)),
+                             _ptr(_c(w_down, np.uint8)), n_experts, stride_gu, stride_dn,
+                             H, F, _ptr(ids), _ptr(rw), T, topk, _ptr(x),
+                             _ptr(out["g"]), _ptr(out["u"]), _ptr(out["h"]),
+                             _ptr(out["hc"]), _ptr(out["hs"]), _ptr(out["hsum"]),
+                             _ptr(out["y"]))
+    return out
