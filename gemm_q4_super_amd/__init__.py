@@ -1,0 +1,27 @@
+"""Q4_K x Q8 matrix products on AMD MI355X (gfx950).
+
+Python binding of libq4k.so (C ABI in include/q4k.h).  The binding only
+marshals arguments: PyTorch supplies device memory and the current stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU or PyTorch fallback: if the library is missing, importing the binding's
+functions raises.
+
+Functions carry the C names:
+    q4k_quantize_act(x, gate=None)                   -> (codes, scales, sums)
+    q4k_gemv(w, N, K, codes, scales, sums)           -> y [M, N]   (M <= 8)
+    q4k_gemm(w, N, K, codes, scales, sums)           -> y [M, N]
+    q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
+                 act_per_slot, workspace=None)       -> y
+"""
+from ._lib import (  # noqa: F401
+    Q4KError,
+    lib,
+    lib_path,
+    q4k_gemm,
+    q4k_gemv,
+    q4k_moe_gemv,
+    q4k_moe_workspace_bytes,
+    q4k_quantize_act,
+    q4k_status_string,
+    EXPORTED_SYMBOLS,
+)

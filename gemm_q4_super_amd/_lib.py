@@ -1,0 +1,137 @@
+"""ctypes marshalling for libq4k.so.  No arithmetic of the products lives here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libq4k.so")
+
+EXPORTED_SYMBOLS = (
+    "q4k_quantize_act",
+    "q4k_gemv",
+    "q4k_gemm",
+    "q4k_moe_gemv",
+    "q4k_moe_workspace_bytes",
+    "q4k_status_string",
+)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+_lib = None
+
+
+class Q4KError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, q4k_status_string(status), status))
+
+
+def lib():
+    """The loaded library (raises if libq4k.so has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError("libq4k.so not built: run `python -m gemm_q4_super_amd.build` "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(lib_path)
+        L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
+        L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+        L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+        L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
+                                   ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+        L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I]
+        L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
+        L.q4k_status_string.argtypes = [ctypes.c_int]
+        L.q4k_status_string.restype = ctypes.c_char_p
+        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_gemm", "q4k_moe_gemv"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def q4k_status_string(status: int) -> str:
+    return lib().q4k_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(st, what):
+    if st != 0:
+        raise Q4KError(st, what)
+
+
+def _dev(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def q4k_quantize_act(x, gate=None, out=None):
+    """Q8 of fp32 x [M, K] (or silu(gate)*x).  Returns (codes, scales, sums)."""
+    import torch
+    _dev(x, "x"); _dev(gate, "gate")
+    M, K = x.shape
+    if out is None:
+        codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        scales = torch.empty((M, K // 32), dtype=torch.float32, device=x.device)
+        sums = torch.empty((M, K // 32), dtype=torch.int32, device=x.device)
+    else:
+        codes, scales, sums = out
+    _check(lib().q4k_quantize_act(_ptr(x), M, K, _ptr(gate), _ptr(codes), _ptr(scales),
+                                  _ptr(sums), _stream(x)), "q4k_quantize_act")
+    return codes, scales, sums
+
+
+def _matrix_call(fn, what, w, N, K, codes, scales, sums, y):
+    import torch
+    for t, n in ((w, "w"), (codes, "codes"), (scales, "scales"), (sums, "sums")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check(fn(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(sums), M, _ptr(y),
+              _stream(codes)), what)
+    return y
+
+
+def q4k_gemv(w, N, K, codes, scales, sums, y=None):
+    return _matrix_call(lib().q4k_gemv, "q4k_gemv", w, N, K, codes, scales, sums, y)
+
+
+def q4k_gemm(w, N, K, codes, scales, sums, y=None):
+    return _matrix_call(lib().q4k_gemm, "q4k_gemm", w, N, K, codes, scales, sums, y)
+
+
+def q4k_moe_workspace_bytes(T, topk, n_experts) -> int:
+    return int(lib().q4k_moe_workspace_bytes(T, topk, n_experts))
+
+
+def q4k_moe_gemv(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales, sums,
+                 act_per_slot, workspace=None, y=None):
+    import torch
+    for t, n in ((w, "w"), (ids, "ids"), (route_w, "route_w"), (codes, "codes"),
+                 (scales, "scales"), (sums, "sums")):
+        _dev(t, n)
+    T, topk = ids.shape
+    if workspace is None:
+        nbytes = q4k_moe_workspace_bytes(T, topk, n_experts)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
+    if y is None:
+        rows = T if route_w is not None else T * topk
+        y = torch.empty((rows, N), dtype=torch.float32, device=codes.device)
+    _check(lib().q4k_moe_gemv(_ptr(w), n_experts, expert_stride, N, K, _ptr(ids),
+                              _ptr(route_w), T, topk, _ptr(codes), _ptr(scales), _ptr(sums),
+                              int(act_per_slot), _ptr(y), _ptr(workspace),
+                              workspace.numel(), _stream(codes)), "q4k_moe_gemv")
+    return y

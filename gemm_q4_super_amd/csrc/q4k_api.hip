@@ -1,0 +1,110 @@
+// C-ABI entry points of libq4k.so (declared in include/q4k.h).
+// Every argument is checked here, on the host, before anything is launched.
+#include "../../include/q4k.h"
+#include "q4k_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int from_hip(hipError_t e) {
+    if (e == hipErrorNotSupported) return Q4K_ENOTIMPL;
+    return e == hipSuccess ? Q4K_OK : Q4K_EHIP;
+}
+
+// Sizes beyond these would overflow the 32-bit grid/index arithmetic of the
+// kernels; far above any projection of the models in scope.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+int check_matrix_args(const void *w, int64_t N, int64_t K, const int8_t *codes,
+                      const float *scales, const int32_t *sums, int64_t M, float *y) {
+    if (!w || !codes || !scales || !sums || !y) return Q4K_EINVAL;
+    if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || M > kMaxDim) return Q4K_ESHAPE;
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(sums, 4) ||
+        !aligned(y, 4))
+        return Q4K_EALIGN;
+    return Q4K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4k_quantize_act(const float *x, int64_t M, int64_t K, const float *gate, int8_t *codes,
+                     float *scales, int32_t *sums, void *stream) {
+    if (!x || !codes || !scales || !sums) return Q4K_EINVAL;
+    if (M < 1 || K < q4k::kQB || K % q4k::kQB != 0) return Q4K_ESHAPE;
+    if (M > kMaxDim || K > kMaxDim || M * (K / q4k::kQB) > (int64_t(1) << 36)) return Q4K_ESHAPE;
+    if (!aligned(x, 16) || !aligned(codes, 16) || (gate && !aligned(gate, 16)) ||
+        !aligned(scales, 4) || !aligned(sums, 4))
+        return Q4K_EALIGN;
+    return from_hip(q4k::launch_quantize(x, M, K, gate, codes, scales, sums,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
+             const int32_t *sums, int64_t M, float *y, void *stream) {
+    int st = check_matrix_args(w, N, K, codes, scales, sums, M, y);
+    if (st != Q4K_OK) return st;
+    if (M > 8) return Q4K_ESHAPE;
+    return from_hip(q4k::launch_gemv(static_cast<const uint8_t *>(w), N, K, codes, scales,
+                                     sums, M, y, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
+             const int32_t *sums, int64_t M, float *y, void *stream) {
+    int st = check_matrix_args(w, N, K, codes, scales, sums, M, y);
+    if (st != Q4K_OK) return st;
+    return from_hip(q4k::launch_gemm(static_cast<const uint8_t *>(w), N, K, codes, scales,
+                                     sums, M, y, static_cast<hipStream_t>(stream)));
+}
+
+size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts) {
+    if (T < 1 || topk < 1 || n_experts < 1 || topk > n_experts || T * topk > 65536 ||
+        n_experts > 65536)
+        return 0;
+    return q4k::moe_workspace_bytes(T, topk, n_experts);
+}
+
+int q4k_moe_gemv(const void *w_experts, int64_t n_experts, int64_t expert_stride_bytes,
+                 int64_t N, int64_t K, const int32_t *ids, const float *route_w, int64_t T,
+                 int64_t topk, const int8_t *codes, const float *scales, const int32_t *sums,
+                 int act_per_slot, float *y, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+    if (!w_experts || !ids || !codes || !scales || !sums || !y) return Q4K_EINVAL;
+    if (act_per_slot != 0 && act_per_slot != 1) return Q4K_EINVAL;
+    if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || N > kMaxDim || K > kMaxDim)
+        return Q4K_ESHAPE;
+    if (n_experts < 1 || n_experts > 65536 || T < 1 || topk < 1 || topk > n_experts ||
+        T * topk > 65536)
+        return Q4K_ESHAPE;
+    if (expert_stride_bytes < N * (K / q4k::kQK) * q4k::kSB || expert_stride_bytes % 16 != 0)
+        return Q4K_ESHAPE;
+    if (!aligned(w_experts, 16) || !aligned(codes, 16) || !aligned(scales, 4) ||
+        !aligned(sums, 4) || !aligned(y, 4) || !aligned(ids, 4) ||
+        (route_w && !aligned(route_w, 4)))
+        return Q4K_EALIGN;
+    const size_t need = q4k::moe_workspace_bytes(T, topk, n_experts);
+    if (!workspace || workspace_bytes < need) return Q4K_EWORKSPACE;
+    if (!aligned(workspace, 256)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_moe_gemv(static_cast<const uint8_t *>(w_experts), n_experts,
+                                         expert_stride_bytes, N, K, ids, route_w, T, topk,
+                                         codes, scales, sums, act_per_slot, y, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+const char *q4k_status_string(int status) {
+    switch (status) {
+    case Q4K_OK: return "ok";
+    case Q4K_EINVAL: return "invalid argument (null pointer or bad value)";
+    case Q4K_EALIGN: return "buffer not aligned as required";
+    case Q4K_ESHAPE: return "size out of range";
+    case Q4K_EWORKSPACE: return "workspace missing or too small";
+    case Q4K_EHIP: return "HIP runtime error at launch";
+    case Q4K_ENOTIMPL: return "operation not available in this build";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Internal declarations shared by the libq4k.so translation units.
+// Launchers validate nothing: the C-ABI layer in q4k_api.hip does that first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+constexpr int kQK = 256;       // weights per Q4_K super-block
+constexpr int kSB = 144;       // bytes per Q4_K super-block
+constexpr int kQB = 32;        // Q8 block / Q4_K sub-block length
+
+hipError_t launch_quantize(const float *x, int64_t M, int64_t K, const float *gate,
+                           int8_t *codes, float *scales, int32_t *sums,
+                           hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
+                       const float *scales, const int32_t *sums, int64_t M, float *y,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
+                       const float *scales, const int32_t *sums, int64_t M, float *y,
+                       hipStream_t stream);
+
+size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts);
+
+hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride,
+                           int64_t N, int64_t K, const int32_t *ids, const float *route_w,
+                           int64_t T, int64_t topk, const int8_t *codes,
+                           const float *scales, const int32_t *sums, int act_per_slot,
+                           float *y, void *workspace, hipStream_t stream);
+
+}  // namespace q4k

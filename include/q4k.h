@@ -1,0 +1,136 @@
+/*
+ * q4k.h -- C ABI of libq4k.so: Q4_K-weight x Q8-activation matrix products on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operations: the matrix products of edge LLM inference against
+ * Q4_K_M-quantized weights described in "genie-ai-runtime: a Jetson edge LLM
+ * inference engine that beats llama.cpp -- designing for unified memory":
+ * batch-1 decode streams every weight once and is bandwidth-bound (section 2,
+ * "The target hardware (and the roofline that dictates strategy)"); prefill is
+ * a compute-bound batched product over all prompt tokens (section 3, Path B
+ * and Path E); verification of several drafted tokens shares one weight read
+ * (section 2 and section 9, speculative decoding).  The routed-expert product
+ * follows the mixture-of-experts layers of "I'm making LLMs work on small and
+ * old devices" (intro, expert pager; "Lessons").
+ *
+ * Formats (the pages name Q4_K_M but print no bytes; the public GGUF Q4_K
+ * layout is used):
+ *   Q4_K matrix W, N rows x K columns, K % 256 == 0: row-major, each row is
+ *     K/256 super-blocks of 144 bytes: fp16 d, fp16 dmin, 12 bytes of 6-bit
+ *     sub-block scales sc[8] and mins mn[8], 128 bytes of 4-bit quants q;
+ *     weight = d*sc[j]*q - dmin*mn[j], j = (column % 256) / 32.
+ *   Q8 activations, M rows x K: codes int8 [M][K] (row-major), scales fp32
+ *     [M][K/32], sums int32 [M][K/32].  Per block of 32 values:
+ *     scale = fl32(max|x| / 127), code = clamp(round-half-even(fl32(x/scale)),
+ *     -127, 127), sum = sum of codes; an all-zero block has scale 0, codes 0.
+ *   Products: y[m][n] = sum_k W[n][k] * scale[m][k/32] * code[m][k], i.e.
+ *     y = x W^T, fp32 [M][N] row-major.
+ *
+ * Conventions for every call:
+ *   - Pointers named as device buffers are device pointers on the current HIP
+ *     device.  The caller owns every buffer; the library never allocates,
+ *     frees, synchronizes, changes device or keeps state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; results are visible after the stream is synced.
+ *   - Inputs are read-only; outputs are fully overwritten (never accumulated).
+ *   - Arguments are checked on the host before anything is launched; a failed
+ *     check returns a negative status and launches nothing.  A launch error
+ *     reported by the runtime returns Q4K_EHIP.  Nothing is printed and no
+ *     C++ exception crosses the ABI.
+ *   - Any N >= 1 and M >= 1 (within a call's limits) runs on the same fast
+ *     kernels, with masked tails: there is no slower fallback for odd sizes.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum q4k_status {
+    Q4K_OK = 0,
+    Q4K_EINVAL = -1,     /* null pointer or invalid value                    */
+    Q4K_EALIGN = -2,     /* a buffer is not aligned as required              */
+    Q4K_ESHAPE = -3,     /* size out of range (K % 256, M range, topk, ...)  */
+    Q4K_EWORKSPACE = -4, /* workspace missing or too small                   */
+    Q4K_EHIP = -5,       /* the HIP runtime reported an error at launch      */
+    Q4K_ENOTIMPL = -6    /* operation not available in this build            */
+};
+
+/* Quantize M rows of K fp32 values (K % 32 == 0, M >= 1) to Q8 blocks of 32.
+ *   x      device fp32 [M][K], 16-byte aligned.
+ *   gate   NULL, or device fp32 [M][K]: then the value quantized is the SwiGLU
+ *          h = silu(gate) * x = gate / (1 + exp(-gate)) * x, evaluated in fp64
+ *          from the fp32 inputs and rounded once to fp32 (the pages name no
+ *          activation function; SwiGLU is this library's reading for the
+ *          routed-expert layer).  16-byte aligned.
+ *   codes  device int8 [M][K], 16-byte aligned.
+ *   scales device fp32 [M][K/32];  sums  device int32 [M][K/32].
+ * Codes and sums are bit-exact with the definition above; non-finite inputs
+ * are outside the contract (no fault, unspecified codes). */
+int q4k_quantize_act(const float *x, int64_t M, int64_t K, const float *gate,
+                     int8_t *codes, float *scales, int32_t *sums, void *stream);
+
+/* Decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T for M = 1..8
+ * (batch-1 decode and the verification of up to 8 drafted tokens, which
+ * shares one read of W).  Bandwidth-bound: W is streamed once with 16-byte
+ * loads; no matrix cores.
+ *   w       device Q4_K bytes, N rows x (K/256)*144 bytes, 16-byte aligned.
+ *   N >= 1, K % 256 == 0, K >= 256, 1 <= M <= 8.
+ *   codes   device int8 [M][K] (16-byte aligned); scales fp32 [M][K/32];
+ *   sums    int32 [M][K/32]   -- as written by q4k_quantize_act.
+ *   y       device fp32 [M][N].
+ * fp32 result; accumulation order differs from the plain definition, within a
+ * relative error of 2e-3 (absolute 1e-4 near zero). */
+int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
+             const float *scales, const int32_t *sums, int64_t M, float *y,
+             void *stream);
+
+/* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (section 3's
+ * batched prefill over all prompt tokens).  Compute-bound: Q4_K tiles are
+ * staged through LDS and the per-32 sub-block integer dot products run on the
+ * matrix cores, followed by the fp32 scale/min epilogue.  Arguments and
+ * result contract as for q4k_gemv, without the M <= 8 limit. */
+int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
+             const float *scales, const int32_t *sums, int64_t M, float *y,
+             void *stream);
+
+/* Routed-expert grouped GEMV.  n_experts Q4_K matrices of N rows x K columns
+ * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of
+ * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].
+ * Pairs are grouped by expert on the device, so each touched expert's weights
+ * are read once per call however many tokens chose it.
+ *   ids          device int32 [T][topk]; each in [0, n_experts) -- not checked
+ *                on the host (device data); an id out of range is undefined.
+ *   route_w      NULL: y is per slot, fp32 [T*topk][N];
+ *                else device fp32 [T][topk]: y[t] = sum_s route_w[t][s] *
+ *                (slot product), summed in slot order 0..topk-1, fp32 [T][N].
+ *   act_per_slot 0: activation row t serves every slot of token t (codes
+ *                [T][K]); 1: slot (t, s) has its own row t*topk+s (codes
+ *                [T*topk][K]).
+ *   codes/scales/sums as for q4k_gemv.
+ *   workspace    device buffer of at least q4k_moe_workspace_bytes(T, topk,
+ *                n_experts) bytes, 256-byte aligned; its contents on entry are
+ *                ignored.
+ * Limits: 1 <= topk <= n_experts, T >= 1, T*topk <= 65536. */
+int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
+                 int64_t expert_stride_bytes, int64_t N, int64_t K,
+                 const int32_t *ids, const float *route_w, int64_t T,
+                 int64_t topk, const int8_t *codes, const float *scales,
+                 const int32_t *sums, int act_per_slot, float *y,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes q4k_moe_gemv needs for these sizes (0 on invalid sizes). */
+size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts);
+
+/* Static description of a status code. */
+const char *q4k_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

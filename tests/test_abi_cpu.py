@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/q4k.h declares, and rejects invalid arguments on the host with the
+documented status codes before anything is launched.
+
+Every call below fails a host-side check, so no device pointer is ever
+dereferenced; the fake addresses are never touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_q4_super_amd as q4k
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, EALIGN, ESHAPE, EWORKSPACE = 0, -1, -2, -3, -4
+A = 0x10000          # a 256-byte aligned fake address (never dereferenced)
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "q4k.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4k_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q4k.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared()
+    assert set(declared) == set(q4k.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert q4k.q4k_status_string(st) != "unknown status"
+    assert q4k.q4k_status_string(7) == "unknown status"
+
+
+def test_gemv_gemm_argument_checks(L):
+    for fn in (L.q4k_gemv, L.q4k_gemm):
+        good = dict(w=A, N=16, K=512, codes=A, scales=A, sums=A, M=1, y=A)
+
+        def call(**kw):
+            a = dict(good, **kw)
+            return fn(a["w"], a["N"], a["K"], a["codes"], a["scales"], a["sums"], a["M"],
+                      a["y"], None)
+        assert call(w=None) == EINVAL
+        assert call(codes=None) == EINVAL
+        assert call(y=None) == EINVAL
+        assert call(K=100) == ESHAPE
+        assert call(K=0) == ESHAPE
+        assert call(K=288) == ESHAPE
+        assert call(N=0) == ESHAPE
+        assert call(M=0) == ESHAPE
+        assert call(N=1 << 25) == ESHAPE
+        assert call(w=A + 8) == EALIGN
+        assert call(codes=A + 4) == EALIGN
+        assert call(y=A + 2) == EALIGN
+    # the GEMV takes at most 8 activation rows
+    assert L.q4k_gemv(A, 16, 512, A, A, A, 9, A, None) == ESHAPE
+
+
+def test_quantize_argument_checks(L):
+    f = L.q4k_quantize_act
+    assert f(None, 1, 32, None, A, A, A, None) == EINVAL
+    assert f(A, 1, 31, None, A, A, A, None) == ESHAPE
+    assert f(A, 0, 32, None, A, A, A, None) == ESHAPE
+    assert f(A + 4, 1, 32, None, A, A, A, None) == EALIGN
+    assert f(A, 1, 32, A + 4, A, A, A, None) == EALIGN
+
+
+def test_moe_argument_checks(L):
+    f = L.q4k_moe_gemv
+    ws = q4k.q4k_moe_workspace_bytes(16, 8, 64)
+    assert ws > 0
+    assert q4k.q4k_moe_workspace_bytes(1, 9, 8) == 0
+    assert q4k.q4k_moe_workspace_bytes(0, 1, 8) == 0
+    stride = 1024 * 8 * 144
+
+    def call(**kw):
+        a = dict(w=A, E=64, stride=stride, N=1024, K=2048, ids=A, rw=A, T=16, topk=8,
+                 codes=A, scales=A, sums=A, aps=0, y=A, ws=A, wsb=ws)
+        a.update(kw)
+        return f(a["w"], a["E"], a["stride"], a["N"], a["K"], a["ids"], a["rw"], a["T"],
+                 a["topk"], a["codes"], a["scales"], a["sums"], a["aps"], a["y"], a["ws"],
+                 a["wsb"], None)
+    assert call(ids=None) == EINVAL
+    assert call(aps=2) == EINVAL
+    assert call(topk=65) == ESHAPE
+    assert call(topk=0) == ESHAPE
+    assert call(T=0) == ESHAPE
+    assert call(stride=stride - 16) == ESHAPE
+    assert call(stride=stride + 8) == ESHAPE
+    assert call(K=2000) == ESHAPE
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=ws - 1) == EWORKSPACE
+    assert call(ws=A + 16) == EALIGN
+    assert call(w=A + 4) == EALIGN

@@ -1,0 +1,191 @@
+"""GPU parity of q4k_quantize_act and q4k_gemv against the CPU oracle.
+
+Q8 codes, scales and sums must be bit-exact; GEMV outputs must be within
+|gpu - oracle| <= max(2e-3 |oracle|, 1e-4) elementwise, and exactly equal in the
+integer-exposing cases where the sub-block dots pass unrounded to the output.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import q4k_inputs as qi
+from _helpers import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    import torch
+    assert torch.cuda.is_available()
+    import gemm_q4_super_amd as m
+    m.lib()
+    return m
+
+
+def _gpu_quant(q4k, x, gate=None):
+    import torch
+    c, s, su = q4k.q4k_quantize_act(to_dev(x), None if gate is None else to_dev(gate))
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), s.cpu().numpy(), su.cpu().numpy()
+
+
+def _gemv(q4k, w, N, K, x, oracle_lib, rows=None, use_gemm=False):
+    import torch
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    fn = q4k.q4k_gemm if use_gemm else q4k.q4k_gemv
+    y = fn(to_dev(w), N, K, to_dev(codes), to_dev(scales), to_dev(sums))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows)
+    if rows is not None:
+        y = y[:, rows]
+    return y, ref
+
+
+# -------------------------------------------------------------- quantizer ----
+
+@pytest.mark.parametrize("M,K,scale", [(1, 1024, 1.0), (3, 2560, 1.0), (512, 4096, 1.0),
+                                       (7, 9728, 1e-3), (2, 32, 300.0), (5, 96, 1.0)])
+def test_quantize_bit_exact(q4k, oracle_lib, M, K, scale):
+    x = qi.make_act(M, K, 77 + M) * np.float32(scale)
+    x[0, :32] = 0.0                    # an all-zero block
+    if K >= 96:
+        x[-1, 64:96] = np.float32(-2.5)  # all-equal block: codes -127
+    c, s, su = _gpu_quant(q4k, x)
+    rc, rs, rsu = oracle_lib.quantize_act(x)
+    assert (c == rc).all() and (su == rsu).all()
+    assert (s.view(np.uint32) == rs.view(np.uint32)).all()
+
+
+def test_quantize_golden_ties(q4k):
+    cases = json.load(open(os.path.join(GOLDEN, "q8_ties.json")))["cases"]
+    x = np.array([c["x"] for c in cases], np.float32)
+    c, s, su = _gpu_quant(q4k, x)
+    for i, case in enumerate(cases):
+        assert c[i].tolist() == case["codes"]
+        assert float(s[i, 0]) == case["scale"] and int(su[i, 0]) == case["sum"]
+
+
+def test_quantize_near_rounding_boundaries(q4k, oracle_lib):
+    """Quotients placed within a few ulps of k+1/2 decide codes by the last bit
+    of the IEEE division; GPU and oracle must agree on every one."""
+    rng = np.random.default_rng(5)
+    rows = []
+    for _ in range(256):
+        amax = np.float32(rng.uniform(0.5, 8.0))
+        s = amax / np.float32(127)
+        blk = np.zeros(32, np.float32)
+        blk[0] = amax
+        for i in range(1, 32):
+            k = int(rng.integers(0, 126))
+            x0 = np.float32((k + 0.5) * float(s))
+            blk[i] = np.float32(x0 + int(rng.integers(-3, 4)) * np.spacing(x0)) * rng.choice([-1, 1])
+        rows.append(blk)
+    x = np.stack(rows).reshape(8, -1)
+    c, sc, su = _gpu_quant(q4k, x)
+    rc, rs, rsu = oracle_lib.quantize_act(x)
+    assert (c == rc).all() and (su == rsu).all() and (sc == rs).all()
+
+
+def test_quantize_swiglu_bit_exact(q4k, oracle_lib):
+    M, K = 16, 1024
+    g = qi.make_act(M, K, 5) * np.float32(4.0)
+    u = qi.make_act(M, K, 6) * np.float32(4.0)
+    c, s, su = _gpu_quant(q4k, u, gate=g)
+    rc, rs, rsu = oracle_lib.quantize_act(oracle_lib.swiglu(g, u))
+    # h is evaluated in fp64 and rounded once on both sides; the two exp()
+    # implementations may differ by an ulp of fp64, which flips the fp32 h (and
+    # possibly a code) with probability ~1e-9 per element.
+    assert (c == rc).all() and (su == rsu).all() and (s == rs).all()
+
+
+# ------------------------------------------------------------------- GEMV ----
+
+def test_gemv_single_1024(q4k, oracle_lib):
+    """1024 x 1024 Q4_K weight (4 super-blocks per row), batch 1, all outputs."""
+    w, _ = qi.make_q4k(1024, 1024, qi.weight_seed(0, 0, 0))
+    x = qi.make_act(1, 1024, qi.act_seed(0))
+    y, ref = _gemv(q4k, w, 1024, 1024, x, oracle_lib)
+    assert_close(y, ref, "gemv 1024x1024")
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (9, 768), (33, 2560), (100, 4096),
+                                 (257, 9728), (1000, 1280), (4097, 2560), (63, 6144)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+def test_gemv_shapes_and_tails(q4k, oracle_lib, N, K, M):
+    w, _ = qi.make_q4k(N, K, 1000 + N + K)
+    x = qi.make_act(M, K, 2000 + N + M)
+    rows = None if N <= 300 else np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 60)])
+    y, ref = _gemv(q4k, w, N, K, x, oracle_lib, rows=rows)
+    assert_close(y, ref, "gemv N=%d K=%d M=%d" % (N, K, M))
+
+
+def test_gemv_integer_exposing_bit_exact(q4k, oracle_lib):
+    """d=1, dmin=0, one-hot sub-block scale, integer activations with a +-127 in
+    every block: each output is an exact integer sub-block dot (< 2^24)."""
+    rng = np.random.default_rng(9)
+    N, K, M = 64, 256, 4
+    for j0 in range(8):
+        f = qi.draw_q4k_fields(N, K, 300 + j0)
+        f.d[:] = np.float16(1.0); f.dmin[:] = np.float16(0.0)
+        f.sc[:] = 0; f.sc[:, :, j0] = 1
+        w = qi.pack_q4k(f)
+        x = rng.integers(-126, 127, size=(M, K)).astype(np.float32)
+        x.reshape(M, 8, 32)[:, :, 0] = rng.choice([-127.0, 127.0], size=(M, 8))
+        y, ref = _gemv(q4k, w, N, K, x, oracle_lib)
+        D = oracle_lib.subblock_dots(w, N, K, oracle_lib.quantize_act(x)[0])
+        assert (y == D[:, :, j0]).all()
+        assert (y == ref).all()
+        # mins only: y = -S_j0
+        f.q[:] = 0; f.sc[:] = 0; f.dmin[:] = np.float16(1.0); f.mn[:] = 0; f.mn[:, :, j0] = 1
+        y, ref = _gemv(q4k, qi.pack_q4k(f), N, K, x, oracle_lib)
+        assert (y == ref).all()
+
+
+def test_gemv_all_ones_closed_form(q4k, oracle_lib):
+    N, K = 512, 2560
+    w, f = qi.make_q4k(N, K, 17)
+    x = np.ones((1, K), np.float32)
+    y, ref = _gemv(q4k, w, N, K, x, oracle_lib)
+    jj = np.arange(256) // 32
+    wf = (f.d.astype(np.float64)[:, :, None] * f.sc[:, :, jj] * f.q
+          - f.dmin.astype(np.float64)[:, :, None] * f.mn[:, :, jj]).reshape(N, K)
+    closed = 127.0 * float(np.float32(1) / np.float32(127)) * wf.sum(axis=1)
+    assert_close(y[0], closed, "all-ones")
+    assert_close(y, ref, "all-ones vs oracle")
+
+
+def test_gemv_zero_scales_exact_zero(q4k, oracle_lib):
+    f = qi.draw_q4k_fields(40, 512, 8)
+    f.d[:] = 0; f.dmin[:] = 0
+    y, _ = _gemv(q4k, qi.pack_q4k(f), 40, 512, qi.make_act(3, 512, 1), oracle_lib)
+    assert (y == 0).all()
+
+
+def test_gemv_power_of_two_scaling_bit_identical(q4k, oracle_lib):
+    N, K = 300, 2560
+    w, f = qi.make_q4k(N, K, 12)
+    x = qi.make_act(2, K, 13)
+    y, _ = _gemv(q4k, w, N, K, x, oracle_lib)
+    f.d = (f.d * np.float16(4)).astype(np.float16)
+    f.dmin = (f.dmin * np.float16(4)).astype(np.float16)
+    y4, _ = _gemv(q4k, qi.pack_q4k(f), N, K, x, oracle_lib)
+    assert (y4 == 4 * y).all()
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_gemv_qwen3_4b_shapes_sampled(q4k, oracle_lib, proj):
+    """Full-size decode projections; 64 random rows plus the first and last
+    checked against the oracle (M = 1 and M = 8)."""
+    name, K, N = qi.QWEN3_4B_LAYER[proj]
+    w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, 0, proj))
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(proj).integers(0, N, 64)])
+    for M in (1, 8):
+        x = qi.make_act(M, K, qi.act_seed(proj * 10 + M))
+        y, ref = _gemv(q4k, w, N, K, x, oracle_lib, rows=rows)
+        assert_close(y, ref, "gemv %s M=%d" % (name, M))
