@@ -1,0 +1,262 @@
+"""Benchmark: Q4_K decode GEMV sweep over 36 Qwen3-4B-shaped layers on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+A step is one batch-1 decode token: for each of 36 layers and each projection
+q, k, v, o, gate, up, down (distinct seeded Q4_K matrices, 2.04 GB in total, so
+nothing stays in the 256 MB last-level cache) the activation of that call (a
+fresh N(0,1) fp32 row) is quantized to Q8 (q4k_quantize_act) and the GEMV runs
+(q4k_gemv): 252 quantizations and 252 GEMVs.  All inputs are resident in HBM
+before timing.  Each step is replayed from HIP graphs (the host cost of 504
+small launches would otherwise be measured instead of the GPU).
+
+Within a step the 252 quantizations run first and the 252 GEMVs after them,
+each GEMV on its own call's activation (the same work as interleaving them).
+One pair of HIP events on the launch stream brackets the GEMV block of every
+timed step; that gives the mean GEMV launch duration for the roofline (an event
+pair around each kernel would add a marker dispatch of several microseconds).
+
+Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
+the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
+8 TB/s), and the CPU oracle timed on a bounded sample of the same sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LAYERS = 36
+METRIC = "Q4_K decode GEMV GB/s (% HBM peak); prefill Q4_K×Q8 GEMM TOPS (% MFMA)"
+
+
+def gemv_bytes(N, K, M=1):
+    """Algorithmic bytes of one GEMV: Q4_K weights once, the Q8 activation
+    (codes + fp32 scale + int32 sum per 32 values), the fp32 output."""
+    return N * K // 256 * 144 + M * K + M * (K // 32) * 8 + 4 * M * N
+
+
+def quant_bytes(K, M=1):
+    """fp32 input read, Q8 codes + scales + sums written."""
+    return 4 * M * K + M * K + M * (K // 32) * 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Decode:
+    """Inputs and graphs of the 36-layer decode sweep."""
+
+    def __init__(self, torch, q4k, qi):
+        self.torch, self.q4k, self.qi = torch, q4k, qi
+        self.L = q4k.lib()
+        dev = torch.device("cuda:0")
+        self.shapes = qi.QWEN3_4B_LAYER
+        self.weights, self.acts, self.host_w = [], [], {}
+        call = 0
+        for layer in range(LAYERS):
+            for p, (name, K, N) in enumerate(self.shapes):
+                w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, layer, p))
+                if layer == 0:
+                    self.host_w[p] = w
+                self.weights.append((torch.from_numpy(w).to(dev), N, K))
+                self.acts.append(torch.from_numpy(qi.make_act(1, K, qi.act_seed(call))).to(dev))
+                call += 1
+        self.qbufs = [(torch.empty((1, K), dtype=torch.int8, device=dev),
+                       torch.empty((1, K // 32), dtype=torch.float32, device=dev),
+                       torch.empty((1, K // 32), dtype=torch.int32, device=dev))
+                      for (_, N, K) in self.weights]
+        self.ys = {N: torch.empty((1, N), dtype=torch.float32, device=dev)
+                   for _, _, N in self.shapes}
+        self.n_gemv = len(self.weights)
+        self.bytes_gemv = sum(gemv_bytes(N, K) for _, N, K in self.weights)
+        self.bytes_quant = sum(quant_bytes(K) for _, N, K in self.weights)
+        torch.cuda.synchronize()
+
+    def quantize(self, i, s):
+        _, N, K = self.weights[i]
+        c, sc, su = self.qbufs[i]
+        if self.L.q4k_quantize_act(self.acts[i].data_ptr(), 1, K, None, c.data_ptr(),
+                                   sc.data_ptr(), su.data_ptr(), s):
+            raise RuntimeError("q4k_quantize_act launch failed")
+
+    def gemv(self, i, s):
+        wt, N, K = self.weights[i]
+        c, sc, su = self.qbufs[i]
+        if self.L.q4k_gemv(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(),
+                           1, self.ys[N].data_ptr(), s):
+            raise RuntimeError("q4k_gemv launch failed")
+
+    def graph(self, fn, indices, stream):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            s = torch.cuda.current_stream().cuda_stream
+            for i in indices:
+                fn(i, s)
+        return g
+
+    def parity(self, oracle):
+        """Quantize + GEMV of layer 0's seven projections; codes bit-exact and
+        34 sampled outputs per projection within tolerance."""
+        torch, q4k = self.torch, self.q4k
+        max_rel, checked = 0.0, 0
+        for p, (name, K, N) in enumerate(self.shapes):
+            wt = self.weights[p][0]
+            c, sc, su = q4k.q4k_quantize_act(self.acts[p])
+            y = q4k.q4k_gemv(wt, N, K, c, sc, su)
+            torch.cuda.synchronize()
+            rc, rs, _ = oracle.quantize_act(self.acts[p].cpu().numpy())
+            if not (c.cpu().numpy() == rc).all():
+                raise SystemExit("parity: Q8 codes differ from the oracle for %s" % name)
+            rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 32)])
+            ref = oracle.matvec(self.host_w[p], N, K, rc, rs, rows=rows)[0]
+            got = y.cpu().numpy()[0, rows].astype(np.float64)
+            err = np.abs(got - ref)
+            if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+                raise SystemExit("parity: GEMV %s outside tolerance" % name)
+            max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
+            checked += rows.size
+        return {"rows_checked": checked, "max_rel_err": max_rel}
+
+
+def cpu_baseline(qi, oracle, shapes, seconds):
+    """The oracle (single thread) over layers of the same sweep until `seconds`
+    of CPU time have been spent or all 36 layers are done."""
+    t_cpu, done_bytes, layers_done = 0.0, 0, 0
+    for layer in range(LAYERS):
+        for p, (name, K, N) in enumerate(shapes):
+            w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, layer, p))
+            x = qi.make_act(1, K, qi.act_seed(layer * len(shapes) + p))
+            ta = time.perf_counter()
+            rc, rs, _ = oracle.quantize_act(x)
+            oracle.matvec(w, N, K, rc, rs)
+            t_cpu += time.perf_counter() - ta
+            done_bytes += gemv_bytes(N, K) + quant_bytes(K)
+        layers_done += 1
+        if t_cpu >= seconds:
+            break
+    return {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "layers 0..%d of the 36-layer decode sweep (%d quantize+GEMV calls, "
+                      "%.2f GB), single thread, %.1f s" % (layers_done - 1,
+                                                          layers_done * len(shapes),
+                                                          done_bytes / 1e9, t_cpu)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no collectives or sharding); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_q4_super_amd as q4k
+    import oracle
+    import q4k_inputs as qi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    oracle.build(force=False)
+    dec = Decode(torch, q4k, qi)
+    parity = dec.parity(oracle)
+
+    steps, warmup = args.steps, args.warmup
+    cap = torch.cuda.Stream()
+    idx = range(dec.n_gemv)
+    g_quant = dec.graph(dec.quantize, idx, cap)
+    g_gemv = dec.graph(dec.gemv, idx, cap)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g_quant.replay()
+        g_gemv.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    # ------------------------------------------------------------ timed
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        g_quant.replay()
+        ev[k][0].record()
+        g_gemv.replay()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # ------------------------------------------------------------------
+
+    block_s = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    mean_gemv_s = float(block_s.mean()) / dec.n_gemv
+
+    # Per-projection breakdown, outside the timed region: a graph of the 36
+    # GEMVs of one projection, replayed 5 times between two events.
+    per_shape = {}
+    for p, (name, K, N) in enumerate(dec.shapes):
+        g = dec.graph(dec.gemv, range(p, dec.n_gemv, len(dec.shapes)), cap)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        d = a.elapsed_time(b) * 1e-3 / (5 * LAYERS)
+        per_shape[name] = {"N": N, "K": K, "us": round(d * 1e6, 3),
+                           "GBps": round(gemv_bytes(N, K) / d / 1e9, 1)}
+
+    value = (dec.bytes_gemv + dec.bytes_quant) * steps / elapsed / 1e9
+    achieved = dec.bytes_gemv / dec.n_gemv / mean_gemv_s / 1e9
+    cpu = None if args.no_cpu else cpu_baseline(qi, oracle, dec.shapes, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4k x q8 (int8 dot4, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV sweep, batch 1: 36 Qwen3-4B-shaped layers x "
+                               "(q 2560->4096, k 2560->1024, v 2560->1024, o 4096->2560, "
+                               "gate 2560->9728, up 2560->9728, down 9728->2560), 2.04 GB of "
+                               "Q4_K weights, Q8 quantization of a fresh N(0,1) row per call",
+                   "layers": LAYERS, "batch": 1,
+                   "tok_per_s": round(steps / elapsed, 1),
+                   "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "mean_launch_us": round(mean_gemv_s * 1e6, 3),
+                     "bytes_per_launch": round(dec.bytes_gemv / dec.n_gemv),
+                     "timing": "HIP events on the launch stream around the 252 back-to-back "
+                               "GEMV dispatches of each timed step (dispatch gaps included)",
+                     "per_shape": per_shape},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,10 @@ def lib():
     """The loaded library (raises if libq4k.so has not been built)."""
     global _lib
     if _lib is None:
+        try:
+            import torch  # noqa: F401  -- load torch's HIP runtime first (same soname)
+        except ImportError:
+            pass
         if not os.path.exists(lib_path):
             raise RuntimeError("libq4k.so not built: run `python -m gemm_q4_super_amd.build` "
                                "(or __graft_entry__.build())")
