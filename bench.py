@@ -34,7 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix peak
 LAYERS = 36
+PREFILL_M = 512
 METRIC = "Q4_K decode GEMV GB/s (% HBM peak); prefill Q4_K×Q8 GEMM TOPS (% MFMA)"
 
 
@@ -56,6 +58,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the secondary prefill-GEMM measurement")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     return ap.parse_args()
 
 
@@ -133,6 +138,121 @@ class Decode:
             max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
             checked += rows.size
         return {"rows_checked": checked, "max_rel_err": max_rel}
+
+
+class Prefill:
+    """Inputs of the prefill GEMM workload: M = 512 prompt tokens through the
+    same seven projection shapes over 36 layers (distinct seeded weights)."""
+
+    def __init__(self, torch, q4k, qi):
+        self.torch, self.q4k = torch, q4k
+        self.L = q4k.lib()
+        dev = torch.device("cuda:0")
+        self.shapes = qi.QWEN3_4B_LAYER
+        self.weights, self.acts, self.host_w = [], [], {}
+        M = PREFILL_M
+        for layer in range(LAYERS):
+            for p, (name, K, N) in enumerate(self.shapes):
+                w = qi.make_q4k_bytes(N, K, qi.weight_seed(2, layer, p))
+                if layer == 0:
+                    self.host_w[p] = w
+                self.weights.append((torch.from_numpy(w).to(dev), N, K))
+        # one N(0,1) 512 x K fp32 activation per projection shape, quantized
+        # again by every call (the data does not change the work)
+        self.act_of = {}
+        for p, (name, K, N) in enumerate(self.shapes):
+            self.act_of[p] = torch.from_numpy(qi.make_act(M, K, qi.act_seed(20000 + p))).to(dev)
+        self.qbufs = {p: (torch.empty((M, K), dtype=torch.int8, device=dev),
+                          torch.empty((M, K // 32), dtype=torch.float32, device=dev),
+                          torch.empty((M, K // 32), dtype=torch.int32, device=dev))
+                      for p, (_, K, N) in enumerate(self.shapes)}
+        self.ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
+                   for _, _, N in self.shapes}
+        self.n = len(self.weights)
+        self.ops = sum(2 * M * N * K for _, N, K in self.weights)
+        torch.cuda.synchronize()
+
+    def quantize(self, i, s):
+        p = i % len(self.shapes)
+        _, N, K = self.weights[i]
+        c, sc, su = self.qbufs[p]
+        if self.L.q4k_quantize_act(self.act_of[p].data_ptr(), PREFILL_M, K, None, c.data_ptr(),
+                                   sc.data_ptr(), su.data_ptr(), s):
+            raise RuntimeError("q4k_quantize_act launch failed")
+
+    def gemm(self, i, s):
+        p = i % len(self.shapes)
+        wt, N, K = self.weights[i]
+        c, sc, su = self.qbufs[p]
+        if self.L.q4k_gemm(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(),
+                           PREFILL_M, self.ys[N].data_ptr(), s):
+            raise RuntimeError("q4k_gemm launch failed")
+
+    def parity(self, oracle):
+        torch, q4k = self.torch, self.q4k
+        max_rel, checked = 0.0, 0
+        for p, (name, K, N) in enumerate(self.shapes):
+            wt = self.weights[p][0]
+            c, sc, su = q4k.q4k_quantize_act(self.act_of[p])
+            y = q4k.q4k_gemm(wt, N, K, c, sc, su)
+            torch.cuda.synchronize()
+            rc, rs, _ = oracle.quantize_act(self.act_of[p].cpu().numpy())
+            rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 6)])
+            ref = oracle.matvec(self.host_w[p], N, K, rc, rs, rows=rows)
+            got = y.cpu().numpy()[:, rows].astype(np.float64)
+            err = np.abs(got - ref)
+            if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+                raise SystemExit("parity: GEMM %s outside tolerance" % name)
+            max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
+            checked += ref.size
+        return {"outputs_checked": checked, "max_rel_err": max_rel}
+
+
+def measure_prefill(torch, q4k, qi, oracle, steps):
+    pre = Prefill(torch, q4k, qi)
+    parity = pre.parity(oracle)
+    cap = torch.cuda.Stream()
+    g_q = Decode.graph(pre, pre.quantize, range(pre.n), cap)
+    g_g = Decode.graph(pre, pre.gemm, range(pre.n), cap)
+    g_q.replay(); g_g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        g_q.replay()
+        ev[k][0].record()
+        g_g.replay()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    per_shape = {}
+    for p, (name, K, N) in enumerate(pre.shapes):
+        g = Decode.graph(pre, pre.gemm, range(p, pre.n, len(pre.shapes)), cap)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        d = a.elapsed_time(b) * 1e-3 / LAYERS
+        per_shape[name] = {"N": N, "K": K, "us": round(d * 1e6, 2),
+                           "TOPS": round(2 * PREFILL_M * N * K / d / 1e12, 1)}
+    tops = pre.ops / gemm_s / 1e12
+    out = {"workload": "prefill GEMM, M=512 tokens x the seven Qwen3-4B projection shapes x "
+                       "36 layers (3.72 T int ops per step)",
+           "steps": steps, "ms_per_step": round(elapsed / steps * 1e3, 3),
+           "tok_per_s": round(PREFILL_M * steps / elapsed, 0),
+           "gemm_ms_per_step": round(gemm_s * 1e3, 3),
+           "roofline": {"bound": "mfma", "kernel": "q4k gemm_i8_kernel",
+                        "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                        "frac": round(tops / INT8_PEAK_TOPS, 4),
+                        "mean_launch_us": round(gemm_s / pre.n * 1e6, 2)},
+           "per_shape": per_shape, "parity": parity}
+    del pre
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(qi, oracle, shapes, seconds):
@@ -221,8 +341,13 @@ def main():
                            "GBps": round(gemv_bytes(N, K) / d / 1e9, 1)}
 
     value = (dec.bytes_gemv + dec.bytes_quant) * steps / elapsed / 1e9
-    achieved = dec.bytes_gemv / dec.n_gemv / mean_gemv_s / 1e9
-    cpu = None if args.no_cpu else cpu_baseline(qi, oracle, dec.shapes, args.cpu_seconds)
+    bytes_per_launch = dec.bytes_gemv / dec.n_gemv
+    achieved = bytes_per_launch / mean_gemv_s / 1e9
+    del g_quant, g_gemv, dec
+    torch.cuda.empty_cache()
+    prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
+                                                           args.prefill_steps)
+    cpu = None if args.no_cpu else cpu_baseline(qi, oracle, qi.QWEN3_4B_LAYER, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -248,12 +373,13 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "mean_launch_us": round(mean_gemv_s * 1e6, 3),
-                     "bytes_per_launch": round(dec.bytes_gemv / dec.n_gemv),
+                     "bytes_per_launch": round(bytes_per_launch),
                      "timing": "HIP events on the launch stream around the 252 back-to-back "
                                "GEMV dispatches of each timed step (dispatch gaps included)",
                      "per_shape": per_shape},
         "cpu_baseline": cpu,
         "parity": parity,
+        "prefill_gemm": prefill,
     }
     print(json.dumps(out))
 

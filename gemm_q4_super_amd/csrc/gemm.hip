@@ -2,20 +2,32 @@
 //
 // Prefill is compute-bound ("genie-ai-runtime ...", section 3: batched
 // layer-major prefill, Path E tensor-core kernel), so the sub-block integer dot
-// products run on the matrix cores:
+// products run on the matrix cores.  With x^ = a*c (Q8) and
+// w = d*sc[j]*q - dmin*mn[j] (Q4_K), one output is
 //
-//  * Workgroup tile BM x BN = 64 x 64 outputs, 4 waves of 32 x 32.
-//  * Per super-block (256 of K): the 64 weight rows are read once (144 B each)
-//    and nibble-expanded into LDS as int8 quants (q in 0..15), with the fp32
-//    factors d*sc[j] and dmin*mn[j] of every row and sub-block; the activation
-//    scales a[m][j] and a[m][j]*S[m][j] of the 64 activation rows are staged
-//    beside them.
-//  * Per 32-element sub-block j: one v_mfma_i32_32x32x32_i8 per wave gives the
-//    exact int32 dots D[m][n] = sum q*c of its 32 x 32 tile; the fp32 epilogue
-//    adds a[m][j]*(d*sc[j])*D - (a*S)[m][j]*(dmin*mn[j]).
+//   y[m][n] = sum_{b,j} a[m,b,j] * (d*sc)[n,b,j] * D[m,n,b,j]
+//           - sum_{b,j} (a*S)[m,b,j] * (dmin*mn)[n,b,j]
 //
-// The weight quants and activation codes are exact small integers, so D is
-// bit-exact; the fp32 epilogue differs from the plain sum only in rounding.
+// with D = sum_{i<32} q*c the exact integer dot of one 32-element sub-block and
+// S the activation block's code sum.
+//
+//  * D: one v_mfma_i32_32x32x32_i8 per sub-block and 32 x 32 tile: activation
+//    codes (A operand, rows m) against nibble-expanded int8 quants (B operand,
+//    columns n), both read from LDS.  Bit-exact.
+//  * First sum: fp32 epilogue per sub-block, acc += float(D) * (a * d*sc).
+//    Activation and weight scales both change every 32 elements of K, so this
+//    costs three VALU operations per output and sub-block: the binding unit.
+//  * Second sum (the min term): a contraction over K/32 of fp32 factors, on the
+//    bf16 matrix cores with each factor split into two bf16 parts (16
+//    significant bits), accumulated over all of K and subtracted at the end.
+//  * Workgroup tile BM x BN (one wave per 32 x 32 sub-tile), chosen per shape
+//    so that the launch has enough workgroups for 256 CUs.  LDS is
+//    double-buffered: the global loads of super-block b+1 are in flight while
+//    b is computed, then expanded into the other buffer; one barrier per
+//    super-block.
+//  * Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs,
+//    so all M tiles of one weight column-block are placed on one XCD and run
+//    together, sharing that XCD's L2 for the weight rows.
 #include "q4k_internal.h"
 
 namespace q4k {
@@ -25,9 +37,21 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 64, BN = 64;
-constexpr int BQ_STRIDE = 256 + 16;   // padded LDS row (bank-conflict-free 16-B reads)
+constexpr int ROW = 256 + 16;         // padded LDS row of 256 int8 (conflict-free 16-B reads)
+constexpr int NXCD = 8;
+
+template <int BM, int BN>
+struct __attribute__((aligned(16))) Buf {
+    int8_t xq[BM][ROW];               // activation codes
+    int8_t wq[BN][ROW];               // weight quants 0..15
+    float as[8][BM];                  // activation scale a[m][j]
+    float ws[8][BN];                  // d * sc[j]
+    unsigned short ph[2][BM][8];      // a*S split hi / lo (bf16 bits)
+    unsigned short qh[2][BN][8];      // dmin*mn split hi / lo (bf16 bits)
+};
 
 __device__ __forceinline__ float half_lo(unsigned v) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFF));
@@ -35,144 +59,232 @@ __device__ __forceinline__ float half_lo(unsigned v) {
 __device__ __forceinline__ float half_hi(unsigned v) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
 }
+// Split fp32 into two bf16 parts by truncation (hi + lo keeps 16 significant bits).
+__device__ __forceinline__ void split_bf16(float v, unsigned short &hi, unsigned short &lo) {
+    const unsigned b = __float_as_uint(v);
+    hi = (unsigned short)(b >> 16);
+    lo = (unsigned short)(__float_as_uint(v - __uint_as_float(b & 0xFFFF0000u)) >> 16);
+}
 
-__global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t *__restrict__ w, int N,
-                                                      int nsb,
-                                                      const int8_t *__restrict__ codes,
-                                                      const float *__restrict__ scales,
-                                                      const int32_t *__restrict__ sums, int M,
-                                                      float *__restrict__ y) {
-    __shared__ __attribute__((aligned(16))) int8_t Bq[BN][BQ_STRIDE];
-    __shared__ float Ws[BN][8];      // d * sc[j]
-    __shared__ float Wm[BN][8];      // dmin * mn[j]
-    __shared__ __attribute__((aligned(16))) float As[8][BM];   // a[m][j]
-    __shared__ __attribute__((aligned(16))) float Ap[8][BM];   // a[m][j] * S[m][j]
+template <int BM, int BN>
+struct Cfg {
+    static constexpr int WAVES = (BM / 32) * (BN / 32);
+    static constexpr int T = 64 * WAVES;
+    static constexpr int WCH = 8 * BN;            // 16-B quant chunks of weights per super-block
+    static constexpr int XCH = 16 * BM;           // 16-B chunks of activation codes
+    static constexpr int SE = 8 * BM;             // activation scale entries
+    static constexpr int NW = (WCH + T - 1) / T;
+    static constexpr int NX = (XCH + T - 1) / T;
+    static constexpr int NS = (SE + T - 1) / T;
+};
+
+template <int BM, int BN>
+struct Regs {
+    u32x4 hd;                         // header of weight row tid (tid < BN)
+    u32x4 wc[Cfg<BM, BN>::NW];
+    i32x4 xc[Cfg<BM, BN>::NX];
+    float a[Cfg<BM, BN>::NS];
+    int s[Cfg<BM, BN>::NS];
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__((64 * (BM / 32) * (BN / 32))) void gemm_i8_kernel(
+    const uint8_t *__restrict__ w, int N, int nsb, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const int32_t *__restrict__ sums, int M,
+    float *__restrict__ y) {
+    using C = Cfg<BM, BN>;
+    __shared__ Buf<BM, BN> buf[2];
+
+    // XCD-aware tile of this workgroup.
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int xcd = blockIdx.x % NXCD, pos = blockIdx.x / NXCD;
+    const int nt = (pos / tiles_m) * NXCD + xcd, mt = pos % tiles_m;
+    if (nt >= tiles_n) return;   // the whole workgroup exits together, before any barrier
+    const int m0 = mt * BM, n0 = nt * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+    constexpr int WN = BN / 32;
+    const int wm = wave / WN, wn = wave % WN;
     const int K = nsb * 256, nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
-
-    // staging roles
-    const int sr = tid >> 2, sq = tid & 3;        // weight row, chunk pair
-    const int an = n0 + sr;                       // weight row index
-    // MFMA operand roles
     const int lr = lane & 31, lh = lane >> 5;
-    const int am = m0 + wm * 32 + lr;             // activation row of the A operand
+
+    auto load = [&](int b, Regs<BM, BN> &r) {
+        r.hd = (u32x4){0u, 0u, 0u, 0u};
+        if (tid < BN && n0 + tid < N)
+            r.hd = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                w + (int64_t)(n0 + tid) * row_bytes + (int64_t)b * 144));
+#pragma unroll
+        for (int i = 0; i < C::NW; ++i) {
+            const int e = tid + i * C::T;
+            r.wc[i] = (u32x4){0u, 0u, 0u, 0u};
+            const int row = e >> 3, ch = e & 7;
+            if (e < C::WCH && n0 + row < N)
+                r.wc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    w + (int64_t)(n0 + row) * row_bytes + (int64_t)b * 144 + 16 + 16 * ch));
+        }
+#pragma unroll
+        for (int i = 0; i < C::NX; ++i) {
+            const int e = tid + i * C::T;
+            r.xc[i] = (i32x4){0, 0, 0, 0};
+            const int row = e >> 4, ch = e & 15;
+            if (e < C::XCH && m0 + row < M)
+                r.xc[i] = *reinterpret_cast<const i32x4 *>(codes + (int64_t)(m0 + row) * K +
+                                                           256 * b + 16 * ch);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) {
+            const int e = tid + i * C::T;
+            r.a[i] = 0.0f;
+            r.s[i] = 0;
+            const int row = e >> 3, j = e & 7;
+            if (e < C::SE && m0 + row < M) {
+                const int64_t o = (int64_t)(m0 + row) * nblk + 8 * b + j;
+                r.a[i] = scales[o];
+                r.s[i] = sums[o];
+            }
+        }
+    };
+    auto store = [&](const Regs<BM, BN> &r, Buf<BM, BN> &B) {
+        if (tid < BN) {
+            // header of weight row tid: fp16 d, dmin and the 6-bit scales/mins
+            const u32x4 v = r.hd;
+            const float d = half_lo(v.x), dmin = half_hi(v.x);
+            const unsigned h1 = v.y, h2 = v.z, h3 = v.w;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                unsigned sc, mn;
+                if (j < 4) {
+                    sc = (h1 >> (8 * j)) & 63u;
+                    mn = (h2 >> (8 * j)) & 63u;
+                } else {
+                    const int s = 8 * (j - 4);
+                    sc = ((h3 >> s) & 15u) | (((h1 >> (s + 6)) & 3u) << 4);
+                    mn = ((h3 >> (s + 4)) & 15u) | (((h2 >> (s + 6)) & 3u) << 4);
+                }
+                B.ws[j][tid] = d * (float)sc;
+                unsigned short qhi, qlo;
+                split_bf16(dmin * (float)mn, qhi, qlo);
+                B.qh[0][tid][j] = qhi;
+                B.qh[1][tid][j] = qlo;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::NW; ++i) {
+            const int e = tid + i * C::T;
+            if (e >= C::WCH) continue;
+            // quant chunk c: low nibbles -> elements 64g+16h+i, high nibbles ->
+            // 64g+32+16h+i (g = c/2, h = c%2)
+            const int row = e >> 3, c = e & 7, g = c >> 1, h = c & 1;
+            const u32x4 v = r.wc[i];
+            u32x4 lo, hi;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                lo[k] = v[k] & 0x0F0F0F0Fu;
+                hi[k] = (v[k] >> 4) & 0x0F0F0F0Fu;
+            }
+            *reinterpret_cast<u32x4 *>(&B.wq[row][64 * g + 16 * h]) = lo;
+            *reinterpret_cast<u32x4 *>(&B.wq[row][64 * g + 32 + 16 * h]) = hi;
+        }
+#pragma unroll
+        for (int i = 0; i < C::NX; ++i) {
+            const int e = tid + i * C::T;
+            if (e < C::XCH)
+                *reinterpret_cast<i32x4 *>(&B.xq[e >> 4][16 * (e & 15)]) = r.xc[i];
+        }
+#pragma unroll
+        for (int i = 0; i < C::NS; ++i) {
+            const int e = tid + i * C::T;
+            if (e >= C::SE) continue;
+            const int row = e >> 3, j = e & 7;
+            B.as[j][row] = r.a[i];
+            unsigned short phi, plo;
+            split_bf16(r.a[i] * (float)r.s[i], phi, plo);
+            B.ph[0][row][j] = phi;
+            B.ph[1][row][j] = plo;
+        }
+    };
 
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-
-    for (int b = 0; b < nsb; ++b) {
-        // Global loads for this super-block.
-        u32x4 q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u}, hd = {0u, 0u, 0u, 0u};
-        if (an < N) {
-            const uint8_t *sb = w + (int64_t)an * row_bytes + (int64_t)b * 144;
-            q0 = *reinterpret_cast<const u32x4 *>(sb + 16 + 32 * sq);
-            q1 = *reinterpret_cast<const u32x4 *>(sb + 32 + 32 * sq);
-            if (sq == 0) hd = *reinterpret_cast<const u32x4 *>(sb);
-        }
-        i32x4 aop[8];
+    f32x16 mins;
 #pragma unroll
+    for (int i = 0; i < 16; ++i) mins[i] = 0.0f;
+
+    const int am = wm * 32 + lr;      // A operand row (activation) within the tile
+    const int bn = wn * 32 + lr;      // B operand column (weight row) within the tile
+
+    // One super-block of work on LDS buffer B.
+    auto compute = [&](const Buf<BM, BN> &B) {
+#pragma unroll 2
         for (int j = 0; j < 8; ++j) {
-            if (am < M)
-                aop[j] = *reinterpret_cast<const i32x4 *>(codes + (int64_t)am * K + 256 * b +
-                                                          32 * j + 16 * lh);
-            else
-                aop[j] = (i32x4){0, 0, 0, 0};
-        }
-        float sa0 = 0.0f, sp0 = 0.0f, sa1 = 0.0f, sp1 = 0.0f;
-        {
-            // 512 (m, j) activation-scale entries, two per thread.
-            const int e0 = tid, e1 = tid + 256;
-            const int m_a = e0 >> 3, j_a = e0 & 7, m_b = e1 >> 3, j_b = e1 & 7;
-            if (m0 + m_a < M) {
-                const int64_t o = (int64_t)(m0 + m_a) * nblk + 8 * b + j_a;
-                sa0 = scales[o];
-                sp0 = sa0 * (float)sums[o];
-            }
-            if (m0 + m_b < M) {
-                const int64_t o = (int64_t)(m0 + m_b) * nblk + 8 * b + j_b;
-                sa1 = scales[o];
-                sp1 = sa1 * (float)sums[o];
+            const i32x4 aop = *reinterpret_cast<const i32x4 *>(&B.xq[am][32 * j + 16 * lh]);
+            const i32x4 bop = *reinterpret_cast<const i32x4 *>(&B.wq[bn][32 * j + 16 * lh]);
+            const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                aop, bop, (i32x16){0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}, 0, 0, 0);
+            const float wsj = B.ws[j][bn];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 a4 =
+                    *reinterpret_cast<const f32x4 *>(&B.as[j][wm * 32 + 8 * rr + 4 * lh]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[4 * rr + t] = fmaf((float)D[4 * rr + t], a4[t] * wsj, acc[4 * rr + t]);
             }
         }
+        const bf16x8 pa_h = *reinterpret_cast<const bf16x8 *>(&B.ph[0][am][0]);
+        const bf16x8 pa_l = *reinterpret_cast<const bf16x8 *>(&B.ph[1][am][0]);
+        const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&B.qh[lh][bn][0]);
+        mins = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_h, qb, mins, 0, 0, 0);
+        mins = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_l, qb, mins, 0, 0, 0);
+    };
 
-        __syncthreads();   // the previous super-block's LDS reads are done
-        // Nibble-expand chunks 2*sq and 2*sq+1 of row sr into int8 quants.
-        {
-            const u32x4 qq[2] = {q0, q1};
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const int c = 2 * sq + c2, g = c >> 1, h = c & 1;
-                u32x4 lo, hi;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    lo[k] = qq[c2][k] & 0x0F0F0F0Fu;
-                    hi[k] = (qq[c2][k] >> 4) & 0x0F0F0F0Fu;
-                }
-                *reinterpret_cast<u32x4 *>(&Bq[sr][64 * g + 16 * h]) = lo;
-                *reinterpret_cast<u32x4 *>(&Bq[sr][64 * g + 32 + 16 * h]) = hi;
-            }
-            if (sq == 0) {
-                const float d = half_lo(hd.x), dmin = half_hi(hd.x);
-                const unsigned h1 = hd.y, h2 = hd.z, h3 = hd.w;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    unsigned sc, mn;
-                    if (j < 4) {
-                        sc = (h1 >> (8 * j)) & 63u;
-                        mn = (h2 >> (8 * j)) & 63u;
-                    } else {
-                        const int s = 8 * (j - 4);
-                        sc = ((h3 >> s) & 15u) | (((h1 >> (s + 6)) & 3u) << 4);
-                        mn = ((h3 >> (s + 4)) & 15u) | (((h2 >> (s + 6)) & 3u) << 4);
-                    }
-                    Ws[sr][j] = d * (float)sc;
-                    Wm[sr][j] = dmin * (float)mn;
-                }
-            }
-            As[tid & 7][tid >> 3] = sa0;
-            Ap[tid & 7][tid >> 3] = sp0;
-            As[(tid + 256) & 7][(tid + 256) >> 3] = sa1;
-            Ap[(tid + 256) & 7][(tid + 256) >> 3] = sp1;
-        }
+    // Software pipeline, prefetch distance 2: while super-block b is computed
+    // from LDS, the registers hold b+1 (loaded one iteration earlier) and the
+    // loads of b+2 are in flight into the other register set.
+    Regs<BM, BN> ra, rb;
+    load(0, ra);
+    store(ra, buf[0]);
+    if (nsb > 1) load(1, ra);
+    __syncthreads();
+    for (int b = 0; b < nsb; b += 2) {
+        // even step: compute b from buf[0]; ra holds b+1
+        if (b + 2 < nsb) load(b + 2, rb);
+        compute(buf[0]);
+        if (b + 1 < nsb) store(ra, buf[1]);
         __syncthreads();
-
-        const int bn = wn * 32 + lr;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const i32x4 bop = *reinterpret_cast<const i32x4 *>(&Bq[bn][32 * j + 16 * lh]);
-            const i32x16 zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-            const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[j], bop, zero, 0, 0, 0);
-            const float ws = Ws[bn][j], wmn = Wm[bn][j];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int mb = wm * 32 + 8 * r + 4 * lh;
-                const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&As[j][mb]);
-                const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&Ap[j][mb]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int i = 4 * r + t;
-                    acc[i] = fmaf((float)D[i], a4[t] * ws, acc[i]);
-                    acc[i] = fmaf(-p4[t], wmn, acc[i]);
-                }
-            }
-        }
+        if (b + 1 >= nsb) break;
+        // odd step: compute b+1 from buf[1]; rb holds b+2
+        if (b + 3 < nsb) load(b + 3, ra);
+        compute(buf[1]);
+        if (b + 2 < nsb) store(rb, buf[0]);
+        __syncthreads();
     }
 
-    const int n = n0 + wn * 32 + lr;
+    const int n = n0 + bn;
     if (n < N) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = m0 + wm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if (m < M) y[(int64_t)m * N + n] = acc[i];
+            if (m < M) y[(int64_t)m * N + n] = acc[i] - mins[i];
         }
     }
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
+                       const float *scales, const int32_t *sums, int64_t M, float *y,
+                       hipStream_t stream) {
+    const int64_t tiles_m = (M + BM - 1) / BM;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t groups = (tiles_n + NXCD - 1) / NXCD;
+    const int64_t grid = groups * NXCD * tiles_m;
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN>), dim3((unsigned)grid), dim3(Cfg<BM, BN>::T), 0,
+                       stream, w, (int)N, nsb, codes, scales, sums, (int)M, y);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -181,11 +293,13 @@ hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    const int64_t tiles = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-    dim3 grid((unsigned)tiles);
-    hipLaunchKernelGGL(gemm_i8_kernel, grid, dim3(256), 0, stream, w, (int)N, nsb, codes, scales,
-                       sums, (int)M, y);
-    return hipGetLastError();
+    // Largest tile that still gives the launch at least half a workgroup per CU.
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(128, 64) >= 128)
+        return launch_tile<128, 64>(w, N, nsb, codes, scales, sums, M, y, stream);
+    if (tiles(64, 32) >= 128)
+        return launch_tile<64, 32>(w, N, nsb, codes, scales, sums, M, y, stream);
+    return launch_tile<32, 32>(w, N, nsb, codes, scales, sums, M, y, stream);
 }
 
 }  // namespace q4k
