@@ -44,7 +44,7 @@ def lib():
         L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
         L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                    ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
-        L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I]
+        L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
@@ -117,8 +117,8 @@ def q4k_gemm(w, N, K, codes, scales, sums, y=None):
     return _matrix_call(lib().q4k_gemm, "q4k_gemm", w, N, K, codes, scales, sums, y)
 
 
-def q4k_moe_workspace_bytes(T, topk, n_experts) -> int:
-    return int(lib().q4k_moe_workspace_bytes(T, topk, n_experts))
+def q4k_moe_workspace_bytes(T, topk, n_experts, N) -> int:
+    return int(lib().q4k_moe_workspace_bytes(T, topk, n_experts, N))
 
 
 def q4k_moe_gemv(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales, sums,
@@ -129,7 +129,7 @@ def q4k_moe_gemv(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales,
         _dev(t, n)
     T, topk = ids.shape
     if workspace is None:
-        nbytes = q4k_moe_workspace_bytes(T, topk, n_experts)
+        nbytes = q4k_moe_workspace_bytes(T, topk, n_experts, N)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
     if y is None:
         rows = T if route_w is not None else T * topk

@@ -21,38 +21,11 @@
 //    column is loaded once per wave and reused over the T row tiles and all 8
 //    groups.  Per-lane sums reduce over the 8 lanes by DPP, then over the W
 //    waves through LDS in a fixed order (deterministic, no atomics).
+#include "q4k_device.h"
 #include "q4k_internal.h"
 
 namespace q4k {
 namespace {
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
-}
-
-__device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-// fp16 bits -> fp32 (exact).
-__device__ __forceinline__ float half_lo(unsigned v) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v & 0xFFFF));
-}
-__device__ __forceinline__ float half_hi(unsigned v) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
-}
 
 constexpr int kMaxWaves = 16;
 
@@ -69,22 +42,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int grp = lane >> 3;     // row within a tile of 8
-    const int l = lane & 7;        // chunk index == sub-block owned after the swap
-    const int g = l >> 1, h = l & 1;
+    const LaneMap L(lane & 7);     // chunk index == sub-block owned after the swap
     const int K = nsb * 256;
     const int nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
     const int row0 = blockIdx.x * (8 * T);
-
-    // Per-lane constants of the 6-bit scale/min decode for sub-block j = l.
-    const int j = l;
-    const int sh = 8 * (j & 3);
-    const bool lo4 = j < 4;
-
-    // Codes this lane multiplies: "A" pairs with the low nibbles, "B" with the
-    // high nibbles of the lane's chunk.
-    const int offA = 64 * g + 16 * h;
-    const int offB = 64 * g + 32 + 16 * h;
 
     float acc[T][M];
 #pragma unroll
@@ -103,7 +65,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
             if (row < N) {
                 const uint8_t *sb = w + (int64_t)row * row_bytes + (int64_t)b * 144;
                 hd[t] = load_stream16(sb);
-                qw[t] = load_stream16(sb + 16 + 16 * l);
+                qw[t] = load_stream16(sb + 16 + 16 * L.l);
             } else {
                 hd[t] = (u32x4){0u, 0u, 0u, 0u};
                 qw[t] = (u32x4){0u, 0u, 0u, 0u};
@@ -116,45 +78,20 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const int8_t *cm = codes + (int64_t)m * K + 256 * b;
-            cA[m] = *reinterpret_cast<const i32x4 *>(cm + offA);
-            cB[m] = *reinterpret_cast<const i32x4 *>(cm + offB);
-            a[m] = scales[(int64_t)m * nblk + 8 * b + j];
-            s[m] = (float)sums[(int64_t)m * nblk + 8 * b + j];
+            cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
+            cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
+            a[m] = scales[(int64_t)m * nblk + 8 * b + L.l];
+            s[m] = (float)sums[(int64_t)m * nblk + 8 * b + L.l];
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const unsigned h0 = hd[t].x, h1 = hd[t].y, h2 = hd[t].z, h3 = hd[t].w;
-            const float d = half_lo(h0), dmin = half_hi(h0);
-            unsigned sc, mn;
-            if (lo4) {
-                sc = (h1 >> sh) & 63u;
-                mn = (h2 >> sh) & 63u;
-            } else {
-                sc = ((h3 >> sh) & 15u) | (((h1 >> (sh + 6)) & 3u) << 4);
-                mn = ((h3 >> (sh + 4)) & 15u) | (((h2 >> (sh + 6)) & 3u) << 4);
-            }
-            const float ds = d * (float)sc;
-            const float dm = dmin * (float)mn;
+            float ds, dm;
+            decode_scale(L, hd[t], ds, dm);
             int qlo[4], qhi[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const unsigned v = qw[t][k];
-                qlo[k] = (int)(v & 0x0F0F0F0Fu);
-                qhi[k] = (int)((v >> 4) & 0x0F0F0F0Fu);
-            }
+            unpack_nibbles(qw[t], qlo, qhi);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                int dA = 0, dB = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    dA = __builtin_amdgcn_sdot4(qlo[k], cA[m][k], dA, false);
-                    dB = __builtin_amdgcn_sdot4(qhi[k], cB[m][k], dB, false);
-                }
-                // Lane h=0 keeps sub-block 2g (its A half + partner's A half),
-                // lane h=1 keeps sub-block 2g+1 (its B half + partner's B half).
-                const int keep = h ? dB : dA;
-                const int send = h ? dA : dB;
-                const int D = keep + dpp_i<kQuadSwap1>(send);
+                const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
                 acc[t][m] = fmaf(a[m], ds * (float)D - dm * s[m], acc[t][m]);
             }
         }
@@ -165,11 +102,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float v = acc[t][m];
-            v += dpp_f<kQuadSwap1>(v);
-            v += dpp_f<kQuadSwap2>(v);
-            v += dpp_f<kRowHalfMirror>(v);
-            if (l == 0) red[wave][8 * t + grp][m] = v;
+            const float v = group8_sum(acc[t][m]);
+            if (L.l == 0) red[wave][8 * t + grp][m] = v;
         }
     __syncthreads();
     for (int i = threadIdx.x; i < 8 * T * M; i += blockDim.x) {

@@ -60,11 +60,11 @@ int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const flo
                                      sums, M, y, static_cast<hipStream_t>(stream)));
 }
 
-size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts) {
-    if (T < 1 || topk < 1 || n_experts < 1 || topk > n_experts || T * topk > 65536 ||
-        n_experts > 65536)
+size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N) {
+    if (T < 1 || topk < 1 || n_experts < 1 || topk > n_experts ||
+        T * topk > q4k::kMoeMaxPairs || n_experts > q4k::kMoeMaxExperts || N < 1 || N > kMaxDim)
         return 0;
-    return q4k::moe_workspace_bytes(T, topk, n_experts);
+    return q4k::moe_workspace_bytes(T, topk, n_experts, N);
 }
 
 int q4k_moe_gemv(const void *w_experts, int64_t n_experts, int64_t expert_stride_bytes,
@@ -76,8 +76,8 @@ int q4k_moe_gemv(const void *w_experts, int64_t n_experts, int64_t expert_stride
     if (act_per_slot != 0 && act_per_slot != 1) return Q4K_EINVAL;
     if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || N > kMaxDim || K > kMaxDim)
         return Q4K_ESHAPE;
-    if (n_experts < 1 || n_experts > 65536 || T < 1 || topk < 1 || topk > n_experts ||
-        T * topk > 65536)
+    if (n_experts < 1 || n_experts > q4k::kMoeMaxExperts || T < 1 || topk < 1 ||
+        topk > n_experts || T * topk > q4k::kMoeMaxPairs)
         return Q4K_ESHAPE;
     if (expert_stride_bytes < N * (K / q4k::kQK) * q4k::kSB || expert_stride_bytes % 16 != 0)
         return Q4K_ESHAPE;
@@ -85,7 +85,7 @@ int q4k_moe_gemv(const void *w_experts, int64_t n_experts, int64_t expert_stride
         !aligned(sums, 4) || !aligned(y, 4) || !aligned(ids, 4) ||
         (route_w && !aligned(route_w, 4)))
         return Q4K_EALIGN;
-    const size_t need = q4k::moe_workspace_bytes(T, topk, n_experts);
+    const size_t need = q4k::moe_workspace_bytes(T, topk, n_experts, N);
     if (!workspace || workspace_bytes < need) return Q4K_EWORKSPACE;
     if (!aligned(workspace, 256)) return Q4K_EALIGN;
     return from_hip(q4k::launch_moe_gemv(static_cast<const uint8_t *>(w_experts), n_experts,

@@ -11,6 +11,10 @@ constexpr int kQK = 256;       // weights per Q4_K super-block
 constexpr int kSB = 144;       // bytes per Q4_K super-block
 constexpr int kQB = 32;        // Q8 block / Q4_K sub-block length
 
+// Routed-expert limits (the route grouping runs in one workgroup's LDS).
+constexpr int kMoeMaxPairs = 4096;     // T * topk
+constexpr int kMoeMaxExperts = 4096;
+
 hipError_t launch_quantize(const float *x, int64_t M, int64_t K, const float *gate,
                            int8_t *codes, float *scales, int32_t *sums,
                            hipStream_t stream);
@@ -23,7 +27,7 @@ hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream);
 
-size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts);
+size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N);
 
 hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride,
                            int64_t N, int64_t K, const int32_t *ids, const float *route_w,

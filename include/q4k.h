@@ -101,10 +101,14 @@ int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
 /* Routed-expert grouped GEMV.  n_experts Q4_K matrices of N rows x K columns
  * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of
  * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].
- * Pairs are grouped by expert on the device, so each touched expert's weights
- * are read once per call however many tokens chose it.
- *   ids          device int32 [T][topk]; each in [0, n_experts) -- not checked
- *                on the host (device data); an id out of range is undefined.
+ * Pairs are grouped by expert on the device (deterministically, in ascending
+ * pair order), so each touched expert's weights are read once per call however
+ * many tokens chose it.  Three kernels are enqueued: grouping, grouped GEMV,
+ * and (with routing weights) the slot-ordered weighted sum.
+ *   ids          device int32 [T][topk], expected in [0, n_experts).  They live
+ *                on the device and are not checked on the host; a pair whose id
+ *                is out of range is skipped on the device (its per-slot output
+ *                row is zero and it adds nothing to a weighted sum).
  *   route_w      NULL: y is per slot, fp32 [T*topk][N];
  *                else device fp32 [T][topk]: y[t] = sum_s route_w[t][s] *
  *                (slot product), summed in slot order 0..topk-1, fp32 [T][N].
@@ -113,9 +117,10 @@ int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
  *                [T*topk][K]).
  *   codes/scales/sums as for q4k_gemv.
  *   workspace    device buffer of at least q4k_moe_workspace_bytes(T, topk,
- *                n_experts) bytes, 256-byte aligned; its contents on entry are
- *                ignored.
- * Limits: 1 <= topk <= n_experts, T >= 1, T*topk <= 65536. */
+ *                n_experts, N) bytes, 256-byte aligned; its contents on entry
+ *                are ignored (grouping tables, and the per-slot products when
+ *                route_w is given).  Calls sharing a workspace must not overlap.
+ * Limits: 1 <= topk <= n_experts <= 4096, T >= 1, T*topk <= 4096. */
 int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
                  int64_t expert_stride_bytes, int64_t N, int64_t K,
                  const int32_t *ids, const float *route_w, int64_t T,
@@ -124,7 +129,7 @@ int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes q4k_moe_gemv needs for these sizes (0 on invalid sizes). */
-size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts);
+size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N);
 
 /* Static description of a status code. */
 const char *q4k_status_string(int status);

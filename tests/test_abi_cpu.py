@@ -76,10 +76,12 @@ def test_quantize_argument_checks(L):
 
 def test_moe_argument_checks(L):
     f = L.q4k_moe_gemv
-    ws = q4k.q4k_moe_workspace_bytes(16, 8, 64)
-    assert ws > 0
-    assert q4k.q4k_moe_workspace_bytes(1, 9, 8) == 0
-    assert q4k.q4k_moe_workspace_bytes(0, 1, 8) == 0
+    ws = q4k.q4k_moe_workspace_bytes(16, 8, 64, 1024)
+    assert ws >= 16 * 8 * 1024 * 4
+    assert q4k.q4k_moe_workspace_bytes(1, 9, 8, 1024) == 0
+    assert q4k.q4k_moe_workspace_bytes(0, 1, 8, 1024) == 0
+    assert q4k.q4k_moe_workspace_bytes(4097, 1, 8, 1024) == 0
+    assert q4k.q4k_moe_workspace_bytes(1, 1, 4097, 1024) == 0
     stride = 1024 * 8 * 144
 
     def call(**kw):
@@ -92,6 +94,7 @@ def test_moe_argument_checks(L):
     assert call(ids=None) == EINVAL
     assert call(aps=2) == EINVAL
     assert call(topk=65) == ESHAPE
+    assert call(T=600, topk=8) == ESHAPE
     assert call(topk=0) == ESHAPE
     assert call(T=0) == ESHAPE
     assert call(stride=stride - 16) == ESHAPE

@@ -1,0 +1,188 @@
+"""GPU parity of the routed-expert path (q4k_moe_gemv and the SwiGLU variant of
+q4k_quantize_act) against the CPU oracle, on the 8B-A1B-style layer shape:
+64 experts, hidden 2048, expert FFN 1024 (gate/up 2048->1024, down 1024->2048),
+top-8 routing with softmax weights, T = 1 and 16 tokens.
+
+Stage by stage the expected values are exact or within the fp32 tolerance:
+  gate/up grouped GEMV             -> tolerance vs oracle g, u
+  Q8 of SwiGLU(oracle g, oracle u) -> bit-exact vs oracle codes/scales/sums
+  down grouped GEMV + routed sum   -> tolerance vs oracle y (on the oracle's Q8(h))
+The whole chain run on the GPU's own intermediates is compared with a bound
+that admits the one place where two correct answers exist: an element of h
+whose quotient h/scale lies next to a rounding boundary may round either way
+when g and u differ in their last fp32 bits.
+"""
+import numpy as np
+import pytest
+
+import q4k_inputs as qi
+from _helpers import assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+E, H, F, TOPK = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
+
+
+@pytest.fixture(scope="module")
+def q4k():
+    import torch
+    assert torch.cuda.is_available()
+    import gemm_q4_super_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def layer():
+    wg = np.concatenate([qi.make_q4k_bytes(F, H, qi.expert_seed(0, e, 0)) for e in range(E)])
+    wu = np.concatenate([qi.make_q4k_bytes(F, H, qi.expert_seed(0, e, 1)) for e in range(E)])
+    wd = np.concatenate([qi.make_q4k_bytes(H, F, qi.expert_seed(0, e, 2)) for e in range(E)])
+    return wg, wu, wd
+
+
+STRIDE_GU = F * (H // 256) * 144
+STRIDE_D = H * (F // 256) * 144
+
+
+def _moe(q4k, w, N, K, ids, rw, codes, scales, sums, act_per_slot, stride):
+    import torch
+    y = q4k.q4k_moe_gemv(to_dev(w), E, stride, N, K, to_dev(ids),
+                         None if rw is None else to_dev(rw), to_dev(codes), to_dev(scales),
+                         to_dev(sums), act_per_slot)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_gate_up_per_slot(q4k, oracle_lib, layer, T):
+    wg, wu, _ = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(T))
+    x = qi.make_act(T, H, qi.act_seed(60000 + T))
+    c, s, su = oracle_lib.quantize_act(x)
+    for w in (wg, wu):
+        y = _moe(q4k, w, F, H, ids, None, c, s, su, 0, STRIDE_GU)
+        ref = oracle_lib.moe_matvec(w, E, STRIDE_GU, F, H, ids, None, c, s, False)
+        assert_close(y, ref, "moe gate/up T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_down_weighted_sum(q4k, oracle_lib, layer, T):
+    _, _, wd = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(100 + T))
+    h = qi.make_act(T * TOPK, F, qi.act_seed(61000 + T)) * np.float32(20.0)
+    c, s, su = oracle_lib.quantize_act(h)
+    y = _moe(q4k, wd, H, F, ids, rw, c, s, su, 1, STRIDE_D)
+    ref = oracle_lib.moe_matvec(wd, E, STRIDE_D, H, F, ids, rw, c, s, True)
+    assert_close(y, ref, "moe down T=%d" % T)
+    # per-slot form of the same call
+    y = _moe(q4k, wd, H, F, ids, None, c, s, su, 1, STRIDE_D)
+    ref = oracle_lib.moe_matvec(wd, E, STRIDE_D, H, F, ids, None, c, s, True)
+    assert_close(y, ref, "moe down per slot T=%d" % T)
+
+
+def test_moe_many_tokens_one_expert_and_bad_ids(q4k, oracle_lib):
+    """20 tokens all routed to expert 3 in slot 0 (more pairs than one 8-row
+    chunk), a repeated expert across slots of different tokens, and ids out of
+    range, which are skipped (zero rows / no contribution)."""
+    n_exp, N, K, T, topk = 8, 96, 512, 20, 2
+    w = np.concatenate([qi.make_q4k_bytes(N, K, 900 + e) for e in range(n_exp)])
+    stride = N * (K // 256) * 144
+    ids = np.zeros((T, topk), np.int32)
+    ids[:, 0] = 3
+    ids[:, 1] = np.arange(T) % n_exp
+    ids[ids[:, 1] == 3, 1] = 5
+    ids[4, 1] = -1
+    ids[7, 1] = n_exp          # out of range
+    rw = np.full((T, topk), 0.5, np.float32)
+    x = qi.make_act(T, K, 77)
+    c, s, su = oracle_lib.quantize_act(x)
+    import torch
+    y = q4k.q4k_moe_gemv(to_dev(w), n_exp, stride, N, K, to_dev(ids), None, to_dev(c),
+                         to_dev(s), to_dev(su), 0)
+    y2 = q4k.q4k_moe_gemv(to_dev(w), n_exp, stride, N, K, to_dev(ids), to_dev(rw), to_dev(c),
+                          to_dev(s), to_dev(su), 0)
+    torch.cuda.synchronize()
+    y, y2 = y.cpu().numpy(), y2.cpu().numpy()
+    valid = (ids >= 0) & (ids < n_exp)
+    safe = np.where(valid, ids, 0)
+    ref = oracle_lib.moe_matvec(w, n_exp, stride, N, K, safe, None, c, s, False)
+    ref[~valid.ravel()] = 0.0
+    assert_close(y, ref, "per-slot with bad ids")
+    assert (y[~valid.ravel()] == 0).all()
+    ref2 = (ref.reshape(T, topk, N) * 0.5).sum(axis=1)
+    assert_close(y2, ref2, "weighted with bad ids")
+
+
+def test_swiglu_quantize_bit_exact_on_oracle_gu(q4k, oracle_lib, layer):
+    import torch
+    wg, wu, wd = layer
+    T = 16
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(7))
+    x = qi.make_act(T, H, qi.act_seed(62000))
+    out = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x)
+    c, s, su = q4k.q4k_quantize_act(to_dev(out["u"]), to_dev(out["g"]))
+    torch.cuda.synchronize()
+    assert (c.cpu().numpy() == out["hc"]).all()
+    assert (s.cpu().numpy() == out["hs"]).all()
+    assert (su.cpu().numpy() == out["hsum"]).all()
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_layer_chain(q4k, oracle_lib, layer, T):
+    """The whole layer on the GPU's own intermediates."""
+    import torch
+    wg, wu, wd = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(T))
+    x = qi.make_act(T, H, qi.act_seed(63000 + T))
+    ref = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x)
+
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    xc, xs, xsu = q4k.q4k_quantize_act(to_dev(x))
+    g = q4k.q4k_moe_gemv(dwg, E, STRIDE_GU, F, H, dids, None, xc, xs, xsu, 0)
+    u = q4k.q4k_moe_gemv(dwu, E, STRIDE_GU, F, H, dids, None, xc, xs, xsu, 0)
+    hc, hs, hsu = q4k.q4k_quantize_act(u, g)
+    y = q4k.q4k_moe_gemv(dwd, E, STRIDE_D, H, F, dids, drw, hc, hs, hsu, 1)
+    torch.cuda.synchronize()
+    g, u, y = g.cpu().numpy(), u.cpu().numpy(), y.cpu().numpy()
+    hc, hs = hc.cpu().numpy(), hs.cpu().numpy()
+
+    assert_close(g, ref["g"], "chain g")
+    assert_close(u, ref["u"], "chain u")
+    # h codes: equal, except +-1 where the oracle's quotient h/scale lies within
+    # what the measured g, u differences can move it of a rounding boundary
+    P = T * TOPK
+    g0, u0 = ref["g"].astype(np.float64), ref["u"].astype(np.float64)
+    dg, du = np.abs(g - g0), np.abs(u - u0)
+    sig = 1.0 / (1.0 + np.exp(-g0))
+    dh = np.abs(sig * (1.0 + g0 * (1.0 - sig))) * dg * np.abs(u0) + np.abs(g0 * sig) * du + dg * du
+    # plus one fp32 ulp of h: both sides round their (different) h to fp32
+    dh = dh + np.spacing(np.abs(ref["h"])).astype(np.float64)
+    dh = dh.reshape(P, F // 32, 32) + 1e-12
+    amax = np.abs(ref["h"].astype(np.float64)).reshape(P, F // 32, 32).max(axis=2)
+    amax = np.maximum(amax, 1e-30)[:, :, None]
+    q = ref["h"].reshape(P, F // 32, 32).astype(np.float64) * 127.0 / amax
+    dq = 127.0 * dh / amax + np.abs(q) * dh.max(axis=2, keepdims=True) / amax
+    frac = np.abs(q - np.floor(q) - 0.5)
+    diff = (hc.astype(np.int64) - ref["hc"].astype(np.int64)).reshape(P, F // 32, 32)
+    mism = diff != 0
+    assert (np.abs(diff) <= 1).all()
+    assert (frac[mism] <= 2.0 * dq[mism] + 1e-6).all(), "code flip away from a boundary"
+    dscale = np.abs(hs.astype(np.float64) - ref["hs"])
+    # scale = fl32(amax / 127): amax moves by at most max dh, plus one ulp of the scale
+    assert (dscale <= 1.01 * dh.max(axis=2) / 127.0
+            + np.spacing(ref["hs"]).astype(np.float64) + 1e-12).all()
+    # y bound: tolerance plus what the admitted flips and scale shifts can move
+    W = {e: np.abs(oracle_lib.dequant(wd[e * H:(e + 1) * H], F)) for e in np.unique(ids)}
+    extra = np.zeros((T, H))
+    for t in range(T):
+        for s_ in range(TOPK):
+            p = t * TOPK + s_
+            d_blk = np.maximum(ref["hs"][p], hs[p]).astype(np.float64).repeat(32)
+            flips = mism[p].ravel().astype(np.float64)
+            shift = dscale[p].repeat(32) * 127.0
+            extra[t] += abs(float(rw[t, s_])) * (W[ids[t, s_]] @ (flips * d_blk + shift))
+    err = np.abs(y.astype(np.float64) - ref["y"])
+    tol = np.maximum(2e-3 * np.abs(ref["y"]), 1e-4) + 1.01 * extra
+    assert (err <= tol).all(), "chain y outside tolerance + admitted-flip bound"
+    print("chain: %d h-code flips of %d, max y err %.3g" % (int(mism.sum()), mism.size,
+                                                          float(err.max())))
