@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the secondary prefill-GEMM measurement")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the small-batch and routed-expert measurements")
     return ap.parse_args()
 
 
@@ -255,6 +257,123 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
     return out
 
 
+def measure_small_batch(torch, dec, steps=5):
+    """Small-batch verification GEMV: M = 2, 4, 8 activation rows against the
+    36-layer sweep's weights, through q4k_gemv and through q4k_gemm.  Only the
+    products are timed (the Q8 rows are prepared once)."""
+    import gemm_q4_super_amd as q4k
+    L = dec.L
+    dev = torch.device("cuda:0")
+    out = {}
+    cap = torch.cuda.Stream()
+    for M in (2, 4, 8):
+        xs = {K: q4k.q4k_quantize_act(torch.randn((M, K), device=dev, dtype=torch.float32))
+              for K in {K for _, _, K in dec.weights}}
+        ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
+              for N in {N for _, N, _ in dec.weights}}
+        res = {}
+        for path, fn in (("gemv", L.q4k_gemv), ("gemm", L.q4k_gemm)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                s = torch.cuda.current_stream().cuda_stream
+                for wt, N, K in dec.weights:
+                    c, sc, su = xs[K]
+                    if fn(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(), M,
+                          ys[N].data_ptr(), s):
+                        raise RuntimeError("launch failed")
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3 / steps
+            nbytes = sum(gemv_bytes(N, K, M) for _, N, K in dec.weights)
+            ops = sum(2 * M * N * K for _, N, K in dec.weights)
+            res[path] = {"us_per_sweep": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
+                         "TOPS": round(ops / t / 1e12, 2)}
+        res["faster"] = min(("gemv", "gemm"), key=lambda k: res[k]["us_per_sweep"])
+        out["M=%d" % M] = res
+    return out
+
+
+def measure_moe(torch, q4k, qi, steps=5, layers=8):
+    """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8):
+    quantize -> grouped gate GEMV -> grouped up GEMV -> SwiGLU + Q8 -> grouped
+    down GEMV with the routing-weighted sum, over `layers` distinct seeded
+    layers per pass (1.81 GB, past the last-level cache), for T = 1 and 16."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    E, H, F, TOPK = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
+    sgu, sdn = F * (H // 256) * 144, H * (F // 256) * 144
+    W = []
+    for l in range(layers):
+        W.append(tuple(torch.from_numpy(np.concatenate(
+            [qi.make_q4k_bytes(*((F, H) if k < 2 else (H, F)), qi.expert_seed(l, e, k))
+             for e in range(E)])).to(dev) for k in range(3)))
+    out = {}
+    cap = torch.cuda.Stream()
+    for T in (1, 16):
+        P = T * TOPK
+        routes = [qi.make_routing(T, E, TOPK, qi.routing_seed(100 * T + l)) for l in range(layers)]
+        ids = [torch.from_numpy(r[0]).to(dev) for r in routes]
+        rws = [torch.from_numpy(r[1]).to(dev) for r in routes]
+        x = torch.from_numpy(qi.make_act(T, H, qi.act_seed(70000 + T))).to(dev)
+        xq = q4k.q4k_quantize_act(x)
+        g = torch.empty((P, F), dtype=torch.float32, device=dev)
+        u = torch.empty((P, F), dtype=torch.float32, device=dev)
+        hq = (torch.empty((P, F), dtype=torch.int8, device=dev),
+              torch.empty((P, F // 32), dtype=torch.float32, device=dev),
+              torch.empty((P, F // 32), dtype=torch.int32, device=dev))
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws_gu = torch.empty(q4k.q4k_moe_workspace_bytes(T, TOPK, E, F), dtype=torch.uint8,
+                            device=dev)
+        ws_dn = torch.empty(q4k.q4k_moe_workspace_bytes(T, TOPK, E, H), dtype=torch.uint8,
+                            device=dev)
+
+        def layer(l, s):
+            wg, wu, wd = W[l]
+            c, sc, su = xq
+            st = L.q4k_quantize_act(x.data_ptr(), T, H, None, c.data_ptr(), sc.data_ptr(),
+                                    su.data_ptr(), s)
+            for wt, dst in ((wg, g), (wu, u)):
+                st |= L.q4k_moe_gemv(wt.data_ptr(), E, sgu, F, H, ids[l].data_ptr(), None, T,
+                                     TOPK, c.data_ptr(), sc.data_ptr(), su.data_ptr(), 0,
+                                     dst.data_ptr(), ws_gu.data_ptr(), ws_gu.numel(), s)
+            st |= L.q4k_quantize_act(u.data_ptr(), P, F, g.data_ptr(), hq[0].data_ptr(),
+                                     hq[1].data_ptr(), hq[2].data_ptr(), s)
+            st |= L.q4k_moe_gemv(wd.data_ptr(), E, sdn, H, F, ids[l].data_ptr(),
+                                 rws[l].data_ptr(), T, TOPK, hq[0].data_ptr(), hq[1].data_ptr(),
+                                 hq[2].data_ptr(), 1, y.data_ptr(), ws_dn.data_ptr(),
+                                 ws_dn.numel(), s)
+            if st:
+                raise RuntimeError("launch failed")
+
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            s = torch.cuda.current_stream().cuda_stream
+            for l in range(layers):
+                layer(l, s)
+        gr.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / (steps * layers)
+        distinct = np.mean([len(np.unique(r[0])) for r in routes])
+        nbytes = distinct * 3 * F * H // 256 * 144
+        out["T=%d" % T] = {"us_per_layer": round(t * 1e6, 2),
+                           "distinct_experts": float(distinct),
+                           "expert_MB_per_layer": round(nbytes / 1e6, 2),
+                           "GBps": round(nbytes / t / 1e9, 1)}
+    del W
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(qi, oracle, shapes, seconds):
     """The oracle (single thread) over layers of the same sweep until `seconds`
     of CPU time have been spent or all 36 layers are done."""
@@ -343,10 +462,12 @@ def main():
     value = (dec.bytes_gemv + dec.bytes_quant) * steps / elapsed / 1e9
     bytes_per_launch = dec.bytes_gemv / dec.n_gemv
     achieved = bytes_per_launch / mean_gemv_s / 1e9
+    small = None if args.no_extra else measure_small_batch(torch, dec)
     del g_quant, g_gemv, dec
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
                                                            args.prefill_steps)
+    moe = None if args.no_extra else measure_moe(torch, q4k, qi)
     cpu = None if args.no_cpu else cpu_baseline(qi, oracle, qi.QWEN3_4B_LAYER, args.cpu_seconds)
 
     out = {
@@ -380,6 +501,8 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "prefill_gemm": prefill,
+        "small_batch_gemv": small,
+        "moe_layer": moe,
     }
     print(json.dumps(out))
 
