@@ -5,16 +5,17 @@
 A step is one batch-1 decode token: for each of 36 layers and each projection
 q, k, v, o, gate, up, down (distinct seeded Q4_K matrices, 2.04 GB in total, so
 nothing stays in the 256 MB last-level cache) the activation of that call (a
-fresh N(0,1) fp32 row) is quantized to Q8 (q4k_quantize_act) and the GEMV runs
-(q4k_gemv): 252 quantizations and 252 GEMVs.  All inputs are resident in HBM
-before timing.  Each step is replayed from HIP graphs (the host cost of 504
-small launches would otherwise be measured instead of the GPU).
-
-Within a step the 252 quantizations run first and the 252 GEMVs after them,
-each GEMV on its own call's activation (the same work as interleaving them).
-One pair of HIP events on the launch stream brackets the GEMV block of every
-timed step; that gives the mean GEMV launch duration for the roofline (an event
-pair around each kernel would add a marker dispatch of several microseconds).
+fresh N(0,1) fp32 row) is quantized to Q8 and multiplied by the matrix: 252
+calls of q4k_quantize_gemv, which does both in one launch (codes bit-identical
+to q4k_quantize_act).  All inputs are resident in HBM before timing.  Each step
+is replayed from a HIP graph (the host cost of 252 small launches would
+otherwise be measured instead of the GPU).  One pair of HIP events on the
+launch stream brackets every timed step, which is exactly the block of 252
+back-to-back GEMV dispatches; that gives the mean launch duration for the
+roofline (an event pair around each kernel would add a marker dispatch of
+several microseconds).  The same sweep as two launches per call
+(q4k_quantize_act, then q4k_gemv) is timed after the timed region and
+reported beside it.
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
 the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
@@ -44,6 +45,12 @@ def gemv_bytes(N, K, M=1):
     """Algorithmic bytes of one GEMV: Q4_K weights once, the Q8 activation
     (codes + fp32 scale + int32 sum per 32 values), the fp32 output."""
     return N * K // 256 * 144 + M * K + M * (K // 32) * 8 + 4 * M * N
+
+
+def fused_bytes(N, K, M=1):
+    """Algorithmic bytes of one fused quantize+GEMV call: Q4_K weights once,
+    the fp32 activation, the fp32 output (the Q8 codes never leave the CU)."""
+    return N * K // 256 * 144 + 4 * M * K + 4 * M * N
 
 
 def quant_bytes(K, M=1):
@@ -93,6 +100,7 @@ class Decode:
         self.n_gemv = len(self.weights)
         self.bytes_gemv = sum(gemv_bytes(N, K) for _, N, K in self.weights)
         self.bytes_quant = sum(quant_bytes(K) for _, N, K in self.weights)
+        self.bytes_fused = sum(fused_bytes(N, K) for _, N, K in self.weights)
         torch.cuda.synchronize()
 
     def quantize(self, i, s):
@@ -109,6 +117,12 @@ class Decode:
                            1, self.ys[N].data_ptr(), s):
             raise RuntimeError("q4k_gemv launch failed")
 
+    def fused(self, i, s):
+        wt, N, K = self.weights[i]
+        if self.L.q4k_quantize_gemv(wt.data_ptr(), N, K, self.acts[i].data_ptr(), 1,
+                                    self.ys[N].data_ptr(), s):
+            raise RuntimeError("q4k_quantize_gemv launch failed")
+
     def graph(self, fn, indices, stream):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
@@ -119,15 +133,19 @@ class Decode:
         return g
 
     def parity(self, oracle):
-        """Quantize + GEMV of layer 0's seven projections; codes bit-exact and
-        34 sampled outputs per projection within tolerance."""
+        """Layer 0's seven projections: Q8 codes bit-exact with the oracle, the
+        fused call bit-identical to quantize + GEMV, and 34 sampled outputs per
+        projection within tolerance of the oracle."""
         torch, q4k = self.torch, self.q4k
         max_rel, checked = 0.0, 0
         for p, (name, K, N) in enumerate(self.shapes):
             wt = self.weights[p][0]
             c, sc, su = q4k.q4k_quantize_act(self.acts[p])
-            y = q4k.q4k_gemv(wt, N, K, c, sc, su)
+            y2 = q4k.q4k_gemv(wt, N, K, c, sc, su)
+            y = q4k.q4k_quantize_gemv(wt, N, K, self.acts[p])
             torch.cuda.synchronize()
+            if not torch.equal(y, y2):
+                raise SystemExit("parity: fused and two-launch GEMV differ for %s" % name)
             rc, rs, _ = oracle.quantize_act(self.acts[p].cpu().numpy())
             if not (c.cpu().numpy() == rc).all():
                 raise SystemExit("parity: Q8 codes differ from the oracle for %s" % name)
@@ -418,12 +436,10 @@ def main():
     steps, warmup = args.steps, args.warmup
     cap = torch.cuda.Stream()
     idx = range(dec.n_gemv)
-    g_quant = dec.graph(dec.quantize, idx, cap)
-    g_gemv = dec.graph(dec.gemv, idx, cap)
+    g_fused = dec.graph(dec.fused, idx, cap)
     torch.cuda.synchronize()
     for _ in range(warmup):
-        g_quant.replay()
-        g_gemv.replay()
+        g_fused.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -432,9 +448,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        g_quant.replay()
         ev[k][0].record()
-        g_gemv.replay()
+        g_fused.replay()
         ev[k][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -443,11 +458,31 @@ def main():
     block_s = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
     mean_gemv_s = float(block_s.mean()) / dec.n_gemv
 
-    # Per-projection breakdown, outside the timed region: a graph of the 36
-    # GEMVs of one projection, replayed 5 times between two events.
+    # The same sweep as two launches per call (quantize, then GEMV).
+    g_quant = dec.graph(dec.quantize, idx, cap)
+    g_gemv = dec.graph(dec.gemv, idx, cap)
+    g_quant.replay(); g_gemv.replay()
+    torch.cuda.synchronize()
+    a2, b2, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    a2.record()
+    for _ in range(5):
+        g_quant.replay()
+    b2.record()
+    for _ in range(5):
+        g_gemv.replay()
+    c2.record()
+    torch.cuda.synchronize()
+    t_q2, t_g2 = a2.elapsed_time(b2) * 1e-3 / 5, b2.elapsed_time(c2) * 1e-3 / 5
+    two_step = {"ms_per_step": round((t_q2 + t_g2) * 1e3, 4),
+                "quantize_ms": round(t_q2 * 1e3, 4), "gemv_ms": round(t_g2 * 1e3, 4),
+                "GBps": round((dec.bytes_gemv + dec.bytes_quant) / (t_q2 + t_g2) / 1e9, 1),
+                "gemv_mean_launch_us": round(t_g2 / dec.n_gemv * 1e6, 3)}
+
+    # Per-projection breakdown (fused call), outside the timed region: a graph
+    # of the 36 calls of one projection, replayed 5 times between two events.
     per_shape = {}
     for p, (name, K, N) in enumerate(dec.shapes):
-        g = dec.graph(dec.gemv, range(p, dec.n_gemv, len(dec.shapes)), cap)
+        g = dec.graph(dec.fused, range(p, dec.n_gemv, len(dec.shapes)), cap)
         g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -457,13 +492,13 @@ def main():
         torch.cuda.synchronize()
         d = a.elapsed_time(b) * 1e-3 / (5 * LAYERS)
         per_shape[name] = {"N": N, "K": K, "us": round(d * 1e6, 3),
-                           "GBps": round(gemv_bytes(N, K) / d / 1e9, 1)}
+                           "GBps": round(fused_bytes(N, K) / d / 1e9, 1)}
 
-    value = (dec.bytes_gemv + dec.bytes_quant) * steps / elapsed / 1e9
-    bytes_per_launch = dec.bytes_gemv / dec.n_gemv
+    value = dec.bytes_fused * steps / elapsed / 1e9
+    bytes_per_launch = dec.bytes_fused / dec.n_gemv
     achieved = bytes_per_launch / mean_gemv_s / 1e9
     small = None if args.no_extra else measure_small_batch(torch, dec)
-    del g_quant, g_gemv, dec
+    del g_quant, g_gemv, g_fused, dec
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
                                                            args.prefill_steps)
@@ -486,18 +521,20 @@ def main():
         "config": {"workload": "decode GEMV sweep, batch 1: 36 Qwen3-4B-shaped layers x "
                                "(q 2560->4096, k 2560->1024, v 2560->1024, o 4096->2560, "
                                "gate 2560->9728, up 2560->9728, down 9728->2560), 2.04 GB of "
-                               "Q4_K weights, Q8 quantization of a fresh N(0,1) row per call",
+                               "Q4_K weights, Q8 quantization of a fresh N(0,1) row per call "
+                               "(q4k_quantize_gemv: quantize + GEMV in one launch)",
                    "layers": LAYERS, "batch": 1,
                    "tok_per_s": round(steps / elapsed, 1),
                    "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1)",
+        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1, fused Q8)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "mean_launch_us": round(mean_gemv_s * 1e6, 3),
                      "bytes_per_launch": round(bytes_per_launch),
                      "timing": "HIP events on the launch stream around the 252 back-to-back "
-                               "GEMV dispatches of each timed step (dispatch gaps included)",
+                               "dispatches of each timed step (dispatch gaps included)",
                      "per_shape": per_shape},
+        "two_launch_path": two_step,
         "cpu_baseline": cpu,
         "parity": parity,
         "prefill_gemm": prefill,

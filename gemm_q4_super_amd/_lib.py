@@ -10,6 +10,7 @@ lib_path = os.path.join(_HERE, "libq4k.so")
 EXPORTED_SYMBOLS = (
     "q4k_quantize_act",
     "q4k_gemv",
+    "q4k_quantize_gemv",
     "q4k_gemm",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
@@ -42,13 +43,15 @@ def lib():
         L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
         L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
         L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+        L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
         L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                    ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
         L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
-        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_gemm", "q4k_moe_gemv"):
+        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv", "q4k_gemm",
+                     "q4k_moe_gemv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -111,6 +114,18 @@ def _matrix_call(fn, what, w, N, K, codes, scales, sums, y):
 
 def q4k_gemv(w, N, K, codes, scales, sums, y=None):
     return _matrix_call(lib().q4k_gemv, "q4k_gemv", w, N, K, codes, scales, sums, y)
+
+
+def q4k_quantize_gemv(w, N, K, x, y=None):
+    """Q8-quantize fp32 x [M, K] and multiply by W^T in one launch."""
+    import torch
+    _dev(w, "w"); _dev(x, "x")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_quantize_gemv(_ptr(w), N, K, _ptr(x), M, _ptr(y), _stream(x)),
+           "q4k_quantize_gemv")
+    return y
 
 
 def q4k_gemm(w, N, K, codes, scales, sums, y=None):

@@ -7,20 +7,22 @@
 //  * Lane <-> 16-byte quant chunk.  A super-block is 144 B = a 16-B header
 //    plus eight 16-B quant chunks; 8 lanes (a "group") take one super-block,
 //    lane l loading chunk l with one 16-B load and the header with another.
-//    Chunk l holds, for g = l/2 and h = l%2, elements 64g+16h+i (low nibbles,
-//    sub-block 2g) and 64g+32+16h+i (high nibbles, sub-block 2g+1), i < 16.
 //    (The pages' Path C reads four packed quant bytes as one 32-bit load; on
 //    gfx950 a lane moves 16 B per load.)
-//  * Sub-block integer dots with v_dot4 (sdot4): 8 per lane per super-block and
-//    activation row.  The two partner lanes of a chunk pair exchange one half
-//    with a DPP quad swap, after which lane l holds the exact int32 dot of
-//    sub-block j = l.  Lane l then applies the fp32 epilogue of sub-block l:
-//    acc += a_j * (d*sc_j*D_j - dmin*mn_j*S_j).
+//  * Sub-block integer dots with v_dot4 (sdot4); the partner lanes of a chunk
+//    pair exchange one half with a DPP quad swap, after which lane l holds the
+//    exact int32 dot of sub-block j = l and applies its fp32 epilogue
+//    acc += a_j * (d*sc_j*D_j - dmin*mn_j*S_j)   (helpers in q4k_device.h).
 //  * Workgroup = W waves splitting the K/256 super-block columns of the same
-//    8*T rows; group g of every wave owns rows 8t+g.  The activation chunk of a
-//    column is loaded once per wave and reused over the T row tiles and all 8
-//    groups.  Per-lane sums reduce over the 8 lanes by DPP, then over the W
-//    waves through LDS in a fixed order (deterministic, no atomics).
+//    8*T rows; group g of every wave owns rows 8t+g.  A wave issues the loads
+//    of all its columns (up to CPW) before any arithmetic, so one DRAM round
+//    trip covers them.  The activation chunk of a column is reused over the T
+//    row tiles and all 8 groups.  Per-lane sums reduce over the 8 lanes by
+//    DPP, then over the W waves through LDS in a fixed order (deterministic).
+//  * Fused variant (q4k_quantize_gemv): the activation arrives as fp32 and
+//    each wave quantizes the Q8 blocks of its own columns into LDS (same
+//    arithmetic as q4k_quantize_act, so the codes are bit-identical) while its
+//    weight loads are in flight -- one launch instead of two per call.
 #include "q4k_device.h"
 #include "q4k_internal.h"
 
@@ -29,14 +31,45 @@ namespace {
 
 constexpr int kMaxWaves = 16;
 
-template <int M, int T>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, dpp_f<kQuadSwap1>(v));
+    v = fmaxf(v, dpp_f<kQuadSwap2>(v));
+    v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
+    return v;
+}
+__device__ __forceinline__ int group8_isum(int v) {
+    v += dpp_i<kQuadSwap1>(v);
+    v += dpp_i<kQuadSwap2>(v);
+    v += dpp_i<kRowHalfMirror>(v);
+    return v;
+}
+// Branch-free: an all-zero block (d == 0) divides by 1 and selects 0.
+__device__ __forceinline__ int quant1(float x, float d) {
+    const bool zero = d == 0.0f;
+    float r = __builtin_rintf(x / (zero ? 1.0f : d));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return zero ? 0 : (int)r;
+}
+
+// Per-wave LDS of the fused variant: Q8 of the wave's CPW columns, M rows.
+template <int M, int CPW>
+struct WaveQ8 {
+    int8_t c[M][CPW][256];
+    float a[M][CPW][8];
+    float s[M][CPW][8];
+};
+
+template <int M, int T, int CPW, bool FUSED>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int N,
-                                                    int nsb, int cpw,
+                                                    int nsb, const float *__restrict__ x,
                                                     const int8_t *__restrict__ codes,
                                                     const float *__restrict__ scales,
                                                     const int32_t *__restrict__ sums,
                                                     float *__restrict__ y) {
     __shared__ float red[kMaxWaves][8 * T][M];
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -47,6 +80,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     const int nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
     const int row0 = blockIdx.x * (8 * T);
+    WaveQ8<M, CPW> *q8 = reinterpret_cast<WaveQ8<M, CPW> *>(dyn) + wave;
 
     float acc[T][M];
 #pragma unroll
@@ -54,47 +88,130 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[t][m] = 0.0f;
 
-    const int b_begin = wave * cpw;
-    const int b_end = min(nsb, b_begin + cpw);
-    for (int b = b_begin; b < b_end; ++b) {
-        // Weights of this column for all T row tiles: issue the loads first.
-        u32x4 hd[T], qw[T];
+    // Columns [b0, b0 + CPW) of this wave; a wave with more than CPW columns
+    // (K beyond 16 * CPW super-blocks) takes them in groups of CPW.
+    // Activation loads go out before the weight loads: the load counter
+    // retires in order, so data wanted first must be requested first (the
+    // quantization, or column 0's dots, then overlaps the weight stream).
+    constexpr bool kActFirst = FUSED || M * CPW * T <= 6;
+    for (int b0 = wave * CPW; b0 < nsb; b0 += nwaves * CPW) {
+        f32x4 xv[FUSED ? M : 1][FUSED ? CPW : 1];
+        i32x4 pA[kActFirst && !FUSED ? CPW : 1][M], pB[kActFirst && !FUSED ? CPW : 1][M];
+        float pa[kActFirst && !FUSED ? CPW : 1][M];
+        int ps[kActFirst && !FUSED ? CPW : 1][M];   // converted at use, after the loads
+        if constexpr (FUSED) {
+            const int blk = lane >> 3, sub = lane & 7;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int row = row0 + 8 * t + grp;
-            if (row < N) {
-                const uint8_t *sb = w + (int64_t)row * row_bytes + (int64_t)b * 144;
-                hd[t] = load_stream16(sb);
-                qw[t] = load_stream16(sb + 16 + 16 * L.l);
-            } else {
-                hd[t] = (u32x4){0u, 0u, 0u, 0u};
-                qw[t] = (u32x4){0u, 0u, 0u, 0u};
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) {
+                    // clamped, branch-free: columns past nsb are never used
+                    const int b = min(b0 + c, nsb - 1);
+                    xv[m][c] = *reinterpret_cast<const f32x4 *>(x + (int64_t)m * K + 256 * b +
+                                                                32 * blk + 4 * sub);
+                }
+        } else if constexpr (kActFirst) {
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int b = min(b0 + c, nsb - 1);   // clamped: unused past nsb
+                    const int8_t *cm = codes + (int64_t)m * K + 256 * b;
+                    pA[c][m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
+                    pB[c][m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
+                    pa[c][m] = scales[(int64_t)m * nblk + 8 * b + L.l];
+                    ps[c][m] = sums[(int64_t)m * nblk + 8 * b + L.l];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // activation loads stay first
+        // Branch-free weight loads from clamped addresses: a load under a
+        // branch makes the compiler wait for every load at the join, which
+        // would serialize the activation work behind the weight stream.  Rows
+        // past N compute on row N-1 and are never written; columns past nsb
+        // are skipped below.
+        u32x4 hd[CPW][T], qw[CPW][T];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int row = row0 + 8 * t + grp, b = b0 + c;
+                const uint8_t *sb = w + (int64_t)min(row, N - 1) * row_bytes +
+                                    (int64_t)min(b, nsb - 1) * 144;
+                hd[c][t] = load_stream16(sb);
+                qw[c][t] = load_stream16(sb + 16 + 16 * L.l);
             }
-        }
-        // Activation chunk of this column, reused over the row tiles.
-        i32x4 cA[M], cB[M];
-        float a[M];
-        float s[M];
+        // Keep every load of the group ahead of the arithmetic below.
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FUSED) {
+            // Quantize this wave's columns: lane -> block lane/8 of the column,
+            // 4 values at 4*(lane%8) within the block.
+            const int blk = lane >> 3, sub = lane & 7;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int8_t *cm = codes + (int64_t)m * K + 256 * b;
-            cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
-            cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
-            a[m] = scales[(int64_t)m * nblk + 8 * b + L.l];
-            s[m] = (float)sums[(int64_t)m * nblk + 8 * b + L.l];
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) {
+                    const f32x4 v = xv[m][c];
+                    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
+                                       fmaxf(fabsf(v[2]), fabsf(v[3])));
+                    amax = group8_max(amax);
+                    const float d = amax / 127.0f;
+                    const int c0 = quant1(v[0], d), c1 = quant1(v[1], d);
+                    const int c2 = quant1(v[2], d), c3 = quant1(v[3], d);
+                    *reinterpret_cast<int *>(&q8->c[m][c][32 * blk + 4 * sub]) =
+                        (c0 & 0xFF) | ((c1 & 0xFF) << 8) | ((c2 & 0xFF) << 16) |
+                        (int)((unsigned)c3 << 24);
+                    const int ssum = group8_isum(c0 + c1 + c2 + c3);
+                    if (sub == 0) {
+                        q8->a[m][c][blk] = d;
+                        q8->s[m][c][blk] = (float)ssum;
+                    }
+                }
+            // LDS written and read by this wave only: wait for the writes.
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+            __builtin_amdgcn_wave_barrier();
         }
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            float ds, dm;
-            decode_scale(L, hd[t], ds, dm);
-            int qlo[4], qhi[4];
-            unpack_nibbles(qw[t], qlo, qhi);
+        for (int c = 0; c < CPW; ++c) {
+            const int b = b0 + c;
+            if (b >= nsb) break;                 // wave-uniform
+            // Activation chunk of this column, reused over the row tiles.
+            i32x4 cA[M], cB[M];
+            float a[M];
+            float s[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
-                acc[t][m] = fmaf(a[m], ds * (float)D - dm * s[m], acc[t][m]);
+                if constexpr (FUSED) {
+                    cA[m] = *reinterpret_cast<const i32x4 *>(&q8->c[m][c][L.offA]);
+                    cB[m] = *reinterpret_cast<const i32x4 *>(&q8->c[m][c][L.offB]);
+                    a[m] = q8->a[m][c][L.l];
+                    s[m] = q8->s[m][c][L.l];
+                } else if constexpr (kActFirst) {
+                    cA[m] = pA[c][m];
+                    cB[m] = pB[c][m];
+                    a[m] = pa[c][m];
+                    s[m] = (float)ps[c][m];
+                } else {
+                    const int8_t *cm = codes + (int64_t)m * K + 256 * b;
+                    cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
+                    cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
+                    a[m] = scales[(int64_t)m * nblk + 8 * b + L.l];
+                    s[m] = (float)sums[(int64_t)m * nblk + 8 * b + L.l];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                float ds, dm;
+                decode_scale(L, hd[c][t], ds, dm);
+                int qlo[4], qhi[4];
+                unpack_nibbles(qw[c][t], qlo, qhi);
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
+                    acc[t][m] = fmaf(a[m], ds * (float)D - dm * s[m], acc[t][m]);
+                }
             }
         }
+        if constexpr (FUSED) __builtin_amdgcn_wave_barrier();   // LDS reuse by the next group
     }
 
     // Reduce the 8 sub-block lanes of each group, then the waves via LDS.
@@ -115,25 +232,51 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     }
 }
 
-template <int M, int T>
-hipError_t launch_mt(const uint8_t *w, int N, int nsb, const int8_t *codes,
-                     const float *scales, const int32_t *sums, float *y, hipStream_t stream) {
-    int cpw = (nsb + kMaxWaves - 1) / kMaxWaves;
-    const int nwaves = (nsb + cpw - 1) / cpw;
+template <int M, int T, int CPW, bool FUSED>
+hipError_t launch_mtc(const uint8_t *w, int N, int nsb, const float *x, const int8_t *codes,
+                      const float *scales, const int32_t *sums, float *y, hipStream_t stream) {
+    const int nwaves = (nsb + CPW - 1) / CPW < kMaxWaves ? (nsb + CPW - 1) / CPW : kMaxWaves;
     const int rows_per_wg = 8 * T;
     const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_kernel<M, T>), dim3(grid), dim3(64 * nwaves), 0, stream, w, N,
-                       nsb, cpw, codes, scales, sums, y);
+    const size_t lds = FUSED ? sizeof(WaveQ8<M, CPW>) * nwaves : 0;
+    hipLaunchKernelGGL((gemv_kernel<M, T, CPW, FUSED>), dim3(grid), dim3(64 * nwaves), lds,
+                       stream, w, N, nsb, x, codes, scales, sums, y);
     return hipGetLastError();
 }
 
-template <int M>
-hipError_t launch_m(const uint8_t *w, int N, int nsb, const int8_t *codes,
+template <int M, bool FUSED>
+hipError_t launch_m(const uint8_t *w, int N, int nsb, const float *x, const int8_t *codes,
                     const float *scales, const int32_t *sums, float *y, hipStream_t stream) {
-    // Two row tiles per workgroup once there are enough rows to fill the chip.
-    if (N >= 4096 && M <= 4)
-        return launch_mt<M, 2>(w, N, nsb, codes, scales, sums, y, stream);
-    return launch_mt<M, 1>(w, N, nsb, codes, scales, sums, y, stream);
+    // Columns per wave: as few as the 16-wave workgroup allows; two row tiles
+    // per workgroup once there are enough rows to fill the chip.
+    const bool t2 = N >= 4096 && M <= 2;
+    if (nsb <= 16)
+        return t2 ? launch_mtc<M, 2, 1, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
+                  : launch_mtc<M, 1, 1, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
+    if (nsb <= 32)
+        return t2 ? launch_mtc<M, 2, 2, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
+                  : launch_mtc<M, 1, 2, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
+    return t2 ? launch_mtc<M, 2, 3, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
+              : launch_mtc<M, 1, 3, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
+}
+
+template <bool FUSED>
+hipError_t dispatch(const uint8_t *w, int64_t N, int64_t K, const float *x, const int8_t *codes,
+                    const float *scales, const int32_t *sums, int64_t M, float *y,
+                    hipStream_t stream) {
+    const int nsb = (int)(K / kQK);
+    const int n = (int)N;
+    switch (M) {
+    case 1: return launch_m<1, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 2: return launch_m<2, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 3: return launch_m<3, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 4: return launch_m<4, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 5: return launch_m<5, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 6: return launch_m<6, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 7: return launch_m<7, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 8: return launch_m<8, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -141,19 +284,12 @@ hipError_t launch_m(const uint8_t *w, int N, int nsb, const int8_t *codes,
 hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
-    const int nsb = (int)(K / kQK);
-    const int n = (int)N;
-    switch (M) {
-    case 1: return launch_m<1>(w, n, nsb, codes, scales, sums, y, stream);
-    case 2: return launch_m<2>(w, n, nsb, codes, scales, sums, y, stream);
-    case 3: return launch_m<3>(w, n, nsb, codes, scales, sums, y, stream);
-    case 4: return launch_m<4>(w, n, nsb, codes, scales, sums, y, stream);
-    case 5: return launch_m<5>(w, n, nsb, codes, scales, sums, y, stream);
-    case 6: return launch_m<6>(w, n, nsb, codes, scales, sums, y, stream);
-    case 7: return launch_m<7>(w, n, nsb, codes, scales, sums, y, stream);
-    case 8: return launch_m<8>(w, n, nsb, codes, scales, sums, y, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch<false>(w, N, K, nullptr, codes, scales, sums, M, y, stream);
+}
+
+hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
+                                int64_t M, float *y, hipStream_t stream) {
+    return dispatch<true>(w, N, K, x, nullptr, nullptr, nullptr, M, y, stream);
 }
 
 }  // namespace q4k

@@ -52,6 +52,16 @@ int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes, const flo
                                      sums, M, y, static_cast<hipStream_t>(stream)));
 }
 
+int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
+                      float *y, void *stream) {
+    if (!w || !x || !y) return Q4K_EINVAL;
+    if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1 || M > 8) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || M * K > q4k::kFusedMaxMK) return Q4K_ESHAPE;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_quantize_gemv(static_cast<const uint8_t *>(w), N, K, x, M, y,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
              const int32_t *sums, int64_t M, float *y, void *stream) {
     int st = check_matrix_args(w, N, K, codes, scales, sums, M, y);

@@ -23,6 +23,11 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream);
 
+// Fused Q8 quantization + GEMV on fp32 activations (M <= 8, M*K <= kFusedMaxMK).
+constexpr int64_t kFusedMaxMK = 32768;
+hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
+                                int64_t M, float *y, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream);

@@ -89,6 +89,15 @@ int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
              const float *scales, const int32_t *sums, int64_t M, float *y,
              void *stream);
 
+/* Quantize-and-GEMV in one launch: y[M][N] = Q8(x)[M][K] * W^T for fp32
+ * activations x (device, [M][K], 16-byte aligned).  Each workgroup quantizes
+ * the Q8 blocks it needs with the same arithmetic as q4k_quantize_act (codes
+ * bit-identical), so the result equals q4k_quantize_act followed by q4k_gemv,
+ * bit for bit, with one launch instead of two.  Limits: 1 <= M <= 8 and
+ * M*K <= 32768 (the Q8 blocks live in LDS); other arguments as for q4k_gemv. */
+int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
+                      int64_t M, float *y, void *stream);
+
 /* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (section 3's
  * batched prefill over all prompt tokens).  Compute-bound: Q4_K tiles are
  * staged through LDS and the per-32 sub-block integer dot products run on the

@@ -65,6 +65,18 @@ def test_gemv_gemm_argument_checks(L):
     assert L.q4k_gemv(A, 16, 512, A, A, A, 9, A, None) == ESHAPE
 
 
+def test_quantize_gemv_argument_checks(L):
+    f = L.q4k_quantize_gemv
+    assert f(None, 16, 512, A, 1, A, None) == EINVAL
+    assert f(A, 16, 512, None, 1, A, None) == EINVAL
+    assert f(A, 16, 500, A, 1, A, None) == ESHAPE
+    assert f(A, 16, 512, A, 9, A, None) == ESHAPE
+    assert f(A, 16, 9728, A, 4, A, None) == ESHAPE      # M*K beyond the LDS limit
+    assert f(A, 0, 512, A, 1, A, None) == ESHAPE
+    assert f(A + 4, 16, 512, A, 1, A, None) == EALIGN
+    assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
+
+
 def test_quantize_argument_checks(L):
     f = L.q4k_quantize_act
     assert f(None, 1, 32, None, A, A, A, None) == EINVAL

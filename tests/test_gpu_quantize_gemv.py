@@ -189,3 +189,29 @@ def test_gemv_qwen3_4b_shapes_sampled(q4k, oracle_lib, proj):
         x = qi.make_act(M, K, qi.act_seed(proj * 10 + M))
         y, ref = _gemv(q4k, w, N, K, x, oracle_lib, rows=rows)
         assert_close(y, ref, "gemv %s M=%d" % (name, M))
+
+
+# ------------------------------------------------- fused quantize + GEMV ----
+
+@pytest.mark.parametrize("N,K,M", [(1, 256, 1), (37, 512, 2), (1000, 2560, 1), (4096, 2560, 1),
+                                   (2560, 4096, 1), (2560, 9728, 1), (9728, 2560, 1),
+                                   (300, 4096, 8), (129, 6144, 5), (2048, 16384, 2),
+                                   (64, 32768, 1)])
+def test_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
+    """One launch (quantize inside the GEMV) equals q4k_quantize_act followed
+    by q4k_gemv bit for bit, and the oracle within tolerance."""
+    import torch
+    w = qi.make_q4k_bytes(N, K, 7000 + N + K)
+    x = qi.make_act(M, K, 8000 + M + K)
+    x[0, :32] = 0.0
+    wd, xd = to_dev(w), to_dev(x)
+    y1 = q4k.q4k_quantize_gemv(wd, N, K, xd)
+    c, s, su = q4k.q4k_quantize_act(xd)
+    y2 = q4k.q4k_gemv(wd, N, K, c, s, su)
+    torch.cuda.synchronize()
+    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    rows = None if N <= 300 else np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 40)])
+    rc, rs, _ = oracle_lib.quantize_act(x)
+    ref = oracle_lib.matvec(w, N, K, rc, rs, rows=rows)
+    assert_close(y1 if rows is None else y1[:, rows], ref, "quantize_gemv N=%d K=%d M=%d" % (N, K, M))
