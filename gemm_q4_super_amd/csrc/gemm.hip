@@ -111,40 +111,36 @@ __global__ __launch_bounds__((64 * (BM / 32) * (BN / 32))) void gemm_i8_kernel(
     const int64_t row_bytes = (int64_t)nsb * 144;
     const int lr = lane & 31, lh = lane >> 5;
 
+    // Global loads of one super-block, branch-free from clamped addresses (a
+    // load under a branch makes the compiler wait for every outstanding load
+    // at the join, which would drain the prefetch pipeline).  Rows past N or M
+    // read row N-1 / M-1: they only feed outputs that are never stored.
     auto load = [&](int b, Regs<BM, BN> &r) {
-        r.hd = (u32x4){0u, 0u, 0u, 0u};
-        if (tid < BN && n0 + tid < N)
+        {
+            const int row = min(n0 + min(tid, BN - 1), N - 1);
             r.hd = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                w + (int64_t)(n0 + tid) * row_bytes + (int64_t)b * 144));
+                w + (int64_t)row * row_bytes + (int64_t)b * 144));
+        }
 #pragma unroll
         for (int i = 0; i < C::NW; ++i) {
-            const int e = tid + i * C::T;
-            r.wc[i] = (u32x4){0u, 0u, 0u, 0u};
-            const int row = e >> 3, ch = e & 7;
-            if (e < C::WCH && n0 + row < N)
-                r.wc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    w + (int64_t)(n0 + row) * row_bytes + (int64_t)b * 144 + 16 + 16 * ch));
+            const int e = min(tid + i * C::T, C::WCH - 1);
+            const int row = min(n0 + (e >> 3), N - 1), ch = e & 7;
+            r.wc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                w + (int64_t)row * row_bytes + (int64_t)b * 144 + 16 + 16 * ch));
         }
 #pragma unroll
         for (int i = 0; i < C::NX; ++i) {
-            const int e = tid + i * C::T;
-            r.xc[i] = (i32x4){0, 0, 0, 0};
-            const int row = e >> 4, ch = e & 15;
-            if (e < C::XCH && m0 + row < M)
-                r.xc[i] = *reinterpret_cast<const i32x4 *>(codes + (int64_t)(m0 + row) * K +
-                                                           256 * b + 16 * ch);
+            const int e = min(tid + i * C::T, C::XCH - 1);
+            const int row = min(m0 + (e >> 4), M - 1), ch = e & 15;
+            r.xc[i] = *reinterpret_cast<const i32x4 *>(codes + (int64_t)row * K + 256 * b + 16 * ch);
         }
 #pragma unroll
         for (int i = 0; i < C::NS; ++i) {
-            const int e = tid + i * C::T;
-            r.a[i] = 0.0f;
-            r.s[i] = 0;
-            const int row = e >> 3, j = e & 7;
-            if (e < C::SE && m0 + row < M) {
-                const int64_t o = (int64_t)(m0 + row) * nblk + 8 * b + j;
-                r.a[i] = scales[o];
-                r.s[i] = sums[o];
-            }
+            const int e = min(tid + i * C::T, C::SE - 1);
+            const int row = min(m0 + (e >> 3), M - 1), j = e & 7;
+            const int64_t o = (int64_t)row * nblk + 8 * b + j;
+            r.a[i] = scales[o];
+            r.s[i] = sums[o];
         }
     };
     auto store = [&](const Regs<BM, BN> &r, Buf<BM, BN> &B) {
