@@ -4,18 +4,20 @@
 
 A step is one batch-1 decode token: for each of 36 layers and each projection
 q, k, v, o, gate, up, down (distinct seeded Q4_K matrices, 2.04 GB in total, so
-nothing stays in the 256 MB last-level cache) the activation of that call (a
-fresh N(0,1) fp32 row) is quantized to Q8 and multiplied by the matrix: 252
-calls of q4k_quantize_gemv, which does both in one launch (codes bit-identical
-to q4k_quantize_act).  All inputs are resident in HBM before timing.  Each step
-is replayed from a HIP graph (the host cost of 252 small launches would
-otherwise be measured instead of the GPU).  One pair of HIP events on the
-launch stream brackets every timed step, which is exactly the block of 252
-back-to-back GEMV dispatches; that gives the mean launch duration for the
-roofline (an event pair around each kernel would add a marker dispatch of
-several microseconds).  The same sweep as two launches per call
-(q4k_quantize_act, then q4k_gemv) is timed after the timed region and
-reported beside it.
+nothing stays in the 256 MB last-level cache) the activation of that product (a
+fresh N(0,1) fp32 row) is quantized to Q8 and multiplied by the matrix.  The
+products that share an input width go out together: per layer one
+q4k_quantize_gemv_batch launch for {q, k, v}, one for {o}, one for {gate, up}
+and one for {down} (144 launches per step, each quantizing inside the GEMV,
+codes bit-identical to q4k_quantize_act).  All inputs are resident in HBM
+before timing.  Each step is replayed from a HIP graph (the host cost of the
+small launches would otherwise be measured instead of the GPU).  One pair of
+HIP events on the launch stream brackets every timed step, which is exactly the
+block of back-to-back GEMV dispatches; that gives the mean launch duration for
+the roofline (an event pair around each kernel would add a marker dispatch of
+several microseconds).  The same sweep as one q4k_quantize_gemv launch per
+product (252 per step), and as two launches per product (q4k_quantize_act, then
+q4k_gemv), are timed after the timed region and reported beside it.
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
 the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
@@ -97,7 +99,23 @@ class Decode:
                       for (_, N, K) in self.weights]
         self.ys = {N: torch.empty((1, N), dtype=torch.float32, device=dev)
                    for _, _, N in self.shapes}
+        # one output per projection for the batched launches (products of one
+        # launch must not share an output)
+        self.yp = [torch.empty((1, N), dtype=torch.float32, device=dev)
+                   for _, _, N in self.shapes]
+        # per layer: {q, k, v}, {o}, {gate, up}, {down} -- same input width
+        self.groups = [[l * len(self.shapes) + p for p in grp]
+                       for l in range(LAYERS) for grp in ((0, 1, 2), (3,), (4, 5), (6,))]
+        self.batches = []
+        for grp in self.groups:
+            arr = (q4k._lib.GemvProblem * len(grp))()
+            for j, i in enumerate(grp):
+                wt, N, K = self.weights[i]
+                arr[j] = q4k._lib.GemvProblem(wt.data_ptr(), self.acts[i].data_ptr(),
+                                              self.yp[i % len(self.shapes)].data_ptr(), N)
+            self.batches.append((arr, len(grp), self.weights[grp[0]][2]))
         self.n_gemv = len(self.weights)
+        self.n_batch = len(self.groups)
         self.bytes_gemv = sum(gemv_bytes(N, K) for _, N, K in self.weights)
         self.bytes_quant = sum(quant_bytes(K) for _, N, K in self.weights)
         self.bytes_fused = sum(fused_bytes(N, K) for _, N, K in self.weights)
@@ -123,6 +141,11 @@ class Decode:
                                     self.ys[N].data_ptr(), s):
             raise RuntimeError("q4k_quantize_gemv launch failed")
 
+    def batch(self, g, s):
+        arr, n, K = self.batches[g]
+        if self.L.q4k_quantize_gemv_batch(arr, n, K, 1, s):
+            raise RuntimeError("q4k_quantize_gemv_batch launch failed")
+
     def graph(self, fn, indices, stream):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
@@ -134,10 +157,14 @@ class Decode:
 
     def parity(self, oracle):
         """Layer 0's seven projections: Q8 codes bit-exact with the oracle, the
-        fused call bit-identical to quantize + GEMV, and 34 sampled outputs per
-        projection within tolerance of the oracle."""
+        batched launches and the fused call bit-identical to quantize + GEMV, and
+        34 sampled outputs per projection within tolerance of the oracle."""
         torch, q4k = self.torch, self.q4k
         max_rel, checked = 0.0, 0
+        s = torch.cuda.current_stream().cuda_stream
+        for g in range(4):
+            self.batch(g, s)
+        torch.cuda.synchronize()
         for p, (name, K, N) in enumerate(self.shapes):
             wt = self.weights[p][0]
             c, sc, su = q4k.q4k_quantize_act(self.acts[p])
@@ -146,6 +173,8 @@ class Decode:
             torch.cuda.synchronize()
             if not torch.equal(y, y2):
                 raise SystemExit("parity: fused and two-launch GEMV differ for %s" % name)
+            if not torch.equal(y, self.yp[p]):
+                raise SystemExit("parity: batched and single fused GEMV differ for %s" % name)
             rc, rs, _ = oracle.quantize_act(self.acts[p].cpu().numpy())
             if not (c.cpu().numpy() == rc).all():
                 raise SystemExit("parity: Q8 codes differ from the oracle for %s" % name)
@@ -436,10 +465,10 @@ def main():
     steps, warmup = args.steps, args.warmup
     cap = torch.cuda.Stream()
     idx = range(dec.n_gemv)
-    g_fused = dec.graph(dec.fused, idx, cap)
+    g_batch = dec.graph(dec.batch, range(dec.n_batch), cap)
     torch.cuda.synchronize()
     for _ in range(warmup):
-        g_fused.replay()
+        g_batch.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -449,56 +478,56 @@ def main():
     t0 = time.perf_counter()
     for k in range(steps):
         ev[k][0].record()
-        g_fused.replay()
+        g_batch.replay()
         ev[k][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     # ------------------------------------------------------------------
 
     block_s = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
-    mean_gemv_s = float(block_s.mean()) / dec.n_gemv
+    mean_launch_s = float(block_s.mean()) / dec.n_batch
 
-    # The same sweep as two launches per call (quantize, then GEMV).
-    g_quant = dec.graph(dec.quantize, idx, cap)
-    g_gemv = dec.graph(dec.gemv, idx, cap)
-    g_quant.replay(); g_gemv.replay()
-    torch.cuda.synchronize()
-    a2, b2, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    a2.record()
-    for _ in range(5):
-        g_quant.replay()
-    b2.record()
-    for _ in range(5):
-        g_gemv.replay()
-    c2.record()
-    torch.cuda.synchronize()
-    t_q2, t_g2 = a2.elapsed_time(b2) * 1e-3 / 5, b2.elapsed_time(c2) * 1e-3 / 5
+    def timed(g, reps=5):
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    # The same sweep as one fused launch per product, and as two launches per
+    # product (quantize, then GEMV).
+    t_single = timed(dec.graph(dec.fused, idx, cap))
+    single = {"ms_per_step": round(t_single * 1e3, 4),
+              "GBps": round(dec.bytes_fused / t_single / 1e9, 1),
+              "launches": dec.n_gemv,
+              "mean_launch_us": round(t_single / dec.n_gemv * 1e6, 3)}
+    t_q2 = timed(dec.graph(dec.quantize, idx, cap))
+    t_g2 = timed(dec.graph(dec.gemv, idx, cap))
     two_step = {"ms_per_step": round((t_q2 + t_g2) * 1e3, 4),
                 "quantize_ms": round(t_q2 * 1e3, 4), "gemv_ms": round(t_g2 * 1e3, 4),
                 "GBps": round((dec.bytes_gemv + dec.bytes_quant) / (t_q2 + t_g2) / 1e9, 1),
                 "gemv_mean_launch_us": round(t_g2 / dec.n_gemv * 1e6, 3)}
 
-    # Per-projection breakdown (fused call), outside the timed region: a graph
-    # of the 36 calls of one projection, replayed 5 times between two events.
-    per_shape = {}
-    for p, (name, K, N) in enumerate(dec.shapes):
-        g = dec.graph(dec.fused, range(p, dec.n_gemv, len(dec.shapes)), cap)
-        g.replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(5):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        d = a.elapsed_time(b) * 1e-3 / (5 * LAYERS)
-        per_shape[name] = {"N": N, "K": K, "us": round(d * 1e6, 3),
-                           "GBps": round(fused_bytes(N, K) / d / 1e9, 1)}
+    # Per-launch-group breakdown, outside the timed region: a graph of the 36
+    # launches of one group, replayed 5 times between two events.
+    per_group = {}
+    for gi, gname in enumerate(("qkv", "o", "gate_up", "down")):
+        d = timed(dec.graph(dec.batch, range(gi, dec.n_batch, 4), cap)) / LAYERS
+        members = dec.groups[gi]
+        nb = sum(fused_bytes(dec.weights[i][1], dec.weights[i][2]) for i in members)
+        per_group[gname] = {"N": [dec.weights[i][1] for i in members],
+                            "K": dec.weights[members[0]][2], "us": round(d * 1e6, 3),
+                            "GBps": round(nb / d / 1e9, 1)}
 
     value = dec.bytes_fused * steps / elapsed / 1e9
-    bytes_per_launch = dec.bytes_fused / dec.n_gemv
-    achieved = bytes_per_launch / mean_gemv_s / 1e9
+    bytes_per_launch = dec.bytes_fused / dec.n_batch
+    achieved = bytes_per_launch / mean_launch_s / 1e9
+    n_launch = dec.n_batch
     small = None if args.no_extra else measure_small_batch(torch, dec)
-    del g_quant, g_gemv, g_fused, dec
+    del g_batch, dec
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
                                                            args.prefill_steps)
@@ -521,19 +550,23 @@ def main():
         "config": {"workload": "decode GEMV sweep, batch 1: 36 Qwen3-4B-shaped layers x "
                                "(q 2560->4096, k 2560->1024, v 2560->1024, o 4096->2560, "
                                "gate 2560->9728, up 2560->9728, down 9728->2560), 2.04 GB of "
-                               "Q4_K weights, Q8 quantization of a fresh N(0,1) row per call "
-                               "(q4k_quantize_gemv: quantize + GEMV in one launch)",
+                               "Q4_K weights, Q8 quantization of a fresh N(0,1) row per "
+                               "product inside the GEMV; q4k_quantize_gemv_batch launches "
+                               "{q,k,v}, {o}, {gate,up}, {down} per layer",
                    "layers": LAYERS, "batch": 1,
                    "tok_per_s": round(steps / elapsed, 1),
                    "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1, fused Q8)",
+        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1, fused Q8, batched)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "mean_launch_us": round(mean_gemv_s * 1e6, 3),
+                     "mean_launch_us": round(mean_launch_s * 1e6, 3),
                      "bytes_per_launch": round(bytes_per_launch),
-                     "timing": "HIP events on the launch stream around the 252 back-to-back "
-                               "dispatches of each timed step (dispatch gaps included)",
-                     "per_shape": per_shape},
+                     "launches_per_step": n_launch,
+                     "timing": "HIP events on the launch stream around the %d back-to-back "
+                               "dispatches of each timed step (dispatch gaps included)"
+                               % n_launch,
+                     "per_group": per_group},
+        "single_call_path": single,
         "two_launch_path": two_step,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -10,6 +10,7 @@ Functions carry the C names:
     q4k_quantize_act(x, gate=None)                   -> (codes, scales, sums)
     q4k_gemv(w, N, K, codes, scales, sums)           -> y [M, N]   (M <= 8)
     q4k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (fp32 x, one launch)
+    q4k_quantize_gemv_batch([(w, N, x), ...], K)     -> [y, ...]   (<= 8 products, one launch)
     q4k_gemm(w, N, K, codes, scales, sums)           -> y [M, N]
     q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
                  act_per_slot, workspace=None)       -> y
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     q4k_moe_workspace_bytes,
     q4k_quantize_act,
     q4k_quantize_gemv,
+    q4k_quantize_gemv_batch,
     q4k_status_string,
     EXPORTED_SYMBOLS,
 )

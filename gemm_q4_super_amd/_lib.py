@@ -11,6 +11,7 @@ EXPORTED_SYMBOLS = (
     "q4k_quantize_act",
     "q4k_gemv",
     "q4k_quantize_gemv",
+    "q4k_quantize_gemv_batch",
     "q4k_gemm",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
@@ -20,6 +21,11 @@ EXPORTED_SYMBOLS = (
 _P = ctypes.c_void_p
 _I = ctypes.c_int64
 _lib = None
+
+
+class GemvProblem(ctypes.Structure):
+    """Mirror of q4k_gemv_problem."""
+    _fields_ = [("w", _P), ("x", _P), ("y", _P), ("N", _I)]
 
 
 class Q4KError(RuntimeError):
@@ -44,14 +50,16 @@ def lib():
         L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
         L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
         L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+        L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
+                                              _I, _P]
         L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                                    ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
         L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
-        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv", "q4k_gemm",
-                     "q4k_moe_gemv"):
+        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
+                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_moe_gemv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -126,6 +134,29 @@ def q4k_quantize_gemv(w, N, K, x, y=None):
     _check(lib().q4k_quantize_gemv(_ptr(w), N, K, _ptr(x), M, _ptr(y), _stream(x)),
            "q4k_quantize_gemv")
     return y
+
+
+def q4k_quantize_gemv_batch(problems, K, ys=None):
+    """Several quantize-and-GEMV products with the same K and M in one launch.
+
+    `problems` is a sequence of (w, N, x) with fp32 x [M, K]; returns the list
+    of outputs y_i [M, N_i] (or fills `ys`)."""
+    import torch
+    problems = list(problems)
+    if not problems:
+        raise ValueError("q4k_quantize_gemv_batch: empty batch")
+    M = problems[0][2].shape[0]
+    if ys is None:
+        ys = [torch.empty((M, N), dtype=torch.float32, device=x.device) for _, N, x in problems]
+    arr = (GemvProblem * len(problems))()
+    for i, ((w, N, x), y) in enumerate(zip(problems, ys)):
+        _dev(w, "w"); _dev(x, "x")
+        if x.shape[0] != M:
+            raise ValueError("q4k_quantize_gemv_batch: every x must have the same M")
+        arr[i] = GemvProblem(_ptr(w), _ptr(x), _ptr(y), N)
+    _check(lib().q4k_quantize_gemv_batch(arr, len(problems), K, M, _stream(problems[0][2])),
+           "q4k_quantize_gemv_batch")
+    return ys
 
 
 def q4k_gemm(w, N, K, codes, scales, sums, y=None):

@@ -30,6 +30,7 @@ namespace q4k {
 namespace {
 
 constexpr int kMaxWaves = 16;
+constexpr int kMaxPieces = 16;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -61,25 +62,67 @@ struct WaveQ8 {
     float s[M][CPW][8];
 };
 
+// Kernel arguments.  The fused variant takes up to kMaxPieces row ranges
+// ("pieces") of one or more products with the same K and M: piece p covers
+// rows [0, N[p]) of the matrix at w[p] and writes y[p][m * ldy[p] + row]; the
+// host cuts large products into pieces of similar size, so that blockIdx.y
+// names the piece and workgroups past a short piece's rows exit at once.  The
+// other variant multiplies prepared Q8 rows by one matrix.  Every value a
+// workgroup needs is addressed from blockIdx alone: one round of scalar loads.
+template <bool FUSED> struct GemvArgs;
+template <> struct GemvArgs<true> {
+    const uint8_t *w[kMaxPieces];
+    const float *x[kMaxPieces];
+    float *y[kMaxPieces];
+    int N[kMaxPieces];
+    int ldy[kMaxPieces];
+};
+template <> struct GemvArgs<false> {
+    const uint8_t *w[1];
+    float *y[1];
+    int N[1];
+    int ldy[1];
+    const int8_t *codes;
+    const float *scales;
+    const int32_t *sums;
+};
+
 template <int M, int T, int CPW, bool FUSED>
-__global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int N,
-                                                    int nsb, const float *__restrict__ x,
-                                                    const int8_t *__restrict__ codes,
-                                                    const float *__restrict__ scales,
-                                                    const int32_t *__restrict__ sums,
-                                                    float *__restrict__ y) {
+__global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int nsb) {
     __shared__ float red[kMaxWaves][8 * T][M];
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
+    const int p = FUSED ? (int)blockIdx.y : 0;
+    const uint8_t *__restrict__ w = B.w[p];
+    float *__restrict__ y = B.y[p];
+    const int N = B.N[p];
+    const int ldy = B.ldy[p];
+    const float *__restrict__ x = nullptr;
+    const int8_t *__restrict__ codes = nullptr;
+    const float *__restrict__ scales = nullptr;
+    const int32_t *__restrict__ sums = nullptr;
+    if constexpr (FUSED) {
+        x = B.x[p];
+        asm volatile("" ::"s"(w), "s"(x), "s"(y), "s"(N), "s"(ldy), "s"(nsb));
+    } else {
+        codes = B.codes;
+        scales = B.scales;
+        sums = B.sums;
+        asm volatile("" ::"s"(w), "s"(codes), "s"(scales), "s"(sums), "s"(y), "s"(N), "s"(nsb));
+    }
+    const int wg = (int)blockIdx.x;
+    if (wg * (8 * T) >= N) return;   // past this piece's rows (whole workgroup)
+
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
+    // the launch's wave count, from the kernel arguments (as the host sizes it)
+    const int nwaves = (nsb + CPW - 1) / CPW < kMaxWaves ? (nsb + CPW - 1) / CPW : kMaxWaves;
     const int grp = lane >> 3;     // row within a tile of 8
     const LaneMap L(lane & 7);     // chunk index == sub-block owned after the swap
     const int K = nsb * 256;
     const int nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
-    const int row0 = blockIdx.x * (8 * T);
+    const int row0 = wg * (8 * T);
     WaveQ8<M, CPW> *q8 = reinterpret_cast<WaveQ8<M, CPW> *>(dyn) + wave;
 
     float acc[T][M];
@@ -207,7 +250,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
-                    acc[t][m] = fmaf(a[m], ds * (float)D - dm * s[m], acc[t][m]);
+                    acc[t][m] = fmaf(a[m], fmaf(ds, (float)D, -(dm * s[m])), acc[t][m]);
                 }
             }
         }
@@ -223,58 +266,121 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
             if (L.l == 0) red[wave][8 * t + grp][m] = v;
         }
     __syncthreads();
-    for (int i = threadIdx.x; i < 8 * T * M; i += blockDim.x) {
+    for (int i = threadIdx.x; i < 8 * T * M; i += 64 * nwaves) {
         const int r = i / M, m = i % M;
         float v = 0.0f;
         for (int wv = 0; wv < nwaves; ++wv) v += red[wv][r][m];
         const int row = row0 + r;
-        if (row < N) y[(int64_t)m * N + row] = v;
+        if (row < N) y[(int64_t)m * ldy + row] = v;
     }
 }
 
 template <int M, int T, int CPW, bool FUSED>
-hipError_t launch_mtc(const uint8_t *w, int N, int nsb, const float *x, const int8_t *codes,
-                      const float *scales, const int32_t *sums, float *y, hipStream_t stream) {
+hipError_t launch_mtc(const GemvArgs<FUSED> &B, int pieces, int nsb, hipStream_t stream) {
     const int nwaves = (nsb + CPW - 1) / CPW < kMaxWaves ? (nsb + CPW - 1) / CPW : kMaxWaves;
     const int rows_per_wg = 8 * T;
-    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
+    int tiles = 0;
+    for (int i = 0; i < pieces; ++i) {
+        const int t = (B.N[i] + rows_per_wg - 1) / rows_per_wg;
+        tiles = t > tiles ? t : tiles;
+    }
     const size_t lds = FUSED ? sizeof(WaveQ8<M, CPW>) * nwaves : 0;
-    hipLaunchKernelGGL((gemv_kernel<M, T, CPW, FUSED>), dim3(grid), dim3(64 * nwaves), lds,
-                       stream, w, N, nsb, x, codes, scales, sums, y);
+    hipLaunchKernelGGL((gemv_kernel<M, T, CPW, FUSED>), dim3(tiles, pieces),
+                       dim3(64 * nwaves), lds, stream, B, nsb);
     return hipGetLastError();
 }
 
+// One call's products as the host received them.
+struct Req {
+    const GemvProblem *probs;   // fused: `count` products
+    int count;
+    const uint8_t *w;           // plain: one matrix and its Q8 rows
+    float *y;
+    int N;
+    const int8_t *codes;
+    const float *scales;
+    const int32_t *sums;
+    int64_t rows;               // sum of the products' N
+};
+
+// Cut the products into pieces of at most C rows, C being one of the
+// products' own row counts (rounded up to whole workgroups): the choice that
+// launches the fewest workgroups (grid = pieces x tiles of C) with at most
+// kMaxPieces pieces.  E.g. N = {4096, 1024, 1024} becomes six pieces of 1024.
+int build_args(const Req &r, int rows_per_wg, int nsb, GemvArgs<true> &B) {
+    auto tiles = [&](int64_t n) { return (n + rows_per_wg - 1) / rows_per_wg; };
+    int64_t C = 0, best = -1;
+    for (int c = 0; c < r.count; ++c) {
+        const int64_t cand = tiles(r.probs[c].N) * rows_per_wg;
+        int64_t pieces = 0;
+        for (int i = 0; i < r.count; ++i) pieces += (r.probs[i].N + cand - 1) / cand;
+        const int64_t cost = pieces * (cand / rows_per_wg);
+        if (pieces <= kMaxPieces && (best < 0 || cost < best || (cost == best && cand > C))) {
+            best = cost;
+            C = cand;
+        }
+    }
+    const int64_t row_bytes = (int64_t)nsb * 144;
+    int n = 0;
+    for (int i = 0; i < r.count; ++i) {
+        const GemvProblem &q = r.probs[i];
+        for (int64_t r0 = 0; r0 < q.N; r0 += C, ++n) {
+            B.w[n] = static_cast<const uint8_t *>(q.w) + r0 * row_bytes;
+            B.x[n] = q.x;
+            B.y[n] = q.y + r0;
+            B.N[n] = (int)(q.N - r0 < C ? q.N - r0 : C);
+            B.ldy[n] = (int)q.N;
+        }
+    }
+    return n;
+}
+
+int build_args(const Req &r, int, int, GemvArgs<false> &B) {
+    B.w[0] = r.w;
+    B.y[0] = r.y;
+    B.N[0] = r.N;
+    B.ldy[0] = r.N;
+    B.codes = r.codes;
+    B.scales = r.scales;
+    B.sums = r.sums;
+    return 1;
+}
+
+template <int M, int T, int CPW, bool FUSED>
+hipError_t go(const Req &r, int nsb, hipStream_t stream) {
+    GemvArgs<FUSED> B = {};
+    const int pieces = build_args(r, 8 * T, nsb, B);
+    return launch_mtc<M, T, CPW, FUSED>(B, pieces, nsb, stream);
+}
+
 template <int M, bool FUSED>
-hipError_t launch_m(const uint8_t *w, int N, int nsb, const float *x, const int8_t *codes,
-                    const float *scales, const int32_t *sums, float *y, hipStream_t stream) {
+hipError_t launch_m(const Req &r, int nsb, hipStream_t stream) {
     // Columns per wave: as few as the 16-wave workgroup allows; two row tiles
-    // per workgroup once there are enough rows to fill the chip.
-    const bool t2 = N >= 4096 && M <= 2;
-    if (nsb <= 16)
-        return t2 ? launch_mtc<M, 2, 1, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
-                  : launch_mtc<M, 1, 1, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
-    if (nsb <= 32)
-        return t2 ? launch_mtc<M, 2, 2, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
-                  : launch_mtc<M, 1, 2, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
-    return t2 ? launch_mtc<M, 2, 3, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream)
-              : launch_mtc<M, 1, 3, FUSED>(w, N, nsb, x, codes, scales, sums, y, stream);
+    // per workgroup once the launch has enough rows to fill the chip.
+    if constexpr (M <= 2) {
+        if (r.rows >= 4096) {
+            if (nsb <= 16) return go<M, 2, 1, FUSED>(r, nsb, stream);
+            if (nsb <= 32) return go<M, 2, 2, FUSED>(r, nsb, stream);
+            return go<M, 2, 3, FUSED>(r, nsb, stream);
+        }
+    }
+    if (nsb <= 16) return go<M, 1, 1, FUSED>(r, nsb, stream);
+    if (nsb <= 32) return go<M, 1, 2, FUSED>(r, nsb, stream);
+    return go<M, 1, 3, FUSED>(r, nsb, stream);
 }
 
 template <bool FUSED>
-hipError_t dispatch(const uint8_t *w, int64_t N, int64_t K, const float *x, const int8_t *codes,
-                    const float *scales, const int32_t *sums, int64_t M, float *y,
-                    hipStream_t stream) {
+hipError_t dispatch(const Req &r, int64_t K, int64_t M, hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    const int n = (int)N;
     switch (M) {
-    case 1: return launch_m<1, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 2: return launch_m<2, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 3: return launch_m<3, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 4: return launch_m<4, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 5: return launch_m<5, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 6: return launch_m<6, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 7: return launch_m<7, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
-    case 8: return launch_m<8, FUSED>(w, n, nsb, x, codes, scales, sums, y, stream);
+    case 1: return launch_m<1, FUSED>(r, nsb, stream);
+    case 2: return launch_m<2, FUSED>(r, nsb, stream);
+    case 3: return launch_m<3, FUSED>(r, nsb, stream);
+    case 4: return launch_m<4, FUSED>(r, nsb, stream);
+    case 5: return launch_m<5, FUSED>(r, nsb, stream);
+    case 6: return launch_m<6, FUSED>(r, nsb, stream);
+    case 7: return launch_m<7, FUSED>(r, nsb, stream);
+    case 8: return launch_m<8, FUSED>(r, nsb, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -284,12 +390,30 @@ hipError_t dispatch(const uint8_t *w, int64_t N, int64_t K, const float *x, cons
 hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
-    return dispatch<false>(w, N, K, nullptr, codes, scales, sums, M, y, stream);
+    Req r = {};
+    r.w = w;
+    r.y = y;
+    r.N = (int)N;
+    r.codes = codes;
+    r.scales = scales;
+    r.sums = sums;
+    r.rows = N;
+    return dispatch<false>(r, K, M, stream);
+}
+
+hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                      int64_t M, hipStream_t stream) {
+    Req r = {};
+    r.probs = probs;
+    r.count = count;
+    for (int i = 0; i < count; ++i) r.rows += probs[i].N;
+    return dispatch<true>(r, K, M, stream);
 }
 
 hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                 int64_t M, float *y, hipStream_t stream) {
-    return dispatch<true>(w, N, K, x, nullptr, nullptr, nullptr, M, y, stream);
+    const GemvProblem p = {w, x, y, N};
+    return launch_quantize_gemv_batch(&p, 1, K, M, stream);
 }
 
 }  // namespace q4k

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(1024) void moe_gemv_kernel(
                 for (int m = 0; m < kChunk; ++m) {
                     if (m < mc) {   // wave-uniform
                         const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
-                        acc[t][m] = fmaf(a[m], ds * (float)D - dm * (float)s[m], acc[t][m]);
+                        acc[t][m] = fmaf(a[m], fmaf(ds, (float)D, -(dm * (float)s[m])), acc[t][m]);
                     }
                 }
             }

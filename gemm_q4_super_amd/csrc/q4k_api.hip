@@ -62,6 +62,23 @@ int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                                               static_cast<hipStream_t>(stream)));
 }
 
+int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K,
+                            int64_t M, void *stream) {
+    if (!problems) return Q4K_EINVAL;
+    if (count < 1 || count > q4k::kMaxGemvBatch) return Q4K_ESHAPE;
+    if (K < q4k::kQK || K % q4k::kQK != 0 || K > kMaxDim || M < 1 || M > 8 ||
+        M * K > q4k::kFusedMaxMK)
+        return Q4K_ESHAPE;
+    for (int i = 0; i < count; ++i) {
+        const q4k_gemv_problem &p = problems[i];
+        if (!p.w || !p.x || !p.y) return Q4K_EINVAL;
+        if (p.N < 1 || p.N > kMaxDim) return Q4K_ESHAPE;
+        if (!aligned(p.w, 16) || !aligned(p.x, 16) || !aligned(p.y, 4)) return Q4K_EALIGN;
+    }
+    return from_hip(q4k::launch_quantize_gemv_batch(problems, count, K, M,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
              const int32_t *sums, int64_t M, float *y, void *stream) {
     int st = check_matrix_args(w, N, K, codes, scales, sums, M, y);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/q4k.h"
+
 namespace q4k {
 
 constexpr int kQK = 256;       // weights per Q4_K super-block
@@ -27,6 +29,10 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
 constexpr int64_t kFusedMaxMK = 32768;
 hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                 int64_t M, float *y, hipStream_t stream);
+using GemvProblem = q4k_gemv_problem;
+constexpr int kMaxGemvBatch = 8;
+hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                      int64_t M, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,

@@ -98,6 +98,24 @@ int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
 int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
                       int64_t M, float *y, void *stream);
 
+/* One product of a batch for q4k_quantize_gemv_batch. */
+typedef struct q4k_gemv_problem {
+    const void *w;     /* device Q4_K weights, N rows x (K/256)*144 bytes, 16-byte aligned */
+    const float *x;    /* device fp32 activations [M][K], 16-byte aligned                */
+    float *y;          /* device fp32 output [M][N]                                      */
+    int64_t N;         /* rows of this matrix, >= 1                                      */
+} q4k_gemv_problem;
+
+/* Several independent quantize-and-GEMV products with the same K and M in one
+ * launch (e.g. the q, k and v projections of a decode step, or gate and up):
+ * for every problem i, y_i = Q8(x_i) * W_i^T, each bit-identical to
+ * q4k_quantize_gemv on that problem alone.  `problems` is a host array of
+ * `count` entries (1 <= count <= 8), read during the call.  The products must
+ * not write overlapping outputs.  Limits and checks as for q4k_quantize_gemv,
+ * applied to every problem. */
+int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K,
+                            int64_t M, void *stream);
+
 /* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (section 3's
  * batched prefill over all prompt tokens).  Compute-bound: Q4_K tiles are
  * staged through LDS and the per-32 sub-block integer dot products run on the

@@ -77,6 +77,28 @@ def test_quantize_gemv_argument_checks(L):
     assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
 
 
+def test_quantize_gemv_batch_argument_checks(L):
+    f = L.q4k_quantize_gemv_batch
+    P = q4k._lib.GemvProblem
+
+    def call(probs, K=512, M=1):
+        arr = (P * max(len(probs), 1))(*[P(*p) for p in probs])
+        return f(arr, len(probs), K, M, None)
+    good = (A, A, A, 16)
+    assert f(None, 1, 512, 1, None) == EINVAL
+    assert call([]) == ESHAPE
+    assert call([good] * 9) == ESHAPE
+    assert call([good], K=500) == ESHAPE
+    assert call([good], M=9) == ESHAPE
+    assert call([good], K=9728, M=4) == ESHAPE
+    assert call([good, (A, A, A, 0)]) == ESHAPE
+    assert call([good, (None, A, A, 16)]) == EINVAL
+    assert call([good, (A, A, None, 16)]) == EINVAL
+    assert call([good, (A + 4, A, A, 16)]) == EALIGN
+    assert call([good, (A, A + 4, A, 16)]) == EALIGN
+    assert call([good, (A, A, A + 2, 16)]) == EALIGN
+
+
 def test_quantize_argument_checks(L):
     f = L.q4k_quantize_act
     assert f(None, 1, 32, None, A, A, A, None) == EINVAL

@@ -215,3 +215,65 @@ def test_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     rc, rs, _ = oracle_lib.quantize_act(x)
     ref = oracle_lib.matvec(w, N, K, rc, rs, rows=rows)
     assert_close(y1 if rows is None else y1[:, rows], ref, "quantize_gemv N=%d K=%d M=%d" % (N, K, M))
+
+
+# ------------------------------------------- batched quantize + GEMV ----
+
+_BATCHES = {
+    "qkv": (2560, 1, [4096, 1024, 1024]),
+    "gate_up": (2560, 1, [9728, 9728]),
+    "qkv_m2": (2560, 2, [4096, 1024, 1024]),
+    "ragged_m3": (512, 3, [1, 37, 300, 4097, 8, 9]),
+    "eight_m1": (1024, 1, [5, 17, 64, 129, 1000, 2048, 3, 700]),
+    "eight_m2_t2": (768, 2, [1000, 1000, 1000, 1000, 70, 1, 33, 2]),
+    "m8": (4096, 8, [300, 257]),
+    "single": (9728, 1, [2560]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_BATCHES))
+def test_quantize_gemv_batch_bit_identical_to_single(q4k, oracle_lib, name):
+    """Each product of a batched launch equals q4k_quantize_gemv on it alone
+    bit for bit (also where the batch's size picks a different row tiling),
+    and the oracle within tolerance."""
+    import torch
+    K, M, Ns = _BATCHES[name]
+    ws = [qi.make_q4k_bytes(N, K, 9100 + i + N) for i, N in enumerate(Ns)]
+    xs = [qi.make_act(M, K, 9300 + i + M) for i in range(len(Ns))]
+    xs[0][0, :32] = 0.0
+    wd = [to_dev(w) for w in ws]
+    xd = [to_dev(x) for x in xs]
+    yb = q4k.q4k_quantize_gemv_batch([(w, N, x) for w, N, x in zip(wd, Ns, xd)], K)
+    ys = [q4k.q4k_quantize_gemv(w, N, K, x) for w, N, x in zip(wd, Ns, xd)]
+    torch.cuda.synchronize()
+    for i, N in enumerate(Ns):
+        a, b = yb[i].cpu().numpy(), ys[i].cpu().numpy()
+        assert a.shape == (M, N)
+        assert (a.view(np.uint32) == b.view(np.uint32)).all(), "problem %d" % i
+        rows = None if N <= 300 else np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 24)])
+        rc, rs, _ = oracle_lib.quantize_act(xs[i])
+        ref = oracle_lib.matvec(ws[i], N, K, rc, rs, rows=rows)
+        assert_close(a if rows is None else a[:, rows], ref, "batch %s problem %d" % (name, i))
+
+
+def test_quantize_gemv_batch_leaves_other_memory_untouched(q4k):
+    """Outputs are written only inside each [M, N_i] block: guard words around
+    every output survive."""
+    import torch
+    K, M, Ns = 512, 2, [3, 40, 9]
+    pad = 64
+    buf = torch.full((sum(M * N + 2 * pad for N in Ns),), 12345.0, device="cuda")
+    probs, views, off = [], [], 0
+    for i, N in enumerate(Ns):
+        off += pad
+        y = buf[off:off + M * N].view(M, N)
+        views.append((off, M * N))
+        off += M * N + pad
+        probs.append((to_dev(qi.make_q4k_bytes(N, K, 50 + i)), N, to_dev(qi.make_act(M, K, 60 + i))))
+    q4k.q4k_quantize_gemv_batch(probs, K, ys=[buf[o:o + n].view(M, -1) for o, n in views])
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    mask = np.ones(h.shape, bool)
+    for o, n in views:
+        mask[o:o + n] = False
+    assert (h[mask] == 12345.0).all()
