@@ -29,9 +29,12 @@ def hipcc() -> str:
 
 
 # Packed fp32 VALU ops are kept out of generated code on purpose; the fp32
-# epilogues are written as scalar fma.
+# epilogues are written as scalar fma.  The leading 16 dwords of every
+# kernel's arguments are preloaded into scalar registers at wave launch (the
+# code keeps a prologue that loads them for firmware without the feature).
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-I" + os.path.join(ROOT, "include")]
 
 

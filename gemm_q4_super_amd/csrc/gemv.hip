@@ -1,4 +1,8 @@
-// Decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T, W in Q4_K, M = 1..8.
+// Plain GEMV on prepared Q8 rows (q4k_gemv): y[M][N] = Q8(x)[M][K] * W^T, W in
+// Q4_K, M = 1..8.  Where the Q8 rows fit in LDS (M*K <= 32768) the call runs
+// the streaming GEMV of stream_gemv.h (the same kernel as the fused
+// q4k_quantize_gemv, so the two are bit-identical); wider rows run the kernel
+// below, which reads the activation straight from memory.
 //
 // Batch-1 decode streams every weight byte once and is bound by memory
 // bandwidth ("genie-ai-runtime ...", section 2, the decode ceiling), so this
@@ -19,99 +23,36 @@
 //    trip covers them.  The activation chunk of a column is reused over the T
 //    row tiles and all 8 groups.  Per-lane sums reduce over the 8 lanes by
 //    DPP, then over the W waves through LDS in a fixed order (deterministic).
-//  * Fused variant (q4k_quantize_gemv): the activation arrives as fp32 and
-//    each wave quantizes the Q8 blocks of its own columns into LDS (same
-//    arithmetic as q4k_quantize_act, so the codes are bit-identical) while its
-//    weight loads are in flight -- one launch instead of two per call.
-#include "q4k_device.h"
-#include "q4k_internal.h"
+//  * The fused quantize + GEMV (q4k_quantize_gemv, ..._batch) lives in
+//    qgemv.hip; this kernel takes prepared Q8 rows (q4k_quantize_act).
+#include "stream_gemv.h"
 
 namespace q4k {
 namespace {
 
 constexpr int kMaxWaves = 16;
-constexpr int kMaxPieces = 16;
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float group8_max(float v) {
-    v = fmaxf(v, dpp_f<kQuadSwap1>(v));
-    v = fmaxf(v, dpp_f<kQuadSwap2>(v));
-    v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
-    return v;
-}
-__device__ __forceinline__ int group8_isum(int v) {
-    v += dpp_i<kQuadSwap1>(v);
-    v += dpp_i<kQuadSwap2>(v);
-    v += dpp_i<kRowHalfMirror>(v);
-    return v;
-}
-// Branch-free: an all-zero block (d == 0) divides by 1 and selects 0.
-__device__ __forceinline__ int quant1(float x, float d) {
-    const bool zero = d == 0.0f;
-    float r = __builtin_rintf(x / (zero ? 1.0f : d));
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return zero ? 0 : (int)r;
-}
-
-// Per-wave LDS of the fused variant: Q8 of the wave's CPW columns, M rows.
-template <int M, int CPW>
-struct WaveQ8 {
-    int8_t c[M][CPW][256];
-    float a[M][CPW][8];
-    float s[M][CPW][8];
-};
-
-// Kernel arguments.  The fused variant takes up to kMaxPieces row ranges
-// ("pieces") of one or more products with the same K and M: piece p covers
-// rows [0, N[p]) of the matrix at w[p] and writes y[p][m * ldy[p] + row]; the
-// host cuts large products into pieces of similar size, so that blockIdx.y
-// names the piece and workgroups past a short piece's rows exit at once.  The
-// other variant multiplies prepared Q8 rows by one matrix.  Every value a
-// workgroup needs is addressed from blockIdx alone: one round of scalar loads.
-template <bool FUSED> struct GemvArgs;
-template <> struct GemvArgs<true> {
-    const uint8_t *w[kMaxPieces];
-    const float *x[kMaxPieces];
-    float *y[kMaxPieces];
-    int N[kMaxPieces];
-    int ldy[kMaxPieces];
-};
-template <> struct GemvArgs<false> {
-    const uint8_t *w[1];
-    float *y[1];
-    int N[1];
-    int ldy[1];
+// Kernel arguments: one matrix and its prepared Q8 rows.
+struct GemvArgs {
+    const uint8_t *w;
+    float *y;
+    int N;
     const int8_t *codes;
     const float *scales;
     const int32_t *sums;
 };
 
-template <int M, int T, int CPW, bool FUSED>
-__global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int nsb) {
+template <int M, int T, int CPW>
+__global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs B, int nsb) {
     __shared__ float red[kMaxWaves][8 * T][M];
-    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
-    const int p = FUSED ? (int)blockIdx.y : 0;
-    const uint8_t *__restrict__ w = B.w[p];
-    float *__restrict__ y = B.y[p];
-    const int N = B.N[p];
-    const int ldy = B.ldy[p];
-    const float *__restrict__ x = nullptr;
-    const int8_t *__restrict__ codes = nullptr;
-    const float *__restrict__ scales = nullptr;
-    const int32_t *__restrict__ sums = nullptr;
-    if constexpr (FUSED) {
-        x = B.x[p];
-        asm volatile("" ::"s"(w), "s"(x), "s"(y), "s"(N), "s"(ldy), "s"(nsb));
-    } else {
-        codes = B.codes;
-        scales = B.scales;
-        sums = B.sums;
-        asm volatile("" ::"s"(w), "s"(codes), "s"(scales), "s"(sums), "s"(y), "s"(N), "s"(nsb));
-    }
-    const int wg = (int)blockIdx.x;
-    if (wg * (8 * T) >= N) return;   // past this piece's rows (whole workgroup)
+    const uint8_t *__restrict__ w = B.w;
+    float *__restrict__ y = B.y;
+    const int N = B.N;
+    const int8_t *__restrict__ codes = B.codes;
+    const float *__restrict__ scales = B.scales;
+    const int32_t *__restrict__ sums = B.sums;
+    asm volatile("" ::"s"(w), "s"(codes), "s"(scales), "s"(sums), "s"(y), "s"(N), "s"(nsb));
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -122,8 +63,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
     const int K = nsb * 256;
     const int nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
-    const int row0 = wg * (8 * T);
-    WaveQ8<M, CPW> *q8 = reinterpret_cast<WaveQ8<M, CPW> *>(dyn) + wave;
+    const int row0 = (int)blockIdx.x * (8 * T);
 
     float acc[T][M];
 #pragma unroll
@@ -133,27 +73,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
 
     // Columns [b0, b0 + CPW) of this wave; a wave with more than CPW columns
     // (K beyond 16 * CPW super-blocks) takes them in groups of CPW.
-    // Activation loads go out before the weight loads: the load counter
-    // retires in order, so data wanted first must be requested first (the
-    // quantization, or column 0's dots, then overlaps the weight stream).
-    constexpr bool kActFirst = FUSED || M * CPW * T <= 6;
+    // Activation loads go out before the weight loads where they fit the
+    // registers: the load counter retires in order, so data wanted first must
+    // be requested first (column 0's dots then overlap the weight stream).
+    constexpr bool kActFirst = M * CPW * T <= 6;
     for (int b0 = wave * CPW; b0 < nsb; b0 += nwaves * CPW) {
-        f32x4 xv[FUSED ? M : 1][FUSED ? CPW : 1];
-        i32x4 pA[kActFirst && !FUSED ? CPW : 1][M], pB[kActFirst && !FUSED ? CPW : 1][M];
-        float pa[kActFirst && !FUSED ? CPW : 1][M];
-        int ps[kActFirst && !FUSED ? CPW : 1][M];   // converted at use, after the loads
-        if constexpr (FUSED) {
-            const int blk = lane >> 3, sub = lane & 7;
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) {
-                    // clamped, branch-free: columns past nsb are never used
-                    const int b = min(b0 + c, nsb - 1);
-                    xv[m][c] = *reinterpret_cast<const f32x4 *>(x + (int64_t)m * K + 256 * b +
-                                                                32 * blk + 4 * sub);
-                }
-        } else if constexpr (kActFirst) {
+        i32x4 pA[kActFirst ? CPW : 1][M], pB[kActFirst ? CPW : 1][M];
+        float pa[kActFirst ? CPW : 1][M];
+        int ps[kActFirst ? CPW : 1][M];   // converted at use, after the loads
+        if constexpr (kActFirst) {
 #pragma unroll
             for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -185,34 +113,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
             }
         // Keep every load of the group ahead of the arithmetic below.
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FUSED) {
-            // Quantize this wave's columns: lane -> block lane/8 of the column,
-            // 4 values at 4*(lane%8) within the block.
-            const int blk = lane >> 3, sub = lane & 7;
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) {
-                    const f32x4 v = xv[m][c];
-                    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
-                                       fmaxf(fabsf(v[2]), fabsf(v[3])));
-                    amax = group8_max(amax);
-                    const float d = amax / 127.0f;
-                    const int c0 = quant1(v[0], d), c1 = quant1(v[1], d);
-                    const int c2 = quant1(v[2], d), c3 = quant1(v[3], d);
-                    *reinterpret_cast<int *>(&q8->c[m][c][32 * blk + 4 * sub]) =
-                        (c0 & 0xFF) | ((c1 & 0xFF) << 8) | ((c2 & 0xFF) << 16) |
-                        (int)((unsigned)c3 << 24);
-                    const int ssum = group8_isum(c0 + c1 + c2 + c3);
-                    if (sub == 0) {
-                        q8->a[m][c][blk] = d;
-                        q8->s[m][c][blk] = (float)ssum;
-                    }
-                }
-            // LDS written and read by this wave only: wait for the writes.
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-            __builtin_amdgcn_wave_barrier();
-        }
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
             const int b = b0 + c;
@@ -223,12 +123,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
             float s[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                if constexpr (FUSED) {
-                    cA[m] = *reinterpret_cast<const i32x4 *>(&q8->c[m][c][L.offA]);
-                    cB[m] = *reinterpret_cast<const i32x4 *>(&q8->c[m][c][L.offB]);
-                    a[m] = q8->a[m][c][L.l];
-                    s[m] = q8->s[m][c][L.l];
-                } else if constexpr (kActFirst) {
+                if constexpr (kActFirst) {
                     cA[m] = pA[c][m];
                     cB[m] = pB[c][m];
                     a[m] = pa[c][m];
@@ -254,7 +149,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
                 }
             }
         }
-        if constexpr (FUSED) __builtin_amdgcn_wave_barrier();   // LDS reuse by the next group
     }
 
     // Reduce the 8 sub-block lanes of each group, then the waves via LDS.
@@ -271,118 +165,33 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs<FUSED> B, int
         float v = 0.0f;
         for (int wv = 0; wv < nwaves; ++wv) v += red[wv][r][m];
         const int row = row0 + r;
-        if (row < N) y[(int64_t)m * ldy + row] = v;
+        if (row < N) y[(int64_t)m * N + row] = v;
     }
 }
 
-template <int M, int T, int CPW, bool FUSED>
-hipError_t launch_mtc(const GemvArgs<FUSED> &B, int pieces, int nsb, hipStream_t stream) {
+template <int M, int T, int CPW>
+hipError_t launch_mtc(const GemvArgs &B, int nsb, hipStream_t stream) {
     const int nwaves = (nsb + CPW - 1) / CPW < kMaxWaves ? (nsb + CPW - 1) / CPW : kMaxWaves;
-    const int rows_per_wg = 8 * T;
-    int tiles = 0;
-    for (int i = 0; i < pieces; ++i) {
-        const int t = (B.N[i] + rows_per_wg - 1) / rows_per_wg;
-        tiles = t > tiles ? t : tiles;
-    }
-    const size_t lds = FUSED ? sizeof(WaveQ8<M, CPW>) * nwaves : 0;
-    hipLaunchKernelGGL((gemv_kernel<M, T, CPW, FUSED>), dim3(tiles, pieces),
-                       dim3(64 * nwaves), lds, stream, B, nsb);
+    const int tiles = (B.N + 8 * T - 1) / (8 * T);
+    hipLaunchKernelGGL((gemv_kernel<M, T, CPW>), dim3(tiles), dim3(64 * nwaves), 0, stream, B,
+                       nsb);
     return hipGetLastError();
 }
 
-// One call's products as the host received them.
-struct Req {
-    const GemvProblem *probs;   // fused: `count` products
-    int count;
-    const uint8_t *w;           // plain: one matrix and its Q8 rows
-    float *y;
-    int N;
-    const int8_t *codes;
-    const float *scales;
-    const int32_t *sums;
-    int64_t rows;               // sum of the products' N
-};
-
-// Cut the products into pieces of at most C rows, C being one of the
-// products' own row counts (rounded up to whole workgroups): the choice that
-// launches the fewest workgroups (grid = pieces x tiles of C) with at most
-// kMaxPieces pieces.  E.g. N = {4096, 1024, 1024} becomes six pieces of 1024.
-int build_args(const Req &r, int rows_per_wg, int nsb, GemvArgs<true> &B) {
-    auto tiles = [&](int64_t n) { return (n + rows_per_wg - 1) / rows_per_wg; };
-    int64_t C = 0, best = -1;
-    for (int c = 0; c < r.count; ++c) {
-        const int64_t cand = tiles(r.probs[c].N) * rows_per_wg;
-        int64_t pieces = 0;
-        for (int i = 0; i < r.count; ++i) pieces += (r.probs[i].N + cand - 1) / cand;
-        const int64_t cost = pieces * (cand / rows_per_wg);
-        if (pieces <= kMaxPieces && (best < 0 || cost < best || (cost == best && cand > C))) {
-            best = cost;
-            C = cand;
-        }
-    }
-    const int64_t row_bytes = (int64_t)nsb * 144;
-    int n = 0;
-    for (int i = 0; i < r.count; ++i) {
-        const GemvProblem &q = r.probs[i];
-        for (int64_t r0 = 0; r0 < q.N; r0 += C, ++n) {
-            B.w[n] = static_cast<const uint8_t *>(q.w) + r0 * row_bytes;
-            B.x[n] = q.x;
-            B.y[n] = q.y + r0;
-            B.N[n] = (int)(q.N - r0 < C ? q.N - r0 : C);
-            B.ldy[n] = (int)q.N;
-        }
-    }
-    return n;
-}
-
-int build_args(const Req &r, int, int, GemvArgs<false> &B) {
-    B.w[0] = r.w;
-    B.y[0] = r.y;
-    B.N[0] = r.N;
-    B.ldy[0] = r.N;
-    B.codes = r.codes;
-    B.scales = r.scales;
-    B.sums = r.sums;
-    return 1;
-}
-
-template <int M, int T, int CPW, bool FUSED>
-hipError_t go(const Req &r, int nsb, hipStream_t stream) {
-    GemvArgs<FUSED> B = {};
-    const int pieces = build_args(r, 8 * T, nsb, B);
-    return launch_mtc<M, T, CPW, FUSED>(B, pieces, nsb, stream);
-}
-
-template <int M, bool FUSED>
-hipError_t launch_m(const Req &r, int nsb, hipStream_t stream) {
+template <int M>
+hipError_t launch_m(const GemvArgs &B, int nsb, hipStream_t stream) {
     // Columns per wave: as few as the 16-wave workgroup allows; two row tiles
     // per workgroup once the launch has enough rows to fill the chip.
     if constexpr (M <= 2) {
-        if (r.rows >= 4096) {
-            if (nsb <= 16) return go<M, 2, 1, FUSED>(r, nsb, stream);
-            if (nsb <= 32) return go<M, 2, 2, FUSED>(r, nsb, stream);
-            return go<M, 2, 3, FUSED>(r, nsb, stream);
+        if (B.N >= 4096) {
+            if (nsb <= 16) return launch_mtc<M, 2, 1>(B, nsb, stream);
+            if (nsb <= 32) return launch_mtc<M, 2, 2>(B, nsb, stream);
+            return launch_mtc<M, 2, 3>(B, nsb, stream);
         }
     }
-    if (nsb <= 16) return go<M, 1, 1, FUSED>(r, nsb, stream);
-    if (nsb <= 32) return go<M, 1, 2, FUSED>(r, nsb, stream);
-    return go<M, 1, 3, FUSED>(r, nsb, stream);
-}
-
-template <bool FUSED>
-hipError_t dispatch(const Req &r, int64_t K, int64_t M, hipStream_t stream) {
-    const int nsb = (int)(K / kQK);
-    switch (M) {
-    case 1: return launch_m<1, FUSED>(r, nsb, stream);
-    case 2: return launch_m<2, FUSED>(r, nsb, stream);
-    case 3: return launch_m<3, FUSED>(r, nsb, stream);
-    case 4: return launch_m<4, FUSED>(r, nsb, stream);
-    case 5: return launch_m<5, FUSED>(r, nsb, stream);
-    case 6: return launch_m<6, FUSED>(r, nsb, stream);
-    case 7: return launch_m<7, FUSED>(r, nsb, stream);
-    case 8: return launch_m<8, FUSED>(r, nsb, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (nsb <= 16) return launch_mtc<M, 1, 1>(B, nsb, stream);
+    if (nsb <= 32) return launch_mtc<M, 1, 2>(B, nsb, stream);
+    return launch_mtc<M, 1, 3>(B, nsb, stream);
 }
 
 }  // namespace
@@ -390,30 +199,24 @@ hipError_t dispatch(const Req &r, int64_t K, int64_t M, hipStream_t stream) {
 hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
-    Req r = {};
-    r.w = w;
-    r.y = y;
-    r.N = (int)N;
-    r.codes = codes;
-    r.scales = scales;
-    r.sums = sums;
-    r.rows = N;
-    return dispatch<false>(r, K, M, stream);
-}
-
-hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
-                                      int64_t M, hipStream_t stream) {
-    Req r = {};
-    r.probs = probs;
-    r.count = count;
-    for (int i = 0; i < count; ++i) r.rows += probs[i].N;
-    return dispatch<true>(r, K, M, stream);
-}
-
-hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
-                                int64_t M, float *y, hipStream_t stream) {
-    const GemvProblem p = {w, x, y, N};
-    return launch_quantize_gemv_batch(&p, 1, K, M, stream);
+    if (M * K <= kFusedMaxMK) {
+        const GemvProblem p = {w, nullptr, y, N};
+        const stream::Prepared Q = {codes, scales, sums};
+        return stream::run<false>(&p, 1, K, M, Q, stream);
+    }
+    const GemvArgs B = {w, y, (int)N, codes, scales, sums};
+    const int nsb = (int)(K / kQK);
+    switch (M) {
+    case 1: return launch_m<1>(B, nsb, stream);
+    case 2: return launch_m<2>(B, nsb, stream);
+    case 3: return launch_m<3>(B, nsb, stream);
+    case 4: return launch_m<4>(B, nsb, stream);
+    case 5: return launch_m<5>(B, nsb, stream);
+    case 6: return launch_m<6>(B, nsb, stream);
+    case 7: return launch_m<7>(B, nsb, stream);
+    case 8: return launch_m<8>(B, nsb, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace q4k
