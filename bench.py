@@ -60,6 +60,24 @@ def quant_bytes(K, M=1):
     return 4 * M * K + M * K + M * (K // 32) * 8
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stream_gemv_decode_qwen3-4b_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode GEMV, as the profiler counters
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size) read them for
+    the kernel sources recorded beside them; None once those sources change."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,7 +90,28 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the small-batch and routed-expert measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 10 times (known bytes, "
+                         "to scale the HBM traffic counters of a profiler run) and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch):
+    """A plain copy of known size: COPY_BYTES read and COPY_BYTES written per
+    dispatch.  Profiler counters of this run give the scale of the same
+    counters read on the GEMV kernels."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": COPY_BYTES,
+                                           "bytes_written_per_dispatch": COPY_BYTES,
+                                           "dispatches": 10}}))
 
 
 class Decode:
@@ -453,11 +492,14 @@ def main():
         sys.exit(2)
 
     import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import gemm_q4_super_amd as q4k
     import oracle
     import q4k_inputs as qi
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     oracle.build(force=False)
     dec = Decode(torch, q4k, qi)
     parity = dec.parity(oracle)
@@ -556,9 +598,10 @@ def main():
                    "layers": LAYERS, "batch": 1,
                    "tok_per_s": round(steps / elapsed, 1),
                    "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "q4k gemv_kernel (M=1, fused Q8, batched)",
+        "roofline": {"bound": "hbm", "kernel": "q4k stream_gemv_kernel (M=1, fused Q8, batched)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (profiler counters)",
                      "mean_launch_us": round(mean_launch_s * 1e6, 3),
                      "bytes_per_launch": round(bytes_per_launch),
                      "launches_per_step": n_launch,
