@@ -20,9 +20,11 @@ constexpr int kQuadSwap1 = 0xB1;      // DPP quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;      // DPP quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141; // DPP lane i <-> 7-i within each 8 lanes
 
+// DPP move within a lane quad or an 8-lane row half: every source lane
+// exists, so no fallback value is needed.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
