@@ -24,11 +24,11 @@
 //    256 CUs: RG = 2, V = 5, one 10-row block per CU).
 //  * Every wave issues the loads of all its V*CPW super-blocks before any
 //    arithmetic: the workgroup's whole block is in flight at once.
-//  * Activation: the waves first stage the Q8 rows of all K columns in LDS,
-//    column b by wave b % W: quantizing fp32 x (same arithmetic as
-//    q4k_quantize_act, so the codes are bit-identical) or copying prepared
-//    codes.  Their loads go out before the weight loads (the load counter
-//    retires in order).
+//  * Activation: each wave stages the Q8 rows of its own S*CPW columns in LDS
+//    (quantizing fp32 x with the same arithmetic as q4k_quantize_act, so the
+//    codes are bit-identical, or copying prepared codes) and reads only those,
+//    so no workgroup barrier waits for the staging.  The activation loads go
+//    out before the weight loads (the load counter retires in order).
 //  * Each super-block's term is summed over its 8 lanes by DPP and parked in
 //    LDS; a row then adds its K/256 terms in column order.  That order does
 //    not depend on (RG, V, CPW), so single, batched, fused and prepared calls
@@ -194,7 +194,8 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
     const int K = nsb * 256;
     const int nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
-    const int col0 = (wave * S + s) * CPW;   // this lane's first column
+    const int wcol0 = wave * S * CPW;        // the wave's columns: [wcol0, wcol0 + S*CPW)
+    const int col0 = wcol0 + s * CPW;        // this lane's first column
 
     int8_t *qc = reinterpret_cast<int8_t *>(lds);                       // [M][nsb][256]
     float *qa = reinterpret_cast<float *>(lds + (size_t)M * nsb * 256);  // [M][nsb][8]
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
     // ---- activation loads (first batch of staged columns), then weights
     constexpr int QB = stage_batch<M>();
     const int blk = lane >> 3, sub = lane & 7;
-    const int ncols = (nsb - wave + nw - 1) / nw;   // staged columns of this wave
+    const int ncols = min(S * CPW, nsb - wcol0);   // the wave's live columns (>= 1)
     f32x4 xv[QB][M];
     int pc[QB][M];
     float psc[QB][M];
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
             // Wave-uniform guard: these loads precede every weight load, so the
             // waits for them stay exact.
             if (j0 + j >= ncols) break;
-            const int b = wave + (j0 + j) * nw;
+            const int b = wcol0 + j0 + j;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 if constexpr (FUSED) {
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
 #pragma unroll
         for (int j = 0; j < QB; ++j) {
             if (j0 + j >= ncols) break;   // wave-uniform
-            const int b = wave + (j0 + j) * nw;
+            const int b = wcol0 + j0 + j;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 int8_t *cm = qc + ((size_t)m * nsb + b) * 256;
@@ -296,7 +297,9 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
         stage_load(j0);
         stage_store(j0);
     }
-    __syncthreads();   // every column staged
+    // LDS written and read by this wave only: wait for its writes.
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
 
     // ---- dots: column c outer (its activation read once), row group v inner.
     // Each super-block's term is summed over its 8 lanes and parked in LDS.
