@@ -32,9 +32,12 @@ def hipcc() -> str:
 # epilogues are written as scalar fma.  The leading 16 dwords of every
 # kernel's arguments are preloaded into scalar registers at wave launch (the
 # code keeps a prologue that loads them for firmware without the feature).
+# Matrix-core results go to ordinary vector registers, where the fp32
+# epilogue reads them without copies.
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-kernarg-preload-count=16",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I" + os.path.join(ROOT, "include")]
 
 

@@ -1,56 +1,90 @@
 // Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T with W in Q4_K, any M >= 1.
 //
 // Prefill is compute-bound ("genie-ai-runtime ...", section 3: batched
-// layer-major prefill, Path E tensor-core kernel), so the sub-block integer dot
-// products run on the matrix cores.  With x^ = a*c (Q8) and
+// layer-major prefill, Path E tensor-core kernel), so the contraction runs on
+// the matrix cores.  With x^ = a*c (Q8: one fp32 scale a per 32 codes c) and
 // w = d*sc[j]*q - dmin*mn[j] (Q4_K), one output is
 //
-//   y[m][n] = sum_{b,j} a[m,b,j] * (d*sc)[n,b,j] * D[m,n,b,j]
-//           - sum_{b,j} (a*S)[m,b,j] * (dmin*mn)[n,b,j]
+//   y[m][n] = sum_b d[n,b] * sum_{k in b} (sc*q)[n,k] * x^[m,k]
+//           - sum_{b,j} (dmin*mn)[n,b,j] * (a*S)[m,b,j]
 //
-// with D = sum_{i<32} q*c the exact integer dot of one 32-element sub-block and
-// S the activation block's code sum.
+// with S the code sum of one activation block.
 //
-//  * D: one v_mfma_i32_32x32x32_i8 per sub-block and 32 x 32 tile: activation
-//    codes (A operand, rows m) against nibble-expanded int8 quants (B operand,
-//    columns n), both read from LDS.  Bit-exact.
-//  * First sum: fp32 epilogue per sub-block, acc += float(D) * (a * d*sc).
-//    Activation and weight scales both change every 32 elements of K, so this
-//    costs three VALU operations per output and sub-block: the binding unit.
-//  * Second sum (the min term): a contraction over K/32 of fp32 factors, on the
-//    bf16 matrix cores with each factor split into two bf16 parts (16
-//    significant bits), accumulated over all of K and subtracted at the end.
-//  * Workgroup tile BM x BN (one wave per 32 x 32 sub-tile), chosen per shape
-//    so that the launch has enough workgroups for 256 CUs.  LDS is
-//    double-buffered: the global loads of super-block b+1 are in flight while
-//    b is computed, then expanded into the other buffer; one barrier per
-//    super-block.
-//  * Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs,
-//    so all M tiles of one weight column-block are placed on one XCD and run
-//    together, sharing that XCD's L2 for the weight rows.
+// Both per-32-element scales sit inside the matrix-core operands, so the
+// only vector-ALU work per output is one fma per super-block:
+//  * weight operand (B, columns n): the integer sc*q <= 945, exact in fp16, made
+//    from the nibbles with one byte permute and one packed fp16 fma per pair
+//    ((1024 + q)*sc - 1024*sc, fused, so exact);
+//  * activation operand (A, rows m): x^ scaled by a power of two 2^-e per
+//    activation row and super-block (e from the largest block scale, which
+//    keeps every value in fp16 range), split into two fp16 parts hi + lo
+//    with 22 significant bits: hi = fp16(c*ah) and lo = fp16((c*ah - hi) +
+//    c*al) where a*2^-e = ah + al; c*ah - hi is exact in fp16 (the error of
+//    an fp16 product), so hi + lo = a*2^-e*c to about 2^-21;
+//  * sc*q*hi and sc*q*lo products are exact in fp32; each super-block's sum
+//    accumulates over 16 v_mfma_f32_32x32x16_f16 per 32x32 tile, then
+//    acc += (d * 2^e) * tmp;
+//  * min term: bf16 matrix cores with both fp32 factors split into two bf16
+//    parts (16 significant bits), accumulated straight into acc.
+// Activation scales make an int8 contraction cost three vector operations
+// per output and 32 elements (convert, scale product, fma); on gfx950 those
+// do not overlap with the matrix cores, which is why this path spends
+// twice the fp16 matrix work instead.
+//
+// Staging: a quarter super-block (64 elements of K: two sub-blocks, which
+// share one 32-byte group of quant bytes) per step, double-buffered in LDS.
+// The waves are specialised: on each SIMD one wave only reads operands from
+// LDS and runs the matrix-core ops, and one only loads raw blocks from
+// global memory and converts them into the other LDS buffer (raw loads two
+// steps ahead, two register sets).  A wave that mixes both stalls its vector
+// ops behind its own matrix ops, while two waves on one SIMD overlap them.
+// One barrier per step.  Workgroup tile (64*WVN) x (32*TM*WVM), one
+// matrix-core wave per 64 x 32*TM outputs.  Tile order is XCD-aware: all M
+// tiles of one weight column-block run on one XCD, sharing its L2.
+#include <type_traits>
+
 #include "q4k_internal.h"
 
 namespace q4k {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int ROW = 256 + 16;         // padded LDS row of 256 int8 (conflict-free 16-B reads)
 constexpr int NXCD = 8;
+constexpr int TN = 2;        // 32-row weight tiles per wave
+constexpr int ASTR = 72;     // fp16 per weight row and step: [kh 2][sub 2][lh 2][8] + 8 pad
+constexpr int BSTR = 136;    // fp16 per activation row and step: [lh 2][sub 2][kh 2][hi/lo 2][8] + 8 pad
 
-template <int BM, int BN>
-struct __attribute__((aligned(16))) Buf {
-    int8_t xq[BM][ROW];               // activation codes
-    int8_t wq[BN][ROW];               // weight quants 0..15
-    float as[8][BM];                  // activation scale a[m][j]
-    float ws[8][BN];                  // d * sc[j]
-    unsigned short ph[2][BM][8];      // a*S split hi / lo (bf16 bits)
-    unsigned short qh[2][BN][8];      // dmin*mn split hi / lo (bf16 bits)
+template <int WN, int WM>
+struct __attribute__((aligned(16))) Lds {
+    _Float16 aw[2][WN][ASTR];        // sc*q of a step's two sub-blocks
+    _Float16 bx[2][WM][BSTR];        // x^ * 2^-e as hi, lo
+    float dn[2][WN];                 // d of the super-block (by super-block parity)
+    float es[2][WM];                 // 2^e of the activation row's super-block
+    unsigned short qh[2][2][WN][8];  // -(dmin*mn) split hi / lo (bf16 bits)
+    unsigned short ph[2][2][WM][8];  // a*S split hi / lo (bf16 bits)
+};
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int WVN, int WVM, int TM>
+struct Cfg {
+    static constexpr int WN = 32 * TN * WVN;
+    static constexpr int WM = 32 * TM * WVM;
+    static constexpr int NC = WVN * WVM;           // matrix-core waves (as many converting waves)
+    static constexpr int P = 64 * NC;              // converting lanes
+    static constexpr int T = 2 * P;
+    static constexpr int CA = 2 * WN;              // 16-byte quant chunks per step
+    static constexpr int CB = 2 * WM;              // 32-code activation blocks per step
+    static constexpr int NA = (CA + P - 1) / P;
+    static constexpr int NB = (CB + P - 1) / P;
 };
 
 __device__ __forceinline__ float half_lo(unsigned v) {
@@ -65,222 +99,415 @@ __device__ __forceinline__ void split_bf16(float v, unsigned short &hi, unsigned
     hi = (unsigned short)(b >> 16);
     lo = (unsigned short)(__float_as_uint(v - __uint_as_float(b & 0xFFFF0000u)) >> 16);
 }
+// Two fp16 of the integers 1024 + (byte 0, byte 1) or (byte 2, byte 3) of v
+// (0x64 is the high byte of fp16 1024, whose unit in the last place is 1).
+__device__ __forceinline__ half2 bias_pair_lo(unsigned v) {
+    return __builtin_bit_cast(half2, __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u));
+}
+__device__ __forceinline__ half2 bias_pair_hi(unsigned v) {
+    return __builtin_bit_cast(half2, __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u));
+}
+__device__ __forceinline__ half8 cat4(half2 a, half2 b, half2 c, half2 d) {
+    return (half8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+// 6-bit scale (or min, with hi = true) of sub-block j from the header dwords.
+template <int J>
+__device__ __forceinline__ unsigned scale6(const u32x4 &h, bool min) {
+    const unsigned lo = min ? h.z : h.y;
+    if (J < 4) return (lo >> (8 * J)) & 63u;
+    const int sh = 8 * (J - 4);
+    return ((h.w >> (sh + (min ? 4 : 0))) & 15u) | (((lo >> (sh + 6)) & 3u) << 4);
+}
 
-template <int BM, int BN>
-struct Cfg {
-    static constexpr int WAVES = (BM / 32) * (BN / 32);
-    static constexpr int T = 64 * WAVES;
-    static constexpr int WCH = 8 * BN;            // 16-B quant chunks of weights per super-block
-    static constexpr int XCH = 16 * BM;           // 16-B chunks of activation codes
-    static constexpr int SE = 8 * BM;             // activation scale entries
-    static constexpr int NW = (WCH + T - 1) / T;
-    static constexpr int NX = (XCH + T - 1) / T;
-    static constexpr int NS = (SE + T - 1) / T;
-};
-
-template <int BM, int BN>
-struct Regs {
-    u32x4 hd;                         // header of weight row tid (tid < BN)
-    u32x4 wc[Cfg<BM, BN>::NW];
-    i32x4 xc[Cfg<BM, BN>::NX];
-    float a[Cfg<BM, BN>::NS];
-    int s[Cfg<BM, BN>::NS];
-};
-
-template <int BM, int BN>
-__global__ __launch_bounds__((64 * (BM / 32) * (BN / 32))) void gemm_i8_kernel(
+template <int WVN, int WVM, int TM>
+__global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
     const uint8_t *__restrict__ w, int N, int nsb, const int8_t *__restrict__ codes,
     const float *__restrict__ scales, const int32_t *__restrict__ sums, int M,
-    float *__restrict__ y) {
-    using C = Cfg<BM, BN>;
-    __shared__ Buf<BM, BN> buf[2];
+    float *__restrict__ y, int splits) {
+    using C = Cfg<WVN, WVM, TM>;
+    constexpr int WN = C::WN, WM = C::WM, P = C::P;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
 
-    // XCD-aware tile of this workgroup.
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
+    // XCD-aware tile and K range of this workgroup: the M tiles and K parts
+    // of one weight column-block run on one XCD.
+    const int tiles_m = (M + WM - 1) / WM;
+    const int tiles_n = (N + WN - 1) / WN;
     const int xcd = blockIdx.x % NXCD, pos = blockIdx.x / NXCD;
-    const int nt = (pos / tiles_m) * NXCD + xcd, mt = pos % tiles_m;
+    const int per = tiles_m * splits;
+    const int nt = (pos / per) * NXCD + xcd, mt = (pos % per) / splits, sp = pos % splits;
     if (nt >= tiles_n) return;   // the whole workgroup exits together, before any barrier
-    const int m0 = mt * BM, n0 = nt * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    constexpr int WN = BN / 32;
-    const int wm = wave / WN, wn = wave % WN;
+    const int n0 = nt * WN, m0 = mt * WM;
+    const int sb0 = (int)((int64_t)nsb * sp / splits);
+    const int nl = (int)((int64_t)nsb * (sp + 1) / splits) - sb0;   // >= 1 (splits <= nsb)
     const int K = nsb * 256, nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
+    const int tid = threadIdx.x;
+
+    if (tid >= P) {
+        // ---------------- converting waves ----------------
+        const int p = tid - P;
+        // Raw loads.  Rows past N or M read row N-1 / M-1 and steps past the
+        // end of the K range read its last super-block (branch-free loads):
+        // they only feed outputs or buffers that are never used.
+        struct Step {                 // one step: quant bytes, activation codes
+            u32x4 q[C::NA];
+            i32x4 c0[C::NB], c1[C::NB];
+        };
+        struct Block {                // one super-block: headers, block scales and sums
+            u32x4 h[C::NA];
+            float a[C::NB][8];
+            int s[C::NB][8];
+        };
+        Step S0, S1;
+        Block cur, nxt;
+
+        auto load = [&](auto setc, auto gc, int b) {
+            constexpr int g = decltype(gc)::value;
+            Step &R = decltype(setc)::value ? S1 : S0;
+            b = sb0 + min(b, nl - 1);
+#pragma unroll
+            for (int i = 0; i < C::NA; ++i) {
+                const int e = min(p + i * P, C::CA - 1);
+                const int row = min(n0 + (e >> 1), N - 1);
+                const uint8_t *src = w + (int64_t)row * row_bytes + (int64_t)b * 144;
+                R.q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
+                if (g == 0) nxt.h[i] = *reinterpret_cast<const u32x4 *>(src);
+            }
+#pragma unroll
+            for (int i = 0; i < C::NB; ++i) {
+                const int e = min(p + i * P, C::CB - 1);
+                const int row = min(m0 + (e >> 1), M - 1);
+                const int8_t *src = codes + (int64_t)row * K + 256 * b + 32 * (2 * g + (e & 1));
+                R.c0[i] = *reinterpret_cast<const i32x4 *>(src);
+                R.c1[i] = *reinterpret_cast<const i32x4 *>(src + 16);
+                if (g == 0) {
+                    const int64_t o = (int64_t)row * nblk + 8 * b;
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(scales + o);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(scales + o + 4);
+                    const i32x4 s0 = *reinterpret_cast<const i32x4 *>(sums + o);
+                    const i32x4 s1 = *reinterpret_cast<const i32x4 *>(sums + o + 4);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        nxt.a[i][k] = a0[k];
+                        nxt.a[i][4 + k] = a1[k];
+                        nxt.s[i][k] = s0[k];
+                        nxt.s[i][4 + k] = s1[k];
+                    }
+                }
+            }
+        };
+
+        // Step g of a super-block (raw step in a register set, super-block data
+        // in B) -> LDS buffer F and super-block parity Q.  The weight quants
+        // become fp16 sc*q (and, on the first step, d and the min factors are
+        // written); the activation codes become fp16 hi, lo.  Lanes that share
+        // a row write identical header values.
+        auto convert = [&](auto setc, auto gc, auto bufc, const Block &B, int Q) {
+            constexpr int g = decltype(gc)::value;
+            constexpr int F = decltype(bufc)::value;
+            const Step &R = decltype(setc)::value ? S1 : S0;
+#pragma unroll
+            for (int i = 0; i < C::NA; ++i) {
+                const int e = p + i * P;
+                if (C::CA % P != 0 && e >= C::CA) continue;   // (no branch when the chunks tile the lanes)
+                const int row = e >> 1, c = e & 1;
+                const u32x4 h = B.h[i], q = R.q[i];
+                // low nibbles: sub-block 2g, high nibbles: sub-block 2g+1; byte t
+                // of the chunk is element 16c + t of both
+                const float sc0 = (float)scale6<2 * g>(h, false), sc1 = (float)scale6<2 * g + 1>(h, false);
+                const half2 sv0 = {(_Float16)sc0, (_Float16)sc0};
+                const half2 bv0 = {(_Float16)(-1024.0f * sc0), (_Float16)(-1024.0f * sc0)};
+                const half2 sv1 = {(_Float16)sc1, (_Float16)sc1};
+                const half2 bv1 = {(_Float16)(-1024.0f * sc1), (_Float16)(-1024.0f * sc1)};
+                u32x4 lo, hi;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    lo[k] = q[k] & 0x0F0F0F0Fu;
+                    hi[k] = (q[k] >> 4) & 0x0F0F0F0Fu;
+                }
+                auto conv = [&](unsigned v0, unsigned v1, half2 sv, half2 bv) {
+                    return cat4(__builtin_elementwise_fma(bias_pair_lo(v0), sv, bv),
+                                __builtin_elementwise_fma(bias_pair_hi(v0), sv, bv),
+                                __builtin_elementwise_fma(bias_pair_lo(v1), sv, bv),
+                                __builtin_elementwise_fma(bias_pair_hi(v1), sv, bv));
+                };
+                // kh = c; the two lanes of a row land 16 banks apart (no conflict)
+                _Float16 *dst = &L.aw[F][row][32 * c];
+                *reinterpret_cast<half8 *>(dst + 0) = conv(lo.x, lo.y, sv0, bv0);
+                *reinterpret_cast<half8 *>(dst + 8) = conv(lo.z, lo.w, sv0, bv0);
+                *reinterpret_cast<half8 *>(dst + 16) = conv(hi.x, hi.y, sv1, bv1);
+                *reinterpret_cast<half8 *>(dst + 24) = conv(hi.z, hi.w, sv1, bv1);
+                if (g == 0) {
+                    L.dn[Q][row] = half_lo(h.x);
+                    const float dmin = half_hi(h.x);
+                    // part c of the bf16 split: c = 0 the truncated high half, c = 1 the rest
+                    auto part = [&](unsigned mn) -> unsigned {
+                        const float v = -dmin * (float)mn;
+                        const unsigned bits = __float_as_uint(v);
+                        const float r = v - __uint_as_float(bits & 0xFFFF0000u);
+                        return (c ? __float_as_uint(r) : bits) >> 16;
+                    };
+                    u32x4 pv;
+                    pv[0] = part(scale6<0>(h, true)) | (part(scale6<1>(h, true)) << 16);
+                    pv[1] = part(scale6<2>(h, true)) | (part(scale6<3>(h, true)) << 16);
+                    pv[2] = part(scale6<4>(h, true)) | (part(scale6<5>(h, true)) << 16);
+                    pv[3] = part(scale6<6>(h, true)) | (part(scale6<7>(h, true)) << 16);
+                    *reinterpret_cast<u32x4 *>(&L.qh[Q][c][row][0]) = pv;
+                }
+            }
+            const half2 m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+            for (int i = 0; i < C::NB; ++i) {
+                const int e = p + i * P;
+                if (C::CB % P != 0 && e >= C::CB) continue;
+                const int row = e >> 1, jb = e & 1;
+                // power-of-two scaling of the row's super-block: largest scale in [1, 2)
+                float amax = B.a[i][0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k) amax = fmaxf(amax, B.a[i][k]);
+                const int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 : 0;
+                // block 2g + jb's scale and sum, as bit selects (an indexed read
+                // would go to scratch)
+                const unsigned msk = 0u - (unsigned)jb;
+                const float a = __uint_as_float((__float_as_uint(B.a[i][2 * g]) & ~msk) |
+                                                (__float_as_uint(B.a[i][2 * g + 1]) & msk));
+                const int sj = (B.s[i][2 * g] & (int)~msk) | (B.s[i][2 * g + 1] & (int)msk);
+                const float as = __builtin_ldexpf(a, -ex);
+                const _Float16 ah = (_Float16)as;
+                const _Float16 al = (_Float16)(as - (float)ah);
+                const half2 ah2 = {ah, ah}, al2 = {al, al};
+                // 8 codes -> hi, lo
+                auto conv = [&](unsigned v0, unsigned v1, half8 &hv, half8 &lv) {
+                    const unsigned u0 = v0 ^ 0x80808080u, u1 = v1 ^ 0x80808080u;
+                    const half2 cc[4] = {bias_pair_lo(u0) + m1152, bias_pair_hi(u0) + m1152,
+                                         bias_pair_lo(u1) + m1152, bias_pair_hi(u1) + m1152};
+                    half2 hh[4], ll[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        hh[k] = cc[k] * ah2;
+                        const half2 r = __builtin_elementwise_fma(cc[k], ah2, -hh[k]);
+                        ll[k] = __builtin_elementwise_fma(cc[k], al2, r);
+                    }
+                    hv = cat4(hh[0], hh[1], hh[2], hh[3]);
+                    lv = cat4(ll[0], ll[1], ll[2], ll[3]);
+                };
+                // sub-block jb; the two lanes of a row land 16 banks apart
+                _Float16 *dst = &L.bx[F][row][32 * jb];
+                const i32x4 c0 = R.c0[i], c1 = R.c1[i];
+                half8 hv, lv;
+                conv(c0.x, c0.y, hv, lv);   // elements 0..7: lh 0, kh 0
+                *reinterpret_cast<half8 *>(dst + 0) = hv;
+                *reinterpret_cast<half8 *>(dst + 8) = lv;
+                conv(c0.z, c0.w, hv, lv);   // elements 8..15: lh 1, kh 0
+                *reinterpret_cast<half8 *>(dst + 64) = hv;
+                *reinterpret_cast<half8 *>(dst + 72) = lv;
+                conv(c1.x, c1.y, hv, lv);   // elements 16..23: lh 0, kh 1
+                *reinterpret_cast<half8 *>(dst + 16) = hv;
+                *reinterpret_cast<half8 *>(dst + 24) = lv;
+                conv(c1.z, c1.w, hv, lv);   // elements 24..31: lh 1, kh 1
+                *reinterpret_cast<half8 *>(dst + 80) = hv;
+                *reinterpret_cast<half8 *>(dst + 88) = lv;
+                if (g == 0) L.es[Q][row] = __builtin_ldexpf(1.0f, ex);   // both lanes of the row
+                unsigned short phi, plo;
+                split_bf16(a * (float)sj, phi, plo);
+                L.ph[Q][0][row][2 * g + jb] = phi;
+                L.ph[Q][1][row][2 * g + jb] = plo;
+            }
+        };
+
+        // Per step s: load step s+2 into the register set step s used,
+        // convert step s+1 into LDS buffer (s+1) & 1, one barrier.
+        load(IC<0>{}, IC<0>{}, 0);
+        load(IC<1>{}, IC<1>{}, 0);
+        cur = nxt;
+        convert(IC<0>{}, IC<0>{}, IC<0>{}, cur, 0);
+        __syncthreads();
+#pragma unroll 1
+        for (int b = 0; b < nl; ++b) {
+            const int Q = b & 1;
+            load(IC<0>{}, IC<2>{}, b);
+            convert(IC<1>{}, IC<1>{}, IC<1>{}, cur, Q);
+            __syncthreads();
+            load(IC<1>{}, IC<3>{}, b);
+            convert(IC<0>{}, IC<2>{}, IC<0>{}, cur, Q);
+            __syncthreads();
+            load(IC<0>{}, IC<0>{}, b + 1);
+            convert(IC<1>{}, IC<3>{}, IC<1>{}, cur, Q);
+            __syncthreads();
+            load(IC<1>{}, IC<1>{}, b + 1);
+            convert(IC<0>{}, IC<0>{}, IC<0>{}, nxt, Q ^ 1);
+            __syncthreads();
+            cur = nxt;
+        }
+        return;
+    }
+
+    // ---------------- matrix-core waves ----------------
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave / WVM, wm = wave % WVM;
     const int lr = lane & 31, lh = lane >> 5;
 
-    // Global loads of one super-block, branch-free from clamped addresses (a
-    // load under a branch makes the compiler wait for every outstanding load
-    // at the join, which would drain the prefetch pipeline).  Rows past N or M
-    // read row N-1 / M-1: they only feed outputs that are never stored.
-    auto load = [&](int b, Regs<BM, BN> &r) {
-        {
-            const int row = min(n0 + min(tid, BN - 1), N - 1);
-            r.hd = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                w + (int64_t)row * row_bytes + (int64_t)b * 144));
+    f32x16 acc[TN][TM], tmp[TN][TM];
+#pragma unroll
+    for (int u = 0; u < TN; ++u)
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc[u][t][i] = 0.0f;
+                tmp[u][t][i] = 0.0f;
+            }
+
+    // Sub-block s of the step in LDS buffer F: 8 matrix-core ops per 32x32 tile.
+    auto compute = [&](auto bufc, int s) {
+        constexpr int F = decltype(bufc)::value;
+        half8 A[TN][2], B[TM][2][2];
+#pragma unroll
+        for (int u = 0; u < TN; ++u) {
+            const _Float16 *src = &L.aw[F][wn * 64 + u * 32 + lr][16 * s + 8 * lh];
+            A[u][0] = *reinterpret_cast<const half8 *>(src);
+            A[u][1] = *reinterpret_cast<const half8 *>(src + 32);
         }
 #pragma unroll
-        for (int i = 0; i < C::NW; ++i) {
-            const int e = min(tid + i * C::T, C::WCH - 1);
-            const int row = min(n0 + (e >> 3), N - 1), ch = e & 7;
-            r.wc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                w + (int64_t)row * row_bytes + (int64_t)b * 144 + 16 + 16 * ch));
+        for (int t = 0; t < TM; ++t) {
+            const _Float16 *src = &L.bx[F][(wm * TM + t) * 32 + lr][64 * lh + 32 * s];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    B[t][kh][hl] = *reinterpret_cast<const half8 *>(src + 16 * kh + 8 * hl);
         }
 #pragma unroll
-        for (int i = 0; i < C::NX; ++i) {
-            const int e = min(tid + i * C::T, C::XCH - 1);
-            const int row = min(m0 + (e >> 4), M - 1), ch = e & 15;
-            r.xc[i] = *reinterpret_cast<const i32x4 *>(codes + (int64_t)row * K + 256 * b + 16 * ch);
-        }
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < C::NS; ++i) {
-            const int e = min(tid + i * C::T, C::SE - 1);
-            const int row = min(m0 + (e >> 3), M - 1), j = e & 7;
-            const int64_t o = (int64_t)row * nblk + 8 * b + j;
-            r.a[i] = scales[o];
-            r.s[i] = sums[o];
-        }
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int u = 0; u < TN; ++u)
+#pragma unroll
+                    for (int t = 0; t < TM; ++t)
+                        tmp[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            B[t][kh][hl], A[u][kh], tmp[u][t], 0, 0, 0);
     };
-    auto store = [&](const Regs<BM, BN> &r, Buf<BM, BN> &B) {
-        if (tid < BN) {
-            // header of weight row tid: fp16 d, dmin and the 6-bit scales/mins
-            const u32x4 v = r.hd;
-            const float d = half_lo(v.x), dmin = half_hi(v.x);
-            const unsigned h1 = v.y, h2 = v.z, h3 = v.w;
+
+    // End of a super-block: acc += (d * 2^e) * tmp, and the min term.  A
+    // lane's outputs share one weight row n (its d) and span 16 activation
+    // rows m (their 2^e).
+    auto finish = [&](int Q) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                unsigned sc, mn;
-                if (j < 4) {
-                    sc = (h1 >> (8 * j)) & 63u;
-                    mn = (h2 >> (8 * j)) & 63u;
-                } else {
-                    const int s = 8 * (j - 4);
-                    sc = ((h3 >> s) & 15u) | (((h1 >> (s + 6)) & 3u) << 4);
-                    mn = ((h3 >> (s + 4)) & 15u) | (((h2 >> (s + 6)) & 3u) << 4);
+        for (int t = 0; t < TM; ++t) {
+            const int x0 = (wm * TM + t) * 32;
+            float ev[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&L.es[Q][x0 + 8 * q + 4 * lh]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ev[4 * q + k] = e4[k];
+            }
+            const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(&L.ph[Q][lh][x0 + lr][0]);
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const int r = wn * 64 + u * 32 + lr;
+                const float dv = L.dn[Q][r];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[u][t][i] = fmaf(dv * ev[i], tmp[u][t][i], acc[u][t][i]);
+                    tmp[u][t][i] = 0.0f;
                 }
-                B.ws[j][tid] = d * (float)sc;
-                unsigned short qhi, qlo;
-                split_bf16(dmin * (float)mn, qhi, qlo);
-                B.qh[0][tid][j] = qhi;
-                B.qh[1][tid][j] = qlo;
+                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(&L.qh[Q][0][r][0]);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(&L.qh[Q][1][r][0]);
+                acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, qh, acc[u][t], 0, 0, 0);
+                acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ql, acc[u][t], 0, 0, 0);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < C::NW; ++i) {
-            const int e = tid + i * C::T;
-            if (e >= C::WCH) continue;
-            // quant chunk c: low nibbles -> elements 64g+16h+i, high nibbles ->
-            // 64g+32+16h+i (g = c/2, h = c%2)
-            const int row = e >> 3, c = e & 7, g = c >> 1, h = c & 1;
-            const u32x4 v = r.wc[i];
-            u32x4 lo, hi;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                lo[k] = v[k] & 0x0F0F0F0Fu;
-                hi[k] = (v[k] >> 4) & 0x0F0F0F0Fu;
-            }
-            *reinterpret_cast<u32x4 *>(&B.wq[row][64 * g + 16 * h]) = lo;
-            *reinterpret_cast<u32x4 *>(&B.wq[row][64 * g + 32 + 16 * h]) = hi;
-        }
-#pragma unroll
-        for (int i = 0; i < C::NX; ++i) {
-            const int e = tid + i * C::T;
-            if (e < C::XCH)
-                *reinterpret_cast<i32x4 *>(&B.xq[e >> 4][16 * (e & 15)]) = r.xc[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::NS; ++i) {
-            const int e = tid + i * C::T;
-            if (e >= C::SE) continue;
-            const int row = e >> 3, j = e & 7;
-            B.as[j][row] = r.a[i];
-            unsigned short phi, plo;
-            split_bf16(r.a[i] * (float)r.s[i], phi, plo);
-            B.ph[0][row][j] = phi;
-            B.ph[1][row][j] = plo;
         }
     };
 
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    f32x16 mins;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mins[i] = 0.0f;
-
-    const int am = wm * 32 + lr;      // A operand row (activation) within the tile
-    const int bn = wn * 32 + lr;      // B operand column (weight row) within the tile
-
-    // One super-block of work on LDS buffer B.
-    auto compute = [&](const Buf<BM, BN> &B) {
-#pragma unroll 2
-        for (int j = 0; j < 8; ++j) {
-            const i32x4 aop = *reinterpret_cast<const i32x4 *>(&B.xq[am][32 * j + 16 * lh]);
-            const i32x4 bop = *reinterpret_cast<const i32x4 *>(&B.wq[bn][32 * j + 16 * lh]);
-            const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                aop, bop, (i32x16){0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}, 0, 0, 0);
-            const float wsj = B.ws[j][bn];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const f32x4 a4 =
-                    *reinterpret_cast<const f32x4 *>(&B.as[j][wm * 32 + 8 * rr + 4 * lh]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    acc[4 * rr + t] = fmaf((float)D[4 * rr + t], a4[t] * wsj, acc[4 * rr + t]);
-            }
-        }
-        const bf16x8 pa_h = *reinterpret_cast<const bf16x8 *>(&B.ph[0][am][0]);
-        const bf16x8 pa_l = *reinterpret_cast<const bf16x8 *>(&B.ph[1][am][0]);
-        const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&B.qh[lh][bn][0]);
-        mins = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_h, qb, mins, 0, 0, 0);
-        mins = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_l, qb, mins, 0, 0, 0);
-    };
-
-    // Software pipeline, prefetch distance 2: while super-block b is computed
-    // from LDS, the registers hold b+1 (loaded one iteration earlier) and the
-    // loads of b+2 are in flight into the other register set.
-    Regs<BM, BN> ra, rb;
-    load(0, ra);
-    store(ra, buf[0]);
-    if (nsb > 1) load(1, ra);
     __syncthreads();
-    for (int b = 0; b < nsb; b += 2) {
-        // even step: compute b from buf[0]; ra holds b+1
-        if (b + 2 < nsb) load(b + 2, rb);
-        compute(buf[0]);
-        if (b + 1 < nsb) store(ra, buf[1]);
+#pragma unroll 1
+    for (int b = 0; b < nl; ++b) {
+        compute(IC<0>{}, 0);
+        compute(IC<0>{}, 1);
         __syncthreads();
-        if (b + 1 >= nsb) break;
-        // odd step: compute b+1 from buf[1]; rb holds b+2
-        if (b + 3 < nsb) load(b + 3, ra);
-        compute(buf[1]);
-        if (b + 2 < nsb) store(rb, buf[0]);
+        compute(IC<1>{}, 0);
+        compute(IC<1>{}, 1);
+        __syncthreads();
+        compute(IC<0>{}, 0);
+        compute(IC<0>{}, 1);
+        __syncthreads();
+        compute(IC<1>{}, 0);
+        compute(IC<1>{}, 1);
+        finish(b & 1);
         __syncthreads();
     }
 
-    const int n = n0 + bn;
-    if (n < N) {
+    // Lanes 0..31 hold 32 consecutive n of one activation row: coalesced
+    // stores, or (K split over several workgroups) fp32 atomic adds into the
+    // zero-filled output.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = m0 + wm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            if (m < M) y[(int64_t)m * N + n] = acc[i] - mins[i];
-        }
+    for (int u = 0; u < TN; ++u) {
+        const int n = n0 + wn * 64 + u * 32 + lr;
+        if (n >= N) continue;
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + (wm * TM + t) * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                if (m >= M) continue;
+                float *dst = y + (int64_t)m * N + n;
+                if (splits == 1)
+                    *dst = acc[u][t][i];
+                else
+                    unsafeAtomicAdd(dst, acc[u][t][i]);
+            }
     }
 }
 
-template <int BM, int BN>
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ y, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        y[i] = 0.0f;
+}
+
+template <int WVN, int WVM, int TM>
 hipError_t launch_tile(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
-                       hipStream_t stream) {
-    const int64_t tiles_m = (M + BM - 1) / BM;
-    const int64_t tiles_n = (N + BN - 1) / BN;
+                       int splits, hipStream_t stream) {
+    using C = Cfg<WVN, WVM, TM>;
+    if (splits > 1) {
+        hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, stream, y, M * N);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t tiles_m = (M + C::WM - 1) / C::WM;
+    const int64_t tiles_n = (N + C::WN - 1) / C::WN;
     const int64_t groups = (tiles_n + NXCD - 1) / NXCD;
-    const int64_t grid = groups * NXCD * tiles_m;
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN>), dim3((unsigned)grid), dim3(Cfg<BM, BN>::T), 0,
-                       stream, w, (int)N, nsb, codes, scales, sums, (int)M, y);
+    const int64_t grid = groups * NXCD * tiles_m * splits;
+    hipLaunchKernelGGL((gemm_f16_kernel<WVN, WVM, TM>), dim3((unsigned)grid), dim3(C::T),
+                       sizeof(Lds<C::WN, C::WM>), stream, w, (int)N, nsb, codes, scales, sums,
+                       (int)M, y, splits);
     return hipGetLastError();
+}
+
+// Number of K parts: fill the CUs (one workgroup each) without paying more
+// for the zero fill and the atomic adds than the split saves.  Workgroups
+// are dealt to the XCDs by weight column-block, so the busiest XCD decides
+// the number of rounds.  Costs in microseconds: one quarter super-block step
+// of a round ~1.3, the zero fill ~3, the atomic adds ~1.3 bytes per ps.
+int choose_splits(int64_t tiles_n, int64_t tiles_m, int nsb, int64_t tile_outputs) {
+    const int64_t per_xcd = (cu_count() + NXCD - 1) / NXCD;
+    const int64_t cols = (tiles_n + NXCD - 1) / NXCD;   // column-blocks on the busiest XCD
+    int best = 1;
+    double best_t = 1e30;
+    for (int s = 1; s <= 8 && s <= nsb; ++s) {
+        const int64_t rounds = (cols * tiles_m * s + per_xcd - 1) / per_xcd;
+        const int steps = 4 * ((nsb + s - 1) / s);
+        double t = 1.3 * (double)(rounds * steps);
+        if (s > 1) t += 3.0 + 4.0 * (double)(tiles_n * tiles_m * s * tile_outputs) / 1.3e6;
+        if (t < best_t) {
+            best_t = t;
+            best = s;
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -289,13 +516,17 @@ hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    // Largest tile that still gives the launch at least half a workgroup per CU.
-    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(128, 64) >= 128)
-        return launch_tile<128, 64>(w, N, nsb, codes, scales, sums, M, y, stream);
-    if (tiles(64, 32) >= 128)
-        return launch_tile<64, 32>(w, N, nsb, codes, scales, sums, M, y, stream);
-    return launch_tile<32, 32>(w, N, nsb, codes, scales, sums, M, y, stream);
+    const int64_t tiles_n = (N + 127) / 128;
+    if (M > 64) {
+        const int s = choose_splits(tiles_n, (M + 127) / 128, nsb, 128 * 128);
+        return launch_tile<2, 2, 2>(w, N, nsb, codes, scales, sums, M, y, s, stream);
+    }
+    if (M > 32) {
+        const int s = choose_splits(tiles_n, (M + 63) / 64, nsb, 128 * 64);
+        return launch_tile<2, 1, 2>(w, N, nsb, codes, scales, sums, M, y, s, stream);
+    }
+    const int s = choose_splits(tiles_n, (M + 31) / 32, nsb, 128 * 32);
+    return launch_tile<2, 1, 1>(w, N, nsb, codes, scales, sums, M, y, s, stream);
 }
 
 }  // namespace q4k

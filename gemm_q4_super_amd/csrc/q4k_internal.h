@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/q4k.h"
 
 namespace q4k {
@@ -12,6 +14,22 @@ namespace q4k {
 constexpr int kQK = 256;       // weights per Q4_K super-block
 constexpr int kSB = 144;       // bytes per Q4_K super-block
 constexpr int kQB = 32;        // Q8 block / Q4_K sub-block length
+
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int cu_count() {
+    static std::atomic<int> n[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = n[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        n[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 
 // Routed-expert limits (the route grouping runs in one workgroup's LDS).
 constexpr int kMoeMaxPairs = 4096;     // T * topk

@@ -349,19 +349,6 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
 
 // ------------------------------------------------------------------- host --
 
-inline int cu_count() {
-    static std::atomic<int> n[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int v = n[dev].load(std::memory_order_relaxed);
-    if (!v) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            v <= 0)
-            v = 256;
-        n[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
 
 struct Plan {
     int lg_rg = 3, v = 1, cpw = 1, waves = 1;
