@@ -255,10 +255,23 @@ class Prefill:
                           torch.empty((M, K // 32), dtype=torch.float32, device=dev),
                           torch.empty((M, K // 32), dtype=torch.int32, device=dev))
                       for p, (_, K, N) in enumerate(self.shapes)}
-        self.ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
-                   for _, _, N in self.shapes}
+        self.ys = {p: torch.empty((M, N), dtype=torch.float32, device=dev)
+                   for p, (_, _, N) in enumerate(self.shapes)}
         self.n = len(self.weights)
         self.ops = sum(2 * M * N * K for _, N, K in self.weights)
+        # the headline path: per layer one q4k_gemm_batch for {q,k,v} and for
+        # {gate,up} (products sharing an activation), one q4k_gemm for o and down
+        self.groups = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+        P = q4k._lib.GemmProblem
+        self.batch_arr = {}
+        for layer in range(LAYERS):
+            for gi, (_, idx) in enumerate(self.groups):
+                if len(idx) > 1:
+                    base = layer * len(self.shapes)
+                    self.batch_arr[(layer, gi)] = (P * len(idx))(*[
+                        P(self.weights[base + p][0].data_ptr(), self.ys[p].data_ptr(),
+                          self.weights[base + p][1]) for p in idx])
+        self.units = LAYERS * len(self.groups)
         torch.cuda.synchronize()
 
     def quantize(self, i, s):
@@ -274,26 +287,50 @@ class Prefill:
         wt, N, K = self.weights[i]
         c, sc, su = self.qbufs[p]
         if self.L.q4k_gemm(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(),
-                           PREFILL_M, self.ys[N].data_ptr(), s):
+                           PREFILL_M, self.ys[p].data_ptr(), s):
             raise RuntimeError("q4k_gemm launch failed")
 
+    def gemm_unit(self, u, s):
+        """Launch unit u of the headline path: layer u // 4, group u % 4."""
+        layer, gi = divmod(u, len(self.groups))
+        idx = self.groups[gi][1]
+        if len(idx) == 1:
+            return self.gemm(layer * len(self.shapes) + idx[0], s)
+        _, _, K = self.weights[layer * len(self.shapes) + idx[0]]
+        c, sc, su = self.qbufs[idx[0]]
+        if self.L.q4k_gemm_batch(self.batch_arr[(layer, gi)], len(idx), K, c.data_ptr(),
+                                 sc.data_ptr(), su.data_ptr(), PREFILL_M, s):
+            raise RuntimeError("q4k_gemm_batch launch failed")
+
     def parity(self, oracle):
+        """Layer 0: every projection through q4k_gemm and through the batched
+        launches of the headline path, 8 sampled weight rows x all 512
+        activation rows each, against the oracle."""
         torch, q4k = self.torch, self.q4k
         max_rel, checked = 0.0, 0
+        batched = {}
+        for _, idx in self.groups:
+            K = self.shapes[idx[0]][1]
+            c, sc, su = q4k.q4k_quantize_act(self.act_of[idx[0]])
+            ys = q4k.q4k_gemm_batch([(self.weights[p][0], self.shapes[p][2]) for p in idx],
+                                    K, c, sc, su)
+            batched.update(zip(idx, ys))
         for p, (name, K, N) in enumerate(self.shapes):
             wt = self.weights[p][0]
-            c, sc, su = q4k.q4k_quantize_act(self.act_of[p])
+            src = self.act_of[p] if p not in (1, 2, 5) else self.act_of[{1: 0, 2: 0, 5: 4}[p]]
+            c, sc, su = q4k.q4k_quantize_act(src)
             y = q4k.q4k_gemm(wt, N, K, c, sc, su)
             torch.cuda.synchronize()
-            rc, rs, _ = oracle.quantize_act(self.act_of[p].cpu().numpy())
+            rc, rs, _ = oracle.quantize_act(src.cpu().numpy())
             rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 6)])
             ref = oracle.matvec(self.host_w[p], N, K, rc, rs, rows=rows)
-            got = y.cpu().numpy()[:, rows].astype(np.float64)
-            err = np.abs(got - ref)
-            if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
-                raise SystemExit("parity: GEMM %s outside tolerance" % name)
-            max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
-            checked += ref.size
+            for out in (y, batched[p]):
+                got = out.cpu().numpy()[:, rows].astype(np.float64)
+                err = np.abs(got - ref)
+                if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+                    raise SystemExit("parity: GEMM %s outside tolerance" % name)
+                max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
+                checked += ref.size
         return {"outputs_checked": checked, "max_rel_err": max_rel}
 
 
@@ -302,7 +339,7 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
     parity = pre.parity(oracle)
     cap = torch.cuda.Stream()
     g_q = Decode.graph(pre, pre.quantize, range(pre.n), cap)
-    g_g = Decode.graph(pre, pre.gemm, range(pre.n), cap)
+    g_g = Decode.graph(pre, pre.gemm_unit, range(pre.units), cap)
     g_q.replay(); g_g.replay()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -316,6 +353,19 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gemm_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    per_group = {}
+    for gi, (gname, idx) in enumerate(pre.groups):
+        g = Decode.graph(pre, pre.gemm_unit, range(gi, pre.units, len(pre.groups)), cap)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        d = a.elapsed_time(b) * 1e-3 / LAYERS
+        ops = sum(2 * PREFILL_M * pre.shapes[p][2] * pre.shapes[p][1] for p in idx)
+        per_group[gname] = {"N": [pre.shapes[p][2] for p in idx], "K": pre.shapes[idx[0]][1],
+                            "us": round(d * 1e6, 2), "TOPS": round(ops / d / 1e12, 1)}
     per_shape = {}
     for p, (name, K, N) in enumerate(pre.shapes):
         g = Decode.graph(pre, pre.gemm, range(p, pre.n, len(pre.shapes)), cap)
@@ -330,7 +380,8 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
                            "TOPS": round(2 * PREFILL_M * N * K / d / 1e12, 1)}
     tops = pre.ops / gemm_s / 1e12
     out = {"workload": "prefill GEMM, M=512 tokens x the seven Qwen3-4B projection shapes x "
-                       "36 layers (3.72 T int ops per step)",
+                       "36 layers (3.72 T int ops per step); q4k_gemm_batch launches {q,k,v} "
+                       "and {gate,up}, q4k_gemm o and down (4 launches per layer)",
            "steps": steps, "ms_per_step": round(elapsed / steps * 1e3, 3),
            "tok_per_s": round(PREFILL_M * steps / elapsed, 0),
            "gemm_ms_per_step": round(gemm_s * 1e3, 3),
@@ -342,8 +393,8 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
                         "frac": round(tops / FP16_PEAK_TFLOPS, 4),
                         "matrix_core_busy": round(2 * tops / FP16_PEAK_TFLOPS, 4),
                         "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-                        "mean_launch_us": round(gemm_s / pre.n * 1e6, 2)},
-           "per_shape": per_shape, "parity": parity}
+                        "mean_launch_us": round(gemm_s / pre.units * 1e6, 2)},
+           "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity}
     del pre
     torch.cuda.empty_cache()
     return out

@@ -12,6 +12,7 @@ Functions carry the C names:
     q4k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (fp32 x, one launch)
     q4k_quantize_gemv_batch([(w, N, x), ...], K)     -> [y, ...]   (<= 8 products, one launch)
     q4k_gemm(w, N, K, codes, scales, sums)           -> y [M, N]
+    q4k_gemm_batch([(w, N), ...], K, codes, scales, sums) -> [y, ...] (<= 8 products, one launch)
     q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
                  act_per_slot, workspace=None)       -> y
 """
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     lib,
     lib_path,
     q4k_gemm,
+    q4k_gemm_batch,
     q4k_gemv,
     q4k_moe_gemv,
     q4k_moe_workspace_bytes,

@@ -13,6 +13,7 @@ EXPORTED_SYMBOLS = (
     "q4k_quantize_gemv",
     "q4k_quantize_gemv_batch",
     "q4k_gemm",
+    "q4k_gemm_batch",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
     "q4k_status_string",
@@ -26,6 +27,11 @@ _lib = None
 class GemvProblem(ctypes.Structure):
     """Mirror of q4k_gemv_problem."""
     _fields_ = [("w", _P), ("x", _P), ("y", _P), ("N", _I)]
+
+
+class GemmProblem(ctypes.Structure):
+    """Mirror of q4k_gemm_problem."""
+    _fields_ = [("w", _P), ("y", _P), ("N", _I)]
 
 
 class Q4KError(RuntimeError):
@@ -49,6 +55,8 @@ def lib():
         L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
         L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
         L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+        L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
+                                     _I, _P]
         L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
         L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
                                               _I, _P]
@@ -59,7 +67,7 @@ def lib():
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
-                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_moe_gemv"):
+                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -161,6 +169,29 @@ def q4k_quantize_gemv_batch(problems, K, ys=None):
 
 def q4k_gemm(w, N, K, codes, scales, sums, y=None):
     return _matrix_call(lib().q4k_gemm, "q4k_gemm", w, N, K, codes, scales, sums, y)
+
+
+def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None):
+    """Several prefill GEMMs against the same Q8 rows in one launch.
+
+    `problems` is a sequence of (w, N); returns the list of outputs y_i [M, N_i]
+    (or fills `ys`)."""
+    import torch
+    problems = list(problems)
+    if not problems:
+        raise ValueError("q4k_gemm_batch: empty batch")
+    for t, n in ((codes, "codes"), (scales, "scales"), (sums, "sums")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if ys is None:
+        ys = [torch.empty((M, N), dtype=torch.float32, device=codes.device) for _, N in problems]
+    arr = (GemmProblem * len(problems))()
+    for i, ((w, N), y) in enumerate(zip(problems, ys)):
+        _dev(w, "w")
+        arr[i] = GemmProblem(_ptr(w), _ptr(y), N)
+    _check(lib().q4k_gemm_batch(arr, len(problems), K, _ptr(codes), _ptr(scales), _ptr(sums), M,
+                                _stream(codes)), "q4k_gemm_batch")
+    return ys
 
 
 def q4k_moe_workspace_bytes(T, topk, n_experts, N) -> int:

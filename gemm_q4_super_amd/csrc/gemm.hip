@@ -41,6 +41,7 @@
 // One barrier per step.  Workgroup tile (64*WVN) x (32*TM*WVM), one
 // matrix-core wave per 64 x 32*TM outputs.  Tile order is XCD-aware: all M
 // tiles of one weight column-block run on one XCD, sharing its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "q4k_internal.h"
@@ -73,6 +74,16 @@ struct __attribute__((aligned(16))) Lds {
 
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+// Products sharing one activation, launched together: product i has N[i]
+// weight rows and owns the virtual column-blocks tile0[i] .. tile0[i+1]-1.
+struct GemmSet {
+    const uint8_t *w[kMaxGemmBatch];
+    float *y[kMaxGemmBatch];
+    int N[kMaxGemmBatch];
+    int tile0[kMaxGemmBatch + 1];
+    int count;
+};
 
 template <int WVN, int WVM, int TM>
 struct Cfg {
@@ -121,23 +132,27 @@ __device__ __forceinline__ unsigned scale6(const u32x4 &h, bool min) {
 
 template <int WVN, int WVM, int TM>
 __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
-    const uint8_t *__restrict__ w, int N, int nsb, const int8_t *__restrict__ codes,
-    const float *__restrict__ scales, const int32_t *__restrict__ sums, int M,
-    float *__restrict__ y, int splits) {
+    const GemmSet set, int nsb, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const int32_t *__restrict__ sums, int M, int splits) {
     using C = Cfg<WVN, WVM, TM>;
     constexpr int WN = C::WN, WM = C::WM, P = C::P;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
 
     // XCD-aware tile and K range of this workgroup: the M tiles and K parts
-    // of one weight column-block run on one XCD.
+    // of one (virtual) weight column-block run on one XCD.
     const int tiles_m = (M + WM - 1) / WM;
-    const int tiles_n = (N + WN - 1) / WN;
     const int xcd = blockIdx.x % NXCD, pos = blockIdx.x / NXCD;
     const int per = tiles_m * splits;
-    const int nt = (pos / per) * NXCD + xcd, mt = (pos % per) / splits, sp = pos % splits;
-    if (nt >= tiles_n) return;   // the whole workgroup exits together, before any barrier
-    const int n0 = nt * WN, m0 = mt * WM;
+    const int vt = (pos / per) * NXCD + xcd, mt = (pos % per) / splits, sp = pos % splits;
+    if (vt >= set.tile0[set.count]) return;   // the whole workgroup exits, before any barrier
+    int pi = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxGemmBatch; ++k) pi += (k < set.count && vt >= set.tile0[k]);
+    const uint8_t *__restrict__ w = set.w[pi];
+    float *__restrict__ y = set.y[pi];
+    const int N = set.N[pi];
+    const int n0 = (vt - set.tile0[pi]) * WN, m0 = mt * WM;
     const int sb0 = (int)((int64_t)nsb * sp / splits);
     const int nl = (int)((int64_t)nsb * (sp + 1) / splits) - sb0;   // >= 1 (splits <= nsb)
     const int K = nsb * 256, nblk = nsb * 8;
@@ -462,28 +477,42 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
     }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ y, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        y[i] = 0.0f;
+// Zero fill of the outputs before K parts add into them: 16-byte stores
+// where an output is 16-byte aligned, else 4-byte stores.
+__global__ __launch_bounds__(256) void zero_kernel(const GemmSet set, int64_t M) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (int p = 0; p < set.count; ++p) {
+        float *y = set.y[p];
+        const int64_t n = M * set.N[p];
+        if ((reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+            f32x4 *y4 = reinterpret_cast<f32x4 *>(y);
+            for (int64_t i = i0; i < n / 4; i += stride) y4[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            if (i0 < (n & 3)) y[(n & ~(int64_t)3) + i0] = 0.0f;
+        } else {
+            for (int64_t i = i0; i < n; i += stride) y[i] = 0.0f;
+        }
+    }
 }
 
 template <int WVN, int WVM, int TM>
-hipError_t launch_tile(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
-                       const float *scales, const int32_t *sums, int64_t M, float *y,
-                       int splits, hipStream_t stream) {
+hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const float *scales,
+                       const int32_t *sums, int64_t M, int splits, hipStream_t stream) {
     using C = Cfg<WVN, WVM, TM>;
     if (splits > 1) {
-        hipLaunchKernelGGL(zero_kernel, dim3(1024), dim3(256), 0, stream, y, M * N);
+        int64_t items = 0;
+        for (int p = 0; p < set.count; ++p) items = std::max<int64_t>(items, M * set.N[p] / 4 + 1);
+        const int64_t blocks = std::min<int64_t>((items + 255) / 256, 2048);
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, set, M);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t tiles_m = (M + C::WM - 1) / C::WM;
-    const int64_t tiles_n = (N + C::WN - 1) / C::WN;
-    const int64_t groups = (tiles_n + NXCD - 1) / NXCD;
+    const int64_t groups = (set.tile0[set.count] + NXCD - 1) / NXCD;
     const int64_t grid = groups * NXCD * tiles_m * splits;
     hipLaunchKernelGGL((gemm_f16_kernel<WVN, WVM, TM>), dim3((unsigned)grid), dim3(C::T),
-                       sizeof(Lds<C::WN, C::WM>), stream, w, (int)N, nsb, codes, scales, sums,
-                       (int)M, y, splits);
+                       sizeof(Lds<C::WN, C::WM>), stream, set, nsb, codes, scales, sums, (int)M,
+                       splits);
     return hipGetLastError();
 }
 
@@ -491,7 +520,7 @@ hipError_t launch_tile(const uint8_t *w, int64_t N, int nsb, const int8_t *codes
 // for the zero fill and the atomic adds than the split saves.  Workgroups
 // are dealt to the XCDs by weight column-block, so the busiest XCD decides
 // the number of rounds.  Costs in microseconds: one quarter super-block step
-// of a round ~1.3, the zero fill ~3, the atomic adds ~1.3 bytes per ps.
+// of a round ~1.3, the zero fill ~5, the atomic adds ~1.3 bytes per ps.
 int choose_splits(int64_t tiles_n, int64_t tiles_m, int nsb, int64_t tile_outputs) {
     const int64_t per_xcd = (cu_count() + NXCD - 1) / NXCD;
     const int64_t cols = (tiles_n + NXCD - 1) / NXCD;   // column-blocks on the busiest XCD
@@ -501,7 +530,7 @@ int choose_splits(int64_t tiles_n, int64_t tiles_m, int nsb, int64_t tile_output
         const int64_t rounds = (cols * tiles_m * s + per_xcd - 1) / per_xcd;
         const int steps = 4 * ((nsb + s - 1) / s);
         double t = 1.3 * (double)(rounds * steps);
-        if (s > 1) t += 3.0 + 4.0 * (double)(tiles_n * tiles_m * s * tile_outputs) / 1.3e6;
+        if (s > 1) t += 5.0 + 4.0 * (double)(tiles_n * tiles_m * s * tile_outputs) / 1.3e6;
         if (t < best_t) {
             best_t = t;
             best = s;
@@ -512,21 +541,37 @@ int choose_splits(int64_t tiles_n, int64_t tiles_m, int nsb, int64_t tile_output
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
-                       const float *scales, const int32_t *sums, int64_t M, float *y,
-                       hipStream_t stream) {
+hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
+                             const int8_t *codes, const float *scales, const int32_t *sums,
+                             int64_t M, hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    const int64_t tiles_n = (N + 127) / 128;
+    GemmSet set = {};
+    set.count = count;
+    set.tile0[0] = 0;
+    for (int p = 0; p < count; ++p) {
+        set.w[p] = static_cast<const uint8_t *>(probs[p].w);
+        set.y[p] = probs[p].y;
+        set.N[p] = (int)probs[p].N;
+        set.tile0[p + 1] = set.tile0[p] + (int)((probs[p].N + 127) / 128);   // WN = 128
+    }
+    const int64_t tiles_n = set.tile0[count];
     if (M > 64) {
         const int s = choose_splits(tiles_n, (M + 127) / 128, nsb, 128 * 128);
-        return launch_tile<2, 2, 2>(w, N, nsb, codes, scales, sums, M, y, s, stream);
+        return launch_tile<2, 2, 2>(set, nsb, codes, scales, sums, M, s, stream);
     }
     if (M > 32) {
         const int s = choose_splits(tiles_n, (M + 63) / 64, nsb, 128 * 64);
-        return launch_tile<2, 1, 2>(w, N, nsb, codes, scales, sums, M, y, s, stream);
+        return launch_tile<2, 1, 2>(set, nsb, codes, scales, sums, M, s, stream);
     }
     const int s = choose_splits(tiles_n, (M + 31) / 32, nsb, 128 * 32);
-    return launch_tile<2, 1, 1>(w, N, nsb, codes, scales, sums, M, y, s, stream);
+    return launch_tile<2, 1, 1>(set, nsb, codes, scales, sums, M, s, stream);
+}
+
+hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
+                       const float *scales, const int32_t *sums, int64_t M, float *y,
+                       hipStream_t stream) {
+    const GemmProblem p = {w, y, N};
+    return launch_gemm_batch(&p, 1, K, codes, scales, sums, M, stream);
 }
 
 }  // namespace q4k

@@ -125,6 +125,25 @@ int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
              const float *scales, const int32_t *sums, int64_t M, float *y,
              void *stream);
 
+/* One product of a batch for q4k_gemm_batch. */
+typedef struct q4k_gemm_problem {
+    const void *w;     /* device Q4_K weights, N rows x (K/256)*144 bytes, 16-byte aligned */
+    float *y;          /* device fp32 output [M][N], 4-byte aligned                      */
+    int64_t N;         /* rows of this matrix, >= 1                                      */
+} q4k_gemm_problem;
+
+/* Several prefill GEMMs against the same Q8 activations in one launch (e.g.
+ * the q, k and v projections of a layer, or gate and up): for every problem
+ * i, y_i = Q8(x)[M][K] * W_i^T, as q4k_gemm on that problem alone (same
+ * arithmetic; the split of K may differ, so results agree to fp32 rounding).
+ * Launching them together fills the GPU where each alone would not.
+ * `problems` is a host array of `count` entries (1 <= count <= 8), read
+ * during the call; outputs must not overlap.  Limits and checks as for
+ * q4k_gemm, applied to every problem. */
+int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,
+                   const int8_t *codes, const float *scales, const int32_t *sums,
+                   int64_t M, void *stream);
+
 /* Routed-expert grouped GEMV.  n_experts Q4_K matrices of N rows x K columns
  * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of
  * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].

@@ -99,6 +99,28 @@ def test_quantize_gemv_batch_argument_checks(L):
     assert call([good, (A, A, A + 2, 16)]) == EALIGN
 
 
+def test_gemm_batch_argument_checks(L):
+    f = L.q4k_gemm_batch
+    P = q4k._lib.GemmProblem
+
+    def call(probs, K=512, M=1, codes=A):
+        arr = (P * max(len(probs), 1))(*[P(*p) for p in probs])
+        return f(arr, len(probs), K, codes, A, A, M, None)
+    good = (A, A, 16)
+    assert f(None, 1, 512, A, A, A, 1, None) == EINVAL
+    assert call([]) == ESHAPE
+    assert call([good] * 9) == ESHAPE
+    assert call([good], K=500) == ESHAPE
+    assert call([good], M=0) == ESHAPE
+    assert call([good], codes=None) == EINVAL
+    assert call([good], codes=A + 4) == EALIGN
+    assert call([good, (A, A, 0)]) == ESHAPE
+    assert call([good, (None, A, 16)]) == EINVAL
+    assert call([good, (A, None, 16)]) == EINVAL
+    assert call([good, (A + 4, A, 16)]) == EALIGN
+    assert call([good, (A, A + 2, 16)]) == EALIGN
+
+
 def test_quantize_argument_checks(L):
     f = L.q4k_quantize_act
     assert f(None, 1, 32, None, A, A, A, None) == EINVAL
