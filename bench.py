@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the small-batch and routed-expert measurements")
+    ap.add_argument("--prefill-group", choices=sorted(PREFILL_GROUPS),
+                    help="only run 3 launches of one prefill launch group (for profiler "
+                         "counter passes) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (known bytes, "
                          "to scale the HBM traffic counters of a profiler run) and exit")
@@ -113,6 +116,30 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": COPY_BYTES,
                                            "bytes_written_per_dispatch": COPY_BYTES,
                                            "dispatches": 10}}))
+
+
+PREFILL_GROUPS = {"qkv": (0, 1, 2), "o": (3,), "gate_up": (4, 5), "down": (6,)}
+
+
+def prefill_group(torch, q4k, qi, name, launches=3):
+    """Only `launches` launches of one prefill launch group (layer 0's weights,
+    M = 512), for profiler counter passes; prints one line and exits."""
+    dev = torch.device("cuda:0")
+    idx = PREFILL_GROUPS[name]
+    K = qi.QWEN3_4B_LAYER[idx[0]][1]
+    probs = [(torch.from_numpy(qi.make_q4k_bytes(qi.QWEN3_4B_LAYER[p][2], K,
+                                                 qi.weight_seed(2, 0, p))).to(dev),
+              qi.QWEN3_4B_LAYER[p][2]) for p in idx]
+    x = torch.from_numpy(qi.make_act(PREFILL_M, K, qi.act_seed(20000 + idx[0]))).to(dev)
+    c, sc, su = q4k.q4k_quantize_act(x)
+    for _ in range(launches):
+        if len(probs) > 1:
+            q4k.q4k_gemm_batch(probs, K, c, sc, su)
+        else:
+            q4k.q4k_gemm(probs[0][0], probs[0][1], K, c, sc, su)
+    torch.cuda.synchronize()
+    print(json.dumps({"prefill_group": {"name": name, "N": [N for _, N in probs], "K": K,
+                                        "M": PREFILL_M, "launches": launches}}))
 
 
 class Decode:
@@ -554,8 +581,11 @@ def main():
         copy_calibration(torch)
         return
     import gemm_q4_super_amd as q4k
-    import oracle
     import q4k_inputs as qi
+    if args.prefill_group:
+        prefill_group(torch, q4k, qi, args.prefill_group)
+        return
+    import oracle
 
     oracle.build(force=False)
     dec = Decode(torch, q4k, qi)
