@@ -39,6 +39,76 @@ __device__ __forceinline__ float group8_sum(float v) {
     return v;
 }
 
+// Q8 quantization of one block of 32 fp32 values held by an aligned group of
+// 8 lanes, 4 consecutive values per lane (lane i of the group: values
+// 4i..4i+3).  Scale d = fl32(amax / 127); code = rne(fl32(x / d)); an
+// all-zero block has d = 0 and codes 0 (the Q8 activation format of q4k.h).
+// Every division is correctly rounded, so the codes are the IEEE ones bit
+// for bit:
+//  * amax / 127: with y = RN(1/127), one correction step
+//    q0 + RN(amax - 127 q0) * y is correctly rounded for every fp32 amax
+//    (checked over all mantissas and exponents);
+//  * x / d: the hardware division sequence without its range scaling -- the
+//    reciprocal refined once, the quotient corrected twice.  For d in
+//    [2^-100, 2^122) every intermediate stays normal when |x / d| >= 1/2
+//    (smaller quotients give code 0 whatever their last bit); scales below
+//    2^-100 take IEEE division instead (a wave-uniform branch, never taken for
+//    ordinary activations).
+// Rounding: adding 1.5 * 2^23 leaves rne(q) in two's complement in the low
+// mantissa bits.  The fast branch needs no clamp: with d normal, |x| <= amax
+// and d >= (amax / 127)(1 - 2^-24) bound |q| by 127 + 2^-17, so codes lie in
+// [-127, 127].  A subnormal d carries fewer significant bits (amax / d can
+// exceed 127.5), so the IEEE branch clamps.
+// Returns this lane's 4 codes (value 4i+k in byte k); d and the block's code
+// sum are the same on all 8 lanes.
+struct Q8Lane {
+    unsigned codes;
+    float d;
+    int sum;
+};
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ Q8Lane quantize_block8(f32x4 v) {
+    // |x| compared as unsigned bit patterns: the same order for non-negative floats
+    unsigned a = max(max(__float_as_uint(v[0]) & 0x7FFFFFFFu, __float_as_uint(v[1]) & 0x7FFFFFFFu),
+                     max(__float_as_uint(v[2]) & 0x7FFFFFFFu, __float_as_uint(v[3]) & 0x7FFFFFFFu));
+    a = max(a, (unsigned)dpp_i<kQuadSwap1>((int)a));
+    a = max(a, (unsigned)dpp_i<kQuadSwap2>((int)a));
+    a = max(a, (unsigned)dpp_i<kRowHalfMirror>((int)a));
+    const float amax = __uint_as_float(a);
+    constexpr float y = 1.0f / 127.0f;
+    const float q0 = amax * y;
+    const float d = __builtin_fmaf(__builtin_fmaf(-127.0f, q0, amax), y, q0);
+    const float dd = d == 0.0f ? 1.0f : d;   // all-zero block: +-0 / 1 gives code 0
+    float q[4];
+    if (__builtin_amdgcn_ballot_w64(dd < 0x1p-100f) != 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[k] / dd, -127.0f, 127.0f);
+    } else {
+        const float r0 = __builtin_amdgcn_rcpf(dd);
+        const float r1 = __builtin_fmaf(__builtin_fmaf(-dd, r0, 1.0f), r0, r0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float t = v[k] * r1;
+            t = __builtin_fmaf(__builtin_fmaf(-dd, t, v[k]), r1, t);
+            q[k] = __builtin_fmaf(__builtin_fmaf(-dd, t, v[k]), r1, t);
+        }
+    }
+    unsigned b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b[k] = __float_as_uint(q[k] + 0x1.8p23f);
+    Q8Lane r;
+    const unsigned lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);   // bytes: b0, b1
+    const unsigned hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);   // bytes: b2, b3
+    r.codes = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    int sum = (int)(b[0] + b[1] + b[2] + b[3] - 4u * 0x4B400000u);
+    sum += dpp_i<kQuadSwap1>(sum);
+    sum += dpp_i<kQuadSwap2>(sum);
+    sum += dpp_i<kRowHalfMirror>(sum);
+    r.d = d;
+    r.sum = sum;
+    return r;
+}
+
 __device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
@@ -91,13 +161,21 @@ __device__ __forceinline__ void unpack_nibbles(u32x4 qw, int qlo[4], int qhi[4])
     }
 }
 
+// sdot4 with a zero accumulator in one instruction (the three-operand form
+// takes the constant; the builtin would first move 0 into a register).
+__device__ __forceinline__ int sdot4_zero(int a, int b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Exact int32 dot of sub-block j = l: this lane's half plus its partner's half.
 // cA pairs with the low nibbles, cB with the high nibbles.
 __device__ __forceinline__ int subblock_dot(const LaneMap &L, const int qlo[4], const int qhi[4],
                                             i32x4 cA, i32x4 cB) {
-    int dA = 0, dB = 0;
+    int dA = sdot4_zero(qlo[0], cA[0]), dB = sdot4_zero(qhi[0], cB[0]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 1; k < 4; ++k) {
         dA = __builtin_amdgcn_sdot4(qlo[k], cA[k], dA, false);
         dB = __builtin_amdgcn_sdot4(qhi[k], cB[k], dB, false);
     }

@@ -25,10 +25,13 @@
 //  * Every wave issues the loads of all its V*CPW super-blocks before any
 //    arithmetic: the workgroup's whole block is in flight at once.
 //  * Activation: each wave stages the Q8 rows of its own S*CPW columns in LDS
-//    (quantizing fp32 x with the same arithmetic as q4k_quantize_act, so the
-//    codes are bit-identical, or copying prepared codes) and reads only those,
-//    so no workgroup barrier waits for the staging.  The activation loads go
-//    out before the weight loads (the load counter retires in order).
+//    (quantizing fp32 x with the quantizer q4k_quantize_act uses,
+//    quantize_block8, so the codes are bit-identical, or copying prepared
+//    codes) and reads only those, so no workgroup barrier waits for the
+//    staging.  The activation loads go out before the weight loads (the load
+//    counter retires in order); waves whose weight loads would queue behind
+//    other waves' (past the first four of a wide workgroup) quantize before
+//    issuing them.
 //  * Each super-block's term is summed over its 8 lanes by DPP and parked in
 //    LDS; a row then adds its K/256 terms in column order.  That order does
 //    not depend on (RG, V, CPW), so single, batched, fused and prepared calls
@@ -52,8 +55,6 @@ namespace stream {
 
 constexpr int kWaves = 16;     // waves per workgroup, at most
 constexpr int kPieces = 16;    // row pieces per launch, at most
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Pieces 1.. of a launch (piece 0 travels in the leading kernel arguments).
 struct Pieces {
@@ -90,26 +91,6 @@ __host__ __device__ constexpr size_t q8_bytes(int M, int nsb) {
 // LDS of the per-super-block terms of a workgroup's block of rows.
 __host__ __device__ constexpr size_t col_bytes(int M, int RB, int nsb) {
     return sizeof(float) * (size_t)RB * nsb * M;
-}
-
-__device__ __forceinline__ float group8_max(float v) {
-    v = fmaxf(v, dpp_f<kQuadSwap1>(v));
-    v = fmaxf(v, dpp_f<kQuadSwap2>(v));
-    v = fmaxf(v, dpp_f<kRowHalfMirror>(v));
-    return v;
-}
-__device__ __forceinline__ int group8_isum(int v) {
-    v += dpp_i<kQuadSwap1>(v);
-    v += dpp_i<kQuadSwap2>(v);
-    v += dpp_i<kRowHalfMirror>(v);
-    return v;
-}
-// Branch-free: an all-zero block (d == 0) divides by 1 and selects 0.
-__device__ __forceinline__ int quant1(float x, float d) {
-    const bool zero = d == 0.0f;
-    float r = __builtin_rintf(x / (zero ? 1.0f : d));
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return zero ? 0 : (int)r;
 }
 
 // The four dwords held by the lanes of this lane's quad (lane 4k+i holds
@@ -243,20 +224,11 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
                 float *sm = qs + ((size_t)m * nsb + b) * 8;
                 if constexpr (FUSED) {
                     // lane -> block lane/8 of the column, 4 values at 4*(lane%8)
-                    const f32x4 v = xv[j][m];
-                    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
-                                       fmaxf(fabsf(v[2]), fabsf(v[3])));
-                    amax = group8_max(amax);
-                    const float d = amax / 127.0f;
-                    const int c0 = quant1(v[0], d), c1 = quant1(v[1], d);
-                    const int c2 = quant1(v[2], d), c3 = quant1(v[3], d);
-                    *reinterpret_cast<int *>(cm + 32 * blk + 4 * sub) =
-                        (c0 & 0xFF) | ((c1 & 0xFF) << 8) | ((c2 & 0xFF) << 16) |
-                        (int)((unsigned)c3 << 24);
-                    const int ssum = group8_isum(c0 + c1 + c2 + c3);
+                    const Q8Lane qb = quantize_block8(xv[j][m]);
+                    *reinterpret_cast<unsigned *>(cm + 32 * blk + 4 * sub) = qb.codes;
                     if (sub == 0) {
-                        am[blk] = d;
-                        sm[blk] = (float)ssum;
+                        am[blk] = qb.d;
+                        sm[blk] = (float)qb.sum;
                     }
                 } else {
                     *reinterpret_cast<int *>(cm + 4 * lane) = pc[j][m];
@@ -269,6 +241,19 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
         }
     };
     stage_load(0);
+    // In a workgroup of 8 or more waves, the loads of waves past the first four
+    // queue behind the first four's data (a CU holds about four waves' loads in
+    // flight), so those waves quantize their columns first: the quantization
+    // then no longer sits between their weights' arrival and the dots.
+    const bool stage_first = nw >= 8 && wave >= 4;   // wave-uniform
+    auto stage_all = [&]() {
+        stage_store(0);
+        for (int j0 = QB; j0 < ncols; j0 += QB) {   // more columns than one batch
+            stage_load(j0);
+            stage_store(j0);
+        }
+    };
+    if (stage_first) stage_all();
     __builtin_amdgcn_sched_barrier(0);
 
     // Branch-free weight loads from clamped addresses (a load under a branch
@@ -277,26 +262,26 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
     // The 16-byte header of a super-block is read as four dwords, one per lane
     // of each lane quad (lane l: dword l % 4), and spread over the quad by DPP
     // at use: a quarter of the address work of a 16-byte load per lane.
+    // Addresses: the workgroup's first row in 64 bits (scalar), then 32-bit
+    // offsets within its block of rows (at most 64 rows of 18 KB).
+    const uint8_t *__restrict__ wb = w + (int64_t)row_base * row_bytes;
+    const unsigned hoff = 4u * (lane & 3), qoff = 16u + 16u * L.l;
     unsigned hd[V][CPW];
     u32x4 qw[V][CPW];
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
-            const int row = min(row_base + v * RG + r, N - 1);
-            const int b = min(col0 + c, nsb - 1);
-            const uint8_t *sb = w + (int64_t)row * row_bytes + (int64_t)b * 144;
-            hd[v][c] = __builtin_nontemporal_load(reinterpret_cast<const unsigned *>(sb) +
-                                                   (lane & 3));
-            qw[v][c] = load_stream16(sb + 16 + 16 * L.l);
+            const unsigned rr = (unsigned)(min(row_base + v * RG + r, N - 1) - row_base);
+            const unsigned b = (unsigned)min(col0 + c, nsb - 1);
+            const unsigned off = __umul24(rr, (unsigned)row_bytes) + b * 144u;
+            hd[v][c] = __builtin_nontemporal_load(
+                reinterpret_cast<const unsigned *>(wb + (off + hoff)));
+            qw[v][c] = load_stream16(wb + (off + qoff));
         }
     __builtin_amdgcn_sched_barrier(0);
 
-    stage_store(0);
-    for (int j0 = QB; j0 < ncols; j0 += QB) {   // more columns than one batch
-        stage_load(j0);
-        stage_store(j0);
-    }
+    if (!stage_first) stage_all();
     // LDS written and read by this wave only: wait for its writes.
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();

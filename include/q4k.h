@@ -118,9 +118,13 @@ int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t
 
 /* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (section 3's
  * batched prefill over all prompt tokens).  Compute-bound: Q4_K tiles are
- * staged through LDS and the per-32 sub-block integer dot products run on the
- * matrix cores, followed by the fp32 scale/min epilogue.  Arguments and
- * result contract as for q4k_gemv, without the M <= 8 limit. */
+ * staged through LDS and the products run on the fp16 matrix cores with
+ * operands that represent the Q4_K weights and Q8 activations exactly,
+ * accumulated in fp32.  When the launch splits K across workgroups to fill
+ * the GPU, y is first cleared on the stream and the partial sums are added
+ * atomically, so y is still fully overwritten but the fp32 summation order
+ * (hence the last bits) may differ between calls.  Arguments and result
+ * contract as for q4k_gemv, without the M <= 8 limit. */
 int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
              const float *scales, const int32_t *sums, int64_t M, float *y,
              void *stream);

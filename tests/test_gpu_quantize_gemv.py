@@ -92,6 +92,56 @@ def test_quantize_near_rounding_boundaries(q4k, oracle_lib):
     assert (c == rc).all() and (su == rsu).all() and (sc == rs).all()
 
 
+def _wide_range_blocks(rng, nblk, emin, emax):
+    """Blocks whose max|x| spans 2^emin .. 2^emax (subnormal to near overflow),
+    each value placed within a few ulps of (k + 1/2) * scale, so every code is
+    decided by the last bit of a correctly rounded quotient at that magnitude."""
+    out = np.zeros((nblk, 32), np.float32)
+    for b in range(nblk):
+        amax = np.float32(np.ldexp(rng.uniform(1.0, 2.0), int(rng.integers(emin, emax + 1))))
+        if amax == 0:
+            amax = np.float32(np.ldexp(1.0, -149))
+        s = amax / np.float32(127)
+        out[b, 0] = amax
+        for i in range(1, 32):
+            x0 = np.float32((int(rng.integers(0, 127)) + 0.5) * float(s))
+            x0 = np.float32(x0 + int(rng.integers(-3, 4)) * np.spacing(x0))
+            out[b, i] = x0 * rng.choice([-1, 1])
+    return out
+
+
+def test_quantize_wide_range_scales(q4k, oracle_lib):
+    """Scales from subnormal to ~2.7e36, including the tiny scales that take the
+    IEEE division branch, agree with the oracle bit for bit."""
+    rng = np.random.default_rng(11)
+    x = _wide_range_blocks(rng, 512, -149, 127).reshape(16, -1)
+    x[3, 64:96] = np.float32(np.ldexp(1.0, -149))     # all-equal subnormal block
+    x[5, :32] = 0.0
+    x[5, 1] = np.float32(-0.0)                          # zeros of both signs
+    c, sc, su = _gpu_quant(q4k, x)
+    rc, rs, rsu = oracle_lib.quantize_act(x)
+    assert (c == rc).all() and (su == rsu).all()
+    assert (sc.view(np.uint32) == rs.view(np.uint32)).all()
+
+
+def test_quantize_gemv_wide_range_scales_bit_identical(q4k, oracle_lib):
+    """The quantizer inside the fused GEMV gives the same codes as
+    q4k_quantize_act for scales far from those of ordinary activations."""
+    import torch
+    N, K = 300, 2560
+    rng = np.random.default_rng(12)
+    x = _wide_range_blocks(rng, K // 32, -140, 60).reshape(1, K)
+    w = qi.make_q4k_bytes(N, K, 4242)
+    wd, xd = to_dev(w), to_dev(x)
+    y1 = q4k.q4k_quantize_gemv(wd, N, K, xd)
+    c, s, su = q4k.q4k_quantize_act(xd)
+    y2 = q4k.q4k_gemv(wd, N, K, c, s, su)
+    torch.cuda.synchronize()
+    rc, rs, rsu = oracle_lib.quantize_act(x)
+    assert (c.cpu().numpy() == rc).all() and (su.cpu().numpy() == rsu).all()
+    assert (y1.cpu().numpy().view(np.uint32) == y2.cpu().numpy().view(np.uint32)).all()
+
+
 def test_quantize_swiglu_bit_exact(q4k, oracle_lib):
     M, K = 16, 1024
     g = qi.make_act(M, K, 5) * np.float32(4.0)
