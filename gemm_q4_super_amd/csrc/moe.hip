@@ -2,50 +2,41 @@
 // work on small and old devices": intro, expert pager; each token touches only
 // its selected experts, so the bytes read per token are those experts').
 //
-// Three launches on the caller's stream:
-//  1. group_kernel (one workgroup): from ids[T][topk] build, per expert, the
-//     count and offset of its (token, slot) pairs and the pair list in
-//     ascending pair order, plus the ascending list of touched experts.
-//     Counts use LDS atomics (order-free), offsets a one-wave scan, and each
-//     pair's slot is its rank among earlier pairs of the same expert, so the
-//     tables are deterministic.  A pair whose id is outside [0, n_experts)
-//     belongs to no expert: it is skipped (its per-slot output row is zero).
-//  2. moe_gemv_kernel: grid = row tiles x touched-expert slots.  Each workgroup
-//     takes one touched expert and one tile of its rows, and computes that
-//     tile for all of the expert's pairs (in chunks of 8 activation rows), so
-//     every touched expert's weights are streamed from HBM once per call.
-//  3. reduce_kernel (only with routing weights): y[t] = sum over slots s in
+// One launch (two with routing weights) on the caller's stream:
+//  1. moe_gemv_kernel: grid = row blocks x touched-expert slots (+ one row of
+//     workgroups that zero the per-slot rows of skipped pairs).  Every
+//     workgroup groups the pairs itself from ids[T][topk] (at most 4096 ids,
+//     in LDS): slot a is the a-th smallest touched expert, and its pairs are
+//     taken in ascending pair order -- deterministic, no tables in memory and
+//     no separate grouping launch.  It then computes one block of that
+//     expert's rows for all of its pairs (the decode GEMV's lane layout,
+//     every load in flight before the arithmetic), MC pairs per pass with the
+//     weights in registers, so every touched expert's weights are streamed
+//     from HBM once per call (again from L2 for each further MC).  A pair
+//     whose id is outside [0, n_experts) belongs to no expert: it is skipped
+//     (its per-slot output row is zero).
+//  2. reduce_kernel (only with routing weights): y[t] = sum over slots s in
 //     order 0..topk-1 of route_w[t][s] * z[t*topk+s] -- fixed order, no float
 //     atomics, bit-reproducible.
+#include <algorithm>
+
 #include "q4k_device.h"
 #include "q4k_internal.h"
 
 namespace q4k {
 namespace {
 
-constexpr int kMaxWaves = 16;
-constexpr int kChunk = 4;            // activation rows per pass over a weight tile
-constexpr int kRowTiles = 2;         // 8-row tiles per workgroup
+constexpr int kMoeWaves = 4;         // waves per workgroup, at most
+constexpr int kMoeV = 8;             // row groups per lane
+constexpr int kMoeMC = 4;            // pairs per pass over a weight block
 
-struct WsLayout {
-    int64_t counts, offsets, act, nact, pairs, z;   // byte offsets
-    size_t bytes;
-};
-
-int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-
-WsLayout layout(int64_t T, int64_t topk, int64_t E, int64_t N) {
-    WsLayout L;
-    const int64_t P = T * topk;
-    L.counts = 0;
-    L.offsets = align256(L.counts + 4 * E);
-    L.act = align256(L.offsets + 4 * (E + 1));
-    L.nact = align256(L.act + 4 * E);
-    L.pairs = align256(L.nact + 4);
-    L.z = align256(L.pairs + 4 * P);
-    L.bytes = (size_t)align256(L.z + 4 * P * N);
-    return L;
+// Workspace: the per-slot products z [T*topk][N] when routing weights are given.
+size_t ws_bytes(int64_t T, int64_t topk, int64_t N) {
+    return (size_t)((4 * T * topk * N + 255) & ~int64_t(255));
 }
+
+// Dynamic LDS of moe_gemv_kernel: ids (padded to 4), expert flags, pair list.
+size_t moe_lds_bytes(int P, int E) { return sizeof(int) * ((size_t)((P + 3) & ~3) + (size_t)E + P); }
 
 // Exclusive prefix sum of v over one wave (64 lanes); returns the lane's
 // exclusive prefix and the wave total in *total.
@@ -61,164 +52,189 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
     return x - v;
 }
 
-__global__ __launch_bounds__(1024) void group_kernel(const int32_t *__restrict__ ids, int P,
-                                                     int E, int *__restrict__ counts,
-                                                     int *__restrict__ offsets,
-                                                     int *__restrict__ act,
-                                                     int *__restrict__ nact,
-                                                     int *__restrict__ pairs,
-                                                     float *__restrict__ y_zero_rows, int N) {
-    __shared__ int s_ids[kMoeMaxPairs];
-    __shared__ int s_cnt[kMoeMaxExperts];
-    __shared__ int s_off[kMoeMaxExperts];
+// One workgroup: the touched expert of slot blockIdx.y and a block of RB = RG*V
+// of its rows; all of that expert's pairs, MC at a time.  Lane layout as in
+// the decode GEMV (stream_gemv.h): 8 lanes per 144-byte super-block, a wave's
+// 8 lane groups are RG rows x S = 8/RG column slots, a lane holds V row
+// groups; W waves x S slots cover W*S super-block columns per pass (more
+// passes when K is wider).  Per pass a wave issues the activation loads of
+// its column for the chunk's pairs and then every weight load of its V row
+// groups before any arithmetic, so the block is in flight at once.  Per lane
+// the terms of a (row, pair) add up over the passes; the 8 lanes of a group
+// (DPP), then the W waves and their S slots (LDS, in a fixed order) complete
+// a row: a fixed order for a given (N, K).
+// With zero_skipped, the last row of workgroups (blockIdx.y == gridDim.y - 1)
+// writes zeros to the rows of pairs whose id is out of range instead.
+template <int V, int MC>
+__global__ __launch_bounds__(256) void moe_gemv_kernel(
+    const uint8_t *__restrict__ w, int64_t stride, int N, int nsb, int lg_rg, int topk,
+    int act_per_slot, const int8_t *__restrict__ codes, const float *__restrict__ scales,
+    const int32_t *__restrict__ sums, const int32_t *__restrict__ ids, int P, int E,
+    int zero_skipped, float *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) int lds_m[];
+    int *s_ids = lds_m;                      // [P rounded up to 4]
+    int *s_flag = s_ids + ((P + 3) & ~3);    // [E] expert touched
+    int *s_pairs = s_flag + E;               // [P] this slot's pairs, ascending
+    __shared__ float red[kMoeWaves][8 * V][MC];
+    __shared__ int s_wt[kMoeWaves];
+    __shared__ int s_e;
+    const int RG = 1 << lg_rg, S = 8 >> lg_rg, RB = RG * V;
+    const int row_base = (int)blockIdx.x * RB;
+    if (row_base >= N) return;                     // uniform per workgroup
     const int tid = threadIdx.x, nt = blockDim.x;
-    for (int e = tid; e < E; e += nt) s_cnt[e] = 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nw = nt >> 6;
+
+    // ---- grouping, in LDS: ids, touched-expert flags
+    for (int p = tid; p < P; p += nt) s_ids[p] = ids[p];
+    for (int e = tid; e < E; e += nt) s_flag[e] = 0;
+    if (tid == 0) s_e = -1;
     __syncthreads();
-    // Counts: LDS atomics (the count does not depend on their order).
-    for (int p = tid; p < P; p += nt) {
-        const int e = ids[p];
-        s_ids[p] = e;
-        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-    }
-    __syncthreads();
-    // Offsets and the touched-expert list: the first wave scans E in chunks
-    // of 64 experts.
-    if (tid < 64) {
-        int base = 0, abase = 0;
-        for (int e0 = 0; e0 < E; e0 += 64) {
-            const int e = e0 + tid;
-            const int c = e < E ? s_cnt[e] : 0;
-            int tot, atot;
-            const int ex = wave_exclusive_scan(c, &tot);
-            const int aex = wave_exclusive_scan(c > 0 ? 1 : 0, &atot);
-            if (e < E) {
-                s_off[e] = base + ex;
-                offsets[e] = base + ex;
-                counts[e] = c;
-                if (c > 0) act[abase + aex] = e;
-            }
-            base += tot;
-            abase += atot;
-        }
-        if (tid == 0) {
-            offsets[E] = base;
-            *nact = abase;
-        }
-    }
-    __syncthreads();
-    // Placement in ascending pair order: the rank of pair p within its expert
-    // is the number of earlier pairs with the same id.
     for (int p = tid; p < P; p += nt) {
         const int e = s_ids[p];
-        if (e < 0 || e >= E) continue;
-        int r = 0;
-        for (int q = 0; q < p; ++q) r += (s_ids[q] == e);
-        pairs[s_off[e] + r] = p;
+        if (e >= 0 && e < E) s_flag[e] = 1;        // same value from every writer
     }
-    // Per-slot output without routing weights: rows of skipped pairs are zero.
-    if (y_zero_rows) {
+    __syncthreads();
+    if (zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
+        // per-slot rows of skipped pairs are zero (this block of rows)
         for (int p = 0; p < P; ++p) {
             const int e = s_ids[p];
             if (e >= 0 && e < E) continue;
-            for (int n = tid; n < N; n += nt) y_zero_rows[(int64_t)p * N + n] = 0.0f;
+            for (int n = row_base + tid; n < min(N, row_base + RB); n += nt)
+                out[(int64_t)p * N + n] = 0.0f;
         }
+        return;
     }
-}
-
-// One workgroup: touched expert act[blockIdx.y], rows [16*blockIdx.x, +16)
-// (two 8-row tiles), all of that expert's pairs in chunks of kChunk
-// activation rows.  Same lane mapping and load discipline as the decode GEMV:
-// activation loads first, then the weight loads of the wave's column, all
-// branch-free from clamped addresses; a wave takes further columns in later
-// passes when K has more than 16 super-blocks.
-__global__ __launch_bounds__(1024) void moe_gemv_kernel(
-    const uint8_t *__restrict__ w, int64_t stride, int N, int nsb, int topk,
-    int act_per_slot, const int8_t *__restrict__ codes, const float *__restrict__ scales,
-    const int32_t *__restrict__ sums, const int *__restrict__ counts,
-    const int *__restrict__ offsets, const int *__restrict__ act, const int *__restrict__ nact,
-    const int *__restrict__ pairs, float *__restrict__ out) {
-    constexpr int R = 8 * kRowTiles;
-    __shared__ float red[kMaxWaves][R][kChunk];
-    if ((int)blockIdx.y >= *nact) return;          // uniform per workgroup
-    const int e = act[blockIdx.y];
-    const int cnt = counts[e], off = offsets[e];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const int grp = lane >> 3;
-    const LaneMap L(lane & 7);
-    const int K = nsb * 256, nblk = nsb * 8;
-    const int64_t row_bytes = (int64_t)nsb * 144;
-    const uint8_t *we = w + (int64_t)e * stride;
-    int row[kRowTiles];
-#pragma unroll
-    for (int t = 0; t < kRowTiles; ++t)   // rows past N: computed, never written
-        row[t] = min((int)blockIdx.x * R + 8 * t + grp, N - 1);
-
-    for (int c0 = 0; c0 < cnt; c0 += kChunk) {
-        const int mc = min(kChunk, cnt - c0);
-        int arow[kChunk];
-#pragma unroll
-        for (int m = 0; m < kChunk; ++m) {
-            const int p = pairs[off + c0 + min(m, mc - 1)];
-            arow[m] = act_per_slot ? p : p / topk;
+    // slot a = blockIdx.y is the a-th smallest touched expert: each thread
+    // counts the flags of a range of experts, a block scan places the ranges
+    {
+        const int a = (int)blockIdx.y;
+        const int per = (E + nt - 1) / nt;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        int c = 0;
+        for (int e = e0; e < e1; ++e) c += s_flag[e];
+        int wtot;
+        const int ex = wave_exclusive_scan(c, &wtot);
+        if (lane == 0) s_wt[wave] = wtot;
+        __syncthreads();
+        int base = ex;
+        for (int k = 0; k < wave; ++k) base += s_wt[k];
+        if (a >= base && a < base + c) {
+            int k = a - base;
+            for (int e = e0; e < e1; ++e)
+                if (s_flag[e] && k-- == 0) {
+                    s_e = e;
+                    break;
+                }
         }
-        float acc[kRowTiles][kChunk];
+        __syncthreads();
+    }
+    const int e = s_e;
+    if (e < 0) return;                             // uniform: slot past the touched experts
+    // the expert's pairs in ascending order: per round of nt pairs, wave
+    // ballots and the earlier waves' counts place each one
+    int cnt = 0;
+    for (int p0 = 0; p0 < P; p0 += nt) {
+        const int p = p0 + tid;
+        const bool f = p < P && s_ids[p] == e;
+        const unsigned long long mask = __ballot(f);
+        const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0));
+        __syncthreads();                           // s_wt free again
+        if (lane == 0) s_wt[wave] = __popcll(mask);
+        __syncthreads();
+        int base = cnt;
+        for (int k = 0; k < wave; ++k) base += s_wt[k];
+        if (f) s_pairs[base + below] = p;
+        for (int k = 0; k < nw; ++k) cnt += s_wt[k];
+    }
+    __syncthreads();
+
+    const int g = lane >> 3, r = g & (RG - 1), sl = g >> lg_rg;
+    const LaneMap L(lane & 7);
+    const ScaleBits SB(lane & 7);
+    const int K = nsb * 256, nblk = nsb * 8;
+    const unsigned row_bytes = (unsigned)nsb * 144u;
+    // the block's first row in 64 bits, 32-bit offsets within it
+    const uint8_t *__restrict__ wb = w + (int64_t)e * stride + (int64_t)row_base * row_bytes;
+    const int span = nw * S;                       // columns per pass
+    const int npass = (nsb + span - 1) / span;
+
+    for (int c0 = 0; c0 < cnt; c0 += MC) {
+        const int mc = min(MC, cnt - c0);
+        int arow[MC];
 #pragma unroll
-        for (int t = 0; t < kRowTiles; ++t)
+        for (int m = 0; m < MC; ++m) {
+            const int pr = s_pairs[c0 + min(m, mc - 1)];
+            arow[m] = act_per_slot ? pr : pr / topk;
+        }
+        float acc[V][MC];
 #pragma unroll
-            for (int m = 0; m < kChunk; ++m) acc[t][m] = 0.0f;
-        for (int b = wave; b < nsb; b += nwaves) {
-            i32x4 cA[kChunk], cB[kChunk];
-            float a[kChunk];
-            int s[kChunk];
+        for (int v = 0; v < V; ++v)
 #pragma unroll
-            for (int m = 0; m < kChunk; ++m) {
-                const int8_t *cm = codes + (int64_t)arow[m] * K + 256 * b;
+            for (int m = 0; m < MC; ++m) acc[v][m] = 0.0f;
+        for (int pass = 0; pass < npass; ++pass) {
+            const int b = (pass * nw + wave) * S + sl;
+            const bool live = b < nsb;                 // per lane group
+            const int bc = min(b, nsb - 1);
+            i32x4 cA[MC], cB[MC];
+            float a[MC], sm[MC];
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const int8_t *cm = codes + (int64_t)arow[m] * K + 256 * bc;
                 cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
                 cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
-                a[m] = scales[(int64_t)arow[m] * nblk + 8 * b + L.l];
-                s[m] = sums[(int64_t)arow[m] * nblk + 8 * b + L.l];
+                a[m] = scales[(int64_t)arow[m] * nblk + 8 * bc + L.l];
+                sm[m] = (float)sums[(int64_t)arow[m] * nblk + 8 * bc + L.l];
             }
             __builtin_amdgcn_sched_barrier(0);
-            u32x4 hd[kRowTiles], qw[kRowTiles];
+            // branch-free weight loads: rows past N read row N-1 (never written);
+            // the header as one dword per lane, spread over the lane quad at use
+            unsigned hd[V];
+            u32x4 qw[V];
 #pragma unroll
-            for (int t = 0; t < kRowTiles; ++t) {
-                const uint8_t *sb = we + (int64_t)row[t] * row_bytes + (int64_t)b * 144;
-                hd[t] = load_stream16(sb);
-                qw[t] = load_stream16(sb + 16 + 16 * L.l);
+            for (int v = 0; v < V; ++v) {
+                const unsigned rr = (unsigned)(min(row_base + v * RG + r, N - 1) - row_base);
+                const unsigned o = rr * row_bytes + (unsigned)bc * 144u;
+                hd[v] = __builtin_nontemporal_load(
+                    reinterpret_cast<const unsigned *>(wb + (o + 4u * (lane & 3))));
+                qw[v] = load_stream16(wb + (o + 16u + 16u * L.l));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < kRowTiles; ++t) {
+            for (int v = 0; v < V; ++v) {
                 float ds, dm;
-                decode_scale(L, hd[t], ds, dm);
+                decode_scale_bits(SB, quad_gather(hd[v]), ds, dm);
                 int qlo[4], qhi[4];
-                unpack_nibbles(qw[t], qlo, qhi);
+                unpack_nibbles(qw[v], qlo, qhi);
 #pragma unroll
-                for (int m = 0; m < kChunk; ++m) {
+                for (int m = 0; m < MC; ++m) {
                     if (m < mc) {   // wave-uniform
                         const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
-                        acc[t][m] = fmaf(a[m], fmaf(ds, (float)D, -(dm * (float)s[m])), acc[t][m]);
+                        const float t = a[m] * fmaf(ds, (float)D, -(dm * sm[m]));
+                        acc[v][m] += live ? t : 0.0f;
                     }
                 }
             }
         }
+        // a row's terms: the 8 lanes of a group (DPP), then over the waves and
+        // each wave's S slots (LDS, wave-major order)
 #pragma unroll
-        for (int t = 0; t < kRowTiles; ++t)
+        for (int v = 0; v < V; ++v)
 #pragma unroll
-            for (int m = 0; m < kChunk; ++m) {
-                const float v = group8_sum(acc[t][m]);
-                if (L.l == 0) red[wave][8 * t + grp][m] = v;
+            for (int m = 0; m < MC; ++m) {
+                const float t = group8_sum(acc[v][m]);
+                if (L.l == 0) red[wave][sl * RB + v * RG + r][m] = t;
             }
         __syncthreads();
-        for (int i = threadIdx.x; i < R * kChunk; i += blockDim.x) {
-            const int r = i / kChunk, m = i % kChunk;
-            const int n = (int)blockIdx.x * R + r;
+        for (int i = threadIdx.x; i < RB * MC; i += blockDim.x) {
+            const int rr = i / MC, m = i % MC;
+            const int n = row_base + rr;
             if (m < mc && n < N) {
-                float v = 0.0f;
-                for (int wv = 0; wv < nwaves; ++wv) v += red[wv][r][m];
-                out[(int64_t)pairs[off + c0 + m] * N + n] = v;
+                float t = 0.0f;
+                for (int wv = 0; wv < nw; ++wv)
+                    for (int k = 0; k < S; ++k) t += red[wv][k * RB + rr][m];
+                out[(int64_t)s_pairs[c0 + m] * N + n] = t;
             }
         }
         __syncthreads();
@@ -245,7 +261,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ z
 }  // namespace
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N) {
-    return layout(T, topk, n_experts, N).bytes;
+    (void)n_experts;
+    return ws_bytes(T, topk, N);
 }
 
 hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, int64_t N,
@@ -253,32 +270,37 @@ hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, 
                            int64_t topk, const int8_t *codes, const float *scales,
                            const int32_t *sums, int act_per_slot, float *y, void *workspace,
                            hipStream_t stream) {
-    const WsLayout Lo = layout(T, topk, n_experts, N);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    int *counts = reinterpret_cast<int *>(ws + Lo.counts);
-    int *offsets = reinterpret_cast<int *>(ws + Lo.offsets);
-    int *act = reinterpret_cast<int *>(ws + Lo.act);
-    int *nact = reinterpret_cast<int *>(ws + Lo.nact);
-    int *pairs = reinterpret_cast<int *>(ws + Lo.pairs);
-    float *z = reinterpret_cast<float *>(ws + Lo.z);
+    float *z = static_cast<float *>(workspace);
     const int P = (int)(T * topk);
-
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, ids, P, (int)n_experts,
-                       counts, offsets, act, nact, pairs, route_w ? nullptr : y, (int)N);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
+    const int E = (int)n_experts;
+    const int slots = P < E ? P : E;
     const int nsb = (int)(K / kQK);
-    const int max_active = (int)(P < n_experts ? P : n_experts);
-    dim3 grid((unsigned)((N + 8 * kRowTiles - 1) / (8 * kRowTiles)), (unsigned)max_active);
+    // Column slots per wave: enough that at most kMoeWaves waves cover K in
+    // one pass (S = 8 at most; wider K takes several passes).
+    int lg_rg = 3;
+    while (lg_rg > 0 && (nsb + (8 >> lg_rg) - 1) / (8 >> lg_rg) > kMoeWaves) --lg_rg;
+    const int S = 8 >> lg_rg;
+    const int nw = std::min(kMoeWaves, (nsb + S - 1) / S);
+    const int RB = (1 << lg_rg) * kMoeV;
+    const int zero_skipped = route_w ? 0 : 1;
+    dim3 grid((unsigned)((N + RB - 1) / RB), (unsigned)(slots + zero_skipped));
     float *dst = route_w ? z : y;
-    // One column per wave and pass; a wave takes further columns in later
-    // passes when K has more than 16 super-blocks.
-    const int nw = nsb < kMaxWaves ? nsb : kMaxWaves;
-    hipLaunchKernelGGL(moe_gemv_kernel, grid, dim3(64 * nw), 0, stream, w, stride, (int)N,
-                       nsb, (int)topk, act_per_slot, codes, scales, sums, counts, offsets, act,
-                       nact, pairs, dst);
-    err = hipGetLastError();
+    const size_t lds = moe_lds_bytes(P, E);
+    // Pairs per pass: an expert has at most T pairs when each token lists
+    // distinct experts, so small T needs no wider pass (more pairs only take
+    // more passes).
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, stream, w, stride, (int)N, nsb, lg_rg,
+                           (int)topk, act_per_slot, codes, scales, sums, ids, P, E, zero_skipped,
+                           dst);
+    };
+    if (T == 1)
+        go(moe_gemv_kernel<kMoeV, 1>);
+    else if (T == 2)
+        go(moe_gemv_kernel<kMoeV, 2>);
+    else
+        go(moe_gemv_kernel<kMoeV, kMoeMC>);
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess || !route_w) return err;
 
     const int64_t total = T * N;

@@ -152,6 +152,45 @@ __device__ __forceinline__ void decode_scale(const LaneMap &L, u32x4 hd, float &
     dm = half_hi(hd.x) * (float)mn;
 }
 
+// The four dwords held by the lanes of this lane's quad (lane 4k+i holds
+// dword i), as one vector.
+__device__ __forceinline__ u32x4 quad_gather(unsigned v) {
+    u32x4 h;
+    h.x = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true);  // [0,0,0,0]
+    h.y = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true);  // [1,1,1,1]
+    h.z = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, true);  // [2,2,2,2]
+    h.w = (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, true);  // [3,3,3,3]
+    return h;
+}
+
+// d*sc_j and dmin*mn_j of sub-block j = lane l of the group, branch-free.
+// With sh = 8*(j & 3) the 6-bit value is 4 bits of X at xs plus 2 bits of Y at
+// ys: sc takes X = h1 (j < 4) or h3 (j >= 4) and Y = h1; mn takes X = h2 or
+// h3 and Y = h2; xs = sh (+4 for mn when j >= 4); ys = sh+4 (j < 4) or sh+6
+// -- the header's packing of 6-bit scales and mins (same values as
+// decode_scale, without a divergent branch).
+struct ScaleBits {
+    bool lo4;
+    int xs_sc, xs_mn, ys;
+    __device__ explicit ScaleBits(int l) {
+        lo4 = l < 4;
+        const int sh = 8 * (l & 3);
+        xs_sc = sh;
+        xs_mn = sh + (lo4 ? 0 : 4);
+        ys = sh + (lo4 ? 4 : 6);
+    }
+};
+__device__ __forceinline__ void decode_scale_bits(const ScaleBits &B, u32x4 h, float &ds,
+                                                  float &dm) {
+    const unsigned xsc = B.lo4 ? h.y : h.w, xmn = B.lo4 ? h.z : h.w;
+    const unsigned sc = __builtin_amdgcn_ubfe(xsc, B.xs_sc, 4) |
+                        (__builtin_amdgcn_ubfe(h.y, B.ys, 2) << 4);
+    const unsigned mn = __builtin_amdgcn_ubfe(xmn, B.xs_mn, 4) |
+                        (__builtin_amdgcn_ubfe(h.z, B.ys, 2) << 4);
+    ds = half_lo(h.x) * (float)sc;
+    dm = half_hi(h.x) * (float)mn;
+}
+
 // Low / high nibbles of the lane's 16-byte quant chunk, as 4 x 4 packed int8.
 __device__ __forceinline__ void unpack_nibbles(u32x4 qw, int qlo[4], int qhi[4]) {
 #pragma unroll

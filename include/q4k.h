@@ -152,9 +152,9 @@ int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,
  * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of
  * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].
  * Pairs are grouped by expert on the device (deterministically, in ascending
- * pair order), so each touched expert's weights are read once per call however
- * many tokens chose it.  Three kernels are enqueued: grouping, grouped GEMV,
- * and (with routing weights) the slot-ordered weighted sum.
+ * pair order, inside the GEMV kernel), so each touched expert's weights are
+ * read once per call however many tokens chose it.  One kernel is enqueued,
+ * and with routing weights a second for the slot-ordered weighted sum.
  *   ids          device int32 [T][topk], expected in [0, n_experts).  They live
  *                on the device and are not checked on the host; a pair whose id
  *                is out of range is skipped on the device (its per-slot output
@@ -168,8 +168,8 @@ int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,
  *   codes/scales/sums as for q4k_gemv.
  *   workspace    device buffer of at least q4k_moe_workspace_bytes(T, topk,
  *                n_experts, N) bytes, 256-byte aligned; its contents on entry
- *                are ignored (grouping tables, and the per-slot products when
- *                route_w is given).  Calls sharing a workspace must not overlap.
+ *                are ignored (it holds the per-slot products when route_w is
+ *                given).  Calls sharing a workspace must not overlap.
  * Limits: 1 <= topk <= n_experts <= 4096, T >= 1, T*topk <= 4096. */
 int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
                  int64_t expert_stride_bytes, int64_t N, int64_t K,
