@@ -468,11 +468,13 @@ def measure_small_batch(torch, dec, steps=5):
     return out
 
 
-def measure_moe(torch, q4k, qi, steps=5, layers=8):
-    """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8):
-    quantize -> grouped gate GEMV -> grouped up GEMV -> SwiGLU + Q8 -> grouped
-    down GEMV with the routing-weighted sum, over `layers` distinct seeded
-    layers per pass (1.81 GB, past the last-level cache), for T = 1 and 16."""
+def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
+    """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8) over
+    `layers` distinct seeded layers per pass (1.81 GB, past the last-level
+    cache), for each T in Ts: q4k_moe_ffn (the reported time), and the six-call
+    chain quantize -> grouped gate GEMV -> grouped up GEMV -> SwiGLU + Q8 ->
+    grouped down GEMV with the routing-weighted sum, whose output the fused
+    layer must equal bit for bit."""
     L = q4k.lib()
     dev = torch.device("cuda:0")
     E, H, F, TOPK = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
@@ -484,7 +486,7 @@ def measure_moe(torch, q4k, qi, steps=5, layers=8):
              for e in range(E)])).to(dev) for k in range(3)))
     out = {}
     cap = torch.cuda.Stream()
-    for T in (1, 16):
+    for T in Ts:
         P = T * TOPK
         routes = [qi.make_routing(T, E, TOPK, qi.routing_seed(100 * T + l)) for l in range(layers)]
         ids = [torch.from_numpy(r[0]).to(dev) for r in routes]
@@ -520,25 +522,44 @@ def measure_moe(torch, q4k, qi, steps=5, layers=8):
             if st:
                 raise RuntimeError("launch failed")
 
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=cap):
-            s = torch.cuda.current_stream().cuda_stream
-            for l in range(layers):
-                layer(l, s)
-        gr.replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
+        ws_ffn = torch.empty(q4k.q4k_moe_ffn_workspace_bytes(T, TOPK, E, H, F),
+                             dtype=torch.uint8, device=dev)
+        y2 = torch.empty_like(y)
+
+        def fused(l, s):
+            wg, wu, wd = W[l]
+            if L.q4k_moe_ffn(wg.data_ptr(), wu.data_ptr(), wd.data_ptr(), E, sgu, sdn, H, F,
+                             ids[l].data_ptr(), rws[l].data_ptr(), T, TOPK, x.data_ptr(),
+                             y2.data_ptr(), ws_ffn.data_ptr(), ws_ffn.numel(), s):
+                raise RuntimeError("launch failed")
+
+        def timed(fn):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap):
+                s = torch.cuda.current_stream().cuda_stream
+                for l in range(layers):
+                    fn(l, s)
             gr.replay()
-        b.record()
-        torch.cuda.synchronize()
-        t = a.elapsed_time(b) * 1e-3 / (steps * layers)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e-3 / (steps * layers)
+
+        t_chain = timed(layer)
+        t = timed(fused)
+        same = bool(torch.equal(y.view(torch.int32), y2.view(torch.int32)))
         distinct = np.mean([len(np.unique(r[0])) for r in routes])
         nbytes = distinct * 3 * F * H // 256 * 144
         out["T=%d" % T] = {"us_per_layer": round(t * 1e6, 2),
                            "distinct_experts": float(distinct),
                            "expert_MB_per_layer": round(nbytes / 1e6, 2),
-                           "GBps": round(nbytes / t / 1e9, 1)}
+                           "GBps": round(nbytes / t / 1e9, 1),
+                           "path": "q4k_moe_ffn (%d launches)" % (3 if T <= 2 else 5),
+                           "six_call_chain_us_per_layer": round(t_chain * 1e6, 2),
+                           "fused_equals_chain_bitwise": same}
     del W
     torch.cuda.empty_cache()
     return out

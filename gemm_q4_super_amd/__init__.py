@@ -15,6 +15,8 @@ Functions carry the C names:
     q4k_gemm_batch([(w, N), ...], K, codes, scales, sums) -> [y, ...] (<= 8 products, one launch)
     q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
                  act_per_slot, workspace=None)       -> y
+    q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H, F,
+                ids, route_w, x, workspace=None)     -> y [T, H]  (whole expert FFN layer)
 """
 from ._lib import (  # noqa: F401
     Q4KError,
@@ -23,6 +25,8 @@ from ._lib import (  # noqa: F401
     q4k_gemm,
     q4k_gemm_batch,
     q4k_gemv,
+    q4k_moe_ffn,
+    q4k_moe_ffn_workspace_bytes,
     q4k_moe_gemv,
     q4k_moe_workspace_bytes,
     q4k_quantize_act,

@@ -16,6 +16,8 @@ EXPORTED_SYMBOLS = (
     "q4k_gemm_batch",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
+    "q4k_moe_ffn",
+    "q4k_moe_ffn_workspace_bytes",
     "q4k_status_string",
 )
 
@@ -64,10 +66,15 @@ def lib():
                                    ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
         L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
+        L.q4k_moe_ffn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
+                                  ctypes.c_size_t, _P]
+        L.q4k_moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
-                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv"):
+                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
+                     "q4k_moe_ffn"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,4 +222,27 @@ def q4k_moe_gemv(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales,
                               _ptr(route_w), T, topk, _ptr(codes), _ptr(scales), _ptr(sums),
                               int(act_per_slot), _ptr(y), _ptr(workspace),
                               workspace.numel(), _stream(codes)), "q4k_moe_gemv")
+    return y
+
+
+def q4k_moe_ffn_workspace_bytes(T, topk, n_experts, H, F) -> int:
+    return int(lib().q4k_moe_ffn_workspace_bytes(T, topk, n_experts, H, F))
+
+
+def q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H, F, ids,
+                route_w, x, workspace=None, y=None):
+    import torch
+    for t, n in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (ids, "ids"),
+                 (route_w, "route_w"), (x, "x")):
+        _dev(t, n)
+    T, topk = ids.shape
+    if workspace is None:
+        nbytes = q4k_moe_ffn_workspace_bytes(T, topk, n_experts, H, F)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_moe_ffn(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n_experts, stride_gate_up,
+                             stride_down, H, F, _ptr(ids), _ptr(route_w), T, topk, _ptr(x),
+                             _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)),
+           "q4k_moe_ffn")
     return y

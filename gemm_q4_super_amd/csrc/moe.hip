@@ -1,23 +1,28 @@
-// Routed-expert grouped GEMV (the mixture-of-experts layers of "I'm making LLMs
-// work on small and old devices": intro, expert pager; each token touches only
-// its selected experts, so the bytes read per token are those experts').
+// Routed-expert grouped GEMV and expert FFN layer (the mixture-of-experts
+// layers of "I'm making LLMs work on small and old devices": intro, expert
+// pager; each token touches only its selected experts, so the bytes read per
+// token are those experts').
 //
-// One launch (two with routing weights) on the caller's stream:
-//  1. moe_gemv_kernel: grid = row blocks x touched-expert slots (+ one row of
-//     workgroups that zero the per-slot rows of skipped pairs).  Every
-//     workgroup groups the pairs itself from ids[T][topk] (at most 4096 ids,
-//     in LDS): slot a is the a-th smallest touched expert, and its pairs are
-//     taken in ascending pair order -- deterministic, no tables in memory and
-//     no separate grouping launch.  It then computes one block of that
-//     expert's rows for all of its pairs (the decode GEMV's lane layout,
-//     every load in flight before the arithmetic), MC pairs per pass with the
-//     weights in registers, so every touched expert's weights are streamed
-//     from HBM once per call (again from L2 for each further MC).  A pair
-//     whose id is outside [0, n_experts) belongs to no expert: it is skipped
-//     (its per-slot output row is zero).
-//  2. reduce_kernel (only with routing weights): y[t] = sum over slots s in
-//     order 0..topk-1 of route_w[t][s] * z[t*topk+s] -- fixed order, no float
-//     atomics, bit-reproducible.
+// moe_kernel: grid = row blocks x touched-expert slots (x 2 when the gate and
+// up projections share a launch; + one row of workgroups that zero the
+// per-slot rows of skipped pairs).  Every workgroup groups the pairs itself
+// from ids[T][topk] (at most 4096 ids, in LDS): slot a is the a-th smallest
+// touched expert, and its pairs are taken in ascending pair order --
+// deterministic, no tables in memory and no separate grouping launch.  It then
+// computes one block of that expert's rows for all of its pairs (the decode
+// GEMV's lane layout, every load in flight before the arithmetic), MC pairs
+// per pass with the weights in registers, so every touched expert's weights
+// are streamed from HBM once per call (again from L2 for each further MC).  A
+// pair whose id is outside [0, n_experts) belongs to no expert: it is skipped
+// (its per-slot output row is zero).  The activation of a pair is
+//  * Q8 rows prepared by q4k_quantize_act (q4k_moe_gemv), or
+//  * fp32 rows quantized in the kernel (the FFN's gate|up launch), or
+//  * SwiGLU(g, u) of fp32 rows, quantized in the kernel (the FFN's down),
+// all through the same quantizer and SwiGLU arithmetic as q4k_quantize_act,
+// so the fused layer's codes equal the unfused chain's bit for bit.
+// reduce_kernel (with routing weights): y[t] = sum over slots s in order
+// 0..topk-1 of route_w[t][s] * z[t*topk+s] -- fixed order, no float atomics,
+// bit-reproducible.
 #include <algorithm>
 
 #include "q4k_device.h"
@@ -29,14 +34,38 @@ namespace {
 constexpr int kMoeWaves = 4;         // waves per workgroup, at most
 constexpr int kMoeV = 8;             // row groups per lane
 constexpr int kMoeMC = 4;            // pairs per pass over a weight block
+constexpr int kStageBytes = 256 + 64;   // one staged column: codes, 8 scales, 8 sums
+constexpr int kStageSlots = 2;          // column slots per wave with fp32 activations, at most
+constexpr int kFuseMaxT = 2;            // tokens up to which the FFN quantizes in its GEMVs
 
-// Workspace: the per-slot products z [T*topk][N] when routing weights are given.
-size_t ws_bytes(int64_t T, int64_t topk, int64_t N) {
-    return (size_t)((4 * T * topk * N + 255) & ~int64_t(255));
+enum { ACT_Q8 = 0, ACT_F32 = 1, ACT_SWIGLU = 2 };
+
+struct MoeArgs {
+    const uint8_t *w[2];       // expert matrices (w[1]: second projection of a shared launch)
+    float *out[2];
+    int64_t stride;            // bytes between experts
+    int N, nsb, lg_rg, topk, act_per_slot, P, E, slots, zero_skipped;
+    const int8_t *codes;       // ACT_Q8
+    const float *scales;
+    const int32_t *sums;
+    const float *xa, *xb;      // ACT_F32: x [.][K]; ACT_SWIGLU: g, u [P][K]
+    const int32_t *ids;
+};
+
+__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
+
+// LDS of the grouping: ids (padded to 4), expert flags, pair list.
+__host__ __device__ constexpr size_t group_bytes(int P, int E) {
+    return sizeof(int) * ((size_t)((P + 3) & ~3) + (size_t)E + P);
 }
 
-// Dynamic LDS of moe_gemv_kernel: ids (padded to 4), expert flags, pair list.
-size_t moe_lds_bytes(int P, int E) { return sizeof(int) * ((size_t)((P + 3) & ~3) + (size_t)E + P); }
+// Dynamic LDS of moe_kernel: the grouping, and for fp32 activations the
+// staged Q8 columns of each wave.
+size_t moe_lds_bytes(int P, int E, int mode, int nw, int S, int MC) {
+    size_t b = group_bytes(P, E);
+    if (mode != ACT_Q8) b = align16(b) + (size_t)nw * S * MC * kStageBytes;
+    return b;
+}
 
 // Exclusive prefix sum of v over one wave (64 lanes); returns the lane's
 // exclusive prefix and the wave total in *total.
@@ -52,26 +81,25 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
     return x - v;
 }
 
-// One workgroup: the touched expert of slot blockIdx.y and a block of RB = RG*V
-// of its rows; all of that expert's pairs, MC at a time.  Lane layout as in
-// the decode GEMV (stream_gemv.h): 8 lanes per 144-byte super-block, a wave's
-// 8 lane groups are RG rows x S = 8/RG column slots, a lane holds V row
-// groups; W waves x S slots cover W*S super-block columns per pass (more
-// passes when K is wider).  Per pass a wave issues the activation loads of
-// its column for the chunk's pairs and then every weight load of its V row
-// groups before any arithmetic, so the block is in flight at once.  Per lane
+// One workgroup: the touched expert of slot a (blockIdx.y, past the first
+// projection's slots for the second) and a block of RB = RG*V of its rows;
+// all of that expert's pairs, MC at a time.  Lane layout as in the decode
+// GEMV (stream_gemv.h): 8 lanes per 144-byte super-block, a wave's 8 lane
+// groups are RG rows x S = 8/RG column slots, a lane holds V row groups; W
+// waves x S slots cover W*S super-block columns per pass (more passes when K
+// is wider).  Per pass a wave issues the activation loads of its columns for
+// the chunk's pairs and then every weight load of its V row groups before any
+// arithmetic, so the block is in flight at once; fp32 activations are then
+// quantized into the wave's own LDS stage (no workgroup barrier).  Per lane
 // the terms of a (row, pair) add up over the passes; the 8 lanes of a group
-// (DPP), then the W waves and their S slots (LDS, in a fixed order) complete
-// a row: a fixed order for a given (N, K).
+// (DPP), then the W waves and their S slots (LDS, in a fixed order) complete a
+// row: a fixed order for a given K (the launch shape depends on K alone).
 // With zero_skipped, the last row of workgroups (blockIdx.y == gridDim.y - 1)
 // writes zeros to the rows of pairs whose id is out of range instead.
-template <int V, int MC>
-__global__ __launch_bounds__(256) void moe_gemv_kernel(
-    const uint8_t *__restrict__ w, int64_t stride, int N, int nsb, int lg_rg, int topk,
-    int act_per_slot, const int8_t *__restrict__ codes, const float *__restrict__ scales,
-    const int32_t *__restrict__ sums, const int32_t *__restrict__ ids, int P, int E,
-    int zero_skipped, float *__restrict__ out) {
+template <int V, int MC, int MODE>
+__global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
     extern __shared__ __attribute__((aligned(16))) int lds_m[];
+    const int P = A.P, E = A.E, N = A.N, nsb = A.nsb, lg_rg = A.lg_rg;
     int *s_ids = lds_m;                      // [P rounded up to 4]
     int *s_flag = s_ids + ((P + 3) & ~3);    // [E] expert touched
     int *s_pairs = s_flag + E;               // [P] this slot's pairs, ascending
@@ -86,7 +114,7 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
     const int nw = nt >> 6;
 
     // ---- grouping, in LDS: ids, touched-expert flags
-    for (int p = tid; p < P; p += nt) s_ids[p] = ids[p];
+    for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
     for (int e = tid; e < E; e += nt) s_flag[e] = 0;
     if (tid == 0) s_e = -1;
     __syncthreads();
@@ -95,20 +123,21 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
         if (e >= 0 && e < E) s_flag[e] = 1;        // same value from every writer
     }
     __syncthreads();
-    if (zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
+    if (A.zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
         // per-slot rows of skipped pairs are zero (this block of rows)
         for (int p = 0; p < P; ++p) {
             const int e = s_ids[p];
             if (e >= 0 && e < E) continue;
             for (int n = row_base + tid; n < min(N, row_base + RB); n += nt)
-                out[(int64_t)p * N + n] = 0.0f;
+                A.out[0][(int64_t)p * N + n] = 0.0f;
         }
         return;
     }
-    // slot a = blockIdx.y is the a-th smallest touched expert: each thread
-    // counts the flags of a range of experts, a block scan places the ranges
+    const int mi = (int)blockIdx.y >= A.slots ? 1 : 0;   // which projection
+    // slot a is the a-th smallest touched expert: each thread counts the
+    // flags of a range of experts, a block scan places the ranges
     {
-        const int a = (int)blockIdx.y;
+        const int a = (int)blockIdx.y - mi * A.slots;
         const int per = (E + nt - 1) / nt;
         const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
         int c = 0;
@@ -155,10 +184,16 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
     const ScaleBits SB(lane & 7);
     const int K = nsb * 256, nblk = nsb * 8;
     const unsigned row_bytes = (unsigned)nsb * 144u;
+    float *__restrict__ out = A.out[mi];
     // the block's first row in 64 bits, 32-bit offsets within it
-    const uint8_t *__restrict__ wb = w + (int64_t)e * stride + (int64_t)row_base * row_bytes;
+    const uint8_t *__restrict__ wb =
+        A.w[mi] + (int64_t)e * A.stride + (int64_t)row_base * row_bytes;
     const int span = nw * S;                       // columns per pass
     const int npass = (nsb + span - 1) / span;
+    // this wave's activation stage: [S][MC] columns of codes, scales, sums
+    uint8_t *stage = reinterpret_cast<uint8_t *>(lds_m) + align16(group_bytes(P, E)) +
+                     (size_t)wave * S * MC * kStageBytes;
+    const int qblk = lane >> 3, qsub = lane & 7;   // quantizer layout: block, 4 values
 
     for (int c0 = 0; c0 < cnt; c0 += MC) {
         const int mc = min(MC, cnt - c0);
@@ -166,7 +201,7 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
             const int pr = s_pairs[c0 + min(m, mc - 1)];
-            arow[m] = act_per_slot ? pr : pr / topk;
+            arow[m] = A.act_per_slot ? pr : pr / A.topk;
         }
         float acc[V][MC];
 #pragma unroll
@@ -174,18 +209,39 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
 #pragma unroll
             for (int m = 0; m < MC; ++m) acc[v][m] = 0.0f;
         for (int pass = 0; pass < npass; ++pass) {
-            const int b = (pass * nw + wave) * S + sl;
+            const int wcol = (pass * nw + wave) * S;   // the wave's first column
+            const int b = wcol + sl;
             const bool live = b < nsb;                 // per lane group
             const int bc = min(b, nsb - 1);
             i32x4 cA[MC], cB[MC];
             float a[MC], sm[MC];
+            // fp32 activations: launches use S <= kStageSlots (so RG >= 4)
+            constexpr int SX = MODE == ACT_Q8 ? 1 : kStageSlots;
+            constexpr int SU = MODE == ACT_SWIGLU ? kStageSlots : 1;
+            f32x4 xv[SX][MC], xu[SU][MC];
+            if constexpr (MODE == ACT_Q8) {
 #pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const int8_t *cm = codes + (int64_t)arow[m] * K + 256 * bc;
-                cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
-                cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
-                a[m] = scales[(int64_t)arow[m] * nblk + 8 * bc + L.l];
-                sm[m] = (float)sums[(int64_t)arow[m] * nblk + 8 * bc + L.l];
+                for (int m = 0; m < MC; ++m) {
+                    const int8_t *cm = A.codes + (int64_t)arow[m] * K + 256 * bc;
+                    cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
+                    cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
+                    a[m] = A.scales[(int64_t)arow[m] * nblk + 8 * bc + L.l];
+                    sm[m] = (float)A.sums[(int64_t)arow[m] * nblk + 8 * bc + L.l];
+                }
+            } else {
+                // fp32 activation of the wave's S columns, quantizer layout
+#pragma unroll
+                for (int j = 0; j < SX; ++j) {
+                    if (j >= S) break;                 // wave-uniform
+                    const int col = min(wcol + j, nsb - 1);
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) {
+                        const int64_t o = (int64_t)arow[m] * K + 256 * col + 32 * qblk + 4 * qsub;
+                        xv[j][m] = *reinterpret_cast<const f32x4 *>(A.xa + o);
+                        if constexpr (MODE == ACT_SWIGLU)
+                            xu[j][m] = *reinterpret_cast<const f32x4 *>(A.xb + o);
+                    }
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             // branch-free weight loads: rows past N read row N-1 (never written);
@@ -201,6 +257,35 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
                 qw[v] = load_stream16(wb + (o + 16u + 16u * L.l));
             }
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MODE != ACT_Q8) {
+                // quantize into the wave's stage, then read it in the dot layout
+#pragma unroll
+                for (int j = 0; j < SX; ++j) {
+                    if (j >= S) break;
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) {
+                        f32x4 v4 = xv[j][m];
+                        if constexpr (MODE == ACT_SWIGLU) v4 = swiglu4(v4, xu[j][m]);
+                        const Q8Lane q = quantize_block8(v4);
+                        uint8_t *st = stage + (size_t)(j * MC + m) * kStageBytes;
+                        *reinterpret_cast<unsigned *>(st + 32 * qblk + 4 * qsub) = q.codes;
+                        if (qsub == 0) {
+                            reinterpret_cast<float *>(st + 256)[qblk] = q.d;
+                            reinterpret_cast<float *>(st + 288)[qblk] = (float)q.sum;
+                        }
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage is written
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int m = 0; m < MC; ++m) {
+                    const uint8_t *st = stage + (size_t)(sl * MC + m) * kStageBytes;
+                    cA[m] = *reinterpret_cast<const i32x4 *>(st + L.offA);
+                    cB[m] = *reinterpret_cast<const i32x4 *>(st + L.offB);
+                    a[m] = reinterpret_cast<const float *>(st + 256)[L.l];
+                    sm[m] = reinterpret_cast<const float *>(st + 288)[L.l];
+                }
+            }
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 float ds, dm;
@@ -215,6 +300,11 @@ __global__ __launch_bounds__(256) void moe_gemv_kernel(
                         acc[v][m] += live ? t : 0.0f;
                     }
                 }
+            }
+            if constexpr (MODE != ACT_Q8) {
+                // the stage is rewritten by the next pass: reads done first
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
             }
         }
         // a row's terms: the 8 lanes of a group (DPP), then over the waves and
@@ -258,11 +348,63 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ z
     y[i] = v;
 }
 
+// Launch shape for K = 256*nsb: column slots per wave enough that at most
+// kMoeWaves waves cover K in one pass (S = kStageSlots at most; wider K takes
+// several passes).  The shape depends on K alone -- not on the activation
+// form -- so the fused layer and the unfused chain add in the same order.
+struct Shape {
+    int lg_rg, S, nw, RB;
+};
+Shape shape(int64_t nsb) {
+    Shape s;
+    s.lg_rg = 3;
+    while ((8 >> s.lg_rg) < kStageSlots &&
+           (nsb + (8 >> s.lg_rg) - 1) / (8 >> s.lg_rg) > kMoeWaves)
+        --s.lg_rg;
+    s.S = 8 >> s.lg_rg;
+    s.nw = (int)std::min<int64_t>(kMoeWaves, (nsb + s.S - 1) / s.S);
+    s.RB = (1 << s.lg_rg) * kMoeV;
+    return s;
+}
+
+// Pairs per pass: an expert has at most T pairs when each token lists
+// distinct experts, so small T needs no wider pass (more pairs only take more
+// passes).
+template <int MODE>
+hipError_t launch_kernel(const MoeArgs &A, int64_t T, int nmat, const Shape &sh,
+                         hipStream_t stream) {
+    dim3 grid((unsigned)((A.N + sh.RB - 1) / sh.RB),
+              (unsigned)(nmat * A.slots + A.zero_skipped));
+    auto go = [&](auto kern, int MC) {
+        hipLaunchKernelGGL(kern, grid, dim3(64 * sh.nw),
+                           moe_lds_bytes(A.P, A.E, MODE, sh.nw, sh.S, MC), stream, A);
+    };
+    if (T == 1)
+        go(moe_kernel<kMoeV, 1, MODE>, 1);
+    else if (T == 2)
+        go(moe_kernel<kMoeV, 2, MODE>, 2);
+    else
+        go(moe_kernel<kMoeV, kMoeMC, MODE>, kMoeMC);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const float *z, const float *route_w, const int32_t *ids, int64_t E,
+                         int64_t T, int64_t topk, int64_t N, float *y, hipStream_t stream) {
+    const int64_t total = T * N;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, z, route_w, ids, (int)E, (int)T, (int)topk, (int)N, y);
+    return hipGetLastError();
+}
+
+size_t f32_bytes(int64_t rows, int64_t cols) {
+    return (size_t)((4 * rows * cols + 255) & ~int64_t(255));
+}
+
 }  // namespace
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N) {
     (void)n_experts;
-    return ws_bytes(T, topk, N);
+    return f32_bytes(T * topk, N);   // per-slot products z
 }
 
 hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, int64_t N,
@@ -271,42 +413,119 @@ hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, 
                            const int32_t *sums, int act_per_slot, float *y, void *workspace,
                            hipStream_t stream) {
     float *z = static_cast<float *>(workspace);
-    const int P = (int)(T * topk);
-    const int E = (int)n_experts;
-    const int slots = P < E ? P : E;
-    const int nsb = (int)(K / kQK);
-    // Column slots per wave: enough that at most kMoeWaves waves cover K in
-    // one pass (S = 8 at most; wider K takes several passes).
-    int lg_rg = 3;
-    while (lg_rg > 0 && (nsb + (8 >> lg_rg) - 1) / (8 >> lg_rg) > kMoeWaves) --lg_rg;
-    const int S = 8 >> lg_rg;
-    const int nw = std::min(kMoeWaves, (nsb + S - 1) / S);
-    const int RB = (1 << lg_rg) * kMoeV;
-    const int zero_skipped = route_w ? 0 : 1;
-    dim3 grid((unsigned)((N + RB - 1) / RB), (unsigned)(slots + zero_skipped));
-    float *dst = route_w ? z : y;
-    const size_t lds = moe_lds_bytes(P, E);
-    // Pairs per pass: an expert has at most T pairs when each token lists
-    // distinct experts, so small T needs no wider pass (more pairs only take
-    // more passes).
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, stream, w, stride, (int)N, nsb, lg_rg,
-                           (int)topk, act_per_slot, codes, scales, sums, ids, P, E, zero_skipped,
-                           dst);
-    };
-    if (T == 1)
-        go(moe_gemv_kernel<kMoeV, 1>);
-    else if (T == 2)
-        go(moe_gemv_kernel<kMoeV, 2>);
-    else
-        go(moe_gemv_kernel<kMoeV, kMoeMC>);
-    hipError_t err = hipGetLastError();
+    const int P = (int)(T * topk), E = (int)n_experts;
+    const Shape sh = shape(K / kQK);
+    MoeArgs A = {};
+    A.w[0] = A.w[1] = w;
+    A.out[0] = A.out[1] = route_w ? z : y;
+    A.stride = stride;
+    A.N = (int)N;
+    A.nsb = (int)(K / kQK);
+    A.lg_rg = sh.lg_rg;
+    A.topk = (int)topk;
+    A.act_per_slot = act_per_slot;
+    A.P = P;
+    A.E = E;
+    A.slots = P < E ? P : E;
+    A.zero_skipped = route_w ? 0 : 1;
+    A.codes = codes;
+    A.scales = scales;
+    A.sums = sums;
+    A.ids = ids;
+    hipError_t err = launch_kernel<ACT_Q8>(A, T, 1, sh, stream);
     if (err != hipSuccess || !route_w) return err;
+    return launch_reduce(z, route_w, ids, n_experts, T, topk, N, y, stream);
+}
 
-    const int64_t total = T * N;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, z, route_w, ids, (int)n_experts, (int)T, (int)topk, (int)N, y);
-    return hipGetLastError();
+// Q8 rows: codes, scales, sums (each 256-byte aligned).
+size_t q8_rows_bytes(int64_t rows, int64_t K) {
+    return f32_bytes(rows, K / 4) + 2 * f32_bytes(rows, K / 32);
+}
+
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t H, int64_t F) {
+    const int64_t P = T * topk;
+    // g, u, z; Q8 of x and of h for the unfused activations of larger T
+    return 2 * f32_bytes(P, F) + f32_bytes(P, H) + q8_rows_bytes(T, H) + q8_rows_bytes(P, F);
+}
+
+hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                          int64_t n_experts, int64_t stride_gu, int64_t stride_down, int64_t H,
+                          int64_t F, const int32_t *ids, const float *route_w, int64_t T,
+                          int64_t topk, const float *x, float *y, void *workspace,
+                          hipStream_t stream) {
+    const int64_t P = T * topk;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *g = reinterpret_cast<float *>(ws);
+    float *u = reinterpret_cast<float *>(ws + f32_bytes(P, F));
+    float *z = reinterpret_cast<float *>(ws + 2 * f32_bytes(P, F));
+    uint8_t *q8 = ws + 2 * f32_bytes(P, F) + f32_bytes(P, H);
+    int8_t *xc = reinterpret_cast<int8_t *>(q8);
+    float *xs = reinterpret_cast<float *>(q8 + f32_bytes(T, H / 4));
+    int32_t *xsu = reinterpret_cast<int32_t *>(q8 + f32_bytes(T, H / 4) + f32_bytes(T, H / 32));
+    uint8_t *hq = q8 + q8_rows_bytes(T, H);
+    int8_t *hc = reinterpret_cast<int8_t *>(hq);
+    float *hs = reinterpret_cast<float *>(hq + f32_bytes(P, F / 4));
+    int32_t *hsu = reinterpret_cast<int32_t *>(hq + f32_bytes(P, F / 4) + f32_bytes(P, F / 32));
+    const int E = (int)n_experts;
+    // In-kernel activations quantize a token's row once per workgroup that
+    // reads it (row blocks x experts); past a few tokens that repetition costs
+    // more than the launches a separate quantizer needs.  Same codes either way.
+    const bool fuse = T <= kFuseMaxT;
+    // gate and up in one launch
+    const Shape sh1 = shape(H / kQK);
+    MoeArgs A = {};
+    A.w[0] = w_gate;
+    A.w[1] = w_up;
+    A.out[0] = g;
+    A.out[1] = u;
+    A.stride = stride_gu;
+    A.N = (int)F;
+    A.nsb = (int)(H / kQK);
+    A.lg_rg = sh1.lg_rg;
+    A.topk = (int)topk;
+    A.act_per_slot = 0;
+    A.P = (int)P;
+    A.E = E;
+    A.slots = (int)(P < E ? P : E);
+    A.zero_skipped = 0;
+    A.ids = ids;
+    hipError_t err;
+    if (fuse) {
+        A.xa = x;
+        err = launch_kernel<ACT_F32>(A, T, 2, sh1, stream);
+    } else {
+        err = launch_quantize(x, T, H, nullptr, xc, xs, xsu, stream);
+        if (err != hipSuccess) return err;
+        A.codes = xc;
+        A.scales = xs;
+        A.sums = xsu;
+        err = launch_kernel<ACT_Q8>(A, T, 2, sh1, stream);
+    }
+    if (err != hipSuccess) return err;
+    // down: SwiGLU(g, u) quantized in the kernel, per-slot products z
+    const Shape sh2 = shape(F / kQK);
+    MoeArgs B = A;
+    B.w[0] = B.w[1] = w_down;
+    B.out[0] = B.out[1] = z;
+    B.stride = stride_down;
+    B.N = (int)H;
+    B.nsb = (int)(F / kQK);
+    B.lg_rg = sh2.lg_rg;
+    B.act_per_slot = 1;
+    if (fuse) {
+        B.xa = g;
+        B.xb = u;
+        err = launch_kernel<ACT_SWIGLU>(B, T, 1, sh2, stream);
+    } else {
+        err = launch_quantize(u, P, F, g, hc, hs, hsu, stream);
+        if (err != hipSuccess) return err;
+        B.codes = hc;
+        B.scales = hs;
+        B.sums = hsu;
+        err = launch_kernel<ACT_Q8>(B, T, 1, sh2, stream);
+    }
+    if (err != hipSuccess) return err;
+    return launch_reduce(z, route_w, ids, n_experts, T, topk, H, y, stream);
 }
 
 }  // namespace q4k

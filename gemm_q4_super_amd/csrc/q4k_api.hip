@@ -134,6 +134,42 @@ int q4k_moe_gemv(const void *w_experts, int64_t n_experts, int64_t expert_stride
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t H,
+                                   int64_t F) {
+    if (T < 1 || topk < 1 || n_experts < 1 || topk > n_experts ||
+        T * topk > q4k::kMoeMaxPairs || n_experts > q4k::kMoeMaxExperts || H < 1 ||
+        H > kMaxDim || F < 1 || F > kMaxDim)
+        return 0;
+    return q4k::moe_ffn_workspace_bytes(T, topk, H, F);
+}
+
+int q4k_moe_ffn(const void *w_gate, const void *w_up, const void *w_down, int64_t n_experts,
+                int64_t stride_gate_up, int64_t stride_down, int64_t H, int64_t F,
+                const int32_t *ids, const float *route_w, int64_t T, int64_t topk,
+                const float *x, float *y, void *workspace, size_t workspace_bytes,
+                void *stream) {
+    if (!w_gate || !w_up || !w_down || !ids || !route_w || !x || !y) return Q4K_EINVAL;
+    if (H < q4k::kQK || H % q4k::kQK != 0 || F < q4k::kQK || F % q4k::kQK != 0 ||
+        H > kMaxDim || F > kMaxDim)
+        return Q4K_ESHAPE;
+    if (n_experts < 1 || n_experts > q4k::kMoeMaxExperts || T < 1 || topk < 1 ||
+        topk > n_experts || T * topk > q4k::kMoeMaxPairs)
+        return Q4K_ESHAPE;
+    if (stride_gate_up < F * (H / q4k::kQK) * q4k::kSB || stride_gate_up % 16 != 0 ||
+        stride_down < H * (F / q4k::kQK) * q4k::kSB || stride_down % 16 != 0)
+        return Q4K_ESHAPE;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
+        !aligned(x, 16) || !aligned(y, 4) || !aligned(ids, 4) || !aligned(route_w, 4))
+        return Q4K_EALIGN;
+    const size_t need = q4k::moe_ffn_workspace_bytes(T, topk, H, F);
+    if (!workspace || workspace_bytes < need) return Q4K_EWORKSPACE;
+    if (!aligned(workspace, 256)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_moe_ffn(
+        static_cast<const uint8_t *>(w_gate), static_cast<const uint8_t *>(w_up),
+        static_cast<const uint8_t *>(w_down), n_experts, stride_gate_up, stride_down, H, F, ids,
+        route_w, T, topk, x, y, workspace, static_cast<hipStream_t>(stream)));
+}
+
 const char *q4k_status_string(int status) {
     switch (status) {
     case Q4K_OK: return "ok";

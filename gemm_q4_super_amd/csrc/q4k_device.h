@@ -109,6 +109,19 @@ __device__ __forceinline__ Q8Lane quantize_block8(f32x4 v) {
     return r;
 }
 
+// SwiGLU of four values, h = silu(g) * u = g / (1 + e^-g) * u, evaluated in
+// fp64 from the fp32 g, u and rounded to fp32 once (the expert FFN's
+// nonlinearity; the same arithmetic wherever h is formed).
+__device__ __forceinline__ f32x4 swiglu4(f32x4 g, f32x4 u) {
+    f32x4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double gd = (double)g[i];
+        h[i] = (float)(gd / (1.0 + exp(-gd)) * (double)u[i]);
+    }
+    return h;
+}
+
 __device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }

@@ -69,4 +69,12 @@ hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride,
                            const float *scales, const int32_t *sums, int act_per_slot,
                            float *y, void *workspace, hipStream_t stream);
 
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t H, int64_t F);
+
+hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
+                          int64_t n_experts, int64_t stride_gu, int64_t stride_down, int64_t H,
+                          int64_t F, const int32_t *ids, const float *route_w, int64_t T,
+                          int64_t topk, const float *x, float *y, void *workspace,
+                          hipStream_t stream);
+
 }  // namespace q4k

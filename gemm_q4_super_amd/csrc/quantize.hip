@@ -30,14 +30,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     if (blk >= nblocks) return;
     const int64_t off = blk * 32 + sub * 4;
     f32x4 v = *reinterpret_cast<const f32x4 *>(x + off);
-    if (GATED) {
-        f32x4 g = *reinterpret_cast<const f32x4 *>(gate + off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double gd = (double)g[i];
-            v[i] = (float)(gd / (1.0 + exp(-gd)) * (double)v[i]);
-        }
-    }
+    if (GATED) v = swiglu4(*reinterpret_cast<const f32x4 *>(gate + off), v);
     const Q8Lane q = quantize_block8(v);
     *reinterpret_cast<unsigned *>(codes + off) = q.codes;
     if (sub == 0) {

@@ -181,6 +181,38 @@ int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
 /* Workspace bytes q4k_moe_gemv needs for these sizes (0 on invalid sizes). */
 size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N);
 
+/* Routed-expert FFN layer (gate, up, SwiGLU, down, routed sum): for each
+ * token t,
+ *   y[t] = sum_s route_w[t][s] * Wd[e] . Q8(h),  h = silu(Wg[e] . Q8(x_t)) * (Wu[e] . Q8(x_t)),
+ * e = ids[t][s], silu(g) = g / (1 + e^-g) in fp64 rounded to fp32 once.  The
+ * result is bit-identical to the unfused chain q4k_quantize_act(x);
+ * q4k_moe_gemv(gate), (up); q4k_quantize_act(u, gate = g);
+ * q4k_moe_gemv(down, route_w, act_per_slot = 1).  The gate and up products
+ * share one launch; for T <= 2 the activations are quantized (and h formed)
+ * inside the GEMV kernels, three launches in all; for larger T, where that
+ * would repeat the work in every workgroup reading a row, the quantizer runs
+ * once per row as its own launch (five in all).
+ *   w_gate, w_up  n_experts Q4_K matrices of F rows x H columns each, at
+ *                 stride_gate_up bytes (>= F*(H/256)*144, multiple of 16)
+ *   w_down        n_experts Q4_K matrices of H rows x F columns, at stride_down
+ *   ids, route_w  device int32 / fp32 [T][topk]; ids as for q4k_moe_gemv
+ *                 (out-of-range ids are skipped); route_w is required
+ *   x             device fp32 [T][H], 16-byte aligned; y: device fp32 [T][H]
+ *   workspace     device buffer of at least q4k_moe_ffn_workspace_bytes(T,
+ *                 topk, n_experts, H, F) bytes, 256-byte aligned (g, u, the
+ *                 per-slot down products and Q8 rows of x and h); contents on
+ *                 entry are ignored; calls sharing a workspace must not overlap.
+ * Limits as for q4k_moe_gemv; H and F multiples of 256. */
+int q4k_moe_ffn(const void *w_gate, const void *w_up, const void *w_down, int64_t n_experts,
+                int64_t stride_gate_up, int64_t stride_down, int64_t H, int64_t F,
+                const int32_t *ids, const float *route_w, int64_t T, int64_t topk,
+                const float *x, float *y, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Workspace bytes q4k_moe_ffn needs for these sizes (0 on invalid sizes). */
+size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t H,
+                                   int64_t F);
+
 /* Static description of a status code. */
 const char *q4k_status_string(int status);
 

@@ -160,3 +160,34 @@ def test_moe_argument_checks(L):
     assert call(wsb=ws - 1) == EWORKSPACE
     assert call(ws=A + 16) == EALIGN
     assert call(w=A + 4) == EALIGN
+
+
+def test_moe_ffn_argument_checks(L):
+    f = L.q4k_moe_ffn
+    H, F, E, T, topk = 2048, 1024, 64, 16, 8
+    ws = q4k.q4k_moe_ffn_workspace_bytes(T, topk, E, H, F)
+    assert ws >= T * topk * (2 * F + H) * 4
+    assert q4k.q4k_moe_ffn_workspace_bytes(1, 9, 8, H, F) == 0
+    assert q4k.q4k_moe_ffn_workspace_bytes(1, 1, 8, 0, F) == 0
+    sgu, sd = F * (H // 256) * 144, H * (F // 256) * 144
+
+    def call(**kw):
+        a = dict(wg=A, wu=A, wd=A, E=E, sgu=sgu, sd=sd, H=H, F=F, ids=A, rw=A, T=T, topk=topk,
+                 x=A, y=A, ws=A, wsb=ws)
+        a.update(kw)
+        return f(a["wg"], a["wu"], a["wd"], a["E"], a["sgu"], a["sd"], a["H"], a["F"],
+                 a["ids"], a["rw"], a["T"], a["topk"], a["x"], a["y"], a["ws"], a["wsb"], None)
+    assert call(rw=None) == EINVAL          # the layer's output is the routed sum
+    assert call(wu=None) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(H=2000) == ESHAPE
+    assert call(F=1000) == ESHAPE
+    assert call(topk=65) == ESHAPE
+    assert call(T=600) == ESHAPE
+    assert call(sgu=sgu - 16) == ESHAPE
+    assert call(sd=sd + 8) == ESHAPE
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=ws - 1) == EWORKSPACE
+    assert call(ws=A + 16) == EALIGN
+    assert call(x=A + 4) == EALIGN
+    assert call(wd=A + 4) == EALIGN

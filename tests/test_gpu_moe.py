@@ -186,3 +186,58 @@ def test_moe_layer_chain(q4k, oracle_lib, layer, T):
     assert (err <= tol).all(), "chain y outside tolerance + admitted-flip bound"
     print("chain: %d h-code flips of %d, max y err %.3g" % (int(mism.sum()), mism.size,
                                                           float(err.max())))
+
+
+def _chain(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_):
+    sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
+    xc, xs, xsu = q4k.q4k_quantize_act(x)
+    g = q4k.q4k_moe_gemv(dwg, n_exp, sgu, F_, H_, dids, None, xc, xs, xsu, 0)
+    u = q4k.q4k_moe_gemv(dwu, n_exp, sgu, F_, H_, dids, None, xc, xs, xsu, 0)
+    hc, hs, hsu = q4k.q4k_quantize_act(u, g)
+    return q4k.q4k_moe_gemv(dwd, n_exp, sd, H_, F_, dids, drw, hc, hs, hsu, 1)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
+def test_moe_ffn_bit_identical_to_chain(q4k, layer, T):
+    """The fused layer (gate|up in one launch; for T <= 2 x quantized and
+    SwiGLU + Q8 formed inside the GEMV kernels, beyond that by the quantizer
+    kernel) equals the six-call chain bit for bit; the chain itself is checked
+    against the oracle by test_moe_layer_chain."""
+    import torch
+    wg, wu, wd = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(200 + T))
+    x = to_dev(qi.make_act(T, H, qi.act_seed(64000 + T)))
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, E, STRIDE_GU, STRIDE_D, H, F, dids, drw, x)
+    y2 = _chain(q4k, dwg, dwu, dwd, dids, drw, x, E, H, F)
+    torch.cuda.synchronize()
+    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.isfinite(y1).all()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+
+
+def test_moe_ffn_repeated_and_bad_ids_and_two_passes(q4k, oracle_lib):
+    """Small experts with K spanning several passes (H = 3072: 12 columns per
+    row), 20 tokens on one expert (several pair chunks), a repeated expert and
+    out-of-range ids: fused equals chain bit for bit."""
+    import torch
+    n_exp, H_, F_, T, topk = 6, 3072, 512, 20, 2
+    wg = np.concatenate([qi.make_q4k_bytes(F_, H_, 1300 + e) for e in range(n_exp)])
+    wu = np.concatenate([qi.make_q4k_bytes(F_, H_, 1400 + e) for e in range(n_exp)])
+    wd = np.concatenate([qi.make_q4k_bytes(H_, F_, 1500 + e) for e in range(n_exp)])
+    ids = np.zeros((T, topk), np.int32)
+    ids[:, 0] = 2
+    ids[:, 1] = np.arange(T) % n_exp
+    ids[ids[:, 1] == 2, 1] = 4
+    ids[3, 1] = -5
+    ids[9, 1] = n_exp
+    rw = np.random.default_rng(3).standard_normal((T, topk)).astype(np.float32)
+    x = to_dev(qi.make_act(T, H_, 91))
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
+    y2 = _chain(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
+    torch.cuda.synchronize()
+    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.isfinite(y1).all()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
