@@ -199,6 +199,8 @@ hipError_t launch_m(const GemvArgs &B, int nsb, hipStream_t stream) {
 hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream) {
+    if (gemv_mfma_preferred(N, K, M, scales, sums))
+        return launch_gemv_mfma(w, N, K, codes, scales, sums, M, y, stream);
     if (M * K <= kFusedMaxMK) {
         const GemvProblem p = {w, nullptr, y, N};
         const stream::Prepared Q = {codes, scales, sums};

@@ -39,6 +39,27 @@ __device__ __forceinline__ float group8_sum(float v) {
     return v;
 }
 
+// The per-sub-block factor f_j = d*sc_j*D_j - dmin*mn_j*S_j of the epilogue
+// a_j * f_j, with the mins product rounded on its own: fma(ds, D, -RN(dm*S)).
+__device__ __forceinline__ float subblock_factor(float ds, int D, float dm, float S) {
+#pragma clang fp contract(off)
+    return fmaf(ds, (float)D, -(dm * S));
+}
+
+// Super-block term of one weight row and activation row: the sum over a lane
+// group of e_j = a_j * f_j, lane l holding sub-block j = l, in one fixed order:
+//   T = (u0 + u2) + (u7 + u5),   u_j = fma(a_j, f_j, RN(a_k * f_k)), k = j ^ 1.
+// Lane 0 of the group returns T.  Written out (no contraction left to the
+// compiler) because the matrix-core small-batch GEMV forms the same T from
+// lanes laid out differently and must match it bit for bit.
+__device__ __forceinline__ float superblock_term(float a, float f) {
+#pragma clang fp contract(off)
+    const float p = a * f;
+    float v = fmaf(a, f, dpp_f<kQuadSwap1>(p));
+    v = v + dpp_f<kQuadSwap2>(v);
+    return v + dpp_f<kRowHalfMirror>(v);
+}
+
 // Q8 quantization of one block of 32 fp32 values held by an aligned group of
 // 8 lanes, 4 consecutive values per lane (lane i of the group: values
 // 4i..4i+3).  Scale d = fl32(amax / 127); code = rne(fl32(x / d)); an

@@ -43,6 +43,15 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        hipStream_t stream);
 
+// Small-batch GEMV on the matrix cores (prepared Q8 rows, M = 2..8), where its
+// LDS holds the rows and scales / sums are 16-byte aligned; the same bits as
+// the streaming GEMV.
+bool gemv_mfma_fits(int64_t K, int64_t M, const void *scales, const void *sums);
+bool gemv_mfma_preferred(int64_t N, int64_t K, int64_t M, const void *scales, const void *sums);
+hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
+                            const float *scales, const int32_t *sums, int64_t M, float *y,
+                            hipStream_t stream);
+
 // Fused Q8 quantization + GEMV on fp32 activations (M <= 8, M*K <= kFusedMaxMK).
 constexpr int64_t kFusedMaxMK = 32768;
 hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int D = subblock_dot(L, qlo, qhi, cA[m], cB[m]);
-                const float t = group8_sum(a[m] * fmaf(ds, (float)D, -(dm * sm[m])));
+                const float t = superblock_term(a[m], subblock_factor(ds, D, dm, sm[m]));
                 if (L.l == 0 && live) cs[v * RG * nsb * M + m] = t;
             }
         }

@@ -77,7 +77,9 @@ int q4k_quantize_act(const float *x, int64_t M, int64_t K, const float *gate,
 /* Decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T for M = 1..8
  * (batch-1 decode and the verification of up to 8 drafted tokens, which
  * shares one read of W).  Bandwidth-bound: W is streamed once with 16-byte
- * loads; no matrix cores.
+ * loads; for several rows on wide products the integer sub-block dots run on
+ * the matrix cores (same result bits as the vector kernel, which runs
+ * otherwise, e.g. when scales / sums are not 16-byte aligned).
  *   w       device Q4_K bytes, N rows x (K/256)*144 bytes, 16-byte aligned.
  *   N >= 1, K % 256 == 0, K >= 256, 1 <= M <= 8.
  *   codes   device int8 [M][K] (16-byte aligned); scales fp32 [M][K/32];

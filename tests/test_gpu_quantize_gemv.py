@@ -246,10 +246,15 @@ def test_gemv_qwen3_4b_shapes_sampled(q4k, oracle_lib, proj):
 @pytest.mark.parametrize("N,K,M", [(1, 256, 1), (37, 512, 2), (1000, 2560, 1), (4096, 2560, 1),
                                    (2560, 4096, 1), (2560, 9728, 1), (9728, 2560, 1),
                                    (300, 4096, 8), (129, 6144, 5), (2048, 16384, 2),
-                                   (64, 32768, 1)])
+                                   (64, 32768, 1), (16, 256, 2), (17, 2560, 3), (1000, 2560, 4),
+                                   (33, 1024, 6), (129, 3840, 7), (4097, 4096, 8),
+                                   (2560, 4096, 8), (1024, 2560, 8), (2048, 512, 4),
+                                   (4096, 768, 3), (2049, 1280, 5), (2500, 3328, 6)])
 def test_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     """One launch (quantize inside the GEMV) equals q4k_quantize_act followed
-    by q4k_gemv bit for bit, and the oracle within tolerance."""
+    by q4k_gemv bit for bit, and the oracle within tolerance.  For M = 2..8 the
+    second call runs the matrix-core GEMV, the first the streaming one: the two
+    must form every super-block term and row sum the same way."""
     import torch
     w = qi.make_q4k_bytes(N, K, 7000 + N + K)
     x = qi.make_act(M, K, 8000 + M + K)
@@ -265,6 +270,32 @@ def test_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     rc, rs, _ = oracle_lib.quantize_act(x)
     ref = oracle_lib.matvec(w, N, K, rc, rs, rows=rows)
     assert_close(y1 if rows is None else y1[:, rows], ref, "quantize_gemv N=%d K=%d M=%d" % (N, K, M))
+
+
+@pytest.mark.parametrize("N,K,M", [(2560, 4096, 8), (4096, 2560, 4), (2100, 1536, 5)])
+def test_gemv_unaligned_scales_same_bits(q4k, oracle_lib, N, K, M):
+    """Q8 scales and sums that are only 4-byte aligned take the streaming GEMV
+    instead of the matrix-core one; both give the same bits."""
+    import torch
+    w = qi.make_q4k_bytes(N, K, 7700 + N + M)
+    x = qi.make_act(M, K, 7800 + K + M)
+    wd = to_dev(w)
+    c, s, su = q4k.q4k_quantize_act(to_dev(x))
+    s_buf = torch.empty(s.numel() + 1, dtype=torch.float32, device="cuda")
+    su_buf = torch.empty(su.numel() + 1, dtype=torch.int32, device="cuda")
+    s_off, su_off = s_buf[1:].view(s.shape), su_buf[1:].view(su.shape)
+    s_off.copy_(s)
+    su_off.copy_(su)
+    assert s_off.data_ptr() % 16 == 4 and su_off.data_ptr() % 16 == 4
+    y1 = q4k.q4k_gemv(wd, N, K, c, s, su)
+    y2 = q4k.q4k_gemv(wd, N, K, c, s_off, su_off)
+    torch.cuda.synchronize()
+    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 40)])
+    rc, rs, _ = oracle_lib.quantize_act(x)
+    assert_close(y1[:, rows], oracle_lib.matvec(w, N, K, rc, rs, rows=rows),
+                 "gemv N=%d K=%d M=%d" % (N, K, M))
 
 
 # ------------------------------------------- batched quantize + GEMV ----
