@@ -108,8 +108,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs B, int nsb) {
                 const int row = row0 + 8 * t + grp, b = b0 + c;
                 const uint8_t *sb = w + (int64_t)min(row, N - 1) * row_bytes +
                                     (int64_t)min(b, nsb - 1) * 144;
-                hd[c][t] = load_stream16(sb);
-                qw[c][t] = load_stream16(sb + 16 + 16 * L.l);
+                hd[c][t] = load_weights16(sb);
+                qw[c][t] = load_weights16(sb + 16 + 16 * L.l);
             }
         // Keep every load of the group ahead of the arithmetic below.
         __builtin_amdgcn_sched_barrier(0);

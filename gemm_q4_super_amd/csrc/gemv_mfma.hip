@@ -112,9 +112,9 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
     for (int c = 0; c < CPW; ++c) {
         const unsigned b = (unsigned)min(wcol0 + c, nsb - 1);
         const unsigned off = __umul24(rr, (unsigned)row_bytes) + b * 144u;
-        hd[c] = load_stream16(wb + off);
-        w0[c] = load_stream16(wb + (off + 16u + 16u * ch0));
-        w1[c] = load_stream16(wb + (off + 16u + 16u * ch1));
+        hd[c] = load_weights16(wb + off);
+        w0[c] = load_weights16(wb + (off + 16u + 16u * ch0));
+        w1[c] = load_weights16(wb + (off + 16u + 16u * ch1));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -254,13 +254,14 @@ bool gemv_mfma_fits(int64_t K, int64_t M, const void *scales, const void *sums) 
 }
 
 // Where the matrix-core GEMV beats the streaming one, measured on MI355X over
-// the decode projections (N = 1024 .. 9728, K = 2560 .. 9728) for M = 2..8: a
-// 16-row tile per workgroup leaves most CUs idle below N = 2048 until M = 7,
-// and at M <= 3 the streaming GEMV's lighter vector work wins except for wide
-// N.
+// the decode projections (N = 1024 .. 9728, K = 2560 .. 9728) for M = 2..8:
+// from M = 3 on wide products; below N = 2048 a 16-row tile per workgroup
+// leaves most CUs idle, and the streaming GEMV keeps up until M = 5 (N = 1024,
+// M = 3: 3.45 against 3.77 us); at M = 2 the streaming GEMV's lighter vector
+// work wins.
 bool gemv_mfma_preferred(int64_t N, int64_t K, int64_t M, const void *scales, const void *sums) {
     if (!gemv_mfma_fits(K, M, scales, sums)) return false;
-    return M >= 7 || (M >= 4 && N >= 2048) || (M == 3 && N >= 4096);
+    return M >= 3 && (N >= 2048 || M >= 5);
 }
 
 hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,

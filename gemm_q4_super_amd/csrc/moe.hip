@@ -34,6 +34,8 @@ namespace {
 constexpr int kMoeWaves = 4;         // waves per workgroup, at most
 constexpr int kMoeV = 8;             // row groups per lane
 constexpr int kMoeMC = 4;            // pairs per pass over a weight block
+constexpr int kMoeMC2MaxT = 8;       // up to this many tokens, 2 pairs per pass (fewer
+                                     // registers, more workgroups per CU: T = 4 46.1 -> 43.9 us)
 constexpr int kStageBytes = 256 + 64;   // one staged column: codes, 8 scales, 8 sums
 constexpr int kStageSlots = 2;          // column slots per wave with fp32 activations, at most
 constexpr int kFuseMaxT = 2;            // tokens up to which the FFN quantizes in its GEMVs
@@ -59,12 +61,10 @@ __host__ __device__ constexpr size_t group_bytes(int P, int E) {
     return sizeof(int) * ((size_t)((P + 3) & ~3) + (size_t)E + P);
 }
 
-// Dynamic LDS of moe_kernel: the grouping, and for fp32 activations the
-// staged Q8 columns of each wave.
-size_t moe_lds_bytes(int P, int E, int mode, int nw, int S, int MC) {
-    size_t b = group_bytes(P, E);
-    if (mode != ACT_Q8) b = align16(b) + (size_t)nw * S * MC * kStageBytes;
-    return b;
+// Dynamic LDS of moe_kernel: the grouping and the staged Q8 columns of each
+// wave.
+size_t moe_lds_bytes(int P, int E, int nw, int S, int MC) {
+    return align16(group_bytes(P, E)) + (size_t)nw * S * MC * kStageBytes;
 }
 
 // Exclusive prefix sum of v over one wave (64 lanes); returns the lane's
@@ -215,19 +215,34 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
             const int bc = min(b, nsb - 1);
             i32x4 cA[MC], cB[MC];
             float a[MC], sm[MC];
-            // fp32 activations: launches use S <= kStageSlots (so RG >= 4)
+            // launches use S <= kStageSlots (so RG >= 4): at most 2 MC staged columns
             constexpr int SX = MODE == ACT_Q8 ? 1 : kStageSlots;
             constexpr int SU = MODE == ACT_SWIGLU ? kStageSlots : 1;
             f32x4 xv[SX][MC], xu[SU][MC];
+            // prepared Q8 rows: column j of pair m is staged as 16 lanes x 16 bytes
+            // of codes (column-pair k = j*MC + m on lanes 16(k%4).., two loads)
+            // and 8 lanes x 4 bytes of scales and of sums (lanes 8k..)
+            constexpr int QK = MODE == ACT_Q8 ? (kStageSlots * MC + 3) / 4 : 1;
+            i32x4 qc[QK];
+            float qa = 0.0f;
+            int qs = 0;
             if constexpr (MODE == ACT_Q8) {
+                auto row_of = [&](int mm) {   // arow[mm] for a per-lane mm (from LDS)
+                    const int pr = s_pairs[c0 + min(mm, mc - 1)];
+                    return A.act_per_slot ? pr : pr / A.topk;
+                };
 #pragma unroll
-                for (int m = 0; m < MC; ++m) {
-                    const int8_t *cm = A.codes + (int64_t)arow[m] * K + 256 * bc;
-                    cA[m] = *reinterpret_cast<const i32x4 *>(cm + L.offA);
-                    cB[m] = *reinterpret_cast<const i32x4 *>(cm + L.offB);
-                    a[m] = A.scales[(int64_t)arow[m] * nblk + 8 * bc + L.l];
-                    sm[m] = (float)A.sums[(int64_t)arow[m] * nblk + 8 * bc + L.l];
+                for (int i = 0; i < QK; ++i) {
+                    const int k = min((lane >> 4) + 4 * i, S * MC - 1);
+                    const int col = min(wcol + k / MC, nsb - 1);
+                    qc[i] = *reinterpret_cast<const i32x4 *>(
+                        A.codes + (int64_t)row_of(k % MC) * K + 256 * col + 16 * (lane & 15));
                 }
+                const int k = min(lane >> 3, S * MC - 1);
+                const int col = min(wcol + k / MC, nsb - 1);
+                const int64_t so = (int64_t)row_of(k % MC) * nblk + 8 * col + (lane & 7);
+                qa = A.scales[so];
+                qs = A.sums[so];
             } else {
                 // fp32 activation of the wave's S columns, quantizer layout
 #pragma unroll
@@ -252,13 +267,26 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
             for (int v = 0; v < V; ++v) {
                 const unsigned rr = (unsigned)(min(row_base + v * RG + r, N - 1) - row_base);
                 const unsigned o = rr * row_bytes + (unsigned)bc * 144u;
-                hd[v] = __builtin_nontemporal_load(
-                    reinterpret_cast<const unsigned *>(wb + (o + 4u * (lane & 3))));
-                qw[v] = load_stream16(wb + (o + 16u + 16u * L.l));
+                hd[v] = *reinterpret_cast<const unsigned *>(wb + (o + 4u * (lane & 3)));
+                qw[v] = load_weights16(wb + (o + 16u + 16u * L.l));
             }
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (MODE != ACT_Q8) {
-                // quantize into the wave's stage, then read it in the dot layout
+            if constexpr (MODE == ACT_Q8) {
+                // copy the prepared rows into the wave's stage
+#pragma unroll
+                for (int i = 0; i < QK; ++i) {
+                    const int k = (lane >> 4) + 4 * i;
+                    if (k < S * MC)
+                        *reinterpret_cast<i32x4 *>(stage + (size_t)k * kStageBytes +
+                                                   16 * (lane & 15)) = qc[i];
+                }
+                if ((lane >> 3) < S * MC) {
+                    uint8_t *st = stage + (size_t)(lane >> 3) * kStageBytes;
+                    reinterpret_cast<float *>(st + 256)[lane & 7] = qa;
+                    reinterpret_cast<float *>(st + 288)[lane & 7] = (float)qs;
+                }
+            } else {
+                // quantize into the wave's stage
 #pragma unroll
                 for (int j = 0; j < SX; ++j) {
                     if (j >= S) break;
@@ -275,16 +303,17 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
                         }
                     }
                 }
-                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage is written
-                __builtin_amdgcn_wave_barrier();
+            }
+            // read the stage in the dot layout
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage is written
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int m = 0; m < MC; ++m) {
-                    const uint8_t *st = stage + (size_t)(sl * MC + m) * kStageBytes;
-                    cA[m] = *reinterpret_cast<const i32x4 *>(st + L.offA);
-                    cB[m] = *reinterpret_cast<const i32x4 *>(st + L.offB);
-                    a[m] = reinterpret_cast<const float *>(st + 256)[L.l];
-                    sm[m] = reinterpret_cast<const float *>(st + 288)[L.l];
-                }
+            for (int m = 0; m < MC; ++m) {
+                const uint8_t *st = stage + (size_t)(sl * MC + m) * kStageBytes;
+                cA[m] = *reinterpret_cast<const i32x4 *>(st + L.offA);
+                cB[m] = *reinterpret_cast<const i32x4 *>(st + L.offB);
+                a[m] = reinterpret_cast<const float *>(st + 256)[L.l];
+                sm[m] = reinterpret_cast<const float *>(st + 288)[L.l];
             }
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -301,11 +330,9 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
                     }
                 }
             }
-            if constexpr (MODE != ACT_Q8) {
-                // the stage is rewritten by the next pass: reads done first
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
-            }
+            // the stage is rewritten by the next pass: reads done first
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
         }
         // a row's terms: the 8 lanes of a group (DPP), then over the waves and
         // each wave's S slots (LDS, wave-major order)
@@ -369,7 +396,7 @@ Shape shape(int64_t nsb) {
 
 // Pairs per pass: an expert has at most T pairs when each token lists
 // distinct experts, so small T needs no wider pass (more pairs only take more
-// passes).
+// passes, the weights then coming from L2).
 template <int MODE>
 hipError_t launch_kernel(const MoeArgs &A, int64_t T, int nmat, const Shape &sh,
                          hipStream_t stream) {
@@ -377,11 +404,11 @@ hipError_t launch_kernel(const MoeArgs &A, int64_t T, int nmat, const Shape &sh,
               (unsigned)(nmat * A.slots + A.zero_skipped));
     auto go = [&](auto kern, int MC) {
         hipLaunchKernelGGL(kern, grid, dim3(64 * sh.nw),
-                           moe_lds_bytes(A.P, A.E, MODE, sh.nw, sh.S, MC), stream, A);
+                           moe_lds_bytes(A.P, A.E, sh.nw, sh.S, MC), stream, A);
     };
     if (T == 1)
         go(moe_kernel<kMoeV, 1, MODE>, 1);
-    else if (T == 2)
+    else if (T <= kMoeMC2MaxT)
         go(moe_kernel<kMoeV, 2, MODE>, 2);
     else
         go(moe_kernel<kMoeV, kMoeMC, MODE>, kMoeMC);

@@ -143,8 +143,11 @@ __device__ __forceinline__ f32x4 swiglu4(f32x4 g, f32x4 u) {
     return h;
 }
 
-__device__ __forceinline__ u32x4 load_stream16(const uint8_t *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+// 16 bytes of weights, a plain (temporal) load: on MI355X the 36-layer decode
+// step ran 0.793 ms with plain weight loads against 0.808 ms with loads marked
+// non-temporal, and the routed-expert layer 2-8 % faster.
+__device__ __forceinline__ u32x4 load_weights16(const uint8_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
 }
 
 __device__ __forceinline__ float half_lo(unsigned v) {

@@ -236,9 +236,8 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
             const unsigned rr = (unsigned)(min(row_base + v * RG + r, N - 1) - row_base);
             const unsigned b = (unsigned)min(col0 + c, nsb - 1);
             const unsigned off = __umul24(rr, (unsigned)row_bytes) + b * 144u;
-            hd[v][c] = __builtin_nontemporal_load(
-                reinterpret_cast<const unsigned *>(wb + (off + hoff)));
-            qw[v][c] = load_stream16(wb + (off + qoff));
+            hd[v][c] = *reinterpret_cast<const unsigned *>(wb + (off + hoff));
+            qw[v][c] = load_weights16(wb + (off + qoff));
         }
     __builtin_amdgcn_sched_barrier(0);
 
