@@ -56,6 +56,9 @@ def _load():
                                   ctypes.c_int, _P],
             "oracle_moe_layer": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                                  _P, _P, _P, _P, _P, _P, _P, _P],
+            "oracle_unpack_q6k": [_P, _P, _P, _P],
+            "oracle_q6k_dequant_row": [_P, _I, _P],
+            "oracle_q6k_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -186,3 +189,38 @@ def moe_layer(w_gate, w_up, w_down, n_experts, H, F, ids, route_w, x):
                              _ptr(out["hc"]), _ptr(out["hs"]), _ptr(out["hsum"]),
                              _ptr(out["y"]))
     return out
+
+
+# ------------------------------------------------------------------ Q6_K ----
+
+Q6_SB_BYTES = 210
+
+
+def unpack_q6k(sb: np.ndarray):
+    """Fields of one 210-byte Q6_K super-block: (d, sc[16] int32, q[256] int32)."""
+    sb = _c(sb, np.uint8)
+    d = ctypes.c_double()
+    sc = np.zeros(16, np.int32)
+    q = np.zeros(256, np.int32)
+    _load().oracle_unpack_q6k(_ptr(sb), ctypes.addressof(d), _ptr(sc), _ptr(q))
+    return d.value, sc, q
+
+
+def q6k_dequant(w: np.ndarray, K: int) -> np.ndarray:
+    """fp64 [N, K] weights of Q6_K rows (uint8 [N, K/256*210])."""
+    w = _c(w, np.uint8).reshape(-1, K // QK * Q6_SB_BYTES)
+    out = np.zeros((w.shape[0], K), np.float64)
+    for n in range(w.shape[0]):
+        _load().oracle_q6k_dequant_row(_ptr(w[n]), K, _ptr(out[n]))
+    return out
+
+
+def q6k_matvec(w, N, K, codes, scales, rows=None) -> np.ndarray:
+    """fp64 [M, len(rows)]: y[m, r] = sum_k w[rows[r], k] * xhat[m, k], Q6_K weights."""
+    codes, scales = _c(codes, np.int8), _c(scales, np.float32)
+    M = codes.size // K
+    r = _rows(rows, N)
+    y = np.zeros((M, r.size), np.float64)
+    _load().oracle_q6k_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
+                              _ptr(r), r.size, _ptr(y))
+    return y

@@ -32,6 +32,13 @@
  *    activation; SwiGLU is the reading), Q8 of h, the expert's down product,
  *    and the routing-weighted sum in slot order.
  *
+ *  - Q6_K weights (public GGUF format; real Q4_K_M files keep some tensors in
+ *    Q6_K and the decode kernels of genie's "Path G" -- section 3 -- are Q6_K
+ *    ones, but the pages do not print the bytes): 256 weights of one row in
+ *    210 bytes, ql[128] low 4 bits and qh[64] high 2 bits of 6-bit quants,
+ *    int8 scales per 16 weights, fp16 d; w = d*sc[e/16]*(q - 32), exact in
+ *    fp64; the same fp64 product against Q8 activations.
+ *
  * Parity pins for every function are in tests/test_oracle_pins.py.
  */
 #include <math.h>
@@ -297,4 +304,62 @@ void oracle_moe_layer(const uint8_t *w_gate, const uint8_t *w_up,
     if (hsum_out) memcpy(hsum_out, hsum, sizeof(int32_t) * P * (F / QB));
     free(xc); free(xs); free(xsum); free(gd); free(ud); free(g); free(u); free(h);
     free(hc); free(hs); free(hsum);
+}
+
+/* ---------------------------------------------------------------- Q6_K -- */
+
+#define Q6_SB_BYTES 210
+
+/* Unpack one 210-byte Q6_K super-block: element e = 128h + 32t + l takes its
+ * low 4 bits from ql[64h + 32(t%2) + l] (low nibble for t < 2, high for t >= 2)
+ * and its high 2 bits from bits 2t..2t+1 of qh[32h + l]. */
+void oracle_unpack_q6k(const uint8_t *sb, double *d, int32_t *sc, int32_t *q)
+{
+    const uint8_t *ql = sb, *qh = sb + 128;
+    *d = half_bits_to_double((uint16_t)(sb[208] | (sb[209] << 8)));
+    for (int j = 0; j < 16; ++j)
+        sc[j] = (int8_t)sb[192 + j];
+    for (int e = 0; e < QK; ++e) {
+        int h = e / 128, t = (e % 128) / 32, l = e % 32;
+        int lo = ql[64 * h + 32 * (t % 2) + l];
+        lo = t < 2 ? (lo & 15) : (lo >> 4);
+        int hi = (qh[32 * h + l] >> (2 * t)) & 3;
+        q[e] = lo | (hi << 4);
+    }
+}
+
+/* Dequantize one Q6_K row of K weights into fp64. */
+void oracle_q6k_dequant_row(const uint8_t *row, int64_t K, double *w)
+{
+    int32_t sc[16], q[QK];
+    double d;
+    for (int64_t b = 0; b < K / QK; ++b) {
+        oracle_unpack_q6k(row + b * Q6_SB_BYTES, &d, sc, q);
+        for (int e = 0; e < QK; ++e)
+            w[b * QK + e] = d * sc[e / 16] * (q[e] - 32);
+    }
+}
+
+/* y[m][r] = sum_k w[n_r][k] * scale[m][k/32] * code[m][k] for Q6_K weights,
+ * fp64, rows as in oracle_matvec. */
+void oracle_q6k_matvec(const uint8_t *w, int64_t N, int64_t K,
+                       const int8_t *codes, const float *scales, int64_t M,
+                       const int64_t *rows, int64_t nrows, double *y)
+{
+    int64_t row_bytes = K / QK * Q6_SB_BYTES;
+    double *wr = (double *)malloc(sizeof(double) * K);
+    (void)N;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t n = rows ? rows[r] : r;
+        oracle_q6k_dequant_row(w + n * row_bytes, K, wr);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xh = (double)scales[m * (K / QB) + k / QB] * (double)codes[m * K + k];
+                acc += wr[k] * xh;
+            }
+            y[m * nrows + r] = acc;
+        }
+    }
+    free(wr);
 }

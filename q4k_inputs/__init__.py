@@ -135,6 +135,85 @@ def make_q4k_bytes(N: int, K: int, seed: int) -> np.ndarray:
     return out.reshape(N, nsb * SB_BYTES)
 
 
+# Q6_K super-block (public GGUF format; real "Q4_K_M" files keep some tensors in
+# Q6_K, and the decode kernels genie's "Path G" targets are Q6_K ones --
+# "genie-ai-runtime ...", section 3 -- but the pages do not print the layout):
+# 256 weights of one row in 210 bytes:
+#
+#     bytes 0..127    ql   low 4 bits of the 6-bit quants
+#     bytes 128..191  qh   high 2 bits of the 6-bit quants
+#     bytes 192..207  sc   int8 scale per 16 weights
+#     bytes 208..209  d    fp16
+#
+# Weight value: w = d*sc[e // 16]*(q[e] - 32).  Element e = 128h + 32t + l
+# (h < 2, t < 4, l < 32) keeps its low 4 bits in ql[64h + 32(t % 2) + l] (low
+# nibble for t < 2, high nibble for t >= 2) and its high 2 bits in bits 2t, 2t+1
+# of qh[32h + l].
+Q6_SB_BYTES = 210
+
+
+@dataclass
+class Q6KFields:
+    """Unpacked Q6_K fields of an N x K matrix (nsb = K // 256 super-blocks per row)."""
+    q: np.ndarray      # uint8 [N, nsb, 256], 0..63, in element order
+    sc: np.ndarray     # int8  [N, nsb, 16]
+    d: np.ndarray      # float16 [N, nsb]
+
+
+def draw_q6k_fields(N: int, K: int, seed: int, d_range=(1e-4, 1e-3)) -> Q6KFields:
+    """Draw the Q6_K fields of an N x K matrix: quants uniform 0..63, scales
+    uniform over all int8 values, d uniform in d_range rounded to fp16."""
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    rng = np.random.default_rng(seed)
+    nsb = K // QK
+    q = rng.integers(0, 64, size=(N, nsb, QK), dtype=np.uint8)
+    sc = rng.integers(-128, 128, size=(N, nsb, 16), dtype=np.int16).astype(np.int8)
+    d = rng.uniform(d_range[0], d_range[1], size=(N, nsb)).astype(np.float16)
+    return Q6KFields(q=q, sc=sc, d=d)
+
+
+def pack_q6k(f: Q6KFields) -> np.ndarray:
+    """Encode fields into GGUF Q6_K bytes: uint8 [N, nsb*210], rows contiguous."""
+    q = f.q.astype(np.uint16)
+    if q.max(initial=0) > 63:
+        raise ValueError("field out of range")
+    N, nsb, _ = q.shape
+    out = np.zeros((N, nsb, Q6_SB_BYTES), dtype=np.uint8)
+    qq = q.reshape(N, nsb, 2, 4, 32)                  # [half h, part t, l]
+    lo, hi = qq & 15, qq >> 4
+    ql = np.zeros((N, nsb, 2, 2, 32), dtype=np.uint16)   # [h, t % 2, l]
+    ql[:, :, :, 0, :] = lo[:, :, :, 0, :] | (lo[:, :, :, 2, :] << 4)
+    ql[:, :, :, 1, :] = lo[:, :, :, 1, :] | (lo[:, :, :, 3, :] << 4)
+    qh = hi[:, :, :, 0, :] | (hi[:, :, :, 1, :] << 2) | (hi[:, :, :, 2, :] << 4) | (hi[:, :, :, 3, :] << 6)
+    out[:, :, 0:128] = ql.reshape(N, nsb, 128).astype(np.uint8)
+    out[:, :, 128:192] = qh.reshape(N, nsb, 64).astype(np.uint8)
+    out[:, :, 192:208] = f.sc.astype(np.int8).view(np.uint8)
+    out[:, :, 208:210] = f.d.astype("<f2").view(np.uint8).reshape(N, nsb, 2)
+    return out.reshape(N, nsb * Q6_SB_BYTES)
+
+
+def make_q6k(N: int, K: int, seed: int) -> tuple[np.ndarray, Q6KFields]:
+    """Packed bytes and fields of a seeded N x K Q6_K matrix."""
+    f = draw_q6k_fields(N, K, seed)
+    return pack_q6k(f), f
+
+
+def make_q6k_bytes(N: int, K: int, seed: int) -> np.ndarray:
+    """Packed Q6_K bytes of a seeded N x K matrix, drawn directly as bytes: every
+    quant bit and scale byte is uniform, so uniform bytes give the field
+    distribution of `make_q6k`; only d is drawn as an fp16 value."""
+    if K % QK:
+        raise ValueError("K must be a multiple of 256")
+    rng = np.random.default_rng(seed)
+    nsb = K // QK
+    out = np.frombuffer(rng.bytes(N * nsb * Q6_SB_BYTES), dtype=np.uint8)
+    out = out.reshape(N, nsb, Q6_SB_BYTES).copy()
+    dd = rng.uniform(1e-4, 1e-3, size=(N, nsb)).astype("<f2")
+    out[:, :, 208:210] = dd.view(np.uint8).reshape(N, nsb, 2)
+    return out.reshape(N, nsb * Q6_SB_BYTES)
+
+
 def make_act(M: int, K: int, seed: int) -> np.ndarray:
     """fp32 [M, K] activations drawn from N(0, 1)."""
     rng = np.random.default_rng(seed)

@@ -335,3 +335,122 @@ def test_moe_layer_identical_experts_reduce_to_dense(oracle_lib):
         assert (out["g"][t * topk:(t + 1) * topk] == g[t]).all()
         ref = sum(float(rw[t, s]) for s in range(topk)) * z[t]
         assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-12 * np.abs(z[t]).max())
+
+
+# ------------------------------------------------------------------ Q6_K ----
+
+def _q6k_block_bytes(b):
+    sb = np.zeros(210, np.uint8)
+    for k, v in b["ql"].items():
+        sb[int(k)] = v
+    for k, v in b["qh"].items():
+        sb[128 + int(k)] = v
+    sb[192:208] = np.array(b["sc"], np.int8).view(np.uint8)
+    sb[208:210] = np.array([int(b["d_bits"], 16)], "<u2").view(np.uint8)
+    return sb
+
+
+def _q6k_fields_to_w(f: qi.Q6KFields) -> np.ndarray:
+    """fp64 Q6_K weights straight from the drawn fields (no byte decoding)."""
+    N, nsb, _ = f.q.shape
+    j = np.arange(256) // 16
+    w = (f.d.astype(np.float64)[:, :, None] * f.sc.astype(np.float64)[:, :, j] *
+         (f.q.astype(np.float64) - 32.0))
+    return w.reshape(N, nsb * 256)
+
+
+def test_q6k_golden_superblock_unpack(oracle_lib):
+    b = _load("q6k_superblock_handbuilt.json")["blocks"][0]
+    sb = _q6k_block_bytes(b)
+    d, sc, q = oracle_lib.unpack_q6k(sb)
+    assert d == b["d"] and sc.tolist() == b["sc"]
+    expect_q = np.zeros(256, np.int32)
+    for k, v in b["q_nonzero"].items():
+        expect_q[int(k)] = v
+    assert q.tolist() == expect_q.tolist()
+    w = oracle_lib.q6k_dequant(sb, 256)[0]
+    for k, v in b["w_expected"].items():
+        assert w[int(k)] == v, (k, w[int(k)], v)
+    assert w.sum() == b["row_sum"]
+
+
+def test_q6k_generator_pack_roundtrip(oracle_lib):
+    for seed in range(12):
+        f = qi.draw_q6k_fields(3, 512, 100 + seed)
+        if seed == 1:
+            f.q[:] = 63; f.sc[:] = 127
+        if seed == 2:
+            f.q[:] = 0; f.sc[:] = -128; f.d[:] = 0
+        if seed == 3:
+            f.d[:] = np.float16(65504)
+        w = qi.pack_q6k(f)
+        for n in range(3):
+            for b in range(2):
+                d, sc, q = oracle_lib.unpack_q6k(w[n, b * 210:(b + 1) * 210])
+                assert d == float(f.d[n, b])
+                assert (sc == f.sc[n, b]).all() and (q == f.q[n, b]).all()
+
+
+def test_q6k_fast_bytes_generator_is_valid(oracle_lib):
+    w = qi.make_q6k_bytes(4, 512, 9)
+    seen_neg = False
+    for n in range(4):
+        for b in range(2):
+            d, sc, q = oracle_lib.unpack_q6k(w[n, b * 210:(b + 1) * 210])
+            assert 1e-4 * 0.99 <= d <= 1e-3 * 1.01
+            assert q.min() >= 0 and q.max() <= 63
+            seen_neg |= bool((sc < 0).any())
+    assert seen_neg   # scales are signed
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 256, 1), (3, 512, 2), (2, 768, 3)])
+def test_q6k_matvec_vs_field_brute_force(oracle_lib, N, K, M):
+    for seed in range(4):
+        w, f = qi.make_q6k(N, K, 200 + seed)
+        x = qi.make_act(M, K, 300 + seed)
+        codes, scales, _ = oracle_lib.quantize_act(x)
+        wf = _q6k_fields_to_w(f)
+        assert np.array_equal(oracle_lib.q6k_dequant(w, K), wf)
+        xh = scales.astype(np.float64).repeat(32, axis=1) * codes.astype(np.float64)
+        ref = xh @ wf.T
+        y = oracle_lib.q6k_matvec(w, N, K, codes, scales)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_q6k_all_ones_activation_closed_form(oracle_lib):
+    w, f = qi.make_q6k(4, 512, 5)
+    codes, scales, _ = oracle_lib.quantize_act(np.ones((1, 512), np.float32))
+    assert (codes == 127).all()
+    d_a = float(np.float32(1.0) / np.float32(127.0))
+    y = oracle_lib.q6k_matvec(w, 4, 512, codes, scales)[0]
+    expect = 127.0 * d_a * _q6k_fields_to_w(f).sum(axis=1)
+    assert np.allclose(y, expect, rtol=1e-12, atol=0)
+
+
+def test_q6k_integer_exposing_special_case(oracle_lib):
+    """d = 1 and one scale = 1: y is the integer dot of one 16-weight sub-block
+    with (q - 32), exact."""
+    rng = np.random.default_rng(11)
+    for j in (0, 5, 9, 15):
+        f = qi.draw_q6k_fields(1, 256, 400 + j)
+        f.d[:] = np.float16(1.0)
+        f.sc[:] = 0
+        f.sc[0, 0, j] = 1
+        w = qi.pack_q6k(f)
+        x = rng.integers(-127, 128, size=(1, 256)).astype(np.float32)
+        x[0, ::32] = 127.0          # every block's max is 127: scale 1, codes = x
+        codes, scales, _ = oracle_lib.quantize_act(x)
+        assert (scales == 1.0).all() and (codes == x).all()
+        e = np.arange(16 * j, 16 * j + 16)
+        expect = float(((f.q[0, 0, e].astype(np.int64) - 32) * x[0, e].astype(np.int64)).sum())
+        assert oracle_lib.q6k_matvec(w, 1, 256, codes, scales)[0, 0] == expect
+
+
+def test_q6k_zero_scale_gives_zero(oracle_lib):
+    f = qi.draw_q6k_fields(2, 512, 12)
+    f.d[0] = 0
+    f.sc[1] = 0
+    w = qi.pack_q6k(f)
+    codes, scales, _ = oracle_lib.quantize_act(qi.make_act(2, 512, 13))
+    y = oracle_lib.q6k_matvec(w, 2, 512, codes, scales)
+    assert (y == 0).all()
