@@ -17,6 +17,7 @@ Functions carry the C names:
                  act_per_slot, workspace=None)       -> y
     q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H, F,
                 ids, route_w, x, workspace=None)     -> y [T, H]  (whole expert FFN layer)
+    q6k_gemv(w, N, K, codes, scales)                 -> y [M, N]   (Q6_K weights, M <= 8)
 """
 from ._lib import (  # noqa: F401
     Q4KError,
@@ -33,5 +34,6 @@ from ._lib import (  # noqa: F401
     q4k_quantize_gemv,
     q4k_quantize_gemv_batch,
     q4k_status_string,
+    q6k_gemv,
     EXPORTED_SYMBOLS,
 )

@@ -18,6 +18,7 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_workspace_bytes",
     "q4k_moe_ffn",
     "q4k_moe_ffn_workspace_bytes",
+    "q6k_gemv",
     "q4k_status_string",
 )
 
@@ -70,11 +71,12 @@ def lib():
                                   ctypes.c_size_t, _P]
         L.q4k_moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+        L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
                      "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                     "q4k_moe_ffn"):
+                     "q4k_moe_ffn", "q6k_gemv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +139,19 @@ def _matrix_call(fn, what, w, N, K, codes, scales, sums, y):
 
 def q4k_gemv(w, N, K, codes, scales, sums, y=None):
     return _matrix_call(lib().q4k_gemv, "q4k_gemv", w, N, K, codes, scales, sums, y)
+
+
+def q6k_gemv(w, N, K, codes, scales, y=None):
+    """Q6_K weights (N rows x K/256*210 bytes) times prepared Q8 rows (M <= 8)."""
+    import torch
+    for t, n in ((w, "w"), (codes, "codes"), (scales, "scales")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    _check(lib().q6k_gemv(_ptr(w), N, K, _ptr(codes), _ptr(scales), M, _ptr(y), _stream(codes)),
+           "q6k_gemv")
+    return y
 
 
 def q4k_quantize_gemv(w, N, K, x, y=None):

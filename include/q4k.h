@@ -215,6 +215,24 @@ int q4k_moe_ffn(const void *w_gate, const void *w_up, const void *w_down, int64_
 size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t H,
                                    int64_t F);
 
+/* Q6_K decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T for M = 1..8
+ * with W in Q6_K, the format real Q4_K_M files keep some tensors in (and the
+ * target of the decode kernels of "genie-ai-runtime ...", section 3, Path G):
+ * per 256 weights of a row 210 bytes -- ql[128] (low 4 bits of each 6-bit
+ * quant q), qh[64] (high 2 bits), int8 sc[16] (one per 16 weights), fp16 d
+ * (public GGUF layout) -- and w = d*sc[e/16]*(q[e] - 32).
+ *   w       device Q6_K bytes, N rows x (K/256)*210 bytes, 16-byte aligned.
+ *   N >= 1, K % 256 == 0, 256 <= K <= 12288, 1 <= M <= 8, M*K <= 32768 (the
+ *           Q8 rows are staged in LDS).
+ *   codes   device int8 [M][K] (16-byte aligned); scales fp32 [M][K/32]
+ *           (4-byte aligned) -- as written by q4k_quantize_act (its block
+ *           sums are not needed).
+ *   y       device fp32 [M][N].
+ * fp32 result within a relative error of 2e-3 (absolute 1e-4 near zero) of
+ * the exact sum. */
+int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
+             const float *scales, int64_t M, float *y, void *stream);
+
 /* Static description of a status code. */
 const char *q4k_status_string(int status);
 

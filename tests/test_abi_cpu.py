@@ -20,7 +20,7 @@ A = 0x10000          # a 256-byte aligned fake address (never dereferenced)
 def _declared():
     src = open(os.path.join(ROOT, "include", "q4k.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4k_[a-z_0-9]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(q[46]k_[a-z_0-9]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -63,6 +63,25 @@ def test_gemv_gemm_argument_checks(L):
         assert call(y=A + 2) == EALIGN
     # the GEMV takes at most 8 activation rows
     assert L.q4k_gemv(A, 16, 512, A, A, A, 9, A, None) == ESHAPE
+
+
+def test_q6k_gemv_argument_checks(L):
+    f = L.q6k_gemv
+    assert f(None, 16, 512, A, A, 1, A, None) == EINVAL
+    assert f(A, 16, 512, None, A, 1, A, None) == EINVAL
+    assert f(A, 16, 512, A, None, 1, A, None) == EINVAL
+    assert f(A, 16, 512, A, A, 1, None, None) == EINVAL
+    assert f(A, 16, 500, A, A, 1, A, None) == ESHAPE
+    assert f(A, 16, 0, A, A, 1, A, None) == ESHAPE
+    assert f(A, 0, 512, A, A, 1, A, None) == ESHAPE
+    assert f(A, 16, 512, A, A, 0, A, None) == ESHAPE
+    assert f(A, 16, 512, A, A, 9, A, None) == ESHAPE
+    assert f(A, 16, 12544, A, A, 1, A, None) == ESHAPE    # K beyond 48 super-blocks
+    assert f(A, 16, 9728, A, A, 4, A, None) == ESHAPE     # M*K beyond the LDS limit
+    assert f(A + 8, 16, 512, A, A, 1, A, None) == EALIGN
+    assert f(A, 16, 512, A + 8, A, 1, A, None) == EALIGN
+    assert f(A, 16, 512, A, A + 2, 1, A, None) == EALIGN
+    assert f(A, 16, 512, A, A, 1, A + 2, None) == EALIGN
 
 
 def test_quantize_gemv_argument_checks(L):
