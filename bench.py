@@ -21,7 +21,10 @@ q4k_gemv), are timed after the timed region and reported beside it.
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
 the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
-8 TB/s), and the CPU oracle timed on a bounded sample of the same sweep.
+8 TB/s), and the CPU oracle timed on a bounded sample of the same sweep.  Beside
+them, outside the timed region: the prefill GEMM (M = 512), the small-batch
+GEMV (M = 2, 4, 8), the routed-expert layer (T = 1, 16) and the Q6_K decode
+GEMV over the same projection shapes.
 """
 from __future__ import annotations
 
@@ -468,6 +471,88 @@ def measure_small_batch(torch, dec, steps=5):
     return out
 
 
+def q6k_bytes(N, K, M=1):
+    """Algorithmic bytes of one Q6_K GEMV: weights once (210 B per 256), the
+    Q8 codes and scales it reads, the fp32 output."""
+    return N * K // 256 * 210 + M * K + M * (K // 32) * 4 + 4 * M * N
+
+
+def measure_q6k(torch, q4k, qi, oracle, steps=5):
+    """Q6_K decode GEMV (q6k_gemv, prepared Q8 rows, M = 1) over the 36-layer
+    sweep's projection shapes with distinct seeded Q6_K matrices (2.98 GB):
+    one graph of the 252 launches, replayed once untimed and `steps` times
+    timed, plus a per-shape breakdown and a sampled check against the oracle."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    shapes = qi.QWEN3_4B_LAYER
+    ws = [[torch.from_numpy(qi.make_q6k_bytes(N, K, qi.weight_seed(5, l, p))).to(dev)
+           for l in range(LAYERS)] for p, (_, K, N) in enumerate(shapes)]
+    acts = {}
+    for K in sorted({K for _, K, _ in shapes}):
+        x = qi.make_act(1, K, qi.act_seed(50000 + K))
+        c, sc, _ = oracle.quantize_act(x)
+        acts[K] = (torch.from_numpy(c).to(dev), torch.from_numpy(sc).to(dev), c, sc)
+    ys = {N: torch.empty((1, N), dtype=torch.float32, device=dev) for _, _, N in shapes}
+    cap = torch.cuda.Stream()
+
+    def graph(ps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            s = torch.cuda.current_stream().cuda_stream
+            for l in range(LAYERS):
+                for p in ps:
+                    _, K, N = shapes[p]
+                    c, sc = acts[K][0], acts[K][1]
+                    if L.q6k_gemv(ws[p][l].data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), 1,
+                                  ys[N].data_ptr(), s):
+                        raise RuntimeError("q6k_gemv launch failed")
+        return g
+
+    def timed(g, reps):
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    t = timed(graph(range(len(shapes))), steps)
+    nbytes = LAYERS * sum(q6k_bytes(N, K) for _, K, N in shapes)
+    per = {}
+    for p, (name, K, N) in enumerate(shapes):
+        d = timed(graph([p]), steps) / LAYERS
+        per[name] = {"N": N, "K": K, "us": round(d * 1e6, 3),
+                     "GBps": round(q6k_bytes(N, K) / d / 1e9, 1)}
+    # sampled parity: layer 0 of each shape, 24 rows, against the oracle
+    worst = 0.0
+    for p, (name, K, N) in enumerate(shapes):
+        c, sc = acts[K][0], acts[K][1]
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        if L.q6k_gemv(ws[p][0].data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), 1, y.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("q6k_gemv launch failed")
+        torch.cuda.synchronize()
+        rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 22)])
+        ref = oracle.q6k_matvec(ws[p][0].cpu().numpy(), N, K, acts[K][2], acts[K][3], rows=rows)[0]
+        got = y.cpu().numpy()[0, rows].astype(np.float64)
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), 0.05)
+        if not (np.abs(got - ref) <= np.maximum(2e-3 * np.abs(ref), 1e-4)).all():
+            raise RuntimeError("q6k_gemv parity failure on %s" % name)
+        worst = max(worst, float(err.max()))
+    del ws
+    torch.cuda.empty_cache()
+    return {"workload": "Q6_K decode GEMV, batch 1, prepared Q8 rows: 36 layers x the seven "
+                        "Qwen3-4B projection shapes in Q6_K (2.98 GB), one q6k_gemv per "
+                        "product (252 launches)",
+            "us_per_sweep": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
+            "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "mean_launch_us": round(t / (LAYERS * len(shapes)) * 1e6, 3),
+            "per_shape": per,
+            "parity": {"rows_checked_per_shape": "24 sampled", "max_rel_err": worst}}
+
+
 def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
     """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8) over
     `layers` distinct seeded layers per pass (1.81 GB, past the last-level
@@ -682,6 +767,7 @@ def main():
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
                                                            args.prefill_steps)
     moe = None if args.no_extra else measure_moe(torch, q4k, qi)
+    q6k = None if args.no_extra else measure_q6k(torch, q4k, qi, oracle)
     cpu = None if args.no_cpu else cpu_baseline(qi, oracle, qi.QWEN3_4B_LAYER, args.cpu_seconds)
 
     out = {
@@ -724,6 +810,7 @@ def main():
         "prefill_gemm": prefill,
         "small_batch_gemv": small,
         "moe_layer": moe,
+        "q6k_decode_gemv": q6k,
     }
     print(json.dumps(out))
 
