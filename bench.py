@@ -543,6 +543,23 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
         worst = max(worst, float(err.max()))
     del ws
     torch.cuda.empty_cache()
+    # one large launch: a Q6_K output head (vocabulary 151936 x hidden 2560, 218 MB),
+    # three distinct copies rotated so the 256 MB last-level cache cannot hold them
+    NH, KH = 151936, 2560
+    heads = [torch.from_numpy(qi.make_q6k_bytes(NH, KH, qi.weight_seed(6, 0, i))).to(dev)
+             for i in range(3)]
+    yh = torch.empty((1, NH), dtype=torch.float32, device=dev)
+    gh = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gh, stream=cap):
+        s = torch.cuda.current_stream().cuda_stream
+        for i in range(3):
+            if L.q6k_gemv(heads[i].data_ptr(), NH, KH, acts[KH][0].data_ptr(),
+                          acts[KH][1].data_ptr(), 1, yh.data_ptr(), s):
+                raise RuntimeError("q6k_gemv launch failed")
+    th = timed(gh, steps) / 3
+    hb = q6k_bytes(NH, KH)
+    del heads
+    torch.cuda.empty_cache()
     return {"workload": "Q6_K decode GEMV, batch 1, prepared Q8 rows: 36 layers x the seven "
                         "Qwen3-4B projection shapes in Q6_K (2.98 GB), one q6k_gemv per "
                         "product (252 launches)",
@@ -550,6 +567,8 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
             "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "mean_launch_us": round(t / (LAYERS * len(shapes)) * 1e6, 3),
             "per_shape": per,
+            "output_head_151936x2560": {"us": round(th * 1e6, 2), "GBps": round(hb / th / 1e9, 1),
+                                        "hbm_frac": round(hb / th / 1e9 / HBM_PEAK_GBS, 4)},
             "parity": {"rows_checked_per_shape": "24 sampled", "max_rel_err": worst}}
 
 
