@@ -477,6 +477,41 @@ def q6k_bytes(N, K, M=1):
     return N * K // 256 * 210 + M * K + M * (K // 32) * 4 + 4 * M * N
 
 
+def measure_large_launch(torch, q4k, qi, steps=5):
+    """The decode GEMV kernel on one large launch, where the per-launch floor no
+    longer dominates: a Q4_K matrix of an output head's shape (151936 x 2560,
+    150 MB; three distinct copies rotated past the 256 MB last-level cache),
+    q4k_quantize_gemv at batch 1 from an HIP graph."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    N, K = 151936, 2560
+    ws = [torch.from_numpy(qi.make_q4k_bytes(N, K, qi.weight_seed(7, 0, i))).to(dev)
+          for i in range(3)]
+    x = torch.from_numpy(qi.make_act(1, K, qi.act_seed(70000))).to(dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        s = torch.cuda.current_stream().cuda_stream
+        for i in range(3):
+            if L.q4k_quantize_gemv(ws[i].data_ptr(), N, K, x.data_ptr(), 1, y.data_ptr(), s):
+                raise RuntimeError("q4k_quantize_gemv launch failed")
+    g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / steps / 3
+    nb = fused_bytes(N, K)
+    del ws
+    torch.cuda.empty_cache()
+    return {"workload": "one q4k_quantize_gemv launch, Q4_K 151936 x 2560 (150 MB), batch 1",
+            "us": round(t * 1e6, 2), "GBps": round(nb / t / 1e9, 1),
+            "hbm_frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def measure_q6k(torch, q4k, qi, oracle, steps=5):
     """Q6_K decode GEMV (q6k_gemv, prepared Q8 rows, M = 1) over the 36-layer
     sweep's projection shapes with distinct seeded Q6_K matrices (2.98 GB):
@@ -787,6 +822,7 @@ def main():
                                                            args.prefill_steps)
     moe = None if args.no_extra else measure_moe(torch, q4k, qi)
     q6k = None if args.no_extra else measure_q6k(torch, q4k, qi, oracle)
+    large = None if args.no_extra else measure_large_launch(torch, q4k, qi)
     cpu = None if args.no_cpu else cpu_baseline(qi, oracle, qi.QWEN3_4B_LAYER, args.cpu_seconds)
 
     out = {
@@ -830,6 +866,7 @@ def main():
         "small_batch_gemv": small,
         "moe_layer": moe,
         "q6k_decode_gemv": q6k,
+        "decode_gemv_one_large_launch": large,
     }
     print(json.dumps(out))
 
