@@ -37,7 +37,7 @@ constexpr int kMoeMC = 4;            // pairs per pass over a weight block
 constexpr int kMoeMC2MaxT = 8;       // up to this many tokens, 2 pairs per pass (fewer
                                      // registers, more workgroups per CU: T = 4 46.1 -> 43.9 us)
 constexpr int kStageBytes = 256 + 64;   // one staged column: codes, 8 scales, 8 sums
-constexpr int kStageSlots = 2;          // column slots per wave with fp32 activations, at most
+constexpr int kStageSlots = 2;          // column slots per wave, at most (the staged columns)
 constexpr int kFuseMaxT = 2;            // tokens up to which the FFN quantizes in its GEMVs
 
 enum { ACT_Q8 = 0, ACT_F32 = 1, ACT_SWIGLU = 2 };
@@ -89,8 +89,10 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
 // waves x S slots cover W*S super-block columns per pass (more passes when K
 // is wider).  Per pass a wave issues the activation loads of its columns for
 // the chunk's pairs and then every weight load of its V row groups before any
-// arithmetic, so the block is in flight at once; fp32 activations are then
-// quantized into the wave's own LDS stage (no workgroup barrier).  Per lane
+// arithmetic, so the block is in flight at once; the activation then goes
+// into the wave's own LDS stage (no workgroup barrier): prepared Q8 rows
+// copied (four wide loads per pass instead of four loads per pair per lane),
+// fp32 rows quantized.  Per lane
 // the terms of a (row, pair) add up over the passes; the 8 lanes of a group
 // (DPP), then the W waves and their S slots (LDS, in a fixed order) complete a
 // row: a fixed order for a given K (the launch shape depends on K alone).
