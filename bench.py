@@ -555,6 +555,19 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
 
     t = timed(graph(range(len(shapes))), steps)
     nbytes = LAYERS * sum(q6k_bytes(N, K) for _, K, N in shapes)
+    # the same sweep with the quantizer inside (q6k_quantize_gemv, fp32 rows)
+    xs = {K: torch.from_numpy(qi.make_act(1, K, qi.act_seed(51000 + K))).to(dev)
+          for K in sorted({K for _, K, _ in shapes})}
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf, stream=cap):
+        s = torch.cuda.current_stream().cuda_stream
+        for l in range(LAYERS):
+            for p, (_, K, N) in enumerate(shapes):
+                if L.q6k_quantize_gemv(ws[p][l].data_ptr(), N, K, xs[K].data_ptr(), 1,
+                                       ys[N].data_ptr(), s):
+                    raise RuntimeError("q6k_quantize_gemv launch failed")
+    tf = timed(gf, steps)
+    fbytes = LAYERS * sum(N * K // 256 * 210 + 4 * K + 4 * N for _, K, N in shapes)
     per = {}
     for p, (name, K, N) in enumerate(shapes):
         d = timed(graph([p]), steps) / LAYERS
@@ -601,6 +614,8 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
             "us_per_sweep": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
             "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "mean_launch_us": round(t / (LAYERS * len(shapes)) * 1e6, 3),
+            "fused_quantizer_sweep": {"us_per_sweep": round(tf * 1e6, 1),
+                                      "GBps": round(fbytes / tf / 1e9, 1)},
             "per_shape": per,
             "output_head_151936x2560": {"us": round(th * 1e6, 2), "GBps": round(hb / th / 1e9, 1),
                                         "hbm_frac": round(hb / th / 1e9 / HBM_PEAK_GBS, 4)},

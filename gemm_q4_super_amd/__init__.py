@@ -18,6 +18,7 @@ Functions carry the C names:
     q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H, F,
                 ids, route_w, x, workspace=None)     -> y [T, H]  (whole expert FFN layer)
     q6k_gemv(w, N, K, codes, scales)                 -> y [M, N]   (Q6_K weights, M <= 8)
+    q6k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (Q6_K, fp32 x, one launch)
 """
 from ._lib import (  # noqa: F401
     Q4KError,
@@ -35,5 +36,6 @@ from ._lib import (  # noqa: F401
     q4k_quantize_gemv_batch,
     q4k_status_string,
     q6k_gemv,
+    q6k_quantize_gemv,
     EXPORTED_SYMBOLS,
 )

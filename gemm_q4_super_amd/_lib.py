@@ -19,6 +19,7 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_ffn",
     "q4k_moe_ffn_workspace_bytes",
     "q6k_gemv",
+    "q6k_quantize_gemv",
     "q4k_status_string",
 )
 
@@ -72,11 +73,12 @@ def lib():
         L.q4k_moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
+        L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
                      "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                     "q4k_moe_ffn", "q6k_gemv"):
+                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -151,6 +153,18 @@ def q6k_gemv(w, N, K, codes, scales, y=None):
         y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     _check(lib().q6k_gemv(_ptr(w), N, K, _ptr(codes), _ptr(scales), M, _ptr(y), _stream(codes)),
            "q6k_gemv")
+    return y
+
+
+def q6k_quantize_gemv(w, N, K, x, y=None):
+    """Q8-quantize fp32 x [M, K] and multiply by Q6_K W^T in one launch."""
+    import torch
+    _dev(w, "w"); _dev(x, "x")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q6k_quantize_gemv(_ptr(w), N, K, _ptr(x), M, _ptr(y), _stream(x)),
+           "q6k_quantize_gemv")
     return y
 
 

@@ -182,6 +182,17 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes, const flo
                                          M, y, static_cast<hipStream_t>(stream)));
 }
 
+int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M, float *y,
+                      void *stream) {
+    if (!w || !x || !y) return Q4K_EINVAL;
+    if (N < 1 || N > kMaxDim || K < q4k::kQK || K % q4k::kQK != 0 || K > q4k::kQ6MaxK ||
+        M < 1 || M > 8 || M * K > q4k::kFusedMaxMK)
+        return Q4K_ESHAPE;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_q6k_quantize_gemv(static_cast<const uint8_t *>(w), N, K, x, M, y,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 const char *q4k_status_string(int status) {
     switch (status) {
     case Q4K_OK: return "ok";

@@ -52,10 +52,13 @@ hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t
                             const float *scales, const int32_t *sums, int64_t M, float *y,
                             hipStream_t stream);
 
-// Q6_K GEMV on prepared Q8 rows (M <= 8, M*K <= kFusedMaxMK, K <= kQ6MaxK).
+// Q6_K GEMV on prepared Q8 rows or fp32 rows quantized inside (M <= 8,
+// M*K <= kFusedMaxMK, K <= kQ6MaxK).
 constexpr int64_t kQ6MaxK = 48 * 256;
 hipError_t launch_q6k_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                            const float *scales, int64_t M, float *y, hipStream_t stream);
+hipError_t launch_q6k_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
+                                    int64_t M, float *y, hipStream_t stream);
 
 // Fused Q8 quantization + GEMV on fp32 activations (M <= 8, M*K <= kFusedMaxMK).
 constexpr int64_t kFusedMaxMK = 32768;

@@ -1,5 +1,7 @@
-// Q6_K decode / small-batch GEMV on prepared Q8 rows (q6k_gemv):
-// y[M][N] = Q8(x)[M][K] * W^T with W in Q6_K, M = 1..8, M*K <= 32768.
+// Q6_K decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T with W in Q6_K,
+// M = 1..8, M*K <= 32768, on prepared Q8 rows (q6k_gemv) or on fp32 rows that
+// each workgroup quantizes with q4k_quantize_act's arithmetic
+// (q6k_quantize_gemv: same codes, so the two give the same bits).
 //
 // Q6_K (public GGUF layout; real Q4_K_M files keep some tensors in it, and the
 // decode kernels of genie's "Path G" -- "genie-ai-runtime ...", section 3 --
@@ -51,10 +53,10 @@ __device__ __forceinline__ u32x4 load12(const uint8_t *p) {   // 4-byte aligned
     return r;
 }
 
-template <int M, int CPW, int V>
+template <int M, int CPW, int V, bool FUSED>
 __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     const uint8_t *__restrict__ w, float *__restrict__ y, const int8_t *__restrict__ codes,
-    const float *__restrict__ scales, int N, int nsb) {
+    const float *__restrict__ scales, const float *__restrict__ x, int N, int nsb) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float red[kQ6Waves][8 * V][M];
 
@@ -69,20 +71,32 @@ __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     const int ncols = min(CPW, nsb - wcol0);   // >= 1 (the host sizes the workgroup)
 
     // ---- stage this wave's columns: lane-order codes, scales, offset terms.
-    // Piece p < 32 of a (column, row) is block j = p/4, quarter u = p%4 (8 codes).
+    // Prepared rows: piece p < 32 of a (column, row) is block j = p/4, quarter
+    // u = p%4 (8 codes).  fp32 rows: lane L holds values 4(L%8).. of block L/8
+    // (the quantizer's layout).
     const int sp = lane & 31, sj = sp >> 2, su = sp & 3;
     const int sdst = (((sj >> 2) * 4 + su) * 4 + (sj & 3));   // slot of the piece
-    uint2 cv[CPW][(M + 1) / 2];
+    constexpr int PC = FUSED ? 1 : (M + 1) / 2;
+    constexpr int PX = FUSED ? M : 1;
+    uint2 cv[CPW][PC];
     float av[CPW];
+    f32x4 xv[CPW][PX];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int b = min(wcol0 + c, nsb - 1);
+        if constexpr (FUSED) {
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; ++k) {
-            const int m = min(2 * k + (lane >> 5), M - 1);
-            cv[c][k] = *reinterpret_cast<const uint2 *>(codes + (int64_t)m * K + 256 * b + 8 * sp);
+            for (int m = 0; m < M; ++m)
+                xv[c][m] = *reinterpret_cast<const f32x4 *>(x + (int64_t)m * K + 256 * b + 4 * lane);
+        } else {
+#pragma unroll
+            for (int k = 0; k < PC; ++k) {
+                const int m = min(2 * k + (lane >> 5), M - 1);
+                cv[c][k] =
+                    *reinterpret_cast<const uint2 *>(codes + (int64_t)m * K + 256 * b + 8 * sp);
+            }
+            av[c] = scales[(int64_t)min(lane >> 3, M - 1) * nblk + 8 * b + (lane & 7)];
         }
-        av[c] = scales[(int64_t)min(lane >> 3, M - 1) * nblk + 8 * b + (lane & 7)];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -122,8 +136,25 @@ __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     for (int c = 0; c < CPW; ++c) {
         if (c >= ncols) continue;   // wave-uniform
         const int b = wcol0 + c;
+        if constexpr (FUSED) {
+            // quantize: lane L -> block j = L/8, values 4i..4i+3 (i = L%8), i.e.
+            // quarter u = i/2, half i%2 of its 8-code piece
+            const int j = lane >> 3, i = lane & 7;
+            const int slot = ((j >> 2) * 4 + (i >> 1)) * 4 + (j & 3);
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; ++k) {
+            for (int m = 0; m < M; ++m) {
+                const Q8Lane q8 = quantize_block8(xv[c][m]);
+                uint8_t *st = lds + ((size_t)b * M + m) * kQ6Stage;
+                *reinterpret_cast<unsigned *>(st + 8 * slot + 4 * (i & 1)) = q8.codes;
+                const int s4 = __builtin_amdgcn_sdot4((int)q8.codes, 0x01010101, 0, false);
+                const int s8 = s4 + dpp_i<kQuadSwap1>(s4);   // the piece's 8 codes
+                if ((i & 1) == 0) reinterpret_cast<int *>(st + 288)[slot] = -32 * s8;
+                if (i == 0) reinterpret_cast<float *>(st + 256)[j] = q8.d;
+            }
+            continue;
+        }
+#pragma unroll
+        for (int k = 0; k < PC; ++k) {
             const int m = 2 * k + (lane >> 5);
             if (m < M) {
                 uint8_t *st = lds + ((size_t)b * M + m) * kQ6Stage;
@@ -218,14 +249,25 @@ __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     }
 }
 
+// Activation of a call: prepared Q8 rows (codes, scales) or fp32 rows x.
+struct Act {
+    const int8_t *codes;
+    const float *scales;
+    const float *x;
+};
+
 template <int M, int CPW, int V>
-hipError_t launch_mcv(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
-                      const float *scales, float *y, hipStream_t stream) {
+hipError_t launch_mcv(const uint8_t *w, int64_t N, int nsb, const Act &a, float *y,
+                      hipStream_t stream) {
     const int waves = (nsb + CPW - 1) / CPW;
     const int blocks = (int)((N + 8 * V - 1) / (8 * V));
     const size_t lds = (size_t)nsb * M * kQ6Stage;
-    hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V>), dim3(blocks), dim3(64 * waves), lds, stream,
-                       w, y, codes, scales, (int)N, nsb);
+    if (a.x)
+        hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, true>), dim3(blocks), dim3(64 * waves),
+                           lds, stream, w, y, nullptr, nullptr, a.x, (int)N, nsb);
+    else
+        hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, false>), dim3(blocks), dim3(64 * waves),
+                           lds, stream, w, y, a.codes, a.scales, nullptr, (int)N, nsb);
     return hipGetLastError();
 }
 
@@ -233,8 +275,8 @@ hipError_t launch_mcv(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
 // workgroup (8 V) so that the workgroups come near one or two per CU; at most 4
 // super-blocks per lane in flight (V * CPW <= 4), 2 past M = 4 (registers).
 template <int M>
-hipError_t launch_m(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
-                    const float *scales, float *y, hipStream_t stream) {
+hipError_t launch_m(const uint8_t *w, int64_t N, int nsb, const Act &a, float *y,
+                    hipStream_t stream) {
     constexpr int kUnits = M <= 4 ? 4 : 2;
     const int cpw = (nsb + kQ6Waves - 1) / kQ6Waves;
     const int64_t rows_per_cu = (N + cu_count() - 1) / cu_count();
@@ -242,37 +284,47 @@ hipError_t launch_m(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
         1, std::min<int64_t>(kUnits / cpw, std::max<int64_t>(1, rows_per_cu / 8)));
     if (cpw == 1) {
         if constexpr (kUnits >= 4)
-            if (v >= 4) return launch_mcv<M, 1, 4>(w, N, nsb, codes, scales, y, stream);
-        if (v >= 2) return launch_mcv<M, 1, 2>(w, N, nsb, codes, scales, y, stream);
-        return launch_mcv<M, 1, 1>(w, N, nsb, codes, scales, y, stream);
+            if (v >= 4) return launch_mcv<M, 1, 4>(w, N, nsb, a, y, stream);
+        if (v >= 2) return launch_mcv<M, 1, 2>(w, N, nsb, a, y, stream);
+        return launch_mcv<M, 1, 1>(w, N, nsb, a, y, stream);
     }
     if (cpw == 2) {
         if constexpr (kUnits >= 4)
-            if (v >= 2) return launch_mcv<M, 2, 2>(w, N, nsb, codes, scales, y, stream);
-        return launch_mcv<M, 2, 1>(w, N, nsb, codes, scales, y, stream);
+            if (v >= 2) return launch_mcv<M, 2, 2>(w, N, nsb, a, y, stream);
+        return launch_mcv<M, 2, 1>(w, N, nsb, a, y, stream);
     }
     // K of 33..48 super-blocks: M * K <= 32768 keeps M <= 3 here
-    if constexpr (M <= 3) return launch_mcv<M, 3, 1>(w, N, nsb, codes, scales, y, stream);
+    if constexpr (M <= 3) return launch_mcv<M, 3, 1>(w, N, nsb, a, y, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t run_q6k(const uint8_t *w, int64_t N, int64_t K, const Act &a, int64_t M, float *y,
+                   hipStream_t stream) {
+    const int nsb = (int)(K / kQK);
+    if (K > kQ6MaxK || M * K > kFusedMaxMK) return hipErrorInvalidValue;
+    switch (M) {
+    case 1: return launch_m<1>(w, N, nsb, a, y, stream);
+    case 2: return launch_m<2>(w, N, nsb, a, y, stream);
+    case 3: return launch_m<3>(w, N, nsb, a, y, stream);
+    case 4: return launch_m<4>(w, N, nsb, a, y, stream);
+    case 5: return launch_m<5>(w, N, nsb, a, y, stream);
+    case 6: return launch_m<6>(w, N, nsb, a, y, stream);
+    case 7: return launch_m<7>(w, N, nsb, a, y, stream);
+    case 8: return launch_m<8>(w, N, nsb, a, y, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_q6k_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                            const float *scales, int64_t M, float *y, hipStream_t stream) {
-    const int nsb = (int)(K / kQK);
-    if (K > kQ6MaxK || M * K > kFusedMaxMK) return hipErrorInvalidValue;
-    switch (M) {
-    case 1: return launch_m<1>(w, N, nsb, codes, scales, y, stream);
-    case 2: return launch_m<2>(w, N, nsb, codes, scales, y, stream);
-    case 3: return launch_m<3>(w, N, nsb, codes, scales, y, stream);
-    case 4: return launch_m<4>(w, N, nsb, codes, scales, y, stream);
-    case 5: return launch_m<5>(w, N, nsb, codes, scales, y, stream);
-    case 6: return launch_m<6>(w, N, nsb, codes, scales, y, stream);
-    case 7: return launch_m<7>(w, N, nsb, codes, scales, y, stream);
-    case 8: return launch_m<8>(w, N, nsb, codes, scales, y, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return run_q6k(w, N, K, Act{codes, scales, nullptr}, M, y, stream);
+}
+
+hipError_t launch_q6k_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
+                                    int64_t M, float *y, hipStream_t stream) {
+    return run_q6k(w, N, K, Act{nullptr, nullptr, x}, M, y, stream);
 }
 
 }  // namespace q4k

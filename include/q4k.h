@@ -233,6 +233,14 @@ size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, i
 int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
              const float *scales, int64_t M, float *y, void *stream);
 
+/* Q6_K quantize-and-GEMV in one launch: y[M][N] = Q8(x)[M][K] * W^T for fp32
+ * activations x (device, [M][K], 16-byte aligned), each workgroup quantizing
+ * its Q8 blocks with q4k_quantize_act's arithmetic, so the result equals
+ * q4k_quantize_act followed by q6k_gemv bit for bit.  Other arguments and
+ * limits as for q6k_gemv. */
+int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
+                      float *y, void *stream);
+
 /* Static description of a status code. */
 const char *q4k_status_string(int status);
 

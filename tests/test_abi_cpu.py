@@ -84,6 +84,19 @@ def test_q6k_gemv_argument_checks(L):
     assert f(A, 16, 512, A, A, 1, A + 2, None) == EALIGN
 
 
+def test_q6k_quantize_gemv_argument_checks(L):
+    f = L.q6k_quantize_gemv
+    assert f(None, 16, 512, A, 1, A, None) == EINVAL
+    assert f(A, 16, 512, None, 1, A, None) == EINVAL
+    assert f(A, 16, 512, A, 1, None, None) == EINVAL
+    assert f(A, 16, 500, A, 1, A, None) == ESHAPE
+    assert f(A, 16, 512, A, 9, A, None) == ESHAPE
+    assert f(A, 16, 9728, A, 4, A, None) == ESHAPE
+    assert f(A, 0, 512, A, 1, A, None) == ESHAPE
+    assert f(A + 4, 16, 512, A, 1, A, None) == EALIGN
+    assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
+
+
 def test_quantize_gemv_argument_checks(L):
     f = L.q4k_quantize_gemv
     assert f(None, 16, 512, A, 1, A, None) == EINVAL

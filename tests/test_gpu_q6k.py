@@ -1,4 +1,5 @@
-"""GPU parity of q6k_gemv (Q6_K weights x prepared Q8 rows) against the CPU oracle.
+"""GPU parity of q6k_gemv (Q6_K weights x prepared Q8 rows) and of
+q6k_quantize_gemv (fp32 rows quantized inside) against the CPU oracle.
 
 Outputs must be within |gpu - oracle| <= max(2e-3 |oracle|, 1e-4) elementwise,
 and exactly equal in the integer-exposing case where the sub-block dots pass
@@ -115,3 +116,26 @@ def test_q6k_gemv_writes_only_its_output(q4k, oracle_lib):
     b = buf.cpu().numpy()
     assert (b[:32] == 12345.0).all() and (b[32 + M * N:] == 12345.0).all()
     assert_close(y.cpu().numpy(), oracle_lib.q6k_matvec(w, N, K, codes, scales), "q6k into a view")
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 256, 1), (9, 768, 1), (33, 2560, 1), (100, 4096, 2),
+                                   (257, 1280, 3), (65, 3328, 5), (40, 4096, 8), (2560, 9728, 3),
+                                   (4096, 2560, 1)])
+def test_q6k_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
+    """One launch (quantize inside) equals q4k_quantize_act followed by
+    q6k_gemv bit for bit, and the oracle within tolerance."""
+    import torch
+    w = qi.make_q6k_bytes(N, K, 800 + N + K)
+    x = qi.make_act(M, K, 810 + M + K)
+    x[0, 32:64] = 0.0
+    wd, xd = to_dev(w), to_dev(x)
+    y1 = q4k.q6k_quantize_gemv(wd, N, K, xd)
+    c, s, _ = q4k.q4k_quantize_act(xd)
+    y2 = q4k.q6k_gemv(wd, N, K, c, s)
+    torch.cuda.synchronize()
+    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    rows = None if N <= 300 else np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 40)])
+    rc, rs, _ = oracle_lib.quantize_act(x)
+    ref = oracle_lib.q6k_matvec(w, N, K, rc, rs, rows=rows)
+    assert_close(y1 if rows is None else y1[:, rows], ref, "q6k_quantize_gemv N=%d K=%d M=%d" % (N, K, M))
