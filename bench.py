@@ -17,7 +17,9 @@ block of back-to-back GEMV dispatches; that gives the mean launch duration for
 the roofline (an event pair around each kernel would add a marker dispatch of
 several microseconds).  The same sweep as one q4k_quantize_gemv launch per
 product (252 per step), and as two launches per product (q4k_quantize_act, then
-q4k_gemv), are timed after the timed region and reported beside it.
+q4k_gemv), are timed after the timed region and reported beside it, and so
+is the step with o and down adding into a residual stream inside their GEMVs
+(q4k_quantize_gemv_residual, in place).
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
 the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
@@ -184,6 +186,8 @@ class Decode:
                 arr[j] = q4k._lib.GemvProblem(wt.data_ptr(), self.acts[i].data_ptr(),
                                               self.yp[i % len(self.shapes)].data_ptr(), N)
             self.batches.append((arr, len(grp), self.weights[grp[0]][2]))
+        # residual stream of the decode step (the o and down outputs add into it)
+        self.resid = torch.zeros((1, self.shapes[3][2]), dtype=torch.float32, device=dev)
         self.n_gemv = len(self.weights)
         self.n_batch = len(self.groups)
         self.bytes_gemv = sum(gemv_bytes(N, K) for _, N, K in self.weights)
@@ -216,6 +220,18 @@ class Decode:
         if self.L.q4k_quantize_gemv_batch(arr, n, K, 1, s):
             raise RuntimeError("q4k_quantize_gemv_batch launch failed")
 
+    def batch_residual(self, g, s):
+        """As batch(), with the single-product groups {o} and {down} adding
+        into the residual stream in place (q4k_quantize_gemv_residual)."""
+        arr, n, K = self.batches[g]
+        if n != 1:
+            return self.batch(g, s)
+        wt, N, _ = self.weights[self.groups[g][0]]
+        if self.L.q4k_quantize_gemv_residual(wt.data_ptr(), N, K,
+                                             self.acts[self.groups[g][0]].data_ptr(), 1,
+                                             self.resid.data_ptr(), self.resid.data_ptr(), s):
+            raise RuntimeError("q4k_quantize_gemv_residual launch failed")
+
     def graph(self, fn, indices, stream):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
@@ -245,6 +261,11 @@ class Decode:
                 raise SystemExit("parity: fused and two-launch GEMV differ for %s" % name)
             if not torch.equal(y, self.yp[p]):
                 raise SystemExit("parity: batched and single fused GEMV differ for %s" % name)
+            if name in ("o", "down"):
+                r = torch.from_numpy(self.qi.make_act(1, N, 77 + p)).to(y.device)
+                yr = q4k.q4k_quantize_gemv_residual(wt, N, K, self.acts[p], r)
+                if not torch.equal(yr, y + r):
+                    raise SystemExit("parity: residual GEMV is not GEMV + residual for %s" % name)
             rc, rs, _ = oracle.quantize_act(self.acts[p].cpu().numpy())
             if not (c.cpu().numpy() == rc).all():
                 raise SystemExit("parity: Q8 codes differ from the oracle for %s" % name)
@@ -826,6 +847,17 @@ def main():
                             "K": dec.weights[members[0]][2], "us": round(d * 1e6, 3),
                             "GBps": round(nb / d / 1e9, 1)}
 
+    # The same step with the residual add of o and down inside their GEMVs
+    # (4 launches per layer as above; N more fp32 reads per o / down launch).
+    residual = None
+    if not args.no_extra:
+        t_res = timed(dec.graph(dec.batch_residual, range(dec.n_batch), cap))
+        t_plain = timed(dec.graph(dec.batch, range(dec.n_batch), cap))
+        residual = {"ms_per_step": round(t_res * 1e3, 4),
+                    "same_graph_without_residual_ms": round(t_plain * 1e3, 4),
+                    "launches": dec.n_batch,
+                    "residual_launches": 2 * LAYERS}
+
     value = dec.bytes_fused * steps / elapsed / 1e9
     bytes_per_launch = dec.bytes_fused / dec.n_batch
     achieved = bytes_per_launch / mean_launch_s / 1e9
@@ -874,6 +906,7 @@ def main():
                                % n_launch,
                      "per_group": per_group},
         "single_call_path": single,
+        "residual_epilogue_path": residual,
         "two_launch_path": two_step,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -10,6 +10,7 @@ Functions carry the C names:
     q4k_quantize_act(x, gate=None)                   -> (codes, scales, sums)
     q4k_gemv(w, N, K, codes, scales, sums)           -> y [M, N]   (M <= 8)
     q4k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (fp32 x, one launch)
+    q4k_quantize_gemv_residual(w, N, K, x, r[, y=r]) -> r + Q8(x) W^T (residual add inside)
     q4k_quantize_gemv_batch([(w, N, x), ...], K)     -> [y, ...]   (<= 8 products, one launch)
     q4k_gemm(w, N, K, codes, scales, sums)           -> y [M, N]
     q4k_gemm_batch([(w, N), ...], K, codes, scales, sums) -> [y, ...] (<= 8 products, one launch)
@@ -34,6 +35,7 @@ from ._lib import (  # noqa: F401
     q4k_quantize_act,
     q4k_quantize_gemv,
     q4k_quantize_gemv_batch,
+    q4k_quantize_gemv_residual,
     q4k_status_string,
     q6k_gemv,
     q6k_quantize_gemv,

@@ -11,6 +11,7 @@ EXPORTED_SYMBOLS = (
     "q4k_quantize_act",
     "q4k_gemv",
     "q4k_quantize_gemv",
+    "q4k_quantize_gemv_residual",
     "q4k_quantize_gemv_batch",
     "q4k_gemm",
     "q4k_gemm_batch",
@@ -62,6 +63,7 @@ def lib():
         L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
                                      _I, _P]
         L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+        L.q4k_quantize_gemv_residual.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P]
         L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
                                               _I, _P]
         L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
@@ -77,6 +79,7 @@ def lib():
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
+                     "q4k_quantize_gemv_residual",
                      "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
                      "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv"):
             getattr(L, name).restype = ctypes.c_int
@@ -177,6 +180,21 @@ def q4k_quantize_gemv(w, N, K, x, y=None):
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _check(lib().q4k_quantize_gemv(_ptr(w), N, K, _ptr(x), M, _ptr(y), _stream(x)),
            "q4k_quantize_gemv")
+    return y
+
+
+def q4k_quantize_gemv_residual(w, N, K, x, residual, y=None):
+    """y = residual + Q8(x) W^T in one launch (fp32 x [M, K], residual [M, N]).
+
+    With y=None the sum goes to a new tensor; y=residual updates it in place."""
+    import torch
+    _dev(w, "w"); _dev(x, "x"); _dev(residual, "residual")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_quantize_gemv_residual(_ptr(w), N, K, _ptr(x), M, _ptr(residual), _ptr(y),
+                                            _stream(x)),
+           "q4k_quantize_gemv_residual")
     return y
 
 

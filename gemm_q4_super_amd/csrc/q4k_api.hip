@@ -62,6 +62,23 @@ int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                                               static_cast<hipStream_t>(stream)));
 }
 
+int q4k_quantize_gemv_residual(const void *w, int64_t N, int64_t K, const float *x,
+                               int64_t M, const float *residual, float *y, void *stream) {
+    if (!w || !x || !y || !residual) return Q4K_EINVAL;
+    if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1 || M > 8) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || M * K > q4k::kFusedMaxMK) return Q4K_ESHAPE;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4))
+        return Q4K_EALIGN;
+    // In place (residual == y) or disjoint: a partial overlap would read
+    // elements another thread has already written.
+    const uintptr_t ry = reinterpret_cast<uintptr_t>(y), rr = reinterpret_cast<uintptr_t>(residual);
+    const uintptr_t n = static_cast<uintptr_t>(M * N) * sizeof(float);
+    if (ry != rr && ry < rr + n && rr < ry + n) return Q4K_EINVAL;
+    return from_hip(q4k::launch_quantize_gemv_residual(static_cast<const uint8_t *>(w), N, K, x, M,
+                                                       residual, y,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K,
                             int64_t M, void *stream) {
     if (!problems) return Q4K_EINVAL;

@@ -64,6 +64,9 @@ hipError_t launch_q6k_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, cons
 constexpr int64_t kFusedMaxMK = 32768;
 hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                 int64_t M, float *y, hipStream_t stream);
+hipError_t launch_quantize_gemv_residual(const uint8_t *w, int64_t N, int64_t K, const float *x,
+                                         int64_t M, const float *residual, float *y,
+                                         hipStream_t stream);
 using GemvProblem = q4k_gemv_problem;
 constexpr int kMaxGemvBatch = 8;
 hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,

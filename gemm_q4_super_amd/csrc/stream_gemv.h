@@ -61,15 +61,19 @@ struct Pieces {
     const uint8_t *w[kPieces];
     const float *x[kPieces];
     float *y[kPieces];
+    const float *r[kPieces];   // residual added to the piece's output, or null
     int N[kPieces];      // rows of the piece
     int ldy[kPieces];    // row stride of y (the product's N)
 };
 
-// Prepared Q8 rows (plain GEMV): one activation for the single product.
+// Per-call inputs beside the products: the prepared Q8 rows of the plain
+// GEMV (null when the kernel quantizes), and a residual [M][N] added to the
+// output of a single product in the last step (null for none).
 struct Prepared {
     const int8_t *codes;
     const float *scales;
     const int32_t *sums;
+    const float *residual = nullptr;
 };
 
 // Launch shape, packed into one kernel argument: lg(RG) in bits 0-1,
@@ -99,10 +103,10 @@ constexpr int stage_batch() {
     return M <= 1 ? 4 : M <= 2 ? 2 : 1;
 }
 
-template <int M, int CPW, int V, bool FUSED>
+template <int M, int CPW, int V, bool FUSED, bool RES>
 __global__ __launch_bounds__(1024) void stream_gemv_kernel(
-    const uint8_t *__restrict__ w0, const float *__restrict__ x0, float *__restrict__ y0, int N0,
-    int ldy0, int nsb, int cfg, const Pieces P, const Prepared Q) {
+    const uint8_t *__restrict__ w0, const float *__restrict__ x0, float *y0, const float *r0,
+    int N0, int ldy0, int nsb, int cfg, const Pieces P, const Prepared Q) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     // Piece of this workgroup: piece 0 from the leading arguments, others
@@ -110,12 +114,17 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
     const int p = (int)blockIdx.y;
     const uint8_t *__restrict__ w = w0;
     const float *__restrict__ x = x0;
-    float *__restrict__ y = y0;
+    // y and res may be the same buffer (an in-place residual add): each
+    // output element is read and then written by one thread.  RES: the call
+    // has a residual (res is not null).
+    float *y = y0;
+    const float *res = r0;
     int N = N0, ldy = ldy0;
     if (p != 0) {
         w = P.w[p];
         x = P.x[p];
         y = P.y[p];
+        res = P.r[p];
         N = P.N[p];
         ldy = P.ldy[p];
     }
@@ -239,6 +248,19 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
             hd[v][c] = *reinterpret_cast<const unsigned *>(wb + (off + hoff));
             qw[v][c] = load_weights16(wb + (off + qoff));
         }
+    // The residual element of this thread's first output in the last step,
+    // requested behind the weights (loads complete in order, so it delays no
+    // earlier wait) and long before its use.  A compile-time switch, not a
+    // branch: a load under a branch leaves the compiler's count of loads in
+    // flight ambiguous, and the waits for the activation would then also wait
+    // for a weight.  The address is clamped into the piece (the value is used
+    // only if in range).
+    float res_first = 0.0f;
+    if constexpr (RES) {
+        const int i = min((int)threadIdx.x, RB * M - 1);
+        const int row = min(row_base + i / M, N - 1);
+        res_first = res[(int64_t)(i % M) * ldy + row];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     if (!stage_first) stage_all();
@@ -281,14 +303,19 @@ __global__ __launch_bounds__(1024) void stream_gemv_kernel(
     __syncthreads();
 
     // ---- a row adds its column terms in column order: the same order for any
-    // (RG, V, CPW), so every launch shape gives the same bits.
+    // (RG, V, CPW), so every launch shape gives the same bits.  A residual is
+    // added to the finished sum, one fp32 rounding.
     for (int i = threadIdx.x; i < RB * M; i += 64 * nw) {
         const int rr = i / M, m = i % M;          // row of the block
         const float *cs = colsum + (size_t)rr * nsb * M + m;
         float t = 0.0f;
         for (int b = 0; b < nsb; ++b) t += cs[(size_t)b * M];
         const int row = row_base + rr;
-        if (row < N) y[(int64_t)m * ldy + row] = t;
+        if (row < N) {
+            const int64_t o = (int64_t)m * ldy + row;
+            if constexpr (RES) t += i == (int)threadIdx.x ? res_first : res[o];
+            y[o] = t;
+        }
     }
 }
 
@@ -346,7 +373,7 @@ inline void consider(Plan &best, const GemvProblem *probs, int count, int nsb, i
     }
 }
 
-template <int M, int CPW, int V, bool FUSED>
+template <int M, int CPW, int V, bool FUSED, bool RES>
 hipError_t launch_plan(const Plan &pl, const GemvProblem *probs, int count, int nsb,
                        const Prepared &Q, hipStream_t stream) {
     const int RB = (1 << pl.lg_rg) * V;
@@ -355,6 +382,7 @@ hipError_t launch_plan(const Plan &pl, const GemvProblem *probs, int count, int 
     const uint8_t *w[kPieces];
     const float *x[kPieces];
     float *y[kPieces];
+    const float *r[kPieces];
     int N[kPieces], ldy[kPieces];
     const int64_t row_bytes = (int64_t)nsb * 144;
     int n = 0;
@@ -364,6 +392,7 @@ hipError_t launch_plan(const Plan &pl, const GemvProblem *probs, int count, int 
             w[n] = static_cast<const uint8_t *>(q.w) + r0 * row_bytes;
             x[n] = q.x;
             y[n] = q.y + r0;
+            r[n] = Q.residual ? Q.residual + r0 : nullptr;
             N[n] = (int)(q.N - r0 < pl.C ? q.N - r0 : pl.C);
             ldy[n] = (int)q.N;
         }
@@ -373,18 +402,19 @@ hipError_t launch_plan(const Plan &pl, const GemvProblem *probs, int count, int 
         P.w[i] = w[i];
         P.x[i] = x[i];
         P.y[i] = y[i];
+        P.r[i] = r[i];
         P.N[i] = N[i];
         P.ldy[i] = ldy[i];
     }
     const int gx = (int)((pl.C + RB - 1) / RB);
-    hipLaunchKernelGGL((stream_gemv_kernel<M, CPW, V, FUSED>), dim3(gx, n), dim3(64 * pl.waves),
-                       lds, stream, w[0], x[0], y[0], N[0], ldy[0], nsb,
+    hipLaunchKernelGGL((stream_gemv_kernel<M, CPW, V, FUSED, RES>), dim3(gx, n), dim3(64 * pl.waves),
+                       lds, stream, w[0], x[0], y[0], r[0], N[0], ldy[0], nsb,
                        pack_cfg(pl.lg_rg, V, pl.waves), P, Q);
     return hipGetLastError();
 }
 
 // Instances: V * CPW <= max_units<M>().
-template <int M, bool FUSED>
+template <int M, bool FUSED, bool RES>
 struct Table {
     static constexpr int U = max_units<M>();
     template <int CPW, int V>
@@ -416,7 +446,7 @@ struct Table {
                    const Prepared &Q, hipStream_t stream) {
         if constexpr (V * CPW <= U) {
             if (pl.cpw == CPW && pl.v == V) {
-                e = launch_plan<M, CPW, V, FUSED>(pl, probs, count, nsb, Q, stream);
+                e = launch_plan<M, CPW, V, FUSED, RES>(pl, probs, count, nsb, Q, stream);
                 return true;
             }
         }
@@ -465,7 +495,7 @@ struct PlanKeyHash {
     }
 };
 
-template <int M, bool FUSED>
+template <int M, bool FUSED, bool RES>
 hipError_t run_m(const GemvProblem *probs, int count, int nsb, const Prepared &Q,
                  hipStream_t stream) {
     static std::mutex mu;
@@ -483,28 +513,30 @@ hipError_t run_m(const GemvProblem *probs, int count, int nsb, const Prepared &Q
         if (it != cache.end()) {
             pl = it->second;
         } else {
-            pl = Table<M, FUSED>::plan(probs, count, nsb);
+            pl = Table<M, FUSED, RES>::plan(probs, count, nsb);
             if (cache.size() > 4096) cache.clear();
             cache.emplace(key, pl);
         }
     }
     if (!pl.ok) return hipErrorInvalidValue;
-    return Table<M, FUSED>::launch(pl, probs, count, nsb, Q, stream);
+    return Table<M, FUSED, RES>::launch(pl, probs, count, nsb, Q, stream);
 }
 
-template <bool FUSED>
+// RES: Q.residual is set (a single product); its kernels are instantiated
+// only in the translation unit of the residual entry point.
+template <bool FUSED, bool RES = false>
 hipError_t run(const GemvProblem *probs, int count, int64_t K, int64_t M, const Prepared &Q,
                hipStream_t stream) {
     const int nsb = (int)(K / kQK);
     switch (M) {
-    case 1: return run_m<1, FUSED>(probs, count, nsb, Q, stream);
-    case 2: return run_m<2, FUSED>(probs, count, nsb, Q, stream);
-    case 3: return run_m<3, FUSED>(probs, count, nsb, Q, stream);
-    case 4: return run_m<4, FUSED>(probs, count, nsb, Q, stream);
-    case 5: return run_m<5, FUSED>(probs, count, nsb, Q, stream);
-    case 6: return run_m<6, FUSED>(probs, count, nsb, Q, stream);
-    case 7: return run_m<7, FUSED>(probs, count, nsb, Q, stream);
-    case 8: return run_m<8, FUSED>(probs, count, nsb, Q, stream);
+    case 1: return run_m<1, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 2: return run_m<2, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 3: return run_m<3, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 4: return run_m<4, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 5: return run_m<5, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 6: return run_m<6, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 7: return run_m<7, FUSED, RES>(probs, count, nsb, Q, stream);
+    case 8: return run_m<8, FUSED, RES>(probs, count, nsb, Q, stream);
     default: return hipErrorInvalidValue;
     }
 }

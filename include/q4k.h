@@ -101,6 +101,20 @@ int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
                       int64_t M, float *y, void *stream);
 
 /* One product of a batch for q4k_quantize_gemv_batch. */
+/* Quantize-and-GEMV with the residual add in its last step:
+ * y[M][N] = residual[M][N] + Q8(x)[M][K] * W^T.  The decode step adds the
+ * output of the attention-output and down projections to the residual stream;
+ * the genie page (section 4, Path C) folds that add into the GEMV, and
+ * (section 6) keeps this single-kernel form over a split-K GEMV.  The product
+ * is the one q4k_quantize_gemv computes, bit for bit, and the add is one fp32
+ * rounding per element, so y equals (float)(residual + q4k_quantize_gemv).
+ *   residual  device fp32 [M][N], 4-byte aligned; either y itself (an
+ *             in-place update of the residual stream) or a buffer that does
+ *             not overlap y (a partial overlap returns Q4K_EINVAL).
+ * Other arguments, limits and checks as for q4k_quantize_gemv. */
+int q4k_quantize_gemv_residual(const void *w, int64_t N, int64_t K, const float *x,
+                               int64_t M, const float *residual, float *y, void *stream);
+
 typedef struct q4k_gemv_problem {
     const void *w;     /* device Q4_K weights, N rows x (K/256)*144 bytes, 16-byte aligned */
     const float *x;    /* device fp32 activations [M][K], 16-byte aligned                */

@@ -136,6 +136,15 @@ def matvec(w, N, K, codes, scales, rows=None) -> np.ndarray:
     return y
 
 
+def matvec_residual(w, N, K, codes, scales, residual, rows=None) -> np.ndarray:
+    """fp64 [M, len(rows)]: residual[m, rows[r]] + matvec(...)[m, r] -- the
+    decode step's residual-stream update with the add taken into the GEMV
+    ("genie-ai-runtime ...", section 4, Path C).  residual is [M, N]."""
+    y = matvec(w, N, K, codes, scales, rows)
+    res = np.asarray(residual, np.float64).reshape(y.shape[0], N)
+    return res[:, _rows(rows, N)] + y
+
+
 def matvec_intform(w, N, K, codes, scales, sums, rows=None) -> np.ndarray:
     codes, scales, sums = _c(codes, np.int8), _c(scales, np.float32), _c(sums, np.int32)
     M = codes.size // K

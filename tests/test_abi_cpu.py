@@ -109,6 +109,22 @@ def test_quantize_gemv_argument_checks(L):
     assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
 
 
+def test_quantize_gemv_residual_argument_checks(L):
+    f = L.q4k_quantize_gemv_residual
+    B = 0x20000                          # disjoint from A's [M][N] fp32 range below
+    assert f(None, 16, 512, A, 1, B, A, None) == EINVAL
+    assert f(A, 16, 512, A, 1, None, A, None) == EINVAL
+    assert f(A, 16, 512, A, 1, B, None, None) == EINVAL
+    assert f(A, 16, 500, A, 1, B, A, None) == ESHAPE
+    assert f(A, 16, 512, A, 9, B, A, None) == ESHAPE
+    assert f(A, 16, 9728, A, 4, B, A, None) == ESHAPE   # M*K beyond the LDS limit
+    assert f(A, 16, 512, A, 1, B + 2, A, None) == EALIGN
+    assert f(A + 4, 16, 512, A, 1, B, A, None) == EALIGN
+    # residual partly overlapping y (not the same buffer) is rejected
+    assert f(A, 16, 512, A, 2, A + 4, A, None) == EINVAL
+    assert f(A, 16, 512, A, 2, A, A + 124, None) == EINVAL
+
+
 def test_quantize_gemv_batch_argument_checks(L):
     f = L.q4k_quantize_gemv_batch
     P = q4k._lib.GemvProblem

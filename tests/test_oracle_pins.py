@@ -64,6 +64,29 @@ def test_golden_superblock_unpack(oracle_lib, idx):
         assert w.sum() == b["row_sum"]
 
 
+def test_golden_residual_matvec(oracle_lib):
+    """y = residual + W x with one-hot Q8 rows (code 1, scale 1) picks single
+    hand-worked weights of the golden blocks: y[m, n] = w_n[k_m] + r[m, n]
+    exactly.  Distinct k per row and r per (m, n) catch a transposed residual
+    or a row / column mix-up."""
+    blocks = _load("q4k_superblock_handbuilt.json")["blocks"][:2]
+    w = np.concatenate([_block_bytes(b) for b in blocks])
+    ks = sorted(set(int(k) for k in blocks[0]["w_expected"]) &
+                set(int(k) for k in blocks[1]["w_expected"]))[:3]
+    assert len(ks) >= 2
+    M, N, K = len(ks), 2, 256
+    codes = np.zeros((M, K), np.int8)
+    for m, k in enumerate(ks):
+        codes[m, k] = 1
+    scales = np.ones((M, K // 32), np.float32)
+    r = np.array([[0.25 * (1 + m) - 4.0 * n for n in range(N)] for m in range(M)])
+    y = oracle_lib.matvec_residual(w, N, K, codes, scales, r)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            assert y[m, n] == blocks[n]["w_expected"][str(k)] + r[m, n]
+    assert (oracle_lib.matvec_residual(w, N, K, codes, scales, r, rows=[1]) == y[:, 1:]).all()
+
+
 def test_generator_pack_roundtrip(oracle_lib):
     for seed in range(20):
         f = qi.draw_q4k_fields(3, 512, seed)
