@@ -33,6 +33,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; results are visible after the stream is synced.
  *   - Inputs are read-only; outputs are fully overwritten (never accumulated).
+ *     The one input that may share memory with the output is the residual of
+ *     q4k_quantize_gemv_residual (an in-place update of the residual stream).
  *   - Arguments are checked on the host before anything is launched; a failed
  *     check returns a negative status and launches nothing.  A launch error
  *     reported by the runtime returns Q4K_EHIP.  Nothing is printed and no
