@@ -95,3 +95,35 @@ def test_residual_writes_only_its_output(q4k, oracle_lib):
     assert (rb[:16] == -7.0).all() and (rb[16 + M * N:] == -7.0).all()
     assert (rb[16:16 + M * N] == r.reshape(-1)).all()
     _check_oracle(y.cpu().numpy(), r, w, N, K, x, oracle_lib, None, "residual into a view")
+
+
+def test_residual_in_place_graph_replays(q4k):
+    """The decode-step use: the o (2560 x 4096) and down (2560 x 9728)
+    products add into one residual stream in place, captured in a HIP graph
+    and replayed three times with eager work between the replays.  After each
+    replay the stream must hold, bit for bit, the fp32 sums built on the host
+    from the two products' q4k_quantize_gemv outputs."""
+    import torch
+    shapes = [(2560, 4096), (2560, 9728)]
+    ws = [to_dev(qi.make_q4k_bytes(N, K, 9800 + i)) for i, (N, K) in enumerate(shapes)]
+    xs = [to_dev(qi.make_act(1, K, 9810 + i)) for i, (N, K) in enumerate(shapes)]
+    r0 = qi.make_act(1, 2560, 9820)
+    ys = [q4k.q4k_quantize_gemv(w, N, K, x).cpu().numpy() for w, x, (N, K) in zip(ws, xs, shapes)]
+    resid = to_dev(r0)
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for w, x, (N, K) in zip(ws, xs, shapes):
+            q4k.q4k_quantize_gemv_residual(w, N, K, x, resid, y=resid)
+    torch.cuda.synchronize()
+    assert (resid.cpu().numpy() == r0).all()          # capture launched nothing
+    expect = r0.copy()
+    for k in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for y in ys:
+            expect = (expect + y).astype(np.float32)
+        got = resid.cpu().numpy()
+        assert (got.view(np.uint32) == expect.view(np.uint32)).all(), "replay %d" % k
+        _ = torch.ones(1024, device="cuda").sum().item()   # eager work between replays
