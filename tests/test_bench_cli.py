@@ -1,0 +1,14 @@
+"""bench.py's command line on the CPU: more than one GPU is refused with a
+message and a non-zero status before anything touches a device."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
