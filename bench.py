@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the secondary prefill-GEMM measurement")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the prefill GEMM measurement (with its parity check) and "
+                         "print it")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the small-batch and routed-expert measurements")
     ap.add_argument("--prefill-group", choices=sorted(PREFILL_GROUPS),
@@ -323,6 +326,9 @@ class Prefill:
                         P(self.weights[base + p][0].data_ptr(), self.ys[p].data_ptr(),
                           self.weights[base + p][1]) for p in idx])
         self.units = LAYERS * len(self.groups)
+        # split-tile workspace (counters zero once; every call leaves them zero)
+        self.ws = q4k.gemm_workspace(dev)
+        self.ws_args = (self.ws.data_ptr(), self.ws.numel())
         torch.cuda.synchronize()
 
     def quantize(self, i, s):
@@ -338,7 +344,7 @@ class Prefill:
         wt, N, K = self.weights[i]
         c, sc, su = self.qbufs[p]
         if self.L.q4k_gemm(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(),
-                           PREFILL_M, self.ys[p].data_ptr(), s):
+                           PREFILL_M, self.ys[p].data_ptr(), *self.ws_args, s):
             raise RuntimeError("q4k_gemm launch failed")
 
     def gemm_unit(self, u, s):
@@ -350,7 +356,7 @@ class Prefill:
         _, _, K = self.weights[layer * len(self.shapes) + idx[0]]
         c, sc, su = self.qbufs[idx[0]]
         if self.L.q4k_gemm_batch(self.batch_arr[(layer, gi)], len(idx), K, c.data_ptr(),
-                                 sc.data_ptr(), su.data_ptr(), PREFILL_M, s):
+                                 sc.data_ptr(), su.data_ptr(), PREFILL_M, *self.ws_args, s):
             raise RuntimeError("q4k_gemm_batch launch failed")
 
     def parity(self, oracle):
@@ -437,12 +443,14 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
            "tok_per_s": round(PREFILL_M * steps / elapsed, 0),
            "gemm_ms_per_step": round(gemm_s * 1e3, 3),
            # achieved: algorithmic Q4_K x Q8 ops (2*M*N*K) per second; the kernel
-           # issues two fp16 matrix ops per algorithmic one (activation hi, lo)
-           "roofline": {"bound": "mfma", "kernel": "q4k gemm_f16_kernel (fp16 matrix cores, "
-                                                   "activation hi/lo, split K)",
+           # issues one fp16 matrix op per algorithmic one on integer-valued
+           # operands, plus 3/16 as many bf16 ones for the min term
+           "roofline": {"bound": "mfma", "kernel": "q4k gemm_kernel (fp16 matrix cores on "
+                                                   "integer operands sc*q and codes, "
+                                                   "deterministic split tiles)",
                         "achieved": round(tops, 1), "peak": FP16_PEAK_TFLOPS, "unit": "TOPS",
                         "frac": round(tops / FP16_PEAK_TFLOPS, 4),
-                        "matrix_core_busy": round(2 * tops / FP16_PEAK_TFLOPS, 4),
+                        "matrix_core_busy": round(tops * (1 + 3 / 16) / FP16_PEAK_TFLOPS, 4),
                         "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
                         "mean_launch_us": round(gemm_s / pre.units * 1e6, 2)},
            "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity}
@@ -466,14 +474,18 @@ def measure_small_batch(torch, dec, steps=5):
         ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
               for N in {N for _, N, _ in dec.weights}}
         res = {}
-        for path, fn in (("gemv", L.q4k_gemv), ("gemm", L.q4k_gemm)):
+        gws = q4k.gemm_workspace(dev)
+        for path in ("gemv", "gemm"):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 s = torch.cuda.current_stream().cuda_stream
                 for wt, N, K in dec.weights:
                     c, sc, su = xs[K]
-                    if fn(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(), M,
-                          ys[N].data_ptr(), s):
+                    a = (wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(), M,
+                         ys[N].data_ptr())
+                    st = (L.q4k_gemv(*a, s) if path == "gemv" else
+                          L.q4k_gemm(*a, gws.data_ptr(), gws.numel(), s))
+                    if st:
                         raise RuntimeError("launch failed")
             g.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -784,6 +796,10 @@ def main():
     import oracle
 
     oracle.build(force=False)
+    if args.prefill_only:
+        print(json.dumps({"prefill_gemm": measure_prefill(torch, q4k, qi, oracle,
+                                                          args.prefill_steps)}))
+        return
     dec = Decode(torch, q4k, qi)
     parity = dec.parity(oracle)
 

@@ -12,8 +12,11 @@ Functions carry the C names:
     q4k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (fp32 x, one launch)
     q4k_quantize_gemv_residual(w, N, K, x, r[, y=r]) -> r + Q8(x) W^T (residual add inside)
     q4k_quantize_gemv_batch([(w, N, x), ...], K)     -> [y, ...]   (<= 8 products, one launch)
-    q4k_gemm(w, N, K, codes, scales, sums)           -> y [M, N]
-    q4k_gemm_batch([(w, N), ...], K, codes, scales, sums) -> [y, ...] (<= 8 products, one launch)
+    q4k_gemm(w, N, K, codes, scales, sums, workspace="auto") -> y [M, N]
+    q4k_gemm_batch([(w, N), ...], K, codes, scales, sums, workspace="auto")
+                                                     -> [y, ...] (<= 8 products, one launch)
+    gemm_workspace(device)                           -> the zero-filled GEMM workspace reused
+                                                        by workspace="auto"
     q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
                  act_per_slot, workspace=None)       -> y
     q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H, F,
@@ -23,6 +26,7 @@ Functions carry the C names:
 """
 from ._lib import (  # noqa: F401
     Q4KError,
+    gemm_workspace,
     lib,
     lib_path,
     q4k_gemm,

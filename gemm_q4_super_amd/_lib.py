@@ -15,6 +15,7 @@ EXPORTED_SYMBOLS = (
     "q4k_quantize_gemv_batch",
     "q4k_gemm",
     "q4k_gemm_batch",
+    "q4k_gemm_workspace_bytes",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
     "q4k_moe_ffn",
@@ -59,9 +60,11 @@ def lib():
         L = ctypes.CDLL(lib_path)
         L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
         L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
-        L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+        L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
         L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
-                                     _I, _P]
+                                     _I, _P, ctypes.c_size_t, _P]
+        L.q4k_gemm_workspace_bytes.argtypes = []
+        L.q4k_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
         L.q4k_quantize_gemv_residual.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P]
         L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
@@ -221,11 +224,50 @@ def q4k_quantize_gemv_batch(problems, K, ys=None):
     return ys
 
 
-def q4k_gemm(w, N, K, codes, scales, sums, y=None):
-    return _matrix_call(lib().q4k_gemm, "q4k_gemm", w, N, K, codes, scales, sums, y)
+_GEMM_WS = {}
 
 
-def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None):
+def gemm_workspace(device):
+    """A zero-filled GEMM workspace for `device`, made once and reused: every
+    call leaves its counters zero again.  Calls on several streams at once
+    must pass workspaces of their own."""
+    import torch
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _GEMM_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(int(lib().q4k_gemm_workspace_bytes()), dtype=torch.uint8, device=dev)
+        _GEMM_WS[key] = ws
+    return ws
+
+
+def _gemm_ws(workspace, device):
+    """(pointer, bytes) of the workspace argument: "auto" -> the cached one,
+    None -> no workspace (whole tiles only), else a uint8 device tensor."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a device tensor")
+        workspace = gemm_workspace(device)
+    _dev(workspace, "workspace")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def q4k_gemm(w, N, K, codes, scales, sums, y=None, workspace="auto"):
+    import torch
+    for t, n in ((w, "w"), (codes, "codes"), (scales, "scales"), (sums, "sums")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    wp, wb = _gemm_ws(workspace, codes.device)
+    _check(lib().q4k_gemm(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(sums), M, _ptr(y),
+                          wp, wb, _stream(codes)), "q4k_gemm")
+    return y
+
+
+def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None, workspace="auto"):
     """Several prefill GEMMs against the same Q8 rows in one launch.
 
     `problems` is a sequence of (w, N); returns the list of outputs y_i [M, N_i]
@@ -243,8 +285,9 @@ def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None):
     for i, ((w, N), y) in enumerate(zip(problems, ys)):
         _dev(w, "w")
         arr[i] = GemmProblem(_ptr(w), _ptr(y), N)
+    wp, wb = _gemm_ws(workspace, codes.device)
     _check(lib().q4k_gemm_batch(arr, len(problems), K, _ptr(codes), _ptr(scales), _ptr(sums), M,
-                                _stream(codes)), "q4k_gemm_batch")
+                                wp, wb, _stream(codes)), "q4k_gemm_batch")
     return ys
 
 

@@ -5,42 +5,55 @@
 // the matrix cores.  With x^ = a*c (Q8: one fp32 scale a per 32 codes c) and
 // w = d*sc[j]*q - dmin*mn[j] (Q4_K), one output is
 //
-//   y[m][n] = sum_b d[n,b] * sum_{k in b} (sc*q)[n,k] * x^[m,k]
-//           - sum_{b,j} (dmin*mn)[n,b,j] * (a*S)[m,b,j]
+//   y[m][n] = sum_b d[n,b] * sum_j a[m,b,j] * E[m,n,b,j]
+//           - sum_b sum_j (dmin*mn)[n,b,j] * (a*S)[m,b,j],
+//   E[m,n,b,j] = sum_{i<32} (sc*q)[n,b,j,i] * c[m,b,j,i]   (an integer),
 //
 // with S the code sum of one activation block.
 //
-// Both per-32-element scales sit inside the matrix-core operands, so the
-// only vector-ALU work per output is one fma per super-block:
-//  * weight operand (B, columns n): the integer sc*q <= 945, exact in fp16, made
-//    from the nibbles with one byte permute and one packed fp16 fma per pair
-//    ((1024 + q)*sc - 1024*sc, fused, so exact);
-//  * activation operand (A, rows m): x^ scaled by a power of two 2^-e per
-//    activation row and super-block (e from the largest block scale, which
-//    keeps every value in fp16 range), split into two fp16 parts hi + lo
-//    with 22 significant bits: hi = fp16(c*ah) and lo = fp16((c*ah - hi) +
-//    c*al) where a*2^-e = ah + al; c*ah - hi is exact in fp16 (the error of
-//    an fp16 product), so hi + lo = a*2^-e*c to about 2^-21;
-//  * sc*q*hi and sc*q*lo products are exact in fp32; each super-block's sum
-//    accumulates over 16 v_mfma_f32_32x32x16_f16 per 32x32 tile, then
-//    acc += (d * 2^e) * tmp;
-//  * min term: bf16 matrix cores with both fp32 factors split into two bf16
-//    parts (16 significant bits), accumulated straight into acc.
-// Activation scales make an int8 contraction cost three vector operations
-// per output and 32 elements (convert, scale product, fma); on gfx950 those
-// do not overlap with the matrix cores, which is why this path spends
-// twice the fp16 matrix work instead.
+// Main term.  Both matrix-core operands hold integers exactly in fp16: the
+// weight operand sc*q <= 945 (made from the nibbles with one byte permute and
+// one fused packed fp16 fma per pair: (1024 + q)*sc - 1024*sc), the activation
+// operand the code c (a byte permute and one packed fp16 add per pair).  Two
+// v_mfma_f32_32x32x16_f16 per 32x32 tile give E exactly (|E| < 2^22, every
+// partial sum an integer below 2^24), which is sc * (the sub-block's integer
+// dot).  The vector ALU then does one fma per output and sub-block,
+// u = a*E + u, with a the same for all 16 outputs of a lane (a lane holds one
+// activation row), and one fma per output and super-block, acc = d*u + acc.
+//
+// Min term.  Per super-block, sum_j (-dmin*mn_j) * (a*S)_j is an 8-long
+// contraction; both factors (fp32; -dmin*mn exactly, a*S rounded once) are
+// split into three bf16 parts hi + mid + lo (each rounded to nearest from
+// the remainder, so the parts sum to the value exactly) and the six products
+// above 2^-24 relative (hh, hm, mh, hl, mm, lh) fill the 48 k-slots of three
+// v_mfma_f32_32x32x16_bf16, accumulated straight into acc.
+//
+// An int8 contraction (v_mfma_i32_32x32x32_i8 on the raw nibbles) needs, per
+// output and sub-block, an int-to-float convert, the product of the two
+// per-32-element scales (one from the weight row, one from the activation
+// row) and an fma: three vector ops where this layout needs one.
 //
 // Staging: a quarter super-block (64 elements of K: two sub-blocks, which
 // share one 32-byte group of quant bytes) per step, double-buffered in LDS.
 // The waves are specialised: on each SIMD one wave only reads operands from
-// LDS and runs the matrix-core ops, and one only loads raw blocks from
-// global memory and converts them into the other LDS buffer (raw loads two
-// steps ahead, two register sets).  A wave that mixes both stalls its vector
-// ops behind its own matrix ops, while two waves on one SIMD overlap them.
-// One barrier per step.  Workgroup tile (64*WVN) x (32*TM*WVM), one
-// matrix-core wave per 64 x 32*TM outputs.  Tile order is XCD-aware: all M
-// tiles of one weight column-block run on one XCD, sharing its L2.
+// LDS and runs the matrix-core ops and their epilogue, and one only loads raw
+// blocks from global memory and converts them into the other LDS buffer (raw
+// loads two steps ahead, two register sets).  One barrier per step.
+// Workgroup tile (64*WVN) weight rows x (32*TM*WVM) activation rows, one
+// matrix-core wave per 64 x 32*TM outputs.
+//
+// Work split (deterministic).  The work is a sequence of units, one per
+// (tile, super-block); tile t = column-block * (M tiles) + M tile, so the M
+// tiles of one weight column-block are adjacent.  Workgroup g takes units
+// [g*U/G, (g+1)*U/G): whole tiles, plus at most a partial tile at each end.
+// Workgroups are numbered so that the 8 XCDs hold contiguous unit ranges
+// (blockIdx % 8 is the XCD), which keeps a column-block's weights in one L2.
+// A whole tile is stored directly.  A partial tile is written to a slot of
+// the workspace, and a per-(tile, wave) counter, incremented after a
+// device-scope release fence, tells the last contributor to arrive; that one
+// adds the parts in contributor order (so the bits do not depend on arrival
+// order), writes y and returns the counter to zero.  Without a workspace the
+// grid has one workgroup per tile and no partial tiles.
 #include <algorithm>
 #include <type_traits>
 
@@ -58,18 +71,17 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NXCD = 8;
-constexpr int TN = 2;        // 32-row weight tiles per wave
-constexpr int ASTR = 72;     // fp16 per weight row and step: [kh 2][sub 2][lh 2][8] + 8 pad
-constexpr int BSTR = 136;    // fp16 per activation row and step: [lh 2][sub 2][kh 2][hi/lo 2][8] + 8 pad
+constexpr int TN = 2;        // 32-row weight tiles per matrix-core wave
+constexpr int OSTR = 72;     // fp16 per operand row and step: [kh 2][s 2][lh 2][8] + 8 pad
 
 template <int WN, int WM>
 struct __attribute__((aligned(16))) Lds {
-    _Float16 aw[2][WN][ASTR];        // sc*q of a step's two sub-blocks
-    _Float16 bx[2][WM][BSTR];        // x^ * 2^-e as hi, lo
-    float dn[2][WN];                 // d of the super-block (by super-block parity)
-    float es[2][WM];                 // 2^e of the activation row's super-block
-    unsigned short qh[2][2][WN][8];  // -(dmin*mn) split hi / lo (bf16 bits)
-    unsigned short ph[2][2][WM][8];  // a*S split hi / lo (bf16 bits)
+    _Float16 aw[2][WN][OSTR];          // sc*q of a step's two sub-blocks
+    _Float16 bx[2][WM][OSTR];          // codes of a step's two sub-blocks
+    float dn[2][WN];                   // d of the super-block (by super-block parity)
+    float as[2][8][WM];                // activation block scale a[j][row]
+    unsigned short wm[2][3][WN][8];    // -(dmin*mn_j) as bf16 hi, mid, lo
+    unsigned short pm[2][3][WM][8];    // (a*S)_j as bf16 hi, mid, lo
 };
 
 template <int V>
@@ -83,6 +95,15 @@ struct GemmSet {
     int N[kMaxGemmBatch];
     int tile0[kMaxGemmBatch + 1];
     int count;
+};
+
+// Unit ranges of the workgroups and the split-tile workspace.
+struct Sched {
+    int64_t units;     // tiles * nsb
+    int groups;        // G, workgroups in the grid
+    int tiles_m;       // M tiles
+    float *part;       // 2 partial-tile slots per workgroup (null: no partial tiles)
+    int *cnt;          // one counter per (tile, matrix-core wave)
 };
 
 template <int WVN, int WVM, int TM>
@@ -104,11 +125,19 @@ __device__ __forceinline__ float half_lo(unsigned v) {
 __device__ __forceinline__ float half_hi(unsigned v) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(v >> 16));
 }
-// Split fp32 into two bf16 parts by truncation (hi + lo keeps 16 significant bits).
-__device__ __forceinline__ void split_bf16(float v, unsigned short &hi, unsigned short &lo) {
+// bf16 bits of v rounded to nearest, ties to even (v finite).
+__device__ __forceinline__ unsigned bf16_rn(float v) {
     const unsigned b = __float_as_uint(v);
-    hi = (unsigned short)(b >> 16);
-    lo = (unsigned short)(__float_as_uint(v - __uint_as_float(b & 0xFFFF0000u)) >> 16);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+// v = hi + mid + lo exactly for any fp32 v (each part rounded to nearest
+// from the remainder left by the parts before it).
+__device__ __forceinline__ void split3(float v, unsigned &hi, unsigned &mid, unsigned &lo) {
+    hi = bf16_rn(v);
+    const float r1 = v - __uint_as_float(hi << 16);
+    mid = bf16_rn(r1);
+    const float r2 = r1 - __uint_as_float(mid << 16);
+    lo = bf16_rn(r2);
 }
 // Two fp16 of the integers 1024 + (byte 0, byte 1) or (byte 2, byte 3) of v
 // (0x64 is the high byte of fp16 1024, whose unit in the last place is 1).
@@ -121,7 +150,7 @@ __device__ __forceinline__ half2 bias_pair_hi(unsigned v) {
 __device__ __forceinline__ half8 cat4(half2 a, half2 b, half2 c, half2 d) {
     return (half8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
-// 6-bit scale (or min, with hi = true) of sub-block j from the header dwords.
+// 6-bit scale (or min) of sub-block J from the header dwords.
 template <int J>
 __device__ __forceinline__ unsigned scale6(const u32x4 &h, bool min) {
     const unsigned lo = min ? h.z : h.y;
@@ -130,31 +159,50 @@ __device__ __forceinline__ unsigned scale6(const u32x4 &h, bool min) {
     return ((h.w >> (sh + (min ? 4 : 0))) & 15u) | (((lo >> (sh + 6)) & 3u) << 4);
 }
 
-template <int WVN, int WVM, int TM>
-__global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
-    const GemmSet set, int nsb, const int8_t *__restrict__ codes,
-    const float *__restrict__ scales, const int32_t *__restrict__ sums, int M, int splits) {
-    using C = Cfg<WVN, WVM, TM>;
-    constexpr int WN = C::WN, WM = C::WM, P = C::P;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-    Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
+// Workgroup -> unit range.  floor(g*U/G) is the first unit of workgroup g; the
+// workgroup holding unit u is floor(((u+1)*G - 1)/U).
+__device__ __forceinline__ int64_t range_begin(int64_t g, const Sched &s) {
+    return g * s.units / s.groups;
+}
+__device__ __forceinline__ int64_t group_of(int64_t u, const Sched &s) {
+    return ((u + 1) * s.groups - 1) / s.units;
+}
 
-    // XCD-aware tile and K range of this workgroup: the M tiles and K parts
-    // of one (virtual) weight column-block run on one XCD.
-    const int tiles_m = (M + WM - 1) / WM;
-    const int xcd = blockIdx.x % NXCD, pos = blockIdx.x / NXCD;
-    const int per = tiles_m * splits;
-    const int vt = (pos / per) * NXCD + xcd, mt = (pos % per) / splits, sp = pos % splits;
-    if (vt >= set.tile0[set.count]) return;   // the whole workgroup exits, before any barrier
+struct Tile {
+    const uint8_t *w;
+    float *y;
+    int N, n0, m0;
+};
+
+template <int WN, int WM>
+__device__ __forceinline__ Tile tile_of(const GemmSet &set, int t, int tiles_m) {
+    const int vt = t / tiles_m, mt = t - vt * tiles_m;
     int pi = 0;
 #pragma unroll
     for (int k = 1; k < kMaxGemmBatch; ++k) pi += (k < set.count && vt >= set.tile0[k]);
-    const uint8_t *__restrict__ w = set.w[pi];
-    float *__restrict__ y = set.y[pi];
-    const int N = set.N[pi];
-    const int n0 = (vt - set.tile0[pi]) * WN, m0 = mt * WM;
-    const int sb0 = (int)((int64_t)nsb * sp / splits);
-    const int nl = (int)((int64_t)nsb * (sp + 1) / splits) - sb0;   // >= 1 (splits <= nsb)
+    Tile r;
+    r.w = set.w[pi];
+    r.y = set.y[pi];
+    r.N = set.N[pi];
+    r.n0 = (vt - set.tile0[pi]) * WN;
+    r.m0 = mt * WM;
+    return r;
+}
+
+template <int WVN, int WVM, int TM>
+__global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
+    const GemmSet set, const Sched sch, int nsb, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const int32_t *__restrict__ sums, int M) {
+    using C = Cfg<WVN, WVM, TM>;
+    constexpr int WN = C::WN, WM = C::WM, P = C::P, NC = C::NC;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
+
+    const int G = sch.groups;
+    const int gi = (G % NXCD == 0) ? (int)(blockIdx.x % NXCD) * (G / NXCD) + (int)(blockIdx.x / NXCD)
+                                   : (int)blockIdx.x;
+    const int64_t ub = range_begin(gi, sch), ue = range_begin(gi + 1, sch);
+    if (ub >= ue) return;   // the whole workgroup exits, before any barrier
     const int K = nsb * 256, nblk = nsb * 8;
     const int64_t row_bytes = (int64_t)nsb * 144;
     const int tid = threadIdx.x;
@@ -162,9 +210,9 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
     if (tid >= P) {
         // ---------------- converting waves ----------------
         const int p = tid - P;
-        // Raw loads.  Rows past N or M read row N-1 / M-1 and steps past the
-        // end of the K range read its last super-block (branch-free loads):
-        // they only feed outputs or buffers that are never used.
+        // Raw loads.  Rows past N or M read row N-1 / M-1 and units past the
+        // end of the range read its last unit (branch-free loads): they only
+        // feed outputs or buffers that are never used.
         struct Step {                 // one step: quant bytes, activation codes
             u32x4 q[C::NA];
             i32x4 c0[C::NB], c1[C::NB];
@@ -177,47 +225,53 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
         Step S0, S1;
         Block cur, nxt;
 
-        auto load = [&](auto setc, auto gc, int b) {
+        // Tile and super-block of unit u (units past the range: its last unit).
+        struct Pos {
+            Tile tl;
+            int b;
+        };
+        auto pos_of = [&](int64_t u) {
+            u = u < ue ? u : ue - 1;
+            const int t = (int)(u / nsb);
+            Pos r;
+            r.tl = tile_of<WN, WM>(set, t, sch.tiles_m);
+            r.b = (int)(u - (int64_t)t * nsb);
+            return r;
+        };
+        auto load = [&](auto setc, auto gc, const Pos &ps) {
             constexpr int g = decltype(gc)::value;
             Step &R = decltype(setc)::value ? S1 : S0;
-            b = sb0 + min(b, nl - 1);
+            const Tile &tl = ps.tl;
+            const int b = ps.b;
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) {
                 const int e = min(p + i * P, C::CA - 1);
-                const int row = min(n0 + (e >> 1), N - 1);
-                const uint8_t *src = w + (int64_t)row * row_bytes + (int64_t)b * 144;
+                const int row = min(tl.n0 + (e >> 1), tl.N - 1);
+                const uint8_t *src = tl.w + (int64_t)row * row_bytes + (int64_t)b * 144;
                 R.q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
                 if (g == 0) nxt.h[i] = *reinterpret_cast<const u32x4 *>(src);
             }
 #pragma unroll
             for (int i = 0; i < C::NB; ++i) {
                 const int e = min(p + i * P, C::CB - 1);
-                const int row = min(m0 + (e >> 1), M - 1);
+                const int row = min(tl.m0 + (e >> 1), M - 1);
                 const int8_t *src = codes + (int64_t)row * K + 256 * b + 32 * (2 * g + (e & 1));
                 R.c0[i] = *reinterpret_cast<const i32x4 *>(src);
                 R.c1[i] = *reinterpret_cast<const i32x4 *>(src + 16);
                 if (g == 0) {
                     const int64_t o = (int64_t)row * nblk + 8 * b;
-                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(scales + o);
-                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(scales + o + 4);
-                    const i32x4 s0 = *reinterpret_cast<const i32x4 *>(sums + o);
-                    const i32x4 s1 = *reinterpret_cast<const i32x4 *>(sums + o + 4);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        nxt.a[i][k] = a0[k];
-                        nxt.a[i][4 + k] = a1[k];
-                        nxt.s[i][k] = s0[k];
-                        nxt.s[i][4 + k] = s1[k];
+                    for (int k = 0; k < 8; ++k) {
+                        nxt.a[i][k] = scales[o + k];
+                        nxt.s[i][k] = sums[o + k];
                     }
                 }
             }
         };
 
         // Step g of a super-block (raw step in a register set, super-block data
-        // in B) -> LDS buffer F and super-block parity Q.  The weight quants
-        // become fp16 sc*q (and, on the first step, d and the min factors are
-        // written); the activation codes become fp16 hi, lo.  Lanes that share
-        // a row write identical header values.
+        // in B) -> LDS buffer F and super-block parity Q.  Lanes that share a
+        // row write identical header values.
         auto convert = [&](auto setc, auto gc, auto bufc, const Block &B, int Q) {
             constexpr int g = decltype(gc)::value;
             constexpr int F = decltype(bufc)::value;
@@ -247,7 +301,7 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
                                 __builtin_elementwise_fma(bias_pair_lo(v1), sv, bv),
                                 __builtin_elementwise_fma(bias_pair_hi(v1), sv, bv));
                 };
-                // kh = c; the two lanes of a row land 16 banks apart (no conflict)
+                // [kh = c][s][lh][8]: the two lanes of a row land 16 banks apart
                 _Float16 *dst = &L.aw[F][row][32 * c];
                 *reinterpret_cast<half8 *>(dst + 0) = conv(lo.x, lo.y, sv0, bv0);
                 *reinterpret_cast<half8 *>(dst + 8) = conv(lo.z, lo.w, sv0, bv0);
@@ -256,19 +310,24 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
                 if (g == 0) {
                     L.dn[Q][row] = half_lo(h.x);
                     const float dmin = half_hi(h.x);
-                    // part c of the bf16 split: c = 0 the truncated high half, c = 1 the rest
-                    auto part = [&](unsigned mn) -> unsigned {
-                        const float v = -dmin * (float)mn;
-                        const unsigned bits = __float_as_uint(v);
-                        const float r = v - __uint_as_float(bits & 0xFFFF0000u);
-                        return (c ? __float_as_uint(r) : bits) >> 16;
-                    };
-                    u32x4 pv;
-                    pv[0] = part(scale6<0>(h, true)) | (part(scale6<1>(h, true)) << 16);
-                    pv[1] = part(scale6<2>(h, true)) | (part(scale6<3>(h, true)) << 16);
-                    pv[2] = part(scale6<4>(h, true)) | (part(scale6<5>(h, true)) << 16);
-                    pv[3] = part(scale6<6>(h, true)) | (part(scale6<7>(h, true)) << 16);
-                    *reinterpret_cast<u32x4 *>(&L.qh[Q][c][row][0]) = pv;
+                    unsigned pt[3][8];
+                    split3(-dmin * (float)scale6<0>(h, true), pt[0][0], pt[1][0], pt[2][0]);
+                    split3(-dmin * (float)scale6<1>(h, true), pt[0][1], pt[1][1], pt[2][1]);
+                    split3(-dmin * (float)scale6<2>(h, true), pt[0][2], pt[1][2], pt[2][2]);
+                    split3(-dmin * (float)scale6<3>(h, true), pt[0][3], pt[1][3], pt[2][3]);
+                    split3(-dmin * (float)scale6<4>(h, true), pt[0][4], pt[1][4], pt[2][4]);
+                    split3(-dmin * (float)scale6<5>(h, true), pt[0][5], pt[1][5], pt[2][5]);
+                    split3(-dmin * (float)scale6<6>(h, true), pt[0][6], pt[1][6], pt[2][6]);
+                    split3(-dmin * (float)scale6<7>(h, true), pt[0][7], pt[1][7], pt[2][7]);
+                    // lane c = 0 stores hi and mid, lane c = 1 stores lo
+#pragma unroll
+                    for (int part = 0; part < 3; ++part) {
+                        if ((part < 2) != (c == 0)) continue;
+                        u32x4 pv;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) pv[k] = pt[part][2 * k] | (pt[part][2 * k + 1] << 16);
+                        *reinterpret_cast<u32x4 *>(&L.wm[Q][part][row][0]) = pv;
+                    }
                 }
             }
             const half2 m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -276,84 +335,68 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
             for (int i = 0; i < C::NB; ++i) {
                 const int e = p + i * P;
                 if (C::CB % P != 0 && e >= C::CB) continue;
-                const int row = e >> 1, jb = e & 1;
-                // power-of-two scaling of the row's super-block: largest scale in [1, 2)
-                float amax = B.a[i][0];
-#pragma unroll
-                for (int k = 1; k < 8; ++k) amax = fmaxf(amax, B.a[i][k]);
-                const int ex = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 : 0;
-                // block 2g + jb's scale and sum, as bit selects (an indexed read
-                // would go to scratch)
-                const unsigned msk = 0u - (unsigned)jb;
-                const float a = __uint_as_float((__float_as_uint(B.a[i][2 * g]) & ~msk) |
-                                                (__float_as_uint(B.a[i][2 * g + 1]) & msk));
-                const int sj = (B.s[i][2 * g] & (int)~msk) | (B.s[i][2 * g + 1] & (int)msk);
-                const float as = __builtin_ldexpf(a, -ex);
-                const _Float16 ah = (_Float16)as;
-                const _Float16 al = (_Float16)(as - (float)ah);
-                const half2 ah2 = {ah, ah}, al2 = {al, al};
-                // 8 codes -> hi, lo
-                auto conv = [&](unsigned v0, unsigned v1, half8 &hv, half8 &lv) {
+                const int row = e >> 1, s = e & 1;
+                // 8 codes -> fp16 (c ^ 0x80 is c + 128 as a byte)
+                auto conv = [&](unsigned v0, unsigned v1) {
                     const unsigned u0 = v0 ^ 0x80808080u, u1 = v1 ^ 0x80808080u;
-                    const half2 cc[4] = {bias_pair_lo(u0) + m1152, bias_pair_hi(u0) + m1152,
-                                         bias_pair_lo(u1) + m1152, bias_pair_hi(u1) + m1152};
-                    half2 hh[4], ll[4];
+                    return cat4(bias_pair_lo(u0) + m1152, bias_pair_hi(u0) + m1152,
+                                bias_pair_lo(u1) + m1152, bias_pair_hi(u1) + m1152);
+                };
+                // sub-block s of the step, [kh][s][lh][8]
+                _Float16 *dst = &L.bx[F][row][16 * s];
+                const i32x4 c0 = R.c0[i], c1 = R.c1[i];
+                *reinterpret_cast<half8 *>(dst + 0) = conv(c0.x, c0.y);    // elements 0..7
+                *reinterpret_cast<half8 *>(dst + 8) = conv(c0.z, c0.w);    // 8..15
+                *reinterpret_cast<half8 *>(dst + 32) = conv(c1.x, c1.y);   // 16..23
+                *reinterpret_cast<half8 *>(dst + 40) = conv(c1.z, c1.w);   // 24..31
+                if (g == 0) {
+                    // lane s of the row: the scales and min-term parts of blocks 4s .. 4s+3
+                    unsigned pt[3][4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        hh[k] = cc[k] * ah2;
-                        const half2 r = __builtin_elementwise_fma(cc[k], ah2, -hh[k]);
-                        ll[k] = __builtin_elementwise_fma(cc[k], al2, r);
+                        const float a = s ? B.a[i][4 + k] : B.a[i][k];
+                        const int sj = s ? B.s[i][4 + k] : B.s[i][k];
+                        L.as[Q][4 * s + k][row] = a;
+                        split3(a * (float)sj, pt[0][k], pt[1][k], pt[2][k]);
                     }
-                    hv = cat4(hh[0], hh[1], hh[2], hh[3]);
-                    lv = cat4(ll[0], ll[1], ll[2], ll[3]);
-                };
-                // sub-block jb; the two lanes of a row land 16 banks apart
-                _Float16 *dst = &L.bx[F][row][32 * jb];
-                const i32x4 c0 = R.c0[i], c1 = R.c1[i];
-                half8 hv, lv;
-                conv(c0.x, c0.y, hv, lv);   // elements 0..7: lh 0, kh 0
-                *reinterpret_cast<half8 *>(dst + 0) = hv;
-                *reinterpret_cast<half8 *>(dst + 8) = lv;
-                conv(c0.z, c0.w, hv, lv);   // elements 8..15: lh 1, kh 0
-                *reinterpret_cast<half8 *>(dst + 64) = hv;
-                *reinterpret_cast<half8 *>(dst + 72) = lv;
-                conv(c1.x, c1.y, hv, lv);   // elements 16..23: lh 0, kh 1
-                *reinterpret_cast<half8 *>(dst + 16) = hv;
-                *reinterpret_cast<half8 *>(dst + 24) = lv;
-                conv(c1.z, c1.w, hv, lv);   // elements 24..31: lh 1, kh 1
-                *reinterpret_cast<half8 *>(dst + 80) = hv;
-                *reinterpret_cast<half8 *>(dst + 88) = lv;
-                if (g == 0) L.es[Q][row] = __builtin_ldexpf(1.0f, ex);   // both lanes of the row
-                unsigned short phi, plo;
-                split_bf16(a * (float)sj, phi, plo);
-                L.ph[Q][0][row][2 * g + jb] = phi;
-                L.ph[Q][1][row][2 * g + jb] = plo;
+#pragma unroll
+                    for (int part = 0; part < 3; ++part) {
+                        const unsigned lo2 = pt[part][0] | (pt[part][1] << 16);
+                        const unsigned hi2 = pt[part][2] | (pt[part][3] << 16);
+                        unsigned *dstp = reinterpret_cast<unsigned *>(&L.pm[Q][part][row][4 * s]);
+                        dstp[0] = lo2;
+                        dstp[1] = hi2;
+                    }
+                }
             }
         };
 
-        // Per step s: load step s+2 into the register set step s used,
-        // convert step s+1 into LDS buffer (s+1) & 1, one barrier.
-        load(IC<0>{}, IC<0>{}, 0);
-        load(IC<1>{}, IC<1>{}, 0);
+        // Per step: load the step two ahead into the register set the current
+        // step used, convert the next step into the other LDS buffer, barrier.
+        Pos pc = pos_of(ub);
+        load(IC<0>{}, IC<0>{}, pc);
+        load(IC<1>{}, IC<1>{}, pc);
         cur = nxt;
         convert(IC<0>{}, IC<0>{}, IC<0>{}, cur, 0);
         __syncthreads();
 #pragma unroll 1
-        for (int b = 0; b < nl; ++b) {
-            const int Q = b & 1;
-            load(IC<0>{}, IC<2>{}, b);
+        for (int64_t u = ub; u < ue; ++u) {
+            const int Q = (int)(u - ub) & 1;
+            const Pos pn = pos_of(u + 1);
+            load(IC<0>{}, IC<2>{}, pc);
             convert(IC<1>{}, IC<1>{}, IC<1>{}, cur, Q);
             __syncthreads();
-            load(IC<1>{}, IC<3>{}, b);
+            load(IC<1>{}, IC<3>{}, pc);
             convert(IC<0>{}, IC<2>{}, IC<0>{}, cur, Q);
             __syncthreads();
-            load(IC<0>{}, IC<0>{}, b + 1);
+            load(IC<0>{}, IC<0>{}, pn);
             convert(IC<1>{}, IC<3>{}, IC<1>{}, cur, Q);
             __syncthreads();
-            load(IC<1>{}, IC<1>{}, b + 1);
+            load(IC<1>{}, IC<1>{}, pn);
             convert(IC<0>{}, IC<0>{}, IC<0>{}, nxt, Q ^ 1);
             __syncthreads();
             cur = nxt;
+            pc = pn;
         }
         return;
     }
@@ -363,187 +406,254 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_f16_kernel(
     const int wn = wave / WVM, wm = wave % WVM;
     const int lr = lane & 31, lh = lane >> 5;
 
-    f32x16 acc[TN][TM], tmp[TN][TM];
-#pragma unroll
-    for (int u = 0; u < TN; ++u)
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                acc[u][t][i] = 0.0f;
-                tmp[u][t][i] = 0.0f;
-            }
+    f32x16 acc[TN][TM], usb[TN][TM];
+    const f32x16 zero16 = {};
 
-    // Sub-block s of the step in LDS buffer F: 8 matrix-core ops per 32x32 tile.
-    auto compute = [&](auto bufc, int s) {
+    // Sub-block J of the super-block (sub-block s of the step in LDS buffer F):
+    // two matrix-core ops per 32x32 tile give E; u = a*E (+ u).
+    auto compute = [&](auto bufc, auto sc, auto jc, int Q) {
         constexpr int F = decltype(bufc)::value;
-        half8 A[TN][2], B[TM][2][2];
+        constexpr int s = decltype(sc)::value;
+        constexpr int J = decltype(jc)::value;
+        half8 A[TN][2], B[TM][2];
+        float a[TM];
 #pragma unroll
         for (int u = 0; u < TN; ++u) {
-            const _Float16 *src = &L.aw[F][wn * 64 + u * 32 + lr][16 * s + 8 * lh];
+            const _Float16 *src = &L.aw[F][(wn * TN + u) * 32 + lr][16 * s + 8 * lh];
             A[u][0] = *reinterpret_cast<const half8 *>(src);
             A[u][1] = *reinterpret_cast<const half8 *>(src + 32);
         }
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const _Float16 *src = &L.bx[F][(wm * TM + t) * 32 + lr][64 * lh + 32 * s];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    B[t][kh][hl] = *reinterpret_cast<const half8 *>(src + 16 * kh + 8 * hl);
+            const int r = (wm * TM + t) * 32 + lr;
+            const _Float16 *src = &L.bx[F][r][16 * s + 8 * lh];
+            B[t][0] = *reinterpret_cast<const half8 *>(src);
+            B[t][1] = *reinterpret_cast<const half8 *>(src + 32);
+            a[t] = L.as[Q][J][r];
         }
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int u = 0; u < TN; ++u)
 #pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
+            for (int t = 0; t < TM; ++t) {
+                f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][0], B[t][0], zero16, 0, 0, 0);
+                e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][1], B[t][1], e, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    usb[u][t][i] = J == 0 ? e[i] * a[t] : fmaf(e[i], a[t], usb[u][t][i]);
+            }
+    };
+
+    // End of a super-block: acc += d * u, then the min term on the matrix
+    // cores.  A lane's outputs share one activation row m and span 16 weight
+    // rows n (their d).
+    constexpr int WP[6] = {0, 0, 1, 0, 1, 2};   // weight part of k-slot group 2p + lh
+    constexpr int AP[6] = {0, 1, 0, 2, 1, 0};   // activation part
+    auto finish = [&](int Q) {
+#pragma unroll
+        for (int u = 0; u < TN; ++u) {
+            const int r0 = (wn * TN + u) * 32;
+            float dv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&L.dn[Q][r0 + 8 * q + 4 * lh]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dv[4 * q + k] = d4[k];
+            }
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[u][t][i] = fmaf(dv[i], usb[u][t][i], acc[u][t][i]);
+        }
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+            bf16x8 W[TN], X[TM];
+            const int wp = lh ? WP[2 * pp + 1] : WP[2 * pp];
+            const int ap = lh ? AP[2 * pp + 1] : AP[2 * pp];
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+                W[u] = *reinterpret_cast<const bf16x8 *>(&L.wm[Q][wp][(wn * TN + u) * 32 + lr][0]);
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                X[t] = *reinterpret_cast<const bf16x8 *>(&L.pm[Q][ap][(wm * TM + t) * 32 + lr][0]);
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(W[u], X[t], acc[u][t], 0, 0, 0);
+        }
+    };
+
+    // Output of the lane for tile (u, t): activation row m, weight rows
+    // n .. n+3 for each quarter q (n = n0 + ... + 8q + 4lh).
+    auto store_y = [&](const Tile &tl) {
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int m = tl.m0 + (wm * TM + t) * 32 + lr;
+            if (m >= M) continue;
+            float *yr = tl.y + (int64_t)m * tl.N;
+            const bool vec = ((tl.N & 3) == 0) && ((reinterpret_cast<uintptr_t>(tl.y) & 15) == 0);
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = tl.n0 + (wn * TN + u) * 32 + 8 * q + 4 * lh;
+                    const f32x4 v = {acc[u][t][4 * q], acc[u][t][4 * q + 1], acc[u][t][4 * q + 2],
+                                     acc[u][t][4 * q + 3]};
+                    if (vec && n + 3 < tl.N) {
+                        *reinterpret_cast<f32x4 *>(yr + n) = v;
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            if (n + k < tl.N) yr[n + k] = v[k];
+                    }
+                }
+        }
+    };
+
+    // Partial-tile slot layout: [wave][u][t][pair q][lane] float pairs.
+    auto slot_ptr = [&](int64_t slot) {
+        return sch.part + slot * (int64_t)(WN * WM) + (int64_t)wave * (TN * TM * 16 * 64);
+    };
+
+    // End of the unit range's part of tile t (units [s0, s1) of it).
+    auto finish_tile = [&](int t, int64_t s0, int64_t s1) {
+        const Tile tl = tile_of<WN, WM>(set, t, sch.tiles_m);
+        const int64_t t0 = (int64_t)t * nsb, t1 = t0 + nsb;
+        if (s0 == t0 && s1 == t1) {   // the whole tile
+            store_y(tl);
+            return;
+        }
+        const int64_t first = group_of(t0, sch), last = group_of(t1 - 1, sch);
+        const int nparts = (int)(last - first + 1);
+        // slot 0 of a workgroup: a tile that began before its range; slot 1:
+        // the tile its range ends in
+        const int64_t my_slot = 2 * (int64_t)gi + (s0 > t0 ? 0 : 1);
+        // Parts go through agent-coherent accesses (relaxed atomic stores and
+        // loads at agent scope), and the counter is only incremented once
+        // every store of the wave has completed.  An agent-scope fence instead
+        // would write back and invalidate the whole L2 of the XCD, evicting
+        // the weight and activation tiles of every workgroup on it.
+        unsigned long long *dst = reinterpret_cast<unsigned long long *>(slot_ptr(my_slot));
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const unsigned long long v =
+                        (unsigned long long)__float_as_uint(acc[u][tt][2 * q]) |
+                        ((unsigned long long)__float_as_uint(acc[u][tt][2 * q + 1]) << 32);
+                    __hip_atomic_store(dst + ((u * TM + tt) * 8 + q) * 64 + lane, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+        __builtin_amdgcn_s_waitcnt(0);   // every store above has completed
+        int *cp = sch.cnt + (int64_t)t * NC + wave;
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0);
+        if (old != nparts - 1) return;
+        // the last to arrive adds the parts in contributor order
+        f32x16 sum[TN][TM];
+        for (int k = 0; k < nparts; ++k) {
+            const int64_t g2 = first + k;
+            if (g2 == gi) {
 #pragma unroll
                 for (int u = 0; u < TN; ++u)
 #pragma unroll
-                    for (int t = 0; t < TM; ++t)
-                        tmp[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            B[t][kh][hl], A[u][kh], tmp[u][t], 0, 0, 0);
-    };
-
-    // End of a super-block: acc += (d * 2^e) * tmp, and the min term.  A
-    // lane's outputs share one weight row n (its d) and span 16 activation
-    // rows m (their 2^e).
-    auto finish = [&](int Q) {
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const int x0 = (wm * TM + t) * 32;
-            float ev[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&L.es[Q][x0 + 8 * q + 4 * lh]);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) ev[4 * q + k] = e4[k];
+                    for (int tt = 0; tt < TM; ++tt) sum[u][tt] = k == 0 ? acc[u][tt] : sum[u][tt] + acc[u][tt];
+                continue;
             }
-            const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(&L.ph[Q][lh][x0 + lr][0]);
+            unsigned long long *src = reinterpret_cast<unsigned long long *>(
+                slot_ptr(2 * g2 + (range_begin(g2, sch) > t0 ? 0 : 1)));
 #pragma unroll
-            for (int u = 0; u < TN; ++u) {
-                const int r = wn * 64 + u * 32 + lr;
-                const float dv = L.dn[Q][r];
+            for (int u = 0; u < TN; ++u)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    acc[u][t][i] = fmaf(dv * ev[i], tmp[u][t][i], acc[u][t][i]);
-                    tmp[u][t][i] = 0.0f;
-                }
-                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(&L.qh[Q][0][r][0]);
-                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(&L.qh[Q][1][r][0]);
-                acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, qh, acc[u][t], 0, 0, 0);
-                acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, ql, acc[u][t], 0, 0, 0);
-            }
+                for (int tt = 0; tt < TM; ++tt)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const unsigned long long v = __hip_atomic_load(
+                            src + ((u * TM + tt) * 8 + q) * 64 + lane, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+                        const float x0 = __uint_as_float((unsigned)v);
+                        const float x1 = __uint_as_float((unsigned)(v >> 32));
+                        sum[u][tt][2 * q] = k == 0 ? x0 : sum[u][tt][2 * q] + x0;
+                        sum[u][tt][2 * q + 1] = k == 0 ? x1 : sum[u][tt][2 * q + 1] + x1;
+                    }
         }
+#pragma unroll
+        for (int u = 0; u < TN; ++u)
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt) acc[u][tt] = sum[u][tt];
+        store_y(tl);
+        if (lane == 0) __hip_atomic_store(cp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
     __syncthreads();
+    int64_t seg0 = ub;   // first unit of the current tile segment
 #pragma unroll 1
-    for (int b = 0; b < nl; ++b) {
-        compute(IC<0>{}, 0);
-        compute(IC<0>{}, 1);
-        __syncthreads();
-        compute(IC<1>{}, 0);
-        compute(IC<1>{}, 1);
-        __syncthreads();
-        compute(IC<0>{}, 0);
-        compute(IC<0>{}, 1);
-        __syncthreads();
-        compute(IC<1>{}, 0);
-        compute(IC<1>{}, 1);
-        finish(b & 1);
-        __syncthreads();
-    }
-
-    // Lanes 0..31 hold 32 consecutive n of one activation row: coalesced
-    // stores, or (K split over several workgroups) fp32 atomic adds into the
-    // zero-filled output.
+    for (int64_t u = ub; u < ue; ++u) {
+        const int Q = (int)(u - ub) & 1;
+        const int t = (int)(u / nsb);
+        const int64_t tend = (int64_t)(t + 1) * nsb;
+        if (u == seg0) {
 #pragma unroll
-    for (int u = 0; u < TN; ++u) {
-        const int n = n0 + wn * 64 + u * 32 + lr;
-        if (n >= N) continue;
+            for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + (wm * TM + t) * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                if (m >= M) continue;
-                float *dst = y + (int64_t)m * N + n;
-                if (splits == 1)
-                    *dst = acc[u][t][i];
-                else
-                    unsafeAtomicAdd(dst, acc[u][t][i]);
-            }
-    }
-}
-
-// Zero fill of the outputs before K parts add into them: 16-byte stores
-// where an output is 16-byte aligned, else 4-byte stores.
-__global__ __launch_bounds__(256) void zero_kernel(const GemmSet set, int64_t M) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (int p = 0; p < set.count; ++p) {
-        float *y = set.y[p];
-        const int64_t n = M * set.N[p];
-        if ((reinterpret_cast<uintptr_t>(y) & 15) == 0) {
-            f32x4 *y4 = reinterpret_cast<f32x4 *>(y);
-            for (int64_t i = i0; i < n / 4; i += stride) y4[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-            if (i0 < (n & 3)) y[(n & ~(int64_t)3) + i0] = 0.0f;
-        } else {
-            for (int64_t i = i0; i < n; i += stride) y[i] = 0.0f;
+                for (int b = 0; b < TM; ++b) acc[a][b] = zero16;
         }
+        compute(IC<0>{}, IC<0>{}, IC<0>{}, Q);
+        compute(IC<0>{}, IC<1>{}, IC<1>{}, Q);
+        __syncthreads();
+        compute(IC<1>{}, IC<0>{}, IC<2>{}, Q);
+        compute(IC<1>{}, IC<1>{}, IC<3>{}, Q);
+        __syncthreads();
+        compute(IC<0>{}, IC<0>{}, IC<4>{}, Q);
+        compute(IC<0>{}, IC<1>{}, IC<5>{}, Q);
+        __syncthreads();
+        compute(IC<1>{}, IC<0>{}, IC<6>{}, Q);
+        compute(IC<1>{}, IC<1>{}, IC<7>{}, Q);
+        finish(Q);
+        if (u + 1 == ue || u + 1 == tend) {
+            finish_tile(t, seg0, u + 1);
+            seg0 = u + 1;
+        }
+        __syncthreads();
     }
 }
 
 template <int WVN, int WVM, int TM>
 hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const float *scales,
-                       const int32_t *sums, int64_t M, int splits, hipStream_t stream) {
+                       const int32_t *sums, int64_t M, void *ws, hipStream_t stream) {
     using C = Cfg<WVN, WVM, TM>;
-    if (splits > 1) {
-        int64_t items = 0;
-        for (int p = 0; p < set.count; ++p) items = std::max<int64_t>(items, M * set.N[p] / 4 + 1);
-        const int64_t blocks = std::min<int64_t>((items + 255) / 256, 2048);
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, set, M);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int64_t tiles_m = (M + C::WM - 1) / C::WM;
-    const int64_t groups = (set.tile0[set.count] + NXCD - 1) / NXCD;
-    const int64_t grid = groups * NXCD * tiles_m * splits;
-    hipLaunchKernelGGL((gemm_f16_kernel<WVN, WVM, TM>), dim3((unsigned)grid), dim3(C::T),
-                       sizeof(Lds<C::WN, C::WM>), stream, set, nsb, codes, scales, sums, (int)M,
-                       splits);
-    return hipGetLastError();
-}
-
-// Number of K parts: fill the CUs (one workgroup each) without paying more
-// for the zero fill and the atomic adds than the split saves.  Workgroups
-// are dealt to the XCDs by weight column-block, so the busiest XCD decides
-// the number of rounds.  Costs in microseconds: one quarter super-block step
-// of a round ~1.3, the zero fill ~5, the atomic adds ~1.3 bytes per ps.
-int choose_splits(int64_t tiles_n, int64_t tiles_m, int nsb, int64_t tile_outputs) {
-    const int64_t per_xcd = (cu_count() + NXCD - 1) / NXCD;
-    const int64_t cols = (tiles_n + NXCD - 1) / NXCD;   // column-blocks on the busiest XCD
-    int best = 1;
-    double best_t = 1e30;
-    for (int s = 1; s <= 8 && s <= nsb; ++s) {
-        const int64_t rounds = (cols * tiles_m * s + per_xcd - 1) / per_xcd;
-        const int steps = 4 * ((nsb + s - 1) / s);
-        double t = 1.3 * (double)(rounds * steps);
-        if (s > 1) t += 5.0 + 4.0 * (double)(tiles_n * tiles_m * s * tile_outputs) / 1.3e6;
-        if (t < best_t) {
-            best_t = t;
-            best = s;
-        }
+    const int64_t tiles = (int64_t)set.tile0[set.count] * tiles_m;
+    Sched s = {};
+    s.tiles_m = (int)tiles_m;
+    s.units = tiles * nsb;
+    s.groups = (int)tiles;
+    const int64_t cus = std::min<int64_t>(cu_count(), kGemmMaxGroups);
+    // Split tiles across workgroups only where whole tiles would leave CUs idle
+    // in the last round, and only where the counters fit the workspace.
+    if (ws && tiles % cus != 0 && tiles * C::NC <= kGemmCounters && s.units >= cus) {
+        s.groups = (int)cus;
+        s.cnt = static_cast<int *>(ws);
+        s.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kGemmCounters * 4);
     }
-    return best;
+    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM>), dim3((unsigned)s.groups), dim3(C::T),
+                       sizeof(Lds<C::WN, C::WM>), stream, set, s, nsb, codes, scales, sums,
+                       (int)M);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemm_workspace_bytes() {
+    return (size_t)kGemmCounters * 4 + (size_t)2 * kGemmMaxGroups * 128 * 128 * 4;
+}
+
 hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
                              const int8_t *codes, const float *scales, const int32_t *sums,
-                             int64_t M, hipStream_t stream) {
+                             int64_t M, void *workspace, hipStream_t stream) {
     const int nsb = (int)(K / kQK);
     GemmSet set = {};
     set.count = count;
@@ -554,24 +664,16 @@ hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
         set.N[p] = (int)probs[p].N;
         set.tile0[p + 1] = set.tile0[p] + (int)((probs[p].N + 127) / 128);   // WN = 128
     }
-    const int64_t tiles_n = set.tile0[count];
-    if (M > 64) {
-        const int s = choose_splits(tiles_n, (M + 127) / 128, nsb, 128 * 128);
-        return launch_tile<2, 2, 2>(set, nsb, codes, scales, sums, M, s, stream);
-    }
-    if (M > 32) {
-        const int s = choose_splits(tiles_n, (M + 63) / 64, nsb, 128 * 64);
-        return launch_tile<2, 1, 2>(set, nsb, codes, scales, sums, M, s, stream);
-    }
-    const int s = choose_splits(tiles_n, (M + 31) / 32, nsb, 128 * 32);
-    return launch_tile<2, 1, 1>(set, nsb, codes, scales, sums, M, s, stream);
+    if (M > 64) return launch_tile<2, 2, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
+    if (M > 32) return launch_tile<2, 1, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
+    return launch_tile<2, 1, 1>(set, nsb, codes, scales, sums, M, workspace, stream);
 }
 
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
-                       hipStream_t stream) {
+                       void *workspace, hipStream_t stream) {
     const GemmProblem p = {w, y, N};
-    return launch_gemm_batch(&p, 1, K, codes, scales, sums, M, stream);
+    return launch_gemm_batch(&p, 1, K, codes, scales, sums, M, workspace, stream);
 }
 
 }  // namespace q4k

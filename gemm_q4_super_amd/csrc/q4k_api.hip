@@ -96,16 +96,31 @@ int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t
                                                     static_cast<hipStream_t>(stream)));
 }
 
+// A workspace is optional (null with 0 bytes); when given it must be large
+// enough and 256-byte aligned.
+static int check_gemm_workspace(const void *workspace, size_t workspace_bytes) {
+    if (!workspace) return workspace_bytes == 0 ? Q4K_OK : Q4K_EWORKSPACE;
+    if (workspace_bytes < q4k::gemm_workspace_bytes()) return Q4K_EWORKSPACE;
+    if (!aligned(workspace, 256)) return Q4K_EALIGN;
+    return Q4K_OK;
+}
+
+size_t q4k_gemm_workspace_bytes(void) { return q4k::gemm_workspace_bytes(); }
+
 int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
-             const int32_t *sums, int64_t M, float *y, void *stream) {
+             const int32_t *sums, int64_t M, float *y, void *workspace, size_t workspace_bytes,
+             void *stream) {
     int st = check_matrix_args(w, N, K, codes, scales, sums, M, y);
     if (st != Q4K_OK) return st;
+    st = check_gemm_workspace(workspace, workspace_bytes);
+    if (st != Q4K_OK) return st;
     return from_hip(q4k::launch_gemm(static_cast<const uint8_t *>(w), N, K, codes, scales,
-                                     sums, M, y, static_cast<hipStream_t>(stream)));
+                                     sums, M, y, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K, const int8_t *codes,
-                   const float *scales, const int32_t *sums, int64_t M, void *stream) {
+                   const float *scales, const int32_t *sums, int64_t M, void *workspace,
+                   size_t workspace_bytes, void *stream) {
     if (!problems) return Q4K_EINVAL;
     if (count < 1 || count > q4k::kMaxGemmBatch) return Q4K_ESHAPE;
     for (int i = 0; i < count; ++i) {
@@ -113,7 +128,9 @@ int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K, const
         int st = check_matrix_args(p.w, p.N, K, codes, scales, sums, M, p.y);
         if (st != Q4K_OK) return st;
     }
-    return from_hip(q4k::launch_gemm_batch(problems, count, K, codes, scales, sums, M,
+    int st = check_gemm_workspace(workspace, workspace_bytes);
+    if (st != Q4K_OK) return st;
+    return from_hip(q4k::launch_gemm_batch(problems, count, K, codes, scales, sums, M, workspace,
                                            static_cast<hipStream_t>(stream)));
 }
 

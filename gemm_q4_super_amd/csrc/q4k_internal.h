@@ -72,14 +72,19 @@ constexpr int kMaxGemvBatch = 8;
 hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
                                       int64_t M, hipStream_t stream);
 
+// Prefill GEMM.  `workspace` (null, or gemm_workspace_bytes() bytes whose
+// first kGemmCounters ints are zero) lets tiles be split across workgroups.
+constexpr int kGemmCounters = 16384;   // split-tile counters (tiles x matrix-core waves)
+constexpr int kGemmMaxGroups = 256;    // workgroups of a split launch
+size_t gemm_workspace_bytes();
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
-                       hipStream_t stream);
+                       void *workspace, hipStream_t stream);
 using GemmProblem = q4k_gemm_problem;
 constexpr int kMaxGemmBatch = 8;
 hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
                              const int8_t *codes, const float *scales, const int32_t *sums,
-                             int64_t M, hipStream_t stream);
+                             int64_t M, void *workspace, hipStream_t stream);
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N);
 

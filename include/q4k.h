@@ -134,18 +134,37 @@ typedef struct q4k_gemv_problem {
 int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K,
                             int64_t M, void *stream);
 
-/* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (section 3's
- * batched prefill over all prompt tokens).  Compute-bound: Q4_K tiles are
- * staged through LDS and the products run on the fp16 matrix cores with
- * operands that represent the Q4_K weights and Q8 activations exactly,
- * accumulated in fp32.  When the launch splits K across workgroups to fill
- * the GPU, y is first cleared on the stream and the partial sums are added
- * atomically, so y is still fully overwritten but the fp32 summation order
- * (hence the last bits) may differ between calls.  Arguments and result
- * contract as for q4k_gemv, without the M <= 8 limit. */
+/* Prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T for any M >= 1 (the batched
+ * prefill over all prompt tokens of "genie-ai-runtime ...", section 3, Path B,
+ * whose tensor-core kernel is Path E).  Compute-bound: Q4_K tiles are staged
+ * through LDS and converted to integer-valued fp16 operands (sc*q and the Q8
+ * codes, both exact), the matrix cores form sc * (each 32-element integer
+ * dot) exactly, and the fp32 vector units apply the activation block scale
+ * and d; the min term runs on bf16 matrix cores with its fp32 factors split
+ * into three exact parts.
+ *   workspace        NULL (with workspace_bytes 0), or a device buffer of at
+ *                    least q4k_gemm_workspace_bytes() bytes, 256-byte aligned.
+ *                    With a workspace, tiles may be split along K across
+ *                    workgroups to fill the GPU: a split tile's parts are
+ *                    added in a fixed order by the last workgroup to finish,
+ *                    so the result bits do not depend on scheduling, and are
+ *                    the same with or without a workspace up to fp32 rounding
+ *                    of that one sum.  The first 65536 bytes of the workspace
+ *                    hold counters that must be zero before the first call
+ *                    that uses it (e.g. hipMemset once after allocation);
+ *                    every call leaves them zero.  The rest holds partial
+ *                    tiles.  Calls sharing a workspace must not overlap.
+ * Results are deterministic: the same inputs give the same bits on every call.
+ * Other arguments and the result contract as for q4k_gemv, without the
+ * M <= 8 limit. */
 int q4k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes,
              const float *scales, const int32_t *sums, int64_t M, float *y,
-             void *stream);
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes q4k_gemm and q4k_gemm_batch can use (a constant of the
+ * library: 65536 bytes of counters plus 2 * 256 partial tiles of 128 x 128
+ * fp32). */
+size_t q4k_gemm_workspace_bytes(void);
 
 /* One product of a batch for q4k_gemm_batch. */
 typedef struct q4k_gemm_problem {
@@ -156,15 +175,14 @@ typedef struct q4k_gemm_problem {
 
 /* Several prefill GEMMs against the same Q8 activations in one launch (e.g.
  * the q, k and v projections of a layer, or gate and up): for every problem
- * i, y_i = Q8(x)[M][K] * W_i^T, as q4k_gemm on that problem alone (same
- * arithmetic; the split of K may differ, so results agree to fp32 rounding).
- * Launching them together fills the GPU where each alone would not.
- * `problems` is a host array of `count` entries (1 <= count <= 8), read
- * during the call; outputs must not overlap.  Limits and checks as for
- * q4k_gemm, applied to every problem. */
+ * i, y_i = Q8(x)[M][K] * W_i^T, the same arithmetic as q4k_gemm on that
+ * problem alone.  Launching them together fills the GPU where each alone
+ * would not.  `problems` is a host array of `count` entries (1 <= count <= 8),
+ * read during the call; outputs must not overlap.  Workspace as for q4k_gemm.
+ * Limits and checks as for q4k_gemm, applied to every problem. */
 int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,
                    const int8_t *codes, const float *scales, const int32_t *sums,
-                   int64_t M, void *stream);
+                   int64_t M, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Routed-expert grouped GEMV.  n_experts Q4_K matrices of N rows x K columns
  * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of

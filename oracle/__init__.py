@@ -27,45 +27,70 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int64
 
 
+_OMP_PATH = os.path.join(_HERE, "liboracle_omp.so")
+_omp = None
+_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc.  Returns the library path."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
-                               "-ffp-contract=off", "-fno-fast-math",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+    """Compile the oracle with gcc, single-threaded and with OpenMP over output
+    rows.  Returns the single-threaded library's path."""
+    for path, extra in ((_LIB_PATH, []), (_OMP_PATH, ["-fopenmp"])):
+        if force or not os.path.exists(path):
+            tmp = path + ".tmp"
+            subprocess.check_call(["gcc"] + _FLAGS + extra + ["-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, path)
     return _LIB_PATH
+
+
+_SIG = {
+    "oracle_unpack_q4k": [_P, _P, _P, _P, _P, _P],
+    "oracle_dequant_row": [_P, _I, _P],
+    "oracle_quantize_act": [_P, _I, _I, _P, _P, _P],
+    "oracle_swiglu": [_P, _P, _I, _P],
+    "oracle_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
+    "oracle_subblock_dots": [_P, _I, _P, _I, _P, _I, _P],
+    "oracle_matvec_intform": [_P, _I, _P, _P, _P, _I, _P, _I, _P],
+    "oracle_moe_matvec": [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P,
+                          ctypes.c_int, _P],
+    "oracle_moe_layer": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+                         _P, _P, _P, _P, _P, _P, _P, _P],
+    "oracle_unpack_q6k": [_P, _P, _P, _P],
+    "oracle_q6k_dequant_row": [_P, _I, _P],
+    "oracle_q6k_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
+}
+
+
+def _open(path):
+    if not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    for name, args in _SIG.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = None
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        sig = {
-            "oracle_unpack_q4k": [_P, _P, _P, _P, _P, _P],
-            "oracle_dequant_row": [_P, _I, _P],
-            "oracle_quantize_act": [_P, _I, _I, _P, _P, _P],
-            "oracle_swiglu": [_P, _P, _I, _P],
-            "oracle_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
-            "oracle_subblock_dots": [_P, _I, _P, _I, _P, _I, _P],
-            "oracle_matvec_intform": [_P, _I, _P, _P, _P, _I, _P, _I, _P],
-            "oracle_moe_matvec": [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P,
-                                  ctypes.c_int, _P],
-            "oracle_moe_layer": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
-                                 _P, _P, _P, _P, _P, _P, _P, _P],
-            "oracle_unpack_q6k": [_P, _P, _P, _P],
-            "oracle_q6k_dequant_row": [_P, _I, _P],
-            "oracle_q6k_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
-        }
-        for name, args in sig.items():
-            fn = getattr(lib, name)
-            fn.argtypes = args
-            fn.restype = None
-        _lib = lib
+        _lib = _open(_LIB_PATH)
     return _lib
+
+
+def _load_omp():
+    global _omp
+    if _omp is None:
+        _omp = _open(_OMP_PATH)
+    return _omp
+
+
+def threads(parallel: bool = True) -> int:
+    """Threads the oracle uses: 1 single-threaded, or the OpenMP team size."""
+    return int((_load_omp() if parallel else _load()).oracle_threads())
 
 
 def _ptr(a):
@@ -125,13 +150,14 @@ def _rows(rows, N):
     return _c(rows, np.int64)
 
 
-def matvec(w, N, K, codes, scales, rows=None) -> np.ndarray:
-    """fp64 [M, len(rows)]: y[m, r] = sum_k w[rows[r], k] * xhat[m, k]."""
+def matvec(w, N, K, codes, scales, rows=None, parallel=False) -> np.ndarray:
+    """fp64 [M, len(rows)]: y[m, r] = sum_k w[rows[r], k] * xhat[m, k].
+    parallel=True runs the output rows on all host cores (same arithmetic)."""
     codes, scales = _c(codes, np.int8), _c(scales, np.float32)
     M = codes.size // K
     r = _rows(rows, N)
     y = np.zeros((M, r.size), np.float64)
-    _load().oracle_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
+    (_load_omp() if parallel else _load()).oracle_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
                           _ptr(r), r.size, _ptr(y))
     return y
 
@@ -224,12 +250,12 @@ def q6k_dequant(w: np.ndarray, K: int) -> np.ndarray:
     return out
 
 
-def q6k_matvec(w, N, K, codes, scales, rows=None) -> np.ndarray:
+def q6k_matvec(w, N, K, codes, scales, rows=None, parallel=False) -> np.ndarray:
     """fp64 [M, len(rows)]: y[m, r] = sum_k w[rows[r], k] * xhat[m, k], Q6_K weights."""
     codes, scales = _c(codes, np.int8), _c(scales, np.float32)
     M = codes.size // K
     r = _rows(rows, N)
     y = np.zeros((M, r.size), np.float64)
-    _load().oracle_q6k_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
+    (_load_omp() if parallel else _load()).oracle_q6k_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
                               _ptr(r), r.size, _ptr(y))
     return y

@@ -40,9 +40,17 @@
  *    fp64; the same fp64 product against Q8 activations.
  *
  * Parity pins for every function are in tests/test_oracle_pins.py.
+ *
+ * Built twice from this one file: single-threaded (liboracle.so) and with
+ * OpenMP over the output rows of the products (liboracle_omp.so, for the
+ * full-size checks and the all-core CPU baseline).  The arithmetic of every
+ * output is the same sequential loop in both.
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -153,21 +161,43 @@ void oracle_matvec(const uint8_t *w, int64_t N, int64_t K,
                    const int64_t *rows, int64_t nrows, double *y)
 {
     int64_t row_bytes = K / QK * SB_BYTES;
-    double *wr = (double *)malloc(sizeof(double) * K);
     (void)N;
-    for (int64_t r = 0; r < nrows; ++r) {
-        int64_t n = rows ? rows[r] : r;
-        oracle_dequant_row(w + n * row_bytes, K, wr);
-        for (int64_t m = 0; m < M; ++m) {
-            double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                double xh = (double)scales[m * (K / QB) + k / QB] * (double)codes[m * K + k];
-                acc += wr[k] * xh;
+    /* Output rows are independent; a build with OpenMP takes them in parallel
+     * (each row's sum is the same sequential loop either way). */
+#pragma omp parallel
+    {
+        double *wr = (double *)malloc(sizeof(double) * K);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t n = rows ? rows[r] : r;
+            oracle_dequant_row(w + n * row_bytes, K, wr);
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double xh = (double)scales[m * (K / QB) + k / QB] * (double)codes[m * K + k];
+                    acc += wr[k] * xh;
+                }
+                y[m * nrows + r] = acc;
             }
-            y[m * nrows + r] = acc;
+        }
+        free(wr);
+    }
+}
+
+/* Threads the OpenMP runtime would use (1 in a build without OpenMP). */
+int oracle_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            n = omp_get_num_threads();
+#endif
         }
     }
-    free(wr);
+    return n;
 }
 
 /* Integer sub-block dots D[m][r][j] = sum_{i<32} q[n_r][32j+i] * code[m][32j+i]. */
@@ -347,19 +377,23 @@ void oracle_q6k_matvec(const uint8_t *w, int64_t N, int64_t K,
                        const int64_t *rows, int64_t nrows, double *y)
 {
     int64_t row_bytes = K / QK * Q6_SB_BYTES;
-    double *wr = (double *)malloc(sizeof(double) * K);
     (void)N;
-    for (int64_t r = 0; r < nrows; ++r) {
-        int64_t n = rows ? rows[r] : r;
-        oracle_q6k_dequant_row(w + n * row_bytes, K, wr);
-        for (int64_t m = 0; m < M; ++m) {
-            double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                double xh = (double)scales[m * (K / QB) + k / QB] * (double)codes[m * K + k];
-                acc += wr[k] * xh;
+#pragma omp parallel
+    {
+        double *wr = (double *)malloc(sizeof(double) * K);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t n = rows ? rows[r] : r;
+            oracle_q6k_dequant_row(w + n * row_bytes, K, wr);
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double xh = (double)scales[m * (K / QB) + k / QB] * (double)codes[m * K + k];
+                    acc += wr[k] * xh;
+                }
+                y[m * nrows + r] = acc;
             }
-            y[m * nrows + r] = acc;
         }
+        free(wr);
     }
-    free(wr);
 }

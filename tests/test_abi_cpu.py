@@ -42,13 +42,15 @@ def test_status_strings(L):
 
 
 def test_gemv_gemm_argument_checks(L):
-    for fn in (L.q4k_gemv, L.q4k_gemm):
+    for gemm in (False, True):
         good = dict(w=A, N=16, K=512, codes=A, scales=A, sums=A, M=1, y=A)
 
         def call(**kw):
             a = dict(good, **kw)
-            return fn(a["w"], a["N"], a["K"], a["codes"], a["scales"], a["sums"], a["M"],
-                      a["y"], None)
+            args = (a["w"], a["N"], a["K"], a["codes"], a["scales"], a["sums"], a["M"], a["y"])
+            if gemm:
+                return L.q4k_gemm(*args, None, 0, None)
+            return L.q4k_gemv(*args, None)
         assert call(w=None) == EINVAL
         assert call(codes=None) == EINVAL
         assert call(y=None) == EINVAL
@@ -153,9 +155,9 @@ def test_gemm_batch_argument_checks(L):
 
     def call(probs, K=512, M=1, codes=A):
         arr = (P * max(len(probs), 1))(*[P(*p) for p in probs])
-        return f(arr, len(probs), K, codes, A, A, M, None)
+        return f(arr, len(probs), K, codes, A, A, M, None, 0, None)
     good = (A, A, 16)
-    assert f(None, 1, 512, A, A, A, 1, None) == EINVAL
+    assert f(None, 1, 512, A, A, A, 1, None, 0, None) == EINVAL
     assert call([]) == ESHAPE
     assert call([good] * 9) == ESHAPE
     assert call([good], K=500) == ESHAPE
@@ -167,6 +169,21 @@ def test_gemm_batch_argument_checks(L):
     assert call([good, (A, None, 16)]) == EINVAL
     assert call([good, (A + 4, A, 16)]) == EALIGN
     assert call([good, (A, A + 2, 16)]) == EALIGN
+
+
+def test_gemm_workspace_checks(L):
+    """The GEMM workspace is optional; when given it must hold
+    q4k_gemm_workspace_bytes() bytes and be 256-byte aligned."""
+    need = int(L.q4k_gemm_workspace_bytes())
+    assert need == 65536 + 2 * 256 * 128 * 128 * 4
+    args = (A, 16, 512, A, A, A, 1, A)
+    assert L.q4k_gemm(*args, None, 16, None) == EWORKSPACE
+    assert L.q4k_gemm(*args, A, need - 1, None) == EWORKSPACE
+    assert L.q4k_gemm(*args, A + 16, need, None) == EALIGN
+    P = q4k._lib.GemmProblem
+    arr = (P * 1)(P(A, A, 16))
+    assert L.q4k_gemm_batch(arr, 1, 512, A, A, A, 1, A, need - 1, None) == EWORKSPACE
+    assert L.q4k_gemm_batch(arr, 1, 512, A, A, A, 1, A + 128, need, None) == EALIGN
 
 
 def test_quantize_argument_checks(L):

@@ -1,10 +1,20 @@
-"""GPU parity of q4k_gemm (matrix-core prefill GEMM) against the CPU oracle.
+"""GPU parity of q4k_gemm / q4k_gemm_batch (matrix-core prefill GEMM) against
+the CPU oracle.
 
-fp32 outputs within |gpu - oracle| <= max(2e-3 |oracle|, 1e-4); the
-integer-exposing cases (d = 1, dmin = 0, one-hot sub-block scale, integer
-activations with a +-127 per block) must reproduce the exact int32 sub-block
-dots through the fp32 output, which also pins the matrix-core operand and
-result layouts.
+fp32 outputs within |gpu - oracle| <= max(2e-3 |oracle|, 1e-4).  Beyond random
+inputs the cases pin what the format and the mathematics fix:
+  - integer-exposing weights (d = 1, dmin = 0, one-hot sub-block scale) and
+    integer activations with a +-127 per block reproduce the exact int32
+    sub-block dots through the fp32 output (operand and result layouts);
+  - an all-ones activation gives 127 * fl32(1/127) * (row sum of the
+    dequantized weights), the closed form;
+  - scaling d and dmin by 2^k and x by 2^k' scales y by exactly 2^(k+k');
+  - activations with outlier blocks (block scales 2^12 apart inside one
+    super-block) stay within tolerance;
+  - every output of one full 512 x 2560 x 9728 layer (the down projection at a
+    512-token prefill) is checked, split across workgroups as the benchmark
+    launches it;
+  - repeated calls give the same bits, with or without a workspace.
 """
 import numpy as np
 import pytest
@@ -24,35 +34,51 @@ def q4k():
     return m
 
 
-def _run(q4k, oracle_lib, w, N, K, x, rows=None):
+def _gemm(q4k, w, N, K, codes, scales, sums, workspace="auto"):
     import torch
-    codes, scales, sums = oracle_lib.quantize_act(x)
-    y = q4k.q4k_gemm(to_dev(w), N, K, to_dev(codes), to_dev(scales), to_dev(sums))
+    y = q4k.q4k_gemm(to_dev(w), N, K, to_dev(codes), to_dev(scales), to_dev(sums),
+                     workspace=workspace)
     torch.cuda.synchronize()
-    y = y.cpu().numpy()
-    ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows)
+    return y.cpu().numpy()
+
+
+def _run(q4k, oracle_lib, w, N, K, x, rows=None, workspace="auto"):
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    y = _gemm(q4k, w, N, K, codes, scales, sums, workspace)
+    ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows, parallel=True)
     if rows is not None:
         y = y[:, rows]
     return y, ref
+
+
+def _counters_zero(q4k):
+    import torch
+    ws = q4k.gemm_workspace("cuda")
+    torch.cuda.synchronize()
+    return int(ws[:65536].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_gemm_single_1024(q4k, oracle_lib):
     w, _ = qi.make_q4k(1024, 1024, qi.weight_seed(0, 0, 0))
     for M in (1, 2, 5, 16):
         x = qi.make_act(M, 1024, qi.act_seed(M))
-        y, ref = _run(q4k, oracle_lib, w, 1024, 1024, x)
-        assert_close(y, ref, "gemm 1024x1024 M=%d" % M)
+        for ws in ("auto", None):
+            y, ref = _run(q4k, oracle_lib, w, 1024, 1024, x, workspace=ws)
+            assert_close(y, ref, "gemm 1024x1024 M=%d ws=%s" % (M, ws))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (3, 33, 512), (63, 64, 256), (64, 65, 768),
                                    (65, 100, 2560), (100, 1000, 1280), (129, 127, 4096),
-                                   (512, 96, 9728), (7, 4099, 256), (200, 260, 6144)])
+                                   (512, 96, 9728), (7, 4099, 256), (200, 260, 6144),
+                                   (300, 2560, 4096)])
 def test_gemm_shapes_and_tails(q4k, oracle_lib, M, N, K):
     w, _ = qi.make_q4k(N, K, 3000 + N + K)
     x = qi.make_act(M, K, 4000 + M + N)
     rows = None if N <= 300 else np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 50)])
-    y, ref = _run(q4k, oracle_lib, w, N, K, x, rows=rows)
-    assert_close(y, ref, "gemm M=%d N=%d K=%d" % (M, N, K))
+    for ws in ("auto", None):
+        y, ref = _run(q4k, oracle_lib, w, N, K, x, rows=rows, workspace=ws)
+        assert_close(y, ref, "gemm M=%d N=%d K=%d ws=%s" % (M, N, K, ws))
+    assert _counters_zero(q4k)
 
 
 def test_gemm_integer_exposing_bit_exact(q4k, oracle_lib):
@@ -75,6 +101,112 @@ def test_gemm_integer_exposing_bit_exact(q4k, oracle_lib):
         assert (y == ref).all()
 
 
+@pytest.mark.parametrize("proj", [0, 3, 4, 6])
+def test_gemm_all_ones_closed_form(q4k, oracle_lib, proj):
+    """x = 1 everywhere: codes 127, scale fl32(1/127), S = 32*127, so
+    y[m][n] = 127 * fl32(1/127) * sum_k w[n][k] for every m (full projection
+    shapes, M = 130 rows: a ragged tail in M)."""
+    name, K, N = qi.QWEN3_4B_LAYER[proj]
+    w = qi.make_q4k_bytes(N, K, qi.weight_seed(2, 1, proj))
+    M = 130
+    x = np.ones((M, K), np.float32)
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    assert (codes == 127).all() and (scales == np.float32(1.0) / np.float32(127.0)).all()
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(proj).integers(0, N, 200)])
+    wsum = oracle_lib.dequant(w.reshape(N, -1)[rows], K).sum(axis=1)
+    closed = 127.0 * float(np.float32(1.0) / np.float32(127.0)) * wsum
+    for ws in ("auto", None):
+        y = _gemm(q4k, w, N, K, codes, scales, sums, ws)
+        assert_close(y[:, rows], np.broadcast_to(closed, (M, rows.size)),
+                     "all-ones %s ws=%s" % (name, ws))
+    # whole tiles: every activation row is the same, so is every row of y
+    assert (y == y[0]).all()
+
+
+def test_gemm_power_of_two_scaling_exact(q4k, oracle_lib):
+    """d, dmin -> 2^3 * (d, dmin) and x -> 2^-5 * x scale y by exactly 2^-2 (every
+    value stays fp16-normal / fp32-normal, so every rounding scales with it)."""
+    N, K, M = 300, 2560, 200
+    f = qi.draw_q4k_fields(N, K, 8800)
+    x = qi.make_act(M, K, 8801)
+    w0 = qi.pack_q4k(f)
+    f.d = (f.d.astype(np.float32) * 8).astype(np.float16)
+    f.dmin = (f.dmin.astype(np.float32) * 8).astype(np.float16)
+    w1 = qi.pack_q4k(f)
+    c0, s0, u0 = oracle_lib.quantize_act(x)
+    c1, s1, u1 = oracle_lib.quantize_act(x * np.float32(2.0 ** -5))
+    assert (c0 == c1).all() and (s1 == s0 * np.float32(2.0 ** -5)).all()
+    y0 = _gemm(q4k, w0, N, K, c0, s0, u0)
+    y1 = _gemm(q4k, w1, N, K, c1, s1, u1)
+    assert (y1 == y0 * np.float32(0.25)).all()
+    assert_close(y0, oracle_lib.matvec(w0, N, K, c0, s0, parallel=True), "pow2 base")
+
+
+@pytest.mark.parametrize("spread", [12, 16, 20])
+def test_gemm_outlier_blocks(q4k, oracle_lib, spread):
+    """Activation rows whose block scales inside one super-block differ by
+    2^spread (a few outlier channels next to small ones), plus whole outlier
+    rows, against the oracle.  Up to 2^16 every output meets the bar.  At 2^20
+    some outputs are sums of terms up to 2^20 times larger than the result
+    itself; fp32 accumulation in any order cannot meet a 2e-3 relative bar on
+    those, so outputs that cancel by more than 2^10 (sum of |w x^| over |y|)
+    are held to the fp32 accumulation bound 2^-20 * sum |w x^| instead, and
+    every other output to the bar."""
+    N, K, M = 520, 2560, 150
+    w = qi.make_q4k_bytes(N, K, 8900 + spread)
+    rng = np.random.default_rng(8901)
+    x = qi.make_act(M, K, 8902 + spread)
+    blocks = x.reshape(M, K // 32, 32)
+    big = rng.random((M, K // 32)) < 0.1
+    blocks[big] *= np.float32(2.0 ** (spread / 2))
+    blocks[~big] *= np.float32(2.0 ** (-spread / 2))
+    x[::17] *= np.float32(1e4)
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    s = scales.reshape(M, K // 256, 8)
+    ratio = s.max(axis=2) / np.maximum(s.min(axis=2), np.float32(1e-30))
+    assert (ratio >= 2.0 ** (spread - 2)).any()
+    y, ref = _run(q4k, oracle_lib, w, N, K, x)
+    if spread <= 16:
+        assert_close(y, ref, "outlier blocks 2^%d" % spread)
+        return
+    xhat = np.abs(codes.astype(np.float64) * np.repeat(scales.astype(np.float64), 32, axis=1))
+    mag = xhat @ np.abs(oracle_lib.dequant(w, K)).T
+    cancel = mag > 2.0 ** 10 * np.abs(ref)
+    assert cancel.mean() < 0.01
+    assert_close(y[~cancel], ref[~cancel], "outlier blocks 2^%d" % spread)
+    assert (np.abs(y - ref)[cancel] <= 2.0 ** -20 * mag[cancel]).all()
+
+
+def test_gemm_full_layer_every_output(q4k, oracle_lib):
+    """The down projection of a 512-token prefill, 512 x 2560 x 9728: every one
+    of the 1.3 M outputs against the oracle, with the workspace (tiles split
+    across workgroups, as the benchmark runs it) and without."""
+    name, K, N = qi.QWEN3_4B_LAYER[6]
+    w = qi.make_q4k_bytes(N, K, qi.weight_seed(2, 0, 6))
+    x = qi.make_act(512, K, qi.act_seed(20006))
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    ref = oracle_lib.matvec(w, N, K, codes, scales, parallel=True)
+    for ws in ("auto", None):
+        y = _gemm(q4k, w, N, K, codes, scales, sums, ws)
+        assert_close(y, ref, "full %s layer ws=%s" % (name, ws))
+
+
+def test_gemm_deterministic(q4k, oracle_lib):
+    """Repeated calls give identical bits, split (workspace) or not; the
+    counters are zero after every call."""
+    import torch
+    M, K, Ns = 512, 4096, [2560]
+    w = to_dev(qi.make_q4k_bytes(Ns[0], K, 9100))
+    codes, scales, sums = (to_dev(a) for a in oracle_lib.quantize_act(qi.make_act(M, K, 9101)))
+    for ws in ("auto", None):
+        a = q4k.q4k_gemm(w, Ns[0], K, codes, scales, sums, workspace=ws)
+        outs = [q4k.q4k_gemm(w, Ns[0], K, codes, scales, sums, workspace=ws) for _ in range(4)]
+        torch.cuda.synchronize()
+        for b in outs:
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), "ws=%s" % ws
+    assert _counters_zero(q4k)
+
+
 def test_gemm_matches_gemv_small_m(q4k, oracle_lib):
     import torch
     N, K = 777, 2560
@@ -91,21 +223,21 @@ def test_gemm_matches_gemv_small_m(q4k, oracle_lib):
 
 @pytest.mark.parametrize("proj", range(7))
 def test_gemm_qwen3_4b_prefill_shapes_sampled(q4k, oracle_lib, proj):
-    """M = 512 prompt tokens against each full-size projection; 40 random weight
-    rows plus the first and last, all 512 activation rows."""
+    """M = 512 prompt tokens against each full-size projection; 100 random
+    weight rows plus the first and last, all 512 activation rows."""
     name, K, N = qi.QWEN3_4B_LAYER[proj]
     w = qi.make_q4k_bytes(N, K, qi.weight_seed(2, 0, proj))
     x = qi.make_act(512, K, qi.act_seed(5000 + proj))
-    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(proj).integers(0, N, 40)])
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(proj).integers(0, N, 100)])
     y, ref = _run(q4k, oracle_lib, w, N, K, x, rows=rows)
     assert_close(y, ref, "gemm %s M=512" % name)
 
 
 @pytest.mark.parametrize("M,N,offset", [(512, 1024, 1), (129, 1023, 0), (129, 1023, 3)])
-def test_gemm_split_k_output_layouts(q4k, oracle_lib, M, N, offset):
-    """Few output tiles, so K is split and the parts add into a zero-filled y:
-    y 16-byte aligned or only 4-byte aligned, M*N a multiple of 4 or not.  The
-    floats around y stay untouched."""
+def test_gemm_output_layouts(q4k, oracle_lib, M, N, offset):
+    """Few output tiles, so tiles are split across workgroups: y 16-byte
+    aligned or only 4-byte aligned, N a multiple of 4 or not.  The floats
+    around y stay untouched."""
     import torch
     K = 2560
     w, _ = qi.make_q4k(N, K, 7100 + N)
@@ -120,7 +252,7 @@ def test_gemm_split_k_output_layouts(q4k, oracle_lib, M, N, offset):
     rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 40)])
     ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows)
     assert_close(got[offset:offset + M * N].reshape(M, N)[:, rows], ref,
-                 "gemm split M=%d N=%d offset=%d" % (M, N, offset))
+                 "gemm M=%d N=%d offset=%d" % (M, N, offset))
 
 
 _GEMM_BATCHES = {
@@ -136,7 +268,8 @@ _GEMM_BATCHES = {
 @pytest.mark.parametrize("name", sorted(_GEMM_BATCHES))
 def test_gemm_batch_matches_single_and_oracle(q4k, oracle_lib, name):
     """Each product of a batched launch agrees with its own q4k_gemm call (to
-    fp32 rounding: the K split may differ) and with the oracle on sampled rows."""
+    fp32 rounding: the split of tiles may differ; bit for bit without a
+    workspace) and with the oracle on sampled rows."""
     import torch
     M, K, Ns = _GEMM_BATCHES[name]
     ws = [qi.make_q4k_bytes(N, K, 7300 + 17 * i + N) for i, N in enumerate(Ns)]
@@ -146,13 +279,17 @@ def test_gemm_batch_matches_single_and_oracle(q4k, oracle_lib, name):
     dws = [to_dev(w) for w in ws]
     ys = q4k.q4k_gemm_batch(list(zip(dws, Ns)), K, dc, ds, dsu)
     singles = [q4k.q4k_gemm(w, N, K, dc, ds, dsu) for w, N in zip(dws, Ns)]
+    ys0 = q4k.q4k_gemm_batch(list(zip(dws, Ns)), K, dc, ds, dsu, workspace=None)
+    singles0 = [q4k.q4k_gemm(w, N, K, dc, ds, dsu, workspace=None) for w, N in zip(dws, Ns)]
     torch.cuda.synchronize()
-    for i, (w, N, y, y1) in enumerate(zip(ws, Ns, ys, singles)):
+    for i, (w, N, y, y1, z, z1) in enumerate(zip(ws, Ns, ys, singles, ys0, singles0)):
+        assert torch.equal(z.view(torch.int32), z1.view(torch.int32)), "%s %d" % (name, i)
         a, b = y.cpu().numpy(), y1.cpu().numpy().astype(np.float64)
         assert_close(a, b, "%s product %d vs single" % (name, i))
         rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N + i).integers(0, N, 12)])
         ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows)
         assert_close(a[:, rows], ref, "%s product %d vs oracle" % (name, i))
+        assert_close(z.cpu().numpy()[:, rows], ref, "%s product %d (no workspace)" % (name, i))
 
 
 def test_gemm_batch_leaves_other_memory_untouched(q4k, oracle_lib):
