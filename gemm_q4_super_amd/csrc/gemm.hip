@@ -37,8 +37,9 @@
 // share one 32-byte group of quant bytes) per step, double-buffered in LDS.
 // The waves are specialised: on each SIMD one wave only reads operands from
 // LDS and runs the matrix-core ops and their epilogue, and one only loads raw
-// blocks from global memory and converts them into the other LDS buffer (raw
-// loads two steps ahead, two register sets).  One barrier per step.
+// blocks from global memory and converts them into the other LDS buffer.  The
+// raw data of a whole super-block is loaded in one burst, four to eight steps
+// before its conversion.  One barrier per step.
 // Workgroup tile (64*WVN) weight rows x (32*TM*WVM) activation rows, one
 // matrix-core wave per 64 x 32*TM outputs.
 //
@@ -106,13 +107,13 @@ struct Sched {
     int *cnt;          // one counter per (tile, matrix-core wave)
 };
 
-template <int WVN, int WVM, int TM>
+template <int WVN, int WVM, int TM, int NV>
 struct Cfg {
     static constexpr int WN = 32 * TN * WVN;
     static constexpr int WM = 32 * TM * WVM;
-    static constexpr int NC = WVN * WVM;           // matrix-core waves (as many converting waves)
-    static constexpr int P = 64 * NC;              // converting lanes
-    static constexpr int T = 2 * P;
+    static constexpr int NC = WVN * WVM;           // matrix-core waves
+    static constexpr int P = 64 * NV;              // converting lanes (NV converting waves)
+    static constexpr int T = 64 * (NC + NV);
     static constexpr int CA = 2 * WN;              // 16-byte quant chunks per step
     static constexpr int CB = 2 * WM;              // 32-code activation blocks per step
     static constexpr int NA = (CA + P - 1) / P;
@@ -174,26 +175,58 @@ struct Tile {
     int N, n0, m0;
 };
 
+// Position in the unit sequence, advanced one unit at a time (no division
+// in the loops): tile t = vt * tiles_m + mt, super-block b, and the tile's
+// product, weight rows and activation rows.  The product is picked with a
+// compile-time select chain over the batch, so its pointers stay in scalar
+// registers.
 template <int WN, int WM>
-__device__ __forceinline__ Tile tile_of(const GemmSet &set, int t, int tiles_m) {
-    const int vt = t / tiles_m, mt = t - vt * tiles_m;
-    int pi = 0;
-#pragma unroll
-    for (int k = 1; k < kMaxGemmBatch; ++k) pi += (k < set.count && vt >= set.tile0[k]);
-    Tile r;
-    r.w = set.w[pi];
-    r.y = set.y[pi];
-    r.N = set.N[pi];
-    r.n0 = (vt - set.tile0[pi]) * WN;
-    r.m0 = mt * WM;
-    return r;
-}
+struct Walk {
+    int t, b, vt, mt;
+    Tile tl;
 
-template <int WVN, int WVM, int TM>
-__global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
+    __device__ __forceinline__ void geometry(const GemmSet &set) {
+        const uint8_t *w = set.w[0];
+        float *y = set.y[0];
+        int N = set.N[0], base = 0;
+#pragma unroll
+        for (int k = 1; k < kMaxGemmBatch; ++k)
+            if (k < set.count && vt >= set.tile0[k]) {
+                w = set.w[k];
+                y = set.y[k];
+                N = set.N[k];
+                base = set.tile0[k];
+            }
+        tl.w = w;
+        tl.y = y;
+        tl.N = N;
+        tl.n0 = (vt - base) * WN;
+        tl.m0 = mt * WM;
+    }
+    __device__ __forceinline__ void start(const GemmSet &set, int64_t u, int nsb, int tiles_m) {
+        t = (int)(u / nsb);
+        b = (int)(u - (int64_t)t * nsb);
+        vt = t / tiles_m;
+        mt = t - vt * tiles_m;
+        geometry(set);
+    }
+    __device__ __forceinline__ void next(const GemmSet &set, int nsb, int tiles_m) {
+        if (++b < nsb) return;
+        b = 0;
+        ++t;
+        if (++mt == tiles_m) {
+            mt = 0;
+            ++vt;
+        }
+        geometry(set);
+    }
+};
+
+template <int WVN, int WVM, int TM, int NV>
+__global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     const GemmSet set, const Sched sch, int nsb, const int8_t *__restrict__ codes,
     const float *__restrict__ scales, const int32_t *__restrict__ sums, int M) {
-    using C = Cfg<WVN, WVM, TM>;
+    using C = Cfg<WVN, WVM, TM, NV>;
     constexpr int WN = C::WN, WM = C::WM, P = C::P, NC = C::NC;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
@@ -207,9 +240,9 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
     const int64_t row_bytes = (int64_t)nsb * 144;
     const int tid = threadIdx.x;
 
-    if (tid >= P) {
+    if (tid >= 64 * NC) {
         // ---------------- converting waves ----------------
-        const int p = tid - P;
+        const int p = tid - 64 * NC;
         // Raw loads.  Rows past N or M read row N-1 / M-1 and units past the
         // end of the range read its last unit (branch-free loads): they only
         // feed outputs or buffers that are never used.
@@ -222,60 +255,80 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
             float a[C::NB][8];
             int s[C::NB][8];
         };
-        Step S0, S1;
-        Block cur, nxt;
+        // Two units' worth of raw data: register set 4k + g holds quarter g of
+        // the unit in slot k.  A unit is loaded in one burst, so the two lanes
+        // of a row read its 144 weight bytes and 256 code bytes as whole cache
+        // lines within a few instructions (loaded one quarter per step, each
+        // line was fetched again for every quarter); it is converted one and
+        // two units later.
+        Step S[8];
+        Block blk[2];
+        const bool vec_as = ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(sums)) & 15) == 0;
 
-        // Tile and super-block of unit u (units past the range: its last unit).
-        struct Pos {
-            Tile tl;
-            int b;
-        };
-        auto pos_of = [&](int64_t u) {
-            u = u < ue ? u : ue - 1;
-            const int t = (int)(u / nsb);
-            Pos r;
-            r.tl = tile_of<WN, WM>(set, t, sch.tiles_m);
-            r.b = (int)(u - (int64_t)t * nsb);
-            return r;
-        };
-        auto load = [&](auto setc, auto gc, const Pos &ps) {
-            constexpr int g = decltype(gc)::value;
-            Step &R = decltype(setc)::value ? S1 : S0;
-            const Tile &tl = ps.tl;
-            const int b = ps.b;
+        // The unit at pw into slot k; pw then moves on (not past the last unit).
+        Walk<WN, WM> pw;
+        int64_t pu = ub;
+        pw.start(set, ub, nsb, sch.tiles_m);
+        auto load_unit = [&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const Tile &tl = pw.tl;
+            const int b = pw.b;
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) {
                 const int e = min(p + i * P, C::CA - 1);
                 const int row = min(tl.n0 + (e >> 1), tl.N - 1);
                 const uint8_t *src = tl.w + (int64_t)row * row_bytes + (int64_t)b * 144;
-                R.q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
-                if (g == 0) nxt.h[i] = *reinterpret_cast<const u32x4 *>(src);
+                blk[k].h[i] = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    S[4 * k + g].q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
             }
 #pragma unroll
             for (int i = 0; i < C::NB; ++i) {
                 const int e = min(p + i * P, C::CB - 1);
                 const int row = min(tl.m0 + (e >> 1), M - 1);
-                const int8_t *src = codes + (int64_t)row * K + 256 * b + 32 * (2 * g + (e & 1));
-                R.c0[i] = *reinterpret_cast<const i32x4 *>(src);
-                R.c1[i] = *reinterpret_cast<const i32x4 *>(src + 16);
-                if (g == 0) {
-                    const int64_t o = (int64_t)row * nblk + 8 * b;
+                const int8_t *src = codes + (int64_t)row * K + 256 * b + 32 * (e & 1);
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        nxt.a[i][k] = scales[o + k];
-                        nxt.s[i][k] = sums[o + k];
+                for (int g = 0; g < 4; ++g) {
+                    S[4 * k + g].c0[i] = *reinterpret_cast<const i32x4 *>(src + 64 * g);
+                    S[4 * k + g].c1[i] = *reinterpret_cast<const i32x4 *>(src + 64 * g + 16);
+                }
+                const int64_t o = (int64_t)row * nblk + 8 * b;
+                if (vec_as) {
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(scales + o);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(scales + o + 4);
+                    const i32x4 s0 = *reinterpret_cast<const i32x4 *>(sums + o);
+                    const i32x4 s1 = *reinterpret_cast<const i32x4 *>(sums + o + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        blk[k].a[i][j] = a0[j];
+                        blk[k].a[i][4 + j] = a1[j];
+                        blk[k].s[i][j] = s0[j];
+                        blk[k].s[i][4 + j] = s1[j];
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        blk[k].a[i][j] = scales[o + j];
+                        blk[k].s[i][j] = sums[o + j];
                     }
                 }
+            }
+            if (pu + 1 < ue) {
+                pw.next(set, nsb, sch.tiles_m);
+                ++pu;
             }
         };
 
         // Step g of a super-block (raw step in a register set, super-block data
         // in B) -> LDS buffer F and super-block parity Q.  Lanes that share a
         // row write identical header values.
-        auto convert = [&](auto setc, auto gc, auto bufc, const Block &B, int Q) {
+        auto convert = [&](auto kc, auto gc, auto bufc, int Q) {
+            constexpr int k = decltype(kc)::value;
             constexpr int g = decltype(gc)::value;
             constexpr int F = decltype(bufc)::value;
-            const Step &R = decltype(setc)::value ? S1 : S0;
+            const Step &R = S[4 * k + g];
+            const Block &B = blk[k];
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) {
                 const int e = p + i * P;
@@ -373,30 +426,36 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
 
         // Per step: load the step two ahead into the register set the current
         // step used, convert the next step into the other LDS buffer, barrier.
-        Pos pc = pos_of(ub);
-        load(IC<0>{}, IC<0>{}, pc);
-        load(IC<1>{}, IC<1>{}, pc);
-        cur = nxt;
-        convert(IC<0>{}, IC<0>{}, IC<0>{}, cur, 0);
+        // Units alternate between slots 0 and 1.  Per unit: convert quarters
+        // 1..3 of it and quarter 0 of the next unit, one per step (the
+        // matrix-core waves read the LDS buffer a step later); once its last
+        // quarter is converted, its slot is reloaded with the unit two ahead.
+        __builtin_amdgcn_s_setprio(2);   // conversion feeds the next step: issue it first
+        load_unit(IC<0>{});
+        load_unit(IC<1>{});
+        convert(IC<0>{}, IC<0>{}, IC<0>{}, 0);
         __syncthreads();
 #pragma unroll 1
-        for (int64_t u = ub; u < ue; ++u) {
-            const int Q = (int)(u - ub) & 1;
-            const Pos pn = pos_of(u + 1);
-            load(IC<0>{}, IC<2>{}, pc);
-            convert(IC<1>{}, IC<1>{}, IC<1>{}, cur, Q);
+        for (int64_t u = ub; u < ue; u += 2) {
+            convert(IC<0>{}, IC<1>{}, IC<1>{}, 0);
             __syncthreads();
-            load(IC<1>{}, IC<3>{}, pc);
-            convert(IC<0>{}, IC<2>{}, IC<0>{}, cur, Q);
+            convert(IC<0>{}, IC<2>{}, IC<0>{}, 0);
             __syncthreads();
-            load(IC<0>{}, IC<0>{}, pn);
-            convert(IC<1>{}, IC<3>{}, IC<1>{}, cur, Q);
+            convert(IC<0>{}, IC<3>{}, IC<1>{}, 0);
+            load_unit(IC<0>{});
             __syncthreads();
-            load(IC<1>{}, IC<1>{}, pn);
-            convert(IC<0>{}, IC<0>{}, IC<0>{}, nxt, Q ^ 1);
+            convert(IC<1>{}, IC<0>{}, IC<0>{}, 1);
             __syncthreads();
-            cur = nxt;
-            pc = pn;
+            if (u + 1 >= ue) break;
+            convert(IC<1>{}, IC<1>{}, IC<1>{}, 1);
+            __syncthreads();
+            convert(IC<1>{}, IC<2>{}, IC<0>{}, 1);
+            __syncthreads();
+            convert(IC<1>{}, IC<3>{}, IC<1>{}, 1);
+            load_unit(IC<1>{});
+            __syncthreads();
+            convert(IC<0>{}, IC<0>{}, IC<0>{}, 0);
+            __syncthreads();
         }
         return;
     }
@@ -516,8 +575,9 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
     };
 
     // End of the unit range's part of tile t (units [s0, s1) of it).
-    auto finish_tile = [&](int t, int64_t s0, int64_t s1) {
-        const Tile tl = tile_of<WN, WM>(set, t, sch.tiles_m);
+    auto finish_tile = [&](const Walk<WN, WM> &w, int64_t s0, int64_t s1) {
+        const int t = w.t;
+        const Tile &tl = w.tl;
         const int64_t t0 = (int64_t)t * nsb, t1 = t0 + nsb;
         if (s0 == t0 && s1 == t1) {   // the whole tile
             store_y(tl);
@@ -589,18 +649,16 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
     };
 
     __syncthreads();
+    Walk<WN, WM> at;
+    at.start(set, ub, nsb, sch.tiles_m);
     int64_t seg0 = ub;   // first unit of the current tile segment
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = zero16;
 #pragma unroll 1
     for (int64_t u = ub; u < ue; ++u) {
         const int Q = (int)(u - ub) & 1;
-        const int t = (int)(u / nsb);
-        const int64_t tend = (int64_t)(t + 1) * nsb;
-        if (u == seg0) {
-#pragma unroll
-            for (int a = 0; a < TN; ++a)
-#pragma unroll
-                for (int b = 0; b < TM; ++b) acc[a][b] = zero16;
-        }
         compute(IC<0>{}, IC<0>{}, IC<0>{}, Q);
         compute(IC<0>{}, IC<1>{}, IC<1>{}, Q);
         __syncthreads();
@@ -613,18 +671,23 @@ __global__ __launch_bounds__(128 * WVN * WVM, 1) void gemm_kernel(
         compute(IC<1>{}, IC<0>{}, IC<6>{}, Q);
         compute(IC<1>{}, IC<1>{}, IC<7>{}, Q);
         finish(Q);
-        if (u + 1 == ue || u + 1 == tend) {
-            finish_tile(t, seg0, u + 1);
+        if (u + 1 == ue || at.b + 1 == nsb) {
+            finish_tile(at, seg0, u + 1);
             seg0 = u + 1;
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int b = 0; b < TM; ++b) acc[a][b] = zero16;
         }
+        at.next(set, nsb, sch.tiles_m);
         __syncthreads();
     }
 }
 
-template <int WVN, int WVM, int TM>
+template <int WVN, int WVM, int TM, int NV>
 hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const float *scales,
                        const int32_t *sums, int64_t M, void *ws, hipStream_t stream) {
-    using C = Cfg<WVN, WVM, TM>;
+    using C = Cfg<WVN, WVM, TM, NV>;
     const int64_t tiles_m = (M + C::WM - 1) / C::WM;
     const int64_t tiles = (int64_t)set.tile0[set.count] * tiles_m;
     Sched s = {};
@@ -639,7 +702,7 @@ hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const f
         s.cnt = static_cast<int *>(ws);
         s.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kGemmCounters * 4);
     }
-    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM>), dim3((unsigned)s.groups), dim3(C::T),
+    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM, NV>), dim3((unsigned)s.groups), dim3(C::T),
                        sizeof(Lds<C::WN, C::WM>), stream, set, s, nsb, codes, scales, sums,
                        (int)M);
     return hipGetLastError();
@@ -664,9 +727,12 @@ hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
         set.N[p] = (int)probs[p].N;
         set.tile0[p + 1] = set.tile0[p] + (int)((probs[p].N + 127) / 128);   // WN = 128
     }
-    if (M > 64) return launch_tile<2, 2, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
-    if (M > 32) return launch_tile<2, 1, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
-    return launch_tile<2, 1, 1>(set, nsb, codes, scales, sums, M, workspace, stream);
+#ifndef GEMM_BIG
+#define GEMM_BIG 2, 2, 2, 4
+#endif
+    if (M > 64) return launch_tile<GEMM_BIG>(set, nsb, codes, scales, sums, M, workspace, stream);
+    if (M > 32) return launch_tile<2, 2, 1, 4>(set, nsb, codes, scales, sums, M, workspace, stream);
+    return launch_tile<2, 1, 1, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
 }
 
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
