@@ -41,6 +41,12 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-I" + os.path.join(ROOT, "include")]
 
 
+# Q4K_GEMM_INT8=1 builds the prefill GEMM's int8 contraction instead of the
+# default fp16 one (same results to fp32 rounding; kept for comparison).
+if os.environ.get("Q4K_GEMM_INT8") == "1":
+    COMMON.append("-DGEMM_I8=true")
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 

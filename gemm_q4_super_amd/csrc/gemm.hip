@@ -60,6 +60,16 @@
 
 #include "q4k_internal.h"
 
+// GEMM_I8 selects the int8 contraction (v_mfma_i32_32x32x32_i8 on the raw
+// quants and codes, exact int32 sub-block dots, fp32 epilogue
+// acc += D * (a * d*sc)) instead of the fp16 one on integer-valued operands.
+// Both are parity-tested; on the 512-token prefill the int8 one measured
+// 1.27x slower (three vector ops per output and sub-block against one), so
+// fp16 is the default.  Build with Q4K_GEMM_INT8=1 for the int8 path.
+#ifndef GEMM_I8
+#define GEMM_I8 false
+#endif
+
 namespace q4k {
 namespace {
 
@@ -67,6 +77,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -75,8 +86,11 @@ constexpr int NXCD = 8;
 constexpr int TN = 2;        // 32-row weight tiles per matrix-core wave
 constexpr int OSTR = 72;     // fp16 per operand row and step: [kh 2][s 2][lh 2][8] + 8 pad
 
+constexpr int QSTR = 80;     // bytes per int8 operand row and step: [s 2][lh 2][16] + 16 pad
+
+// fp16 operands: integer-valued sc*q and codes.
 template <int WN, int WM>
-struct __attribute__((aligned(16))) Lds {
+struct __attribute__((aligned(16))) LdsF {
     _Float16 aw[2][WN][OSTR];          // sc*q of a step's two sub-blocks
     _Float16 bx[2][WM][OSTR];          // codes of a step's two sub-blocks
     float dn[2][WN];                   // d of the super-block (by super-block parity)
@@ -84,6 +98,18 @@ struct __attribute__((aligned(16))) Lds {
     unsigned short wm[2][3][WN][8];    // -(dmin*mn_j) as bf16 hi, mid, lo
     unsigned short pm[2][3][WM][8];    // (a*S)_j as bf16 hi, mid, lo
 };
+// int8 operands: the 4-bit quants q and the codes as they are.
+template <int WN, int WM>
+struct __attribute__((aligned(16))) LdsI {
+    uint8_t aq[2][WN][QSTR];           // q of a step's two sub-blocks
+    int8_t bc[2][WM][QSTR];            // codes of a step's two sub-blocks
+    float ws[2][8][WN];                // d*sc_j per weight row
+    float as[2][8][WM];
+    unsigned short wm[2][3][WN][8];
+    unsigned short pm[2][3][WM][8];
+};
+template <int WN, int WM, bool I8>
+using Lds = typename std::conditional<I8, LdsI<WN, WM>, LdsF<WN, WM>>::type;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -222,14 +248,14 @@ struct Walk {
     }
 };
 
-template <int WVN, int WVM, int TM, int NV>
+template <int WVN, int WVM, int TM, int NV, bool I8>
 __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     const GemmSet set, const Sched sch, int nsb, const int8_t *__restrict__ codes,
     const float *__restrict__ scales, const int32_t *__restrict__ sums, int M) {
     using C = Cfg<WVN, WVM, TM, NV>;
     constexpr int WN = C::WN, WM = C::WM, P = C::P, NC = C::NC;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-    Lds<WN, WM> &L = *reinterpret_cast<Lds<WN, WM> *>(lds_raw);
+    Lds<WN, WM, I8> &L = *reinterpret_cast<Lds<WN, WM, I8> *>(lds_raw);
 
     const int G = sch.groups;
     const int gi = (G % NXCD == 0) ? (int)(blockIdx.x % NXCD) * (G / NXCD) + (int)(blockIdx.x / NXCD)
@@ -337,6 +363,29 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 const u32x4 h = B.h[i], q = R.q[i];
                 // low nibbles: sub-block 2g, high nibbles: sub-block 2g+1; byte t
                 // of the chunk is element 16c + t of both
+                if constexpr (I8) {
+                    u32x4 lo, hi;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        lo[k] = q[k] & 0x0F0F0F0Fu;
+                        hi[k] = (q[k] >> 4) & 0x0F0F0F0Fu;
+                    }
+                    // [s][lh = c][16]
+                    *reinterpret_cast<u32x4 *>(&L.aq[F][row][16 * c]) = lo;
+                    *reinterpret_cast<u32x4 *>(&L.aq[F][row][32 + 16 * c]) = hi;
+                    if (g == 0) {
+                        // lane c of the row: d*sc_j for j = 4c .. 4c+3
+                        const float d = half_lo(h.x);
+                        const float w0 = d * (float)(c ? scale6<4>(h, false) : scale6<0>(h, false));
+                        const float w1 = d * (float)(c ? scale6<5>(h, false) : scale6<1>(h, false));
+                        const float w2 = d * (float)(c ? scale6<6>(h, false) : scale6<2>(h, false));
+                        const float w3 = d * (float)(c ? scale6<7>(h, false) : scale6<3>(h, false));
+                        L.ws[Q][4 * c + 0][row] = w0;
+                        L.ws[Q][4 * c + 1][row] = w1;
+                        L.ws[Q][4 * c + 2][row] = w2;
+                        L.ws[Q][4 * c + 3][row] = w3;
+                    }
+                } else {
                 const float sc0 = (float)scale6<2 * g>(h, false), sc1 = (float)scale6<2 * g + 1>(h, false);
                 const half2 sv0 = {(_Float16)sc0, (_Float16)sc0};
                 const half2 bv0 = {(_Float16)(-1024.0f * sc0), (_Float16)(-1024.0f * sc0)};
@@ -360,8 +409,10 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 *reinterpret_cast<half8 *>(dst + 8) = conv(lo.z, lo.w, sv0, bv0);
                 *reinterpret_cast<half8 *>(dst + 16) = conv(hi.x, hi.y, sv1, bv1);
                 *reinterpret_cast<half8 *>(dst + 24) = conv(hi.z, hi.w, sv1, bv1);
+                if constexpr (!I8)
+                    if (g == 0) L.dn[Q][row] = half_lo(h.x);
+                }
                 if (g == 0) {
-                    L.dn[Q][row] = half_lo(h.x);
                     const float dmin = half_hi(h.x);
                     unsigned pt[3][8];
                     split3(-dmin * (float)scale6<0>(h, true), pt[0][0], pt[1][0], pt[2][0]);
@@ -389,6 +440,11 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 const int e = p + i * P;
                 if (C::CB % P != 0 && e >= C::CB) continue;
                 const int row = e >> 1, s = e & 1;
+                if constexpr (I8) {
+                    // [s][lh][16]: elements 0..15 and 16..31 of sub-block s
+                    *reinterpret_cast<i32x4 *>(&L.bc[F][row][32 * s]) = R.c0[i];
+                    *reinterpret_cast<i32x4 *>(&L.bc[F][row][32 * s + 16]) = R.c1[i];
+                } else {
                 // 8 codes -> fp16 (c ^ 0x80 is c + 128 as a byte)
                 auto conv = [&](unsigned v0, unsigned v1) {
                     const unsigned u0 = v0 ^ 0x80808080u, u1 = v1 ^ 0x80808080u;
@@ -402,6 +458,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 *reinterpret_cast<half8 *>(dst + 8) = conv(c0.z, c0.w);    // 8..15
                 *reinterpret_cast<half8 *>(dst + 32) = conv(c1.x, c1.y);   // 16..23
                 *reinterpret_cast<half8 *>(dst + 40) = conv(c1.z, c1.w);   // 24..31
+                }
                 if (g == 0) {
                     // lane s of the row: the scales and min-term parts of blocks 4s .. 4s+3
                     unsigned pt[3][4];
@@ -468,38 +525,68 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     f32x16 acc[TN][TM], usb[TN][TM];
     const f32x16 zero16 = {};
 
-    // Sub-block J of the super-block (sub-block s of the step in LDS buffer F):
-    // two matrix-core ops per 32x32 tile give E; u = a*E (+ u).
+    // Sub-block J of the super-block (sub-block s of the step in LDS buffer F).
+    // fp16: two matrix-core ops per 32x32 tile give E; u = a*E (+ u).
+    // int8: one gives the integer dot D; acc += D * (a * d*sc_J).
     auto compute = [&](auto bufc, auto sc, auto jc, int Q) {
         constexpr int F = decltype(bufc)::value;
         constexpr int s = decltype(sc)::value;
         constexpr int J = decltype(jc)::value;
-        half8 A[TN][2], B[TM][2];
         float a[TM];
 #pragma unroll
-        for (int u = 0; u < TN; ++u) {
-            const _Float16 *src = &L.aw[F][(wn * TN + u) * 32 + lr][16 * s + 8 * lh];
-            A[u][0] = *reinterpret_cast<const half8 *>(src);
-            A[u][1] = *reinterpret_cast<const half8 *>(src + 32);
-        }
+        for (int t = 0; t < TM; ++t) a[t] = L.as[Q][J][(wm * TM + t) * 32 + lr];
+        if constexpr (I8) {
+            i32x4 A[TN], B[TM];
+            float w[TN][16];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const int r = (wm * TM + t) * 32 + lr;
-            const _Float16 *src = &L.bx[F][r][16 * s + 8 * lh];
-            B[t][0] = *reinterpret_cast<const half8 *>(src);
-            B[t][1] = *reinterpret_cast<const half8 *>(src + 32);
-            a[t] = L.as[Q][J][r];
-        }
+            for (int u = 0; u < TN; ++u) {
+                const int r0 = (wn * TN + u) * 32;
+                A[u] = *reinterpret_cast<const i32x4 *>(&L.aq[F][r0 + lr][32 * s + 16 * lh]);
 #pragma unroll
-        for (int u = 0; u < TN; ++u)
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&L.ws[Q][J][r0 + 8 * q + 4 * lh]);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[u][4 * q + k] = w4[k];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                B[t] = *reinterpret_cast<const i32x4 *>(&L.bc[F][(wm * TM + t) * 32 + lr][32 * s + 16 * lh]);
+            const i32x16 zi = {};
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[u], B[t], zi, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[u][t][i] = fmaf((float)D[i], a[t] * w[u][i], acc[u][t][i]);
+                }
+        } else {
+            half8 A[TN][2], B[TM][2];
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const _Float16 *src = &L.aw[F][(wn * TN + u) * 32 + lr][16 * s + 8 * lh];
+                A[u][0] = *reinterpret_cast<const half8 *>(src);
+                A[u][1] = *reinterpret_cast<const half8 *>(src + 32);
+            }
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
-                f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][0], B[t][0], zero16, 0, 0, 0);
-                e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][1], B[t][1], e, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    usb[u][t][i] = J == 0 ? e[i] * a[t] : fmaf(e[i], a[t], usb[u][t][i]);
+                const _Float16 *src = &L.bx[F][(wm * TM + t) * 32 + lr][16 * s + 8 * lh];
+                B[t][0] = *reinterpret_cast<const half8 *>(src);
+                B[t][1] = *reinterpret_cast<const half8 *>(src + 32);
             }
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][0], B[t][0], zero16, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[u][1], B[t][1], e, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        usb[u][t][i] = J == 0 ? e[i] * a[t] : fmaf(e[i], a[t], usb[u][t][i]);
+                }
+        }
     };
 
     // End of a super-block: acc += d * u, then the min term on the matrix
@@ -509,12 +596,13 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     constexpr int AP[6] = {0, 1, 0, 2, 1, 0};   // activation part
     auto finish = [&](int Q) {
 #pragma unroll
-        for (int u = 0; u < TN; ++u) {
+        for (int u = 0; u < TN * !I8; ++u) {
             const int r0 = (wn * TN + u) * 32;
             float dv[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&L.dn[Q][r0 + 8 * q + 4 * lh]);
+                f32x4 d4 = {};
+                if constexpr (!I8) d4 = *reinterpret_cast<const f32x4 *>(&L.dn[Q][r0 + 8 * q + 4 * lh]);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) dv[4 * q + k] = d4[k];
             }
@@ -684,7 +772,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     }
 }
 
-template <int WVN, int WVM, int TM, int NV>
+template <int WVN, int WVM, int TM, int NV, bool I8 = GEMM_I8>
 hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const float *scales,
                        const int32_t *sums, int64_t M, void *ws, hipStream_t stream) {
     using C = Cfg<WVN, WVM, TM, NV>;
@@ -702,8 +790,8 @@ hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const f
         s.cnt = static_cast<int *>(ws);
         s.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kGemmCounters * 4);
     }
-    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM, NV>), dim3((unsigned)s.groups), dim3(C::T),
-                       sizeof(Lds<C::WN, C::WM>), stream, set, s, nsb, codes, scales, sums,
+    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM, NV, I8>), dim3((unsigned)s.groups), dim3(C::T),
+                       sizeof(Lds<C::WN, C::WM, I8>), stream, set, s, nsb, codes, scales, sums,
                        (int)M);
     return hipGetLastError();
 }
