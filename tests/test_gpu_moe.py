@@ -127,43 +127,30 @@ def test_swiglu_quantize_bit_exact_on_oracle_gu(q4k, oracle_lib, layer):
     assert (su.cpu().numpy() == out["hsum"]).all()
 
 
-@pytest.mark.parametrize("T", [1, 16])
-def test_moe_layer_chain(q4k, oracle_lib, layer, T):
-    """The whole layer on the GPU's own intermediates."""
-    import torch
-    wg, wu, wd = layer
-    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(T))
-    x = qi.make_act(T, H, qi.act_seed(63000 + T))
-    ref = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x)
-
-    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
-    xc, xs, xsu = q4k.q4k_quantize_act(to_dev(x))
-    g = q4k.q4k_moe_gemv(dwg, E, STRIDE_GU, F, H, dids, None, xc, xs, xsu, 0)
-    u = q4k.q4k_moe_gemv(dwu, E, STRIDE_GU, F, H, dids, None, xc, xs, xsu, 0)
-    hc, hs, hsu = q4k.q4k_quantize_act(u, g)
-    y = q4k.q4k_moe_gemv(dwd, E, STRIDE_D, H, F, dids, drw, hc, hs, hsu, 1)
-    torch.cuda.synchronize()
-    g, u, y = g.cpu().numpy(), u.cpu().numpy(), y.cpu().numpy()
-    hc, hs = hc.cpu().numpy(), hs.cpu().numpy()
-
-    assert_close(g, ref["g"], "chain g")
-    assert_close(u, ref["u"], "chain u")
-    # h codes: equal, except +-1 where the oracle's quotient h/scale lies within
-    # what the measured g, u differences can move it of a rounding boundary
-    P = T * TOPK
+def _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y, ids, rw, wd, H_, F_, what):
+    """y (a whole layer computed on the GPU, whose intermediates are g, u and
+    Q8(h) = hc, hs) against the oracle layer `ref`: g and u within the fp32
+    tolerance; h codes equal except +-1 where the oracle's quotient h/scale
+    lies within what the measured g, u differences can move it of a rounding
+    boundary; y within the tolerance plus what those flips and scale shifts
+    can move it."""
+    T, topk = ids.shape
+    P = T * topk
+    assert_close(g, ref["g"], what + " g")
+    assert_close(u, ref["u"], what + " u")
     g0, u0 = ref["g"].astype(np.float64), ref["u"].astype(np.float64)
     dg, du = np.abs(g - g0), np.abs(u - u0)
     sig = 1.0 / (1.0 + np.exp(-g0))
     dh = np.abs(sig * (1.0 + g0 * (1.0 - sig))) * dg * np.abs(u0) + np.abs(g0 * sig) * du + dg * du
     # plus one fp32 ulp of h: both sides round their (different) h to fp32
     dh = dh + np.spacing(np.abs(ref["h"])).astype(np.float64)
-    dh = dh.reshape(P, F // 32, 32) + 1e-12
-    amax = np.abs(ref["h"].astype(np.float64)).reshape(P, F // 32, 32).max(axis=2)
+    dh = dh.reshape(P, F_ // 32, 32) + 1e-12
+    amax = np.abs(ref["h"].astype(np.float64)).reshape(P, F_ // 32, 32).max(axis=2)
     amax = np.maximum(amax, 1e-30)[:, :, None]
-    q = ref["h"].reshape(P, F // 32, 32).astype(np.float64) * 127.0 / amax
+    q = ref["h"].reshape(P, F_ // 32, 32).astype(np.float64) * 127.0 / amax
     dq = 127.0 * dh / amax + np.abs(q) * dh.max(axis=2, keepdims=True) / amax
     frac = np.abs(q - np.floor(q) - 0.5)
-    diff = (hc.astype(np.int64) - ref["hc"].astype(np.int64)).reshape(P, F // 32, 32)
+    diff = (hc.astype(np.int64) - ref["hc"].astype(np.int64)).reshape(P, F_ // 32, 32)
     mism = diff != 0
     assert (np.abs(diff) <= 1).all()
     assert (frac[mism] <= 2.0 * dq[mism] + 1e-6).all(), "code flip away from a boundary"
@@ -171,30 +158,71 @@ def test_moe_layer_chain(q4k, oracle_lib, layer, T):
     # scale = fl32(amax / 127): amax moves by at most max dh, plus one ulp of the scale
     assert (dscale <= 1.01 * dh.max(axis=2) / 127.0
             + np.spacing(ref["hs"]).astype(np.float64) + 1e-12).all()
-    # y bound: tolerance plus what the admitted flips and scale shifts can move
-    W = {e: np.abs(oracle_lib.dequant(wd[e * H:(e + 1) * H], F)) for e in np.unique(ids)}
-    extra = np.zeros((T, H))
+    W = {e: np.abs(oracle_lib.dequant(wd[e * H_:(e + 1) * H_], F_)) for e in np.unique(ids)}
+    extra = np.zeros((T, H_))
     for t in range(T):
-        for s_ in range(TOPK):
-            p = t * TOPK + s_
+        for s_ in range(topk):
+            p = t * topk + s_
             d_blk = np.maximum(ref["hs"][p], hs[p]).astype(np.float64).repeat(32)
             flips = mism[p].ravel().astype(np.float64)
             shift = dscale[p].repeat(32) * 127.0
             extra[t] += abs(float(rw[t, s_])) * (W[ids[t, s_]] @ (flips * d_blk + shift))
     err = np.abs(y.astype(np.float64) - ref["y"])
     tol = np.maximum(2e-3 * np.abs(ref["y"]), 1e-4) + 1.01 * extra
-    assert (err <= tol).all(), "chain y outside tolerance + admitted-flip bound"
-    print("chain: %d h-code flips of %d, max y err %.3g" % (int(mism.sum()), mism.size,
-                                                          float(err.max())))
+    assert (err <= tol).all(), what + ": y outside tolerance + admitted-flip bound"
+    return int(mism.sum()), float(err.max())
 
 
-def _chain(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_):
+def _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_):
+    """The six-call chain; returns (g, u, hc, hs, y) on the host."""
+    import torch
     sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
     xc, xs, xsu = q4k.q4k_quantize_act(x)
     g = q4k.q4k_moe_gemv(dwg, n_exp, sgu, F_, H_, dids, None, xc, xs, xsu, 0)
     u = q4k.q4k_moe_gemv(dwu, n_exp, sgu, F_, H_, dids, None, xc, xs, xsu, 0)
     hc, hs, hsu = q4k.q4k_quantize_act(u, g)
-    return q4k.q4k_moe_gemv(dwd, n_exp, sd, H_, F_, dids, drw, hc, hs, hsu, 1)
+    y = q4k.q4k_moe_gemv(dwd, n_exp, sd, H_, F_, dids, drw, hc, hs, hsu, 1)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().numpy() for t in (g, u, hc, hs, y))
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_moe_layer_chain(q4k, oracle_lib, layer, T):
+    """The whole layer on the GPU's own intermediates."""
+    wg, wu, wd = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(T))
+    x = qi.make_act(T, H, qi.act_seed(63000 + T))
+    ref = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x)
+    g, u, hc, hs, y = _chain_parts(q4k, to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids),
+                                   to_dev(rw), to_dev(x), E, H, F)
+    flips, err = _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y, ids, rw, wd, H, F, "chain")
+    print("chain: %d h-code flips, max y err %.3g" % (flips, err))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
+def test_moe_ffn_vs_oracle(q4k, oracle_lib, layer, T):
+    """q4k_moe_ffn (for T <= 2 with Q8 and SwiGLU inside the GEMV kernels) on
+    the chain test's inputs against the oracle layer, with the same
+    flip-aware bound; the bound's intermediates are the chain's, which the
+    fused layer equals bit for bit (asserted here too)."""
+    import torch
+    wg, wu, wd = layer
+    ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(T))
+    x = qi.make_act(T, H, qi.act_seed(63000 + T))
+    ref = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x)
+    dwg, dwu, dwd, dids, drw, dx = (to_dev(a) for a in (wg, wu, wd, ids, rw, x))
+    g, u, hc, hs, y2 = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, dx, E, H, F)
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, E, STRIDE_GU, STRIDE_D, H, F, dids, drw, dx)
+    torch.cuda.synchronize()
+    y1 = y1.cpu().numpy()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids, rw, wd, H, F, "moe_ffn T=%d" % T)
+
+
+def _chain(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_):
+    import torch
+    y = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)[4]
+    return torch.from_numpy(y)
 
 
 @pytest.mark.parametrize("T", [1, 2, 4, 16])
@@ -236,8 +264,23 @@ def test_moe_ffn_repeated_and_bad_ids_and_two_passes(q4k, oracle_lib):
     dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
     sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
     y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
-    y2 = _chain(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
+    g, u, hc, hs, y2 = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
     torch.cuda.synchronize()
-    y1, y2 = y1.cpu().numpy(), y2.cpu().numpy()
+    y1 = y1.cpu().numpy()
     assert np.isfinite(y1).all()
     assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    # against the oracle: a skipped pair (out-of-range id) adds nothing, which
+    # the oracle's layer gives with routing weight 0 on any valid expert; the
+    # skipped pairs' g, u and h are not compared
+    bad = (ids < 0) | (ids >= n_exp)
+    ids_o, rw_o = np.where(bad, 0, ids).astype(np.int32), np.where(bad, 0, rw).astype(np.float32)
+    ref = oracle_lib.moe_layer(wg, wu, wd, n_exp, H_, F_, ids_o, rw_o, x.cpu().numpy())
+    keep = ~bad.ravel()
+    for k in ("g", "u", "h", "hc", "hs"):
+        ref[k] = np.where(keep[:, None], ref[k], 0).astype(ref[k].dtype)
+    g[~keep] = 0.0
+    u[~keep] = 0.0
+    hc[~keep] = 0
+    hs[~keep] = 0.0
+    _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids_o, rw_o, wd, H_, F_,
+                        "moe_ffn repeated/bad ids")
