@@ -16,6 +16,7 @@ EXPORTED_SYMBOLS = (
     "q4k_gemm",
     "q4k_gemm_batch",
     "q4k_gemm_workspace_bytes",
+    "q4k_gemm_batch_noalloc",
     "q4k_moe_gemv",
     "q4k_moe_workspace_bytes",
     "q4k_moe_ffn",
@@ -63,6 +64,9 @@ def lib():
         L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
         L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
                                      _I, _P, ctypes.c_size_t, _P]
+        L.q4k_gemm_batch_noalloc.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P,
+                                             _P, _P, _I, _P]
+        L.q4k_gemm_batch_noalloc.restype = ctypes.c_int
         L.q4k_gemm_workspace_bytes.argtypes = []
         L.q4k_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]

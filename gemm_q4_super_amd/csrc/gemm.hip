@@ -56,6 +56,8 @@
 // order), writes y and returns the counter to zero.  Without a workspace the
 // grid has one workgroup per tile and no partial tiles.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "q4k_internal.h"
@@ -796,7 +798,48 @@ hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const f
     return hipGetLastError();
 }
 
+// Clears the split-tile counters of a workspace.
+__global__ __launch_bounds__(256) void clear_counters_kernel(int *cnt) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < kGemmCounters) cnt[i] = 0;
+}
+
+// Scratch of the allocation-free entry point: the split-tile counters and
+// partial tiles of one GEMM launch, the same layout as a caller workspace.
+constexpr size_t kScratchBytes = (size_t)kGemmCounters * 4 + (size_t)2 * kGemmMaxGroups * 128 * 128 * 4;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 }  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy of the array); null if the runtime
+// cannot resolve it.  The host-side name `scratch` is not a device address
+// and is never passed to a kernel.
+void *gemm_static_scratch() {
+    static std::atomic<void *> ptr[64];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *p = ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        ptr[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
+size_t gemm_static_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_clear_counters(void *workspace, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((kGemmCounters + 255) / 256), dim3(256), 0,
+                       stream, static_cast<int *>(workspace));
+    return hipGetLastError();
+}
 
 size_t gemm_workspace_bytes() {
     return (size_t)kGemmCounters * 4 + (size_t)2 * kGemmMaxGroups * 128 * 128 * 4;

@@ -134,6 +134,25 @@ int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K, const
                                            static_cast<hipStream_t>(stream)));
 }
 
+int q4k_gemm_batch_noalloc(const q4k_gemm_problem *problems, int count, int64_t K,
+                           const int8_t *codes, const float *scales, const int32_t *sums,
+                           int64_t M, void *stream) {
+    if (!problems) return Q4K_EINVAL;
+    if (count < 1 || count > q4k::kMaxGemmBatch) return Q4K_ESHAPE;
+    for (int i = 0; i < count; ++i) {
+        const q4k_gemm_problem &p = problems[i];
+        int st = check_matrix_args(p.w, p.N, K, codes, scales, sums, M, p.y);
+        if (st != Q4K_OK) return st;
+    }
+    if (q4k::gemm_static_scratch_bytes() < q4k::gemm_workspace_bytes()) return Q4K_EWORKSPACE;
+    void *ws = q4k::gemm_static_scratch();
+    if (!ws) return Q4K_EHIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = q4k::launch_clear_counters(ws, s);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(q4k::launch_gemm_batch(problems, count, K, codes, scales, sums, M, ws, s));
+}
+
 size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N) {
     if (T < 1 || topk < 1 || n_experts < 1 || topk > n_experts ||
         T * topk > q4k::kMoeMaxPairs || n_experts > q4k::kMoeMaxExperts || N < 1 || N > kMaxDim)

@@ -77,6 +77,12 @@ hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64
 constexpr int kGemmCounters = 16384;   // split-tile counters (tiles x matrix-core waves)
 constexpr int kGemmMaxGroups = 256;    // workgroups of a split launch
 size_t gemm_workspace_bytes();
+// The library's own GEMM scratch on the current device (a static device array
+// of gemm_static_scratch_bytes() bytes; null if it cannot be resolved), and a
+// launch that zeroes the counters at the start of a workspace.
+void *gemm_static_scratch();
+size_t gemm_static_scratch_bytes();
+hipError_t launch_clear_counters(void *workspace, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                        const float *scales, const int32_t *sums, int64_t M, float *y,
                        void *workspace, hipStream_t stream);

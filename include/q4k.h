@@ -184,6 +184,27 @@ int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,
                    const int8_t *codes, const float *scales, const int32_t *sums,
                    int64_t M, void *workspace, size_t workspace_bytes, void *stream);
 
+/* q4k_gemm_batch without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory or take a caller buffer:
+ * code under HIP graph capture, serving loops that forbid allocation on the
+ * hot path, harnesses that disallow hipMalloc.  The split-tile counters and
+ * partial tiles live in a static device array of the library (33 619 968
+ * bytes: 65 536 bytes of counters plus 2 * 256 partial tiles of 128 x 128
+ * fp32), one copy per GPU, held from the library's first use on that GPU
+ * until the process ends.  Its device address is resolved on the first call
+ * on each device.  Every call first clears the counters with a small kernel
+ * on `stream` (no memset), then runs the same kernel as q4k_gemm_batch with
+ * that array as the workspace, so results equal q4k_gemm_batch with a
+ * workspace bit for bit.  No size is refused for want of scratch: a launch
+ * whose split-tile counters would not fit runs with whole tiles.  All calls
+ * on one GPU share the array: calls that overlap in time on that GPU (on
+ * different streams) race and give wrong results.  Returns Q4K_EHIP if the
+ * array's address cannot be resolved.  Arguments, limits and checks as for
+ * q4k_gemm_batch. */
+int q4k_gemm_batch_noalloc(const q4k_gemm_problem *problems, int count, int64_t K,
+                           const int8_t *codes, const float *scales, const int32_t *sums,
+                           int64_t M, void *stream);
+
 /* Routed-expert grouped GEMV.  n_experts Q4_K matrices of N rows x K columns
  * at expert_stride_bytes from each other (stride >= N*(K/256)*144, multiple of
  * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].
