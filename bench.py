@@ -22,11 +22,17 @@ is the step with o and down adding into a residual stream inside their GEMVs
 (q4k_quantize_gemv_residual, in place).
 
 Printed: one JSON line with the whole-job rate (algorithmic bytes / wall time),
-the GEMV roofline (algorithmic bytes per launch / mean launch duration, against
-8 TB/s), and the CPU oracle timed on a bounded sample of the same sweep.  Beside
-them, outside the timed region: the prefill GEMM (M = 512), the small-batch
-GEMV (M = 2, 4, 8), the routed-expert layer (T = 1, 16) and the Q6_K decode
-GEMV over the same projection shapes.
+the per-step distribution (median, p10, p90 over the timed steps), the GEMV
+roofline (algorithmic bytes per launch / mean launch duration, against
+8 TB/s), and the CPU oracle timed on this host on a bounded sample of the same
+sweep, single-threaded and on all cores (OpenMP over output rows).  Beside
+them, outside the timed region: the practical decode ceilings (a plain
+16-byte stream read of each launch group's bytes and an empty kernel), the
+prefill GEMM (M = 512, 20 steps, with the shader clock sampled during the
+steps for a measured-clock peak), the small-batch GEMV (M = 2, 4, 8), the
+routed-expert layer (T = 1, 16) and the Q6_K decode GEMV over the same
+projection shapes -- each checked against the oracle before it is timed --
+and the oracle's own rate on each of those workloads.
 """
 from __future__ import annotations
 
@@ -47,6 +53,70 @@ FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak (the prefill GEMM's 
 LAYERS = 36
 PREFILL_M = 512
 METRIC = "Q4_K decode GEMV GB/s (% HBM peak); prefill Q4_K×Q8 GEMM TOPS (% MFMA)"
+
+
+def dist(seconds):
+    """median / p10 / p90 / mean of per-pass times, in the unit given."""
+    a = np.asarray(seconds, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "passes": int(a.size)}
+
+
+def dist_ms(seconds):
+    return {k: (round(v * 1e3, 4) if k != "passes" else v) for k, v in dist(seconds).items()}
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (MHz) from sysfs while running, in a
+    background thread; mean() is None where the clock cannot be read."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period, self.samples, self.stop = period, [], threading.Event()
+        self.thread = threading.Thread(target=self.run, daemon=True)
+
+    def read(self):
+        for f in self.files:
+            try:
+                for line in open(f):
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().lower().rstrip("*").strip()
+                                     .replace("mhz", "").strip())
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def run(self):
+        while not self.stop.is_set():
+            v = self.read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+
+    def mean(self):
+        return float(np.mean(self.samples)) if self.samples else None
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
 
 
 def gemv_bytes(N, K, M=1):
@@ -93,7 +163,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the secondary prefill-GEMM measurement")
-    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill GEMM measurement (with its parity check) and "
                          "print it")
@@ -401,15 +471,17 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
-    for k in range(steps):
-        g_q.replay()
-        ev[k][0].record()
-        g_g.replay()
-        ev[k][1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gemm_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for k in range(steps):
+            g_q.replay()
+            ev[k][0].record()
+            g_g.replay()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_s = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    gemm_s = float(np.median(step_s))
     per_group = {}
     for gi, (gname, idx) in enumerate(pre.groups):
         g = Decode.graph(pre, pre.gemm_unit, range(gi, pre.units, len(pre.groups)), cap)
@@ -436,12 +508,23 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
         per_shape[name] = {"N": N, "K": K, "us": round(d * 1e6, 2),
                            "TOPS": round(2 * PREFILL_M * N * K / d / 1e12, 1)}
     tops = pre.ops / gemm_s / 1e12
+    sclk = clk.mean()
+    # the matrix-core peak at the clock measured during the run (peaks scale
+    # with the clock; the published figures are at 2400 MHz)
+    clock_peak = None if sclk is None else {
+        "sclk_mhz_mean": round(sclk, 1), "samples": len(clk.samples),
+        "fp16_peak_TFLOPS": round(FP16_PEAK_TFLOPS * sclk / 2400.0, 1),
+        "int8_peak_TOPS": round(INT8_PEAK_TOPS * sclk / 2400.0, 1),
+        "frac_of_fp16_peak_at_clock": round(tops / (FP16_PEAK_TFLOPS * sclk / 2400.0), 4),
+        "frac_of_int8_peak_at_clock": round(tops / (INT8_PEAK_TOPS * sclk / 2400.0), 4)}
     out = {"workload": "prefill GEMM, M=512 tokens x the seven Qwen3-4B projection shapes x "
                        "36 layers (3.72 T int ops per step); q4k_gemm_batch launches {q,k,v} "
                        "and {gate,up}, q4k_gemm o and down (4 launches per layer)",
            "steps": steps, "ms_per_step": round(elapsed / steps * 1e3, 3),
            "tok_per_s": round(PREFILL_M * steps / elapsed, 0),
            "gemm_ms_per_step": round(gemm_s * 1e3, 3),
+           "gemm_ms_per_step_dist": dist_ms(step_s),
+           "measured_clock_peak": clock_peak,
            # achieved: algorithmic Q4_K x Q8 ops (2*M*N*K) per second; the kernel
            # issues one fp16 matrix op per algorithmic one on integer-valued
            # operands, plus 3/16 as many bf16 ones for the min term
@@ -452,29 +535,51 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
                         "frac": round(tops / FP16_PEAK_TFLOPS, 4),
                         "matrix_core_busy": round(tops * (1 + 3 / 16) / FP16_PEAK_TFLOPS, 4),
                         "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-                        "mean_launch_us": round(gemm_s / pre.units * 1e6, 2)},
+                        "mean_launch_us": round(gemm_s / pre.units * 1e6, 2),
+                        "timing": "median over %d steps of HIP events around the %d GEMM "
+                                  "launches of a step" % (steps, pre.units)},
            "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity}
     del pre
     torch.cuda.empty_cache()
     return out
 
 
-def measure_small_batch(torch, dec, steps=5):
-    """Small-batch verification GEMV: M = 2, 4, 8 activation rows against the
-    36-layer sweep's weights, through q4k_gemv and through q4k_gemm.  Only the
-    products are timed (the Q8 rows are prepared once)."""
+def measure_small_batch(torch, dec, oracle, steps=5):
+    """Small-batch verification GEMV: M = 2, 4, 8 seeded N(0,1) activation rows
+    against the 36-layer sweep's weights, through q4k_gemv and through q4k_gemm.
+    Only the products are timed (the Q8 rows are prepared once).  Before
+    timing, layer 0's seven products through both paths are checked against
+    the oracle on sampled weight rows (all M activation rows)."""
     import gemm_q4_super_amd as q4k
     L = dec.L
     dev = torch.device("cuda:0")
     out = {}
     cap = torch.cuda.Stream()
     for M in (2, 4, 8):
-        xs = {K: q4k.q4k_quantize_act(torch.randn((M, K), device=dev, dtype=torch.float32))
-              for K in {K for _, _, K in dec.weights}}
+        host = {K: dec.qi.make_act(M, K, dec.qi.act_seed(30000 + 100 * M + K // 256))
+                for K in sorted({K for _, _, K in dec.weights})}
+        xs = {K: q4k.q4k_quantize_act(torch.from_numpy(x).to(dev)) for K, x in host.items()}
         ys = {N: torch.empty((M, N), dtype=torch.float32, device=dev)
               for N in {N for _, N, _ in dec.weights}}
-        res = {}
         gws = q4k.gemm_workspace(dev)
+        # spot check: layer 0, both paths, against the oracle
+        worst, checked = 0.0, 0
+        for p, (name, K, N) in enumerate(dec.shapes):
+            wt = dec.weights[p][0]
+            c, sc, su = xs[K]
+            rc, rs, _ = oracle.quantize_act(host[K])
+            if not (c.cpu().numpy() == rc).all():
+                raise SystemExit("small batch: Q8 codes differ from the oracle (M=%d)" % M)
+            rows = np.unique(np.r_[0, N - 1, np.random.default_rng(M * 7 + p).integers(0, N, 12)])
+            ref = oracle.matvec(dec.host_w[p], N, K, rc, rs, rows=rows, parallel=True)
+            for y in (q4k.q4k_gemv(wt, N, K, c, sc, su), q4k.q4k_gemm(wt, N, K, c, sc, su)):
+                got = y.cpu().numpy()[:, rows].astype(np.float64)
+                err = np.abs(got - ref)
+                if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+                    raise SystemExit("small batch: %s M=%d outside tolerance" % (name, M))
+                worst = max(worst, float((err / np.maximum(np.abs(ref), 0.05)).max()))
+                checked += ref.size
+        res = {"parity": {"outputs_checked": checked, "max_rel_err": worst}}
         for path in ("gemv", "gemm"):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
@@ -488,20 +593,77 @@ def measure_small_batch(torch, dec, steps=5):
                     if st:
                         raise RuntimeError("launch failed")
             g.replay()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            ts = []
             for _ in range(steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
                 g.replay()
-            b.record()
+                b.record()
+                ts.append((a, b))
             torch.cuda.synchronize()
-            t = a.elapsed_time(b) * 1e-3 / steps
+            ts = [a.elapsed_time(b) * 1e-3 for a, b in ts]
+            t = float(np.median(ts))
             nbytes = sum(gemv_bytes(N, K, M) for _, N, K in dec.weights)
             ops = sum(2 * M * N * K for _, N, K in dec.weights)
             res[path] = {"us_per_sweep": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
-                         "TOPS": round(ops / t / 1e12, 2)}
+                         "TOPS": round(ops / t / 1e12, 2), "us_dist": {
+                             k: (round(v * 1e6, 1) if k != "passes" else v)
+                             for k, v in dist(ts).items()}}
         res["faster"] = min(("gemv", "gemm"), key=lambda k: res[k]["us_per_sweep"])
         out["M=%d" % M] = res
     return out
+
+
+def measure_ceilings(torch, q4k, dec, reps=5):
+    """Practical per-launch ceilings of the decode step: a plain 16-byte stream
+    read of each launch group's bytes (the fused GEMV's algorithmic bytes), 36
+    launches on distinct regions of one 2.1 GB buffer per group (as the
+    weights, nothing stays in the last-level cache), best of several grids;
+    and an empty kernel's duration per launch (graph of 144)."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    groups = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+    gbytes = {n: sum(fused_bytes(dec.shapes[p][2], dec.shapes[p][1]) for p in idx)
+              for n, idx in groups}
+    stride = max((b + 4095) // 4096 * 4096 for b in gbytes.values())
+    buf = torch.ones(LAYERS * stride // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    cap = torch.cuda.Stream()
+
+    def timed(fn, n_launch):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            s = torch.cuda.current_stream().cuda_stream
+            for i in range(n_launch):
+                if fn(i, s):
+                    raise RuntimeError("ceiling launch failed")
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / (reps * n_launch)
+
+    out = {}
+    for name, _ in groups:
+        nb = gbytes[name] // 16 * 16
+        best = None
+        for grid in (256, 512, 1024, 2048):
+            t = timed(lambda i, s, grid=grid: L.q4k_ceiling_stream_read(
+                buf.data_ptr() + i * stride, nb, grid, sink.data_ptr(), s), LAYERS)
+            if best is None or t < best[0]:
+                best = (t, grid)
+        out[name] = {"bytes": nb, "us": round(best[0] * 1e6, 3),
+                     "GBps": round(nb / best[0] / 1e9, 1), "grid": best[1]}
+    empty = {}
+    for grid in (1, 256, 1024):
+        empty["grid_%d" % grid] = round(timed(lambda i, s, grid=grid: L.q4k_ceiling_empty(grid, s),
+                                              4 * LAYERS) * 1e6, 3)
+    del buf
+    torch.cuda.empty_cache()
+    return {"stream_read_per_launch_group": out, "empty_kernel_us_per_launch": empty}
 
 
 def q6k_bytes(N, K, M=1):
@@ -655,7 +817,7 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
             "parity": {"rows_checked_per_shape": "24 sampled", "max_rel_err": worst}}
 
 
-def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
+def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
     """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8) over
     `layers` distinct seeded layers per pass (1.81 GB, past the last-level
     cache), for each T in Ts: q4k_moe_ffn (the reported time), and the six-call
@@ -666,11 +828,14 @@ def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
     dev = torch.device("cuda:0")
     E, H, F, TOPK = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
     sgu, sdn = F * (H // 256) * 144, H * (F // 256) * 144
-    W = []
+    W, W_host = [], []
     for l in range(layers):
-        W.append(tuple(torch.from_numpy(np.concatenate(
+        host = tuple(np.concatenate(
             [qi.make_q4k_bytes(*((F, H) if k < 2 else (H, F)), qi.expert_seed(l, e, k))
-             for e in range(E)])).to(dev) for k in range(3)))
+             for e in range(E)]) for k in range(3))
+        if l == 0:
+            W_host.append(host)
+        W.append(tuple(torch.from_numpy(h).to(dev) for h in host))
     out = {}
     cap = torch.cuda.Stream()
     for T in Ts:
@@ -735,6 +900,22 @@ def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
             torch.cuda.synchronize()
             return a.elapsed_time(b) * 1e-3 / (steps * layers)
 
+        # spot check before timing: layer 0 through q4k_moe_ffn against the
+        # oracle layer (codes of h may differ by one next to a rounding
+        # boundary, so a few outputs may exceed the bar by what such a flip
+        # moves them; the exact flip-aware bound is checked by the tests)
+        fused(0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(W_host[0][0], W_host[0][1], W_host[0][2], E, H, F, routes[0][0],
+                               routes[0][1], x.cpu().numpy(), parallel=True)["y"]
+        got = y2.cpu().numpy().astype(np.float64)
+        bar = np.maximum(2e-3 * np.abs(ref), 1e-4)
+        over = np.abs(got - ref) / bar
+        if (over > 1).mean() > 0.01 or over.max() > 20:
+            raise SystemExit("moe: T=%d layer outside the spot-check bound" % T)
+        spot = {"outputs_checked": int(ref.size), "outputs_over_bar": int((over > 1).sum()),
+                "max_err_over_bar": round(float(over.max()), 3),
+                "max_rel_err": float((np.abs(got - ref) / np.maximum(np.abs(ref), 0.05)).max())}
         t_chain = timed(layer)
         t = timed(fused)
         same = bool(torch.equal(y.view(torch.int32), y2.view(torch.int32)))
@@ -746,34 +927,114 @@ def measure_moe(torch, q4k, qi, steps=5, layers=8, Ts=(1, 16)):
                            "GBps": round(nbytes / t / 1e9, 1),
                            "path": "q4k_moe_ffn (%d launches)" % (3 if T <= 2 else 5),
                            "six_call_chain_us_per_layer": round(t_chain * 1e6, 2),
-                           "fused_equals_chain_bitwise": same}
+                           "fused_equals_chain_bitwise": same, "oracle_spot_check": spot}
     del W
     torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(qi, oracle, shapes, seconds):
-    """The oracle (single thread) over layers of the same sweep until `seconds`
-    of CPU time have been spent or all 36 layers are done."""
-    t_cpu, done_bytes, layers_done = 0.0, 0, 0
-    for layer in range(LAYERS):
+def cpu_baselines(qi, oracle, seconds):
+    """The oracle as it stands (plain C, fp64 products), timed on this host:
+    single-threaded and with OpenMP over output rows on all cores (the same
+    arithmetic), each on a bounded sample of a workload.  Returns the decode
+    figure (the headline's unit, all cores) and one entry per workload."""
+    shapes = qi.QWEN3_4B_LAYER
+    threads = oracle.threads(True)
+    info = dict(cpu_info(), omp_threads=threads)
+
+    def decode(parallel, budget):
+        t_cpu, nbytes, done = 0.0, 0, 0
+        for layer in range(LAYERS):
+            for p, (name, K, N) in enumerate(shapes):
+                w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, layer, p))
+                x = qi.make_act(1, K, qi.act_seed(layer * len(shapes) + p))
+                ta = time.perf_counter()
+                rc, rs, _ = oracle.quantize_act(x)
+                oracle.matvec(w, N, K, rc, rs, parallel=parallel)
+                t_cpu += time.perf_counter() - ta
+                nbytes += gemv_bytes(N, K) + quant_bytes(K)
+            done += 1
+            if t_cpu >= budget:
+                break
+        return {"GBps": round(nbytes / t_cpu / 1e9, 4), "seconds": round(t_cpu, 2),
+                "sample": "layers 0..%d of the 36-layer decode sweep (%d quantize+GEMV calls, "
+                          "%.2f GB)" % (done - 1, done * len(shapes), nbytes / 1e9)}
+
+    def prefill(parallel, rows_per_proj):
+        t_cpu = 0.0
+        step_est = 0.0
         for p, (name, K, N) in enumerate(shapes):
-            w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, layer, p))
-            x = qi.make_act(1, K, qi.act_seed(layer * len(shapes) + p))
+            w = qi.make_q4k_bytes(N, K, qi.weight_seed(2, 0, p))
+            x = qi.make_act(PREFILL_M, K, qi.act_seed(20000 + p))
+            rows = np.arange(min(rows_per_proj, N))
             ta = time.perf_counter()
             rc, rs, _ = oracle.quantize_act(x)
-            oracle.matvec(w, N, K, rc, rs)
-            t_cpu += time.perf_counter() - ta
-            done_bytes += gemv_bytes(N, K) + quant_bytes(K)
-        layers_done += 1
-        if t_cpu >= seconds:
-            break
-    return {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "layers 0..%d of the 36-layer decode sweep (%d quantize+GEMV calls, "
-                      "%.2f GB), single thread, %.1f s" % (layers_done - 1,
-                                                          layers_done * len(shapes),
-                                                          done_bytes / 1e9, t_cpu)}
+            oracle.matvec(w, N, K, rc, rs, rows=rows, parallel=parallel)
+            dt = time.perf_counter() - ta
+            t_cpu += dt
+            step_est += dt * N / rows.size
+        step_est *= LAYERS
+        ops = sum(2 * PREFILL_M * N * K for _, K, N in shapes) * LAYERS
+        return {"TOPS": round(ops / step_est / 1e12, 6), "ms_per_step_extrapolated":
+                round(step_est * 1e3, 1), "seconds": round(t_cpu, 2),
+                "sample": "%d weight rows of each of layer 0's seven projections x 512 "
+                          "activation rows; scaled to all rows and 36 layers (extrapolated)"
+                          % rows_per_proj}
+
+    def small(M, parallel, rows_per_proj):
+        t_cpu, nbytes, est = 0.0, 0, 0.0
+        for p, (name, K, N) in enumerate(shapes):
+            w = qi.make_q4k_bytes(N, K, qi.weight_seed(1, 0, p))
+            x = qi.make_act(M, K, qi.act_seed(30000 + 100 * M + K // 256))
+            rows = np.arange(min(rows_per_proj, N))
+            ta = time.perf_counter()
+            rc, rs, _ = oracle.quantize_act(x)
+            oracle.matvec(w, N, K, rc, rs, rows=rows, parallel=parallel)
+            dt = time.perf_counter() - ta
+            t_cpu += dt
+            est += dt * N / rows.size
+            nbytes += gemv_bytes(N, K, M)
+        return {"GBps": round(nbytes / est / 1e9, 4), "seconds": round(t_cpu, 2),
+                "sample": "%s weight rows of each of layer 0's seven projections, M = %d"
+                          % ("all" if rows_per_proj >= 9728 else str(rows_per_proj), M)}
+
+    def moe(T, parallel):
+        E, H, F, TOPK = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
+        ids, rw = qi.make_routing(T, E, TOPK, qi.routing_seed(100 * T))
+        touched = np.unique(ids)
+        # only the touched experts' matrices are needed; untouched ones stay zero
+        wg = np.zeros(E * F * (H // 256) * 144, np.uint8)
+        wu, wd = np.zeros_like(wg), np.zeros(E * H * (F // 256) * 144, np.uint8)
+        sgu, sdn = F * (H // 256) * 144, H * (F // 256) * 144
+        for e in touched:
+            wg[e * sgu:(e + 1) * sgu] = qi.make_q4k_bytes(F, H, qi.expert_seed(0, e, 0)).ravel()
+            wu[e * sgu:(e + 1) * sgu] = qi.make_q4k_bytes(F, H, qi.expert_seed(0, e, 1)).ravel()
+            wd[e * sdn:(e + 1) * sdn] = qi.make_q4k_bytes(H, F, qi.expert_seed(0, e, 2)).ravel()
+        x = qi.make_act(T, H, qi.act_seed(70000 + T))
+        ta = time.perf_counter()
+        oracle.moe_layer(wg, wu, wd, E, H, F, ids, rw, x, parallel=parallel)
+        dt = time.perf_counter() - ta
+        nbytes = len(touched) * (sgu * 2 + sdn)
+        return {"us_per_layer": round(dt * 1e6, 1), "GBps": round(nbytes / dt / 1e9, 4),
+                "distinct_experts": int(len(touched))}
+
+    budget = max(seconds / 3.0, 1.0)
+    dec1, decN = decode(False, budget), decode(True, budget / 2)
+    out = {
+        "host": info,
+        "decode": {"1_thread": dec1, "all_cores": decN},
+        "prefill": {"1_thread": prefill(False, 48), "all_cores": prefill(True, 96 * threads)},
+        "small_batch": {"M=%d" % M: {"1_thread": small(M, False, 768),
+                                     "all_cores": small(M, True, 9728)}
+                        for M in (2, 4, 8)},
+        "moe_layer": {"T=1": {"1_thread": moe(1, False), "all_cores": moe(1, True)},
+                      "T=16": {"all_cores": moe(16, True)}},
+    }
+    headline = {"value": decN["GBps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": decN["sample"] + ", OpenMP over output rows on all host cores",
+                "single_thread": {"value": dec1["GBps"], "cores": 1, "sample": dec1["sample"]},
+                "cpu_model": info["cpu_model"]}
+    return headline, out
 
 
 def main():
@@ -878,15 +1139,16 @@ def main():
     bytes_per_launch = dec.bytes_fused / dec.n_batch
     achieved = bytes_per_launch / mean_launch_s / 1e9
     n_launch = dec.n_batch
-    small = None if args.no_extra else measure_small_batch(torch, dec)
+    small = None if args.no_extra else measure_small_batch(torch, dec, oracle)
+    ceilings = None if args.no_extra else measure_ceilings(torch, q4k, dec)
     del g_batch, dec
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
                                                            args.prefill_steps)
-    moe = None if args.no_extra else measure_moe(torch, q4k, qi)
+    moe = None if args.no_extra else measure_moe(torch, q4k, qi, oracle)
     q6k = None if args.no_extra else measure_q6k(torch, q4k, qi, oracle)
     large = None if args.no_extra else measure_large_launch(torch, q4k, qi)
-    cpu = None if args.no_cpu else cpu_baseline(qi, oracle, qi.QWEN3_4B_LAYER, args.cpu_seconds)
+    cpu, cpu_all = (None, None) if args.no_cpu else cpu_baselines(qi, oracle, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -896,6 +1158,7 @@ def main():
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "step_ms_dist": dist_ms(block_s),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -925,6 +1188,8 @@ def main():
         "residual_epilogue_path": residual,
         "two_launch_path": two_step,
         "cpu_baseline": cpu,
+        "cpu_baselines": cpu_all,
+        "decode_ceilings": ceilings,
         "parity": parity,
         "prefill_gemm": prefill,
         "small_batch_gemv": small,

@@ -23,6 +23,8 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_ffn_workspace_bytes",
     "q6k_gemv",
     "q6k_quantize_gemv",
+    "q4k_ceiling_stream_read",
+    "q4k_ceiling_empty",
     "q4k_status_string",
 )
 
@@ -83,6 +85,10 @@ def lib():
         L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
         L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+        L.q4k_ceiling_stream_read.argtypes = [_P, _I, _I, _P, _P]
+        L.q4k_ceiling_stream_read.restype = ctypes.c_int
+        L.q4k_ceiling_empty.argtypes = [_I, _P]
+        L.q4k_ceiling_empty.restype = ctypes.c_int
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",

@@ -246,6 +246,19 @@ int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int q4k_ceiling_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
+                            void *stream) {
+    if (!buf || !sink) return Q4K_EINVAL;
+    if (bytes < 16 || bytes % 16 != 0 || grid < 1 || grid > (int64_t(1) << 20)) return Q4K_ESHAPE;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_stream_read(buf, bytes, grid, sink, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_ceiling_empty(int64_t grid, void *stream) {
+    if (grid < 1 || grid > (int64_t(1) << 20)) return Q4K_ESHAPE;
+    return from_hip(q4k::launch_empty(grid, static_cast<hipStream_t>(stream)));
+}
+
 const char *q4k_status_string(int status) {
     switch (status) {
     case Q4K_OK: return "ok";

@@ -108,4 +108,9 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
                           int64_t topk, const float *x, float *y, void *workspace,
                           hipStream_t stream);
 
+// Measurement aids (not on the product path).
+hipError_t launch_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
+                              hipStream_t stream);
+hipError_t launch_empty(int64_t grid, hipStream_t stream);
+
 }  // namespace q4k

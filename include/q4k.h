@@ -296,6 +296,19 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
 int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
                       float *y, void *stream);
 
+/* Measurement aids, not on the product path: the practical ceilings that
+ * bench.py reports beside the decode launches.
+ * q4k_ceiling_stream_read: `grid` workgroups of 256 threads read `bytes`
+ *   (multiple of 16) of the device buffer `buf` (16-byte aligned) in 16-byte
+ *   loads, grid-stride, and write one word per workgroup to `sink` (device,
+ *   >= grid words): the bytes of a launch moved with no arithmetic.
+ * q4k_ceiling_empty: `grid` workgroups of an empty kernel: the cost of a
+ *   kernel boundary alone.
+ * 1 <= grid <= 2^20. */
+int q4k_ceiling_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
+                            void *stream);
+int q4k_ceiling_empty(int64_t grid, void *stream);
+
 /* Static description of a status code. */
 const char *q4k_status_string(int status);
 

@@ -1,12 +1,14 @@
 """CPU oracle for the Q4_K x Q8 products -- TEST INFRASTRUCTURE ONLY.
 
-Thin numpy/ctypes wrapper over `q4k_oracle.c` (plain single-threaded C, fp64
-products, bit-exact fp32 activation quantizer).  Only the tests, the smoke check
+Thin numpy/ctypes wrapper over `q4k_oracle.c` (plain C, fp64 products,
+bit-exact fp32 activation quantizer), built single-threaded and, for the
+full-size checks and the all-core CPU baseline, with OpenMP over the output
+rows of each product (the same arithmetic per output).  Only the tests, the smoke check
 and the benchmark's CPU-baseline leg may import this package; the GPU product
 path neither imports it nor shares any code with it.
 
 `build()` compiles the C file with gcc (no fast-math, no FMA contraction) into
-`liboracle.so` next to it.
+`liboracle.so` and `liboracle_omp.so` next to it.
 """
 from __future__ import annotations
 
@@ -205,9 +207,10 @@ def moe_matvec(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales,
     return y
 
 
-def moe_layer(w_gate, w_up, w_down, n_experts, H, F, ids, route_w, x):
+def moe_layer(w_gate, w_up, w_down, n_experts, H, F, ids, route_w, x, parallel=False):
     """Whole routed-expert FFN layer.  Returns dict with y (fp64 [T, H]) and the
-    intermediates g, u, h (fp32 [T*topk, F]) and hc/hs/hsum (Q8 of h)."""
+    intermediates g, u, h (fp32 [T*topk, F]) and hc/hs/hsum (Q8 of h).
+    parallel=True runs each product's output rows on all host cores."""
     ids, rw, x = _c(ids, np.int32), _c(route_w, np.float32), _c(x, np.float32)
     T, topk = ids.shape
     P = T * topk
@@ -217,7 +220,8 @@ def moe_layer(w_gate, w_up, w_down, n_experts, H, F, ids, route_w, x):
                h=np.zeros((P, F), np.float32), hc=np.zeros((P, F), np.int8),
                hs=np.zeros((P, F // QB), np.float32), hsum=np.zeros((P, F // QB), np.int32),
                y=np.zeros((T, H), np.float64))
-    _load().oracle_moe_layer(_ptr(_c(w_gate, np.uint8)), _ptr(_c(w_up, np.uint8)),
+    (_load_omp() if parallel else _load()).oracle_moe_layer(
+                             _ptr(_c(w_gate, np.uint8)), _ptr(_c(w_up, np.uint8)),
                              _ptr(_c(w_down, np.uint8)), n_experts, stride_gu, stride_dn,
                              H, F, _ptr(ids), _ptr(rw), T, topk, _ptr(x),
                              _ptr(out["g"]), _ptr(out["u"]), _ptr(out["h"]),

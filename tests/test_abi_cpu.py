@@ -186,6 +186,15 @@ def test_gemm_workspace_checks(L):
     assert L.q4k_gemm_batch(arr, 1, 512, A, A, A, 1, A + 128, need, None) == EALIGN
 
 
+def test_ceiling_argument_checks(L):
+    assert L.q4k_ceiling_stream_read(None, 1024, 1, A, None) == EINVAL
+    assert L.q4k_ceiling_stream_read(A, 1024, 1, None, None) == EINVAL
+    assert L.q4k_ceiling_stream_read(A, 1000, 1, A, None) == ESHAPE
+    assert L.q4k_ceiling_stream_read(A, 1024, 0, A, None) == ESHAPE
+    assert L.q4k_ceiling_stream_read(A + 4, 1024, 1, A, None) == EALIGN
+    assert L.q4k_ceiling_empty(0, None) == ESHAPE
+
+
 def test_quantize_argument_checks(L):
     f = L.q4k_quantize_act
     assert f(None, 1, 32, None, A, A, A, None) == EINVAL
