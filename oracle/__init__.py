@@ -60,6 +60,9 @@ _SIG = {
     "oracle_unpack_q6k": [_P, _P, _P, _P],
     "oracle_q6k_dequant_row": [_P, _I, _P],
     "oracle_q6k_matvec": [_P, _I, _I, _P, _P, _I, _P, _I, _P],
+    "oracle_kv_quantize": [_P, _I, _I, _P, _P],
+    "oracle_attn_int8kv": [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
+                           ctypes.c_double, _P],
 }
 
 
@@ -263,3 +266,35 @@ def q6k_matvec(w, N, K, codes, scales, rows=None, parallel=False) -> np.ndarray:
     (_load_omp() if parallel else _load()).oracle_q6k_matvec(_ptr(_c(w, np.uint8)), N, K, _ptr(codes), _ptr(scales), M,
                               _ptr(r), r.size, _ptr(y))
     return y
+
+
+# --------------------------------------------------------- INT8 KV cache ----
+
+def kv_quantize(x: np.ndarray):
+    """Q8 of fp32 vectors [..., hd], one scale per vector (a cache entry of one
+    position and kv-head).  Returns (codes int8 [..., hd], scales fp32 [...])."""
+    x = _c(x, np.float32)
+    hd = x.shape[-1]
+    R = x.size // hd
+    codes = np.zeros(x.shape, np.int8)
+    scales = np.zeros(x.shape[:-1], np.float32)
+    _load().oracle_kv_quantize(_ptr(x), R, hd, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def attn_int8kv(q, kc, ks, vc, vs, n_ctx, scale, parallel=False) -> np.ndarray:
+    """fp64 [M, n_head, hd] decode attention over one layer's INT8 cache.
+
+    q fp32 [M, n_head, hd]; kc, vc int8 [n_kv, cap, hd]; ks, vs fp32 [n_kv, cap].
+    Query token m sees the first n_ctx - (M - 1 - m) positions.  parallel=True
+    runs the (token, head) pairs on all host cores (same arithmetic)."""
+    q = _c(q, np.float32)
+    M, n_head, hd = q.shape
+    kc, vc = _c(kc, np.int8), _c(vc, np.int8)
+    ks, vs = _c(ks, np.float32), _c(vs, np.float32)
+    n_kv, cap, _ = kc.shape
+    out = np.zeros((M, n_head, hd), np.float64)
+    (_load_omp() if parallel else _load()).oracle_attn_int8kv(
+        _ptr(q), M, n_head, n_kv, hd, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+        cap, n_ctx, float(scale), _ptr(out))
+    return out

@@ -33,11 +33,19 @@
  *    and the routing-weighted sum in slot order.
  *
  *  - Q6_K weights (public GGUF format; real Q4_K_M files keep some tensors in
- *    Q6_K and the decode kernels of genie's "Path G" -- section 3 -- are Q6_K
- *    ones, but the pages do not print the bytes): 256 weights of one row in
+ *    Q6_K and the decode kernels of genie's "Path G" -- section 6, "The
+ *    negatives I kept" -- are Q6_K ones, but the pages do not print the
+ *    bytes): 256 weights of one row in
  *    210 bytes, ql[128] low 4 bits and qh[64] high 2 bits of 6-bit quants,
  *    int8 scales per 16 weights, fp16 d; w = d*sc[e/16]*(q - 32), exact in
  *    fp64; the same fp64 product against Q8 activations.
+ *  - INT8 KV cache and decode attention (genie's Path I, section 4, "Memory-
+ *    first: making every byte count"): each (layer, position, kv-head) vector
+ *    of head_dim values is kept as int8 codes with one fp32 absmax scale,
+ *    quantized by the Q8 rule above over the whole vector.  Attention is the
+ *    transformer's scaled dot-product softmax attention (the pages name the
+ *    model, Qwen3-4B, not the formula) with grouped kv heads, read from the
+ *    dequantized cache scale*code and evaluated in fp64.
  *
  * Parity pins for every function are in tests/test_oracle_pins.py.
  *
@@ -395,5 +403,85 @@ void oracle_q6k_matvec(const uint8_t *w, int64_t N, int64_t K,
             }
         }
         free(wr);
+    }
+}
+
+/* ------------------------------------------------------- INT8 KV cache -- */
+
+/* Q8 of R vectors of hd fp32 values, one scale per vector (the cache entry of
+ * one position and kv-head): scale = fl32(amax/127), code =
+ * clamp(rne(fl32(x/scale)), -127, 127); an all-zero vector has scale 0 and
+ * codes 0.  Evaluated in fp32, bit for bit. */
+void oracle_kv_quantize(const float *x, int64_t R, int64_t hd, int8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        const float *xr = x + r * hd;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < hd; ++i) {
+            float a = fabsf(xr[i]);
+            if (a > amax)
+                amax = a;
+        }
+        float d = amax / 127.0f;
+        for (int64_t i = 0; i < hd; ++i) {
+            int c = 0;
+            if (d != 0.0f) {
+                float t = xr[i] / d;
+                float v = rintf(t);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                c = (int)v;
+            }
+            codes[r * hd + i] = (int8_t)c;
+        }
+        scales[r] = d;
+    }
+}
+
+/* Decode attention of M query tokens over one layer's INT8 cache, in fp64.
+ *   q      fp32 [M][n_head][hd]   (keys and queries already position-encoded)
+ *   kc, vc int8 [n_kv][cap][hd],  ks, vs fp32 [n_kv][cap]
+ *   out    fp64 [M][n_head][hd]
+ * Query token m sits at position n_ctx - M + m and sees the positions
+ * t < n_ctx - (M - 1 - m) (causal).  Head h reads kv head h / (n_head/n_kv).
+ * s_t = scale * sum_i q[i] * ks[t]*kc[t][i];  p = softmax(s) over the visible
+ * t;  out[i] = sum_t p_t * vs[t]*vc[t][i]. */
+void oracle_attn_int8kv(const float *q, int64_t M, int64_t n_head, int64_t n_kv, int64_t hd,
+                        const int8_t *kc, const float *ks, const int8_t *vc, const float *vs,
+                        int64_t cap, int64_t n_ctx, double scale, double *out)
+{
+    const int64_t group = n_head / n_kv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t mh = 0; mh < M * n_head; ++mh) {
+        const int64_t m = mh / n_head, h = mh % n_head, g = h / group;
+        const int64_t L = n_ctx - (M - 1 - m);
+        const float *qv = q + mh * hd;
+        double *s = (double *)malloc(sizeof(double) * (size_t)L);
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < L; ++t) {
+            const int8_t *kr = kc + (g * cap + t) * hd;
+            const double kscale = (double)ks[g * cap + t];
+            double dot = 0.0;
+            for (int64_t i = 0; i < hd; ++i)
+                dot += (double)qv[i] * (kscale * (double)kr[i]);
+            s[t] = scale * dot;
+            if (s[t] > smax)
+                smax = s[t];
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            s[t] = exp(s[t] - smax);
+            denom += s[t];
+        }
+        double *o = out + mh * hd;
+        for (int64_t i = 0; i < hd; ++i)
+            o[i] = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const int8_t *vr = vc + (g * cap + t) * hd;
+            const double w = s[t] / denom * (double)vs[g * cap + t];
+            for (int64_t i = 0; i < hd; ++i)
+                o[i] += w * (double)vr[i];
+        }
+        free(s);
     }
 }

@@ -43,6 +43,11 @@ QWEN3_4B_LAYER = (
 )
 QWEN3_4B_LAYERS = 36
 
+# Qwen3-4B attention: 32 query heads sharing 8 kv heads, head_dim 128.
+QWEN3_4B_HEADS = 32
+QWEN3_4B_KV_HEADS = 8
+QWEN3_4B_HEAD_DIM = 128
+
 # 8B-A1B-style routed-expert layer.
 MOE_EXPERTS = 64
 MOE_HIDDEN = 2048
@@ -236,6 +241,23 @@ def make_routing(T: int, n_experts: int, topk: int, seed: int):
     return ids, w
 
 
+def make_kv(n_pos: int, n_kv: int, hd: int, seed: int):
+    """fp32 keys and values [n_pos, n_kv, hd], each drawn from N(0, 1) (the
+    per-head vectors after the model's q/k normalisation have unit-scale
+    elements)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n_pos, n_kv, hd), dtype=np.float32)
+    v = rng.standard_normal((n_pos, n_kv, hd), dtype=np.float32)
+    return k, v
+
+
+def make_query(M: int, n_head: int, hd: int, seed: int, gain: float = 1.0) -> np.ndarray:
+    """fp32 queries [M, n_head, hd] drawn from gain * N(0, 1); a larger gain
+    gives peakier attention."""
+    rng = np.random.default_rng(seed)
+    return (gain * rng.standard_normal((M, n_head, hd))).astype(np.float32)
+
+
 # Seed scheme of the synthetic workloads.
 def weight_seed(workload: int, layer: int, proj: int) -> int:
     return 1000 * workload + 10 * layer + proj
@@ -252,3 +274,11 @@ def act_seed(call_index: int) -> int:
 
 def routing_seed(layer: int) -> int:
     return 700000 + layer
+
+
+def kv_seed(layer: int) -> int:
+    return 800000 + layer
+
+
+def query_seed(layer: int) -> int:
+    return 850000 + layer

@@ -477,3 +477,137 @@ def test_q6k_zero_scale_gives_zero(oracle_lib):
     codes, scales, _ = oracle_lib.quantize_act(qi.make_act(2, 512, 13))
     y = oracle_lib.q6k_matvec(w, 2, 512, codes, scales)
     assert (y == 0).all()
+
+
+# ------------------------------------------------- INT8 KV cache, attention --
+# Cache entries and decode attention of genie-ai-runtime's Path I (section 4,
+# "Memory-first: making every byte count").
+
+def _golden_kv(case, hd):
+    x = np.zeros(hd, np.float32)
+    for k, v in case["x"].items():
+        x[int(k)] = v
+    codes = np.zeros(hd, np.int64)
+    for k, v in case["codes"].items():
+        codes[int(k)] = v
+    return x, codes
+
+
+@pytest.mark.parametrize("idx", range(3))
+def test_kv_quantize_golden(oracle_lib, idx):
+    g = _load("kv_int8_handbuilt.json")
+    c = g["cases"][idx]
+    x, want = _golden_kv(c, g["head_dim"])
+    codes, scales = oracle_lib.kv_quantize(x[None])
+    assert codes[0].astype(np.int64).tolist() == want.tolist()
+    assert float(scales[0]) == c["scale"]
+
+
+def test_kv_quantize_roundtrip_bound(oracle_lib):
+    k, v = qi.make_kv(40, 8, 128, 5)
+    x = np.concatenate([k, 7.0 * v]).reshape(-1, 128)
+    x[3] = 0.0
+    codes, scales = oracle_lib.kv_quantize(x)
+    s = scales.astype(np.float64)[:, None]
+    c = codes.astype(np.int64)
+    assert (np.abs(x - s * c) <= s * (0.5 + 2.0 ** -17)).all()
+    amax = np.abs(x).max(axis=1)
+    assert (scales == amax / np.float32(127)).all()
+    nz = amax > 0
+    assert (np.abs(c).max(axis=1)[nz] == 127).all()
+    assert (c[~nz] == 0).all()
+
+
+def _cache(rng, n_kv, cap, hd=128):
+    kc = rng.integers(-127, 128, size=(n_kv, cap, hd)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(n_kv, cap, hd)).astype(np.int8)
+    ks = rng.uniform(0.001, 0.03, size=(n_kv, cap)).astype(np.float32)
+    vs = rng.uniform(0.001, 0.03, size=(n_kv, cap)).astype(np.float32)
+    return kc, ks, vc, vs
+
+
+def test_attn_zero_query_is_mean_of_visible_values(oracle_lib):
+    rng = np.random.default_rng(1)
+    kc, ks, vc, vs = _cache(rng, 2, 40)
+    n_ctx, M = 37, 3
+    q = np.zeros((M, 4, 128), np.float32)
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, n_ctx, 0.088)
+    vhat = vs.astype(np.float64)[:, :, None] * vc
+    for m in range(M):
+        L = n_ctx - (M - 1 - m)
+        for h in range(4):
+            np.testing.assert_allclose(out[m, h], vhat[h // 2, :L].mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
+def test_attn_one_hot_query_selects_one_position(oracle_lib):
+    rng = np.random.default_rng(2)
+    kc, ks, vc, vs = _cache(rng, 1, 64)
+    j, t_star = 17, 41
+    kc[0, :, j] = 0
+    kc[0, t_star, j] = 127
+    ks[0, t_star] = 1.0
+    q = np.zeros((1, 1, 128), np.float32)
+    q[0, 0, j] = 100.0
+    # score gap 100*127*0.0884 > 1100: e^-1100 is 0 in fp64
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, 64, 128 ** -0.5)
+    assert (out[0, 0] == vs[0, t_star].astype(np.float64) * vc[0, t_star]).all()
+
+
+def test_attn_two_positions_logistic_form(oracle_lib):
+    rng = np.random.default_rng(3)
+    kc, ks, vc, vs = _cache(rng, 1, 2)
+    q = rng.standard_normal((1, 1, 128)).astype(np.float32) * 4
+    scale = 128 ** -0.5
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, 2, scale)
+    kh = ks.astype(np.float64)[0, :, None] * kc[0]
+    vh = vs.astype(np.float64)[0, :, None] * vc[0]
+    s0, s1 = (scale * (kh @ q[0, 0].astype(np.float64))).tolist()
+    want = vh[1] + (vh[0] - vh[1]) / (1.0 + np.exp(s1 - s0))
+    np.testing.assert_allclose(out[0, 0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_attn_grouped_heads_read_their_own_kv_head(oracle_lib):
+    # n_head = 8 over n_kv = 4: head h reads kv head h // 2.  Each kv head g has
+    # its key spike at its own position t_g, so head h must return v[g][t_g].
+    rng = np.random.default_rng(4)
+    kc, ks, vc, vs = _cache(rng, 4, 32)
+    kc[:, :, 0] = 0
+    t = [3, 29, 11, 20]
+    for g in range(4):
+        kc[g, t[g], 0] = 127
+        ks[g, t[g]] = 1.0
+    q = np.zeros((1, 8, 128), np.float32)
+    q[0, :, 0] = 100.0
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, 32, 128 ** -0.5)
+    for h in range(8):
+        g = h // 2
+        assert (out[0, h] == vs[g, t[g]].astype(np.float64) * vc[g, t[g]]).all(), h
+
+
+def test_attn_causal_rows_equal_shorter_single_queries(oracle_lib):
+    rng = np.random.default_rng(5)
+    kc, ks, vc, vs = _cache(rng, 2, 50)
+    q = qi.make_query(4, 8, 128, 6)
+    n_ctx = 45
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, n_ctx, 0.09)
+    for m in range(4):
+        one = oracle_lib.attn_int8kv(q[m:m + 1], kc, ks, vc, vs, n_ctx - 3 + m, 0.09)
+        assert (out[m] == one[0]).all()
+
+
+def test_attn_position_permutation_and_convex_hull(oracle_lib):
+    rng = np.random.default_rng(7)
+    kc, ks, vc, vs = _cache(rng, 1, 30)
+    q = qi.make_query(1, 3, 128, 8, gain=3.0)
+    out = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, 30, 0.0884)
+    perm = rng.permutation(30)
+    outp = oracle_lib.attn_int8kv(q, kc[:, perm], ks[:, perm], vc[:, perm], vs[:, perm], 30, 0.0884)
+    np.testing.assert_allclose(outp, out, rtol=1e-12, atol=1e-15)
+    vh = vs.astype(np.float64)[0, :, None] * vc[0]
+    assert (out[0] <= vh.max(axis=0) + 1e-15).all() and (out[0] >= vh.min(axis=0) - 1e-15).all()
+    # positions beyond n_ctx are never read
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:, 25:], vc2[:, 25:] = 99, -99
+    a = oracle_lib.attn_int8kv(q, kc, ks, vc, vs, 25, 0.0884)
+    b = oracle_lib.attn_int8kv(q, kc2, ks, vc2, vs, 25, 0.0884)
+    assert (a == b).all()
