@@ -23,14 +23,22 @@ Functions carry the C names:
                 ids, route_w, x, workspace=None)     -> y [T, H]  (whole expert FFN layer)
     q6k_gemv(w, N, K, codes, scales)                 -> y [M, N]   (Q6_K weights, M <= 8)
     q6k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (Q6_K, fp32 x, one launch)
+    q4k_kv_store(k, v, pos0, k_codes, k_scales, v_codes, v_scales)
+                                                     (INT8 KV cache entries of M positions)
+    q4k_attn_decode(q, k_codes, k_scales, v_codes, v_scales, n_ctx, scale, workspace="auto")
+                                                     -> out [M, n_head, 128]
 """
 from ._lib import (  # noqa: F401
     Q4KError,
+    attn_workspace,
     gemm_workspace,
     lib,
     lib_path,
     q4k_gemm,
     q4k_gemm_batch,
+    q4k_kv_store,
+    q4k_attn_decode,
+    q4k_attn_workspace_bytes,
     q4k_gemv,
     q4k_moe_ffn,
     q4k_moe_ffn_workspace_bytes,

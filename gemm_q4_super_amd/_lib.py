@@ -23,6 +23,9 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_ffn_workspace_bytes",
     "q6k_gemv",
     "q6k_quantize_gemv",
+    "q4k_kv_store",
+    "q4k_attn_workspace_bytes",
+    "q4k_attn_decode",
     "q4k_ceiling_stream_read",
     "q4k_ceiling_empty",
     "q4k_status_string",
@@ -85,6 +88,11 @@ def lib():
         L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
         L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+        L.q4k_kv_store.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+        L.q4k_attn_workspace_bytes.argtypes = [_I, _I, _I]
+        L.q4k_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.q4k_attn_decode.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
+                                      ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
         L.q4k_ceiling_stream_read.argtypes = [_P, _I, _I, _P, _P]
         L.q4k_ceiling_stream_read.restype = ctypes.c_int
         L.q4k_ceiling_empty.argtypes = [_I, _P]
@@ -94,7 +102,8 @@ def lib():
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
                      "q4k_quantize_gemv_residual",
                      "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv"):
+                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q4k_kv_store",
+                     "q4k_attn_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -346,3 +355,63 @@ def q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H,
                              _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)),
            "q4k_moe_ffn")
     return y
+
+
+# ------------------------------------------------------------ INT8 KV cache --
+
+def q4k_kv_store(k, v, pos0, k_codes, k_scales, v_codes, v_scales):
+    """Quantize fp32 k, v [M, n_kv, 128] into cache positions pos0..pos0+M-1 of
+    k_codes/v_codes int8 [n_kv, cap, 128] and k_scales/v_scales fp32 [n_kv, cap]."""
+    for t, n in ((k, "k"), (v, "v"), (k_codes, "k_codes"), (k_scales, "k_scales"),
+                 (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, n)
+    M, n_kv, hd = k.shape
+    cap = k_codes.shape[1]
+    _check(lib().q4k_kv_store(_ptr(k), _ptr(v), M, n_kv, hd, pos0, cap, _ptr(k_codes),
+                              _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _stream(k)),
+           "q4k_kv_store")
+
+
+def q4k_attn_workspace_bytes(M, n_head, n_kv) -> int:
+    return int(lib().q4k_attn_workspace_bytes(M, n_head, n_kv))
+
+
+_ATTN_WS = {}
+
+
+def attn_workspace(device, nbytes):
+    """A zero-filled attention workspace of at least `nbytes` for `device`,
+    reused across calls (every call leaves its counters zero)."""
+    import torch
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _ATTN_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(int(nbytes), dtype=torch.uint8, device=dev)
+        _ATTN_WS[key] = ws
+    return ws
+
+
+def q4k_attn_decode(q, k_codes, k_scales, v_codes, v_scales, n_ctx, scale, out=None,
+                    workspace="auto"):
+    """Decode attention of q fp32 [M, n_head, 128] over the first n_ctx positions
+    of one layer's INT8 cache (token m sees n_ctx - (M - 1 - m) positions)."""
+    import torch
+    for t, n in ((q, "q"), (k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                 (v_scales, "v_scales")):
+        _dev(t, n)
+    M, n_head, hd = q.shape
+    n_kv, cap, _ = k_codes.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a device tensor")
+        workspace = attn_workspace(q.device, q4k_attn_workspace_bytes(M, n_head, n_kv))
+    _dev(workspace, "workspace")
+    _check(lib().q4k_attn_decode(_ptr(q), M, n_head, n_kv, hd, _ptr(k_codes), _ptr(k_scales),
+                                 _ptr(v_codes), _ptr(v_scales), cap, n_ctx, float(scale),
+                                 _ptr(out), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(q)),
+           "q4k_attn_decode")
+    return out

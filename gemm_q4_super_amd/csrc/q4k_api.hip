@@ -1,5 +1,7 @@
 // C-ABI entry points of libq4k.so (declared in include/q4k.h).
 // Every argument is checked here, on the host, before anything is launched.
+#include <math.h>
+
 #include "../../include/q4k.h"
 #include "q4k_internal.h"
 
@@ -244,6 +246,47 @@ int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_EALIGN;
     return from_hip(q4k::launch_q6k_quantize_gemv(static_cast<const uint8_t *>(w), N, K, x, M, y,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+int q4k_kv_store(const float *k, const float *v, int64_t M, int64_t n_kv, int64_t head_dim,
+                 int64_t pos0, int64_t cap, int8_t *k_codes, float *k_scales, int8_t *v_codes,
+                 float *v_scales, void *stream) {
+    if (!k || !v || !k_codes || !k_scales || !v_codes || !v_scales) return Q4K_EINVAL;
+    if (head_dim != q4k::kAttnHeadDim || M < 1 || M > 4096 || n_kv < 1 ||
+        n_kv > q4k::kAttnMaxKvHeads || pos0 < 0 || cap > (int64_t(1) << 24) || pos0 + M > cap)
+        return Q4K_ESHAPE;
+    if (!aligned(k, 8) || !aligned(v, 8) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_scales, 4) || !aligned(v_scales, 4))
+        return Q4K_EALIGN;
+    return from_hip(q4k::launch_kv_store(k, v, M, n_kv, pos0, cap, k_codes, k_scales, v_codes,
+                                         v_scales, static_cast<hipStream_t>(stream)));
+}
+
+size_t q4k_attn_workspace_bytes(int64_t M, int64_t n_head, int64_t n_kv) {
+    if (M < 1 || n_kv < 1 || n_head < n_kv || n_head % n_kv != 0) return 0;
+    return q4k::attn_workspace_bytes(M, n_head, n_kv);
+}
+
+int q4k_attn_decode(const float *q, int64_t M, int64_t n_head, int64_t n_kv, int64_t head_dim,
+                    const int8_t *k_codes, const float *k_scales, const int8_t *v_codes,
+                    const float *v_scales, int64_t cap, int64_t n_ctx, float scale, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !out) return Q4K_EINVAL;
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return Q4K_EINVAL;
+    if (head_dim != q4k::kAttnHeadDim || M < 1 || M > q4k::kAttnMaxM || n_kv < 1 ||
+        n_kv > q4k::kAttnMaxKvHeads || n_head < n_kv || n_head % n_kv != 0 ||
+        n_head / n_kv > q4k::kAttnMaxGroup || n_ctx < M || n_ctx > cap ||
+        cap > (int64_t(1) << 24))
+        return Q4K_ESHAPE;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_scales, 4) || !aligned(v_scales, 4))
+        return Q4K_EALIGN;
+    if (!workspace || workspace_bytes < q4k::attn_workspace_bytes(M, n_head, n_kv))
+        return Q4K_EWORKSPACE;
+    if (!aligned(workspace, 256)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_attn(q, M, n_head, n_kv, k_codes, k_scales, v_codes, v_scales,
+                                     cap, n_ctx, scale, out, workspace,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int q4k_ceiling_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,

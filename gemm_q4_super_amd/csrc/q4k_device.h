@@ -87,6 +87,28 @@ struct Q8Lane {
     float d;
     int sum;
 };
+
+// fl32(amax / 127), correctly rounded: with y = RN(1/127), one correction step
+// q0 + RN(amax - 127 q0) * y.
+__device__ __forceinline__ float q8_scale(float amax) {
+    constexpr float y = 1.0f / 127.0f;
+    const float q0 = amax * y;
+    return __builtin_fmaf(__builtin_fmaf(-127.0f, q0, amax), y, q0);
+}
+
+// The reciprocal of d refined once, for q8_quotient.
+__device__ __forceinline__ float q8_recip(float d) {
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+}
+
+// RN(x / d) for d in [2^-100, 2^122) and |x / d| >= 1/2 (smaller quotients
+// round to code 0 whatever their last bit): the quotient x * r1 corrected twice.
+__device__ __forceinline__ float q8_quotient(float x, float d, float r1) {
+    float t = x * r1;
+    t = __builtin_fmaf(__builtin_fmaf(-d, t, x), r1, t);
+    return __builtin_fmaf(__builtin_fmaf(-d, t, x), r1, t);
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Q8Lane quantize_block8(f32x4 v) {
     // |x| compared as unsigned bit patterns: the same order for non-negative floats
@@ -96,23 +118,16 @@ __device__ __forceinline__ Q8Lane quantize_block8(f32x4 v) {
     a = max(a, (unsigned)dpp_i<kQuadSwap2>((int)a));
     a = max(a, (unsigned)dpp_i<kRowHalfMirror>((int)a));
     const float amax = __uint_as_float(a);
-    constexpr float y = 1.0f / 127.0f;
-    const float q0 = amax * y;
-    const float d = __builtin_fmaf(__builtin_fmaf(-127.0f, q0, amax), y, q0);
+    const float d = q8_scale(amax);
     const float dd = d == 0.0f ? 1.0f : d;   // all-zero block: +-0 / 1 gives code 0
     float q[4];
     if (__builtin_amdgcn_ballot_w64(dd < 0x1p-100f) != 0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(v[k] / dd, -127.0f, 127.0f);
     } else {
-        const float r0 = __builtin_amdgcn_rcpf(dd);
-        const float r1 = __builtin_fmaf(__builtin_fmaf(-dd, r0, 1.0f), r0, r0);
+        const float r1 = q8_recip(dd);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float t = v[k] * r1;
-            t = __builtin_fmaf(__builtin_fmaf(-dd, t, v[k]), r1, t);
-            q[k] = __builtin_fmaf(__builtin_fmaf(-dd, t, v[k]), r1, t);
-        }
+        for (int k = 0; k < 4; ++k) q[k] = q8_quotient(v[k], dd, r1);
     }
     unsigned b[4];
 #pragma unroll

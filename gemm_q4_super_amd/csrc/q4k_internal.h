@@ -108,6 +108,26 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
                           int64_t topk, const float *x, float *y, void *workspace,
                           hipStream_t stream);
 
+// INT8 KV cache and decode attention (head_dim 128).
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnMaxM = 8;           // query tokens per call
+constexpr int kAttnMaxGroup = 8;       // query heads per kv head
+constexpr int kAttnMaxKvHeads = 64;
+constexpr int kMaxAttnChunks = 32;     // position chunks per (kv head, query block)
+constexpr int kAttnTargetGroups = 256; // workgroups the chunking aims at
+constexpr size_t kAttnCounterBytes = 4096;   // one counter per (kv head, query block)
+
+size_t attn_workspace_bytes(int64_t M, int64_t n_head, int64_t n_kv);
+
+hipError_t launch_kv_store(const float *k, const float *v, int64_t M, int64_t n_kv, int64_t pos0,
+                           int64_t cap, int8_t *kc, float *ks, int8_t *vc, float *vs,
+                           hipStream_t stream);
+
+hipError_t launch_attn(const float *q, int64_t M, int64_t n_head, int64_t n_kv, const int8_t *kc,
+                       const float *ks, const int8_t *vc, const float *vs, int64_t cap,
+                       int64_t n_ctx, float scale, float *out, void *workspace,
+                       hipStream_t stream);
+
 // Measurement aids (not on the product path).
 hipError_t launch_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
                               hipStream_t stream);

@@ -296,6 +296,55 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
 int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
                       float *y, void *stream);
 
+/* INT8 KV cache (genie-ai-runtime's Path I, section 4 "Memory-first: making
+ * every byte count": one absmax scale per (layer, position, kv-head)).  One
+ * layer's cache is four device buffers, head-major so that the positions of a
+ * kv head are one contiguous stream:
+ *   k_codes, v_codes   int8 [n_kv][cap][head_dim]   (16-byte aligned)
+ *   k_scales, v_scales fp32 [n_kv][cap]             (4-byte aligned)
+ * Entry (h, t) is the vector x of head_dim values of position t and kv head h:
+ * scale = fl32(max|x| / 127), code = clamp(round-half-even(fl32(x / scale)),
+ * -127, 127); an all-zero vector has scale 0 and codes 0.  The value read back
+ * is scale * code.  head_dim is 128 (the only size built).
+ *
+ * q4k_kv_store: quantize M new positions into the cache:
+ *   k, v     device fp32 [M][n_kv][head_dim] (the k and v projection outputs
+ *            of M tokens, already position-encoded), 8-byte aligned.
+ *   entries (h, pos0 + m) for m < M, h < n_kv are written, nothing else.
+ *   1 <= M <= 4096, 1 <= n_kv <= 64, 0 <= pos0, pos0 + M <= cap <= 2^24.
+ * Codes and scales are exact (bit for bit the IEEE ones). */
+int q4k_kv_store(const float *k, const float *v, int64_t M, int64_t n_kv, int64_t head_dim,
+                 int64_t pos0, int64_t cap, int8_t *k_codes, float *k_scales,
+                 int8_t *v_codes, float *v_scales, void *stream);
+
+/* Workspace bytes q4k_attn_decode needs for M query tokens and n_head query
+ * heads over n_kv kv heads (independent of the context length). */
+size_t q4k_attn_workspace_bytes(int64_t M, int64_t n_head, int64_t n_kv);
+
+/* Decode attention over one layer's INT8 cache: M query tokens, the last M
+ * positions of a context of n_ctx (token m sits at position n_ctx - M + m and
+ * sees positions t < n_ctx - (M - 1 - m)); query head h reads kv head
+ * h / (n_head / n_kv) (grouped heads).  For each token m and head h:
+ *   s_t = scale * sum_i q[m][h][i] * k_scales[g][t] * k_codes[g][t][i],
+ *   p = softmax(s) over the visible t,
+ *   out[m][h][i] = sum_t p_t * v_scales[g][t] * v_codes[g][t][i].
+ *   q, out     device fp32 [M][n_head][head_dim], 16-byte aligned.
+ *   1 <= M <= 8, n_head % n_kv == 0, n_head / n_kv <= 8, n_kv <= 64,
+ *   M <= n_ctx <= cap <= 2^24, head_dim == 128.
+ *   workspace  device buffer of at least q4k_attn_workspace_bytes(M, n_head,
+ *              n_kv) bytes, 256-byte aligned; its first 4096 bytes are
+ *              counters that must be zero before the first call that uses it
+ *              (e.g. hipMemset once after allocation); every call leaves them
+ *              zero.  Calls sharing a workspace must not overlap.
+ * One kernel is enqueued.  The context is split into chunks across
+ * workgroups; the chunk partials are merged in chunk order, so the result bits
+ * do not depend on scheduling.  fp32 result within a relative error of 2e-3
+ * (absolute 1e-4 near zero) of the exact value of the formula above. */
+int q4k_attn_decode(const float *q, int64_t M, int64_t n_head, int64_t n_kv, int64_t head_dim,
+                    const int8_t *k_codes, const float *k_scales, const int8_t *v_codes,
+                    const float *v_scales, int64_t cap, int64_t n_ctx, float scale, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Measurement aids, not on the product path: the practical ceilings that
  * bench.py reports beside the decode launches.
  * q4k_ceiling_stream_read: `grid` workgroups of 256 threads read `bytes`

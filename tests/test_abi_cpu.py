@@ -265,3 +265,41 @@ def test_moe_ffn_argument_checks(L):
     assert call(ws=A + 16) == EALIGN
     assert call(x=A + 4) == EALIGN
     assert call(wd=A + 4) == EALIGN
+
+
+def test_attn_argument_checks(L):
+    ws = int(L.q4k_attn_workspace_bytes(1, 32, 8))
+    assert ws >= 4096
+    assert L.q4k_attn_workspace_bytes(1, 30, 8) == 0
+    f = L.q4k_attn_decode
+    ok = (A, 1, 32, 8, 128, A, A, A, A, 1024, 1024, 0.088, A, A, ws, None)
+
+    def call(**kw):
+        names = ("q", "M", "n_head", "n_kv", "hd", "kc", "ks", "vc", "vs", "cap", "n_ctx",
+                 "scale", "out", "ws", "wsb", "stream")
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*[a[n] for n in names])
+
+    assert call(q=None) == EINVAL
+    assert call(scale=float("nan")) == EINVAL
+    assert call(hd=64) == ESHAPE
+    assert call(M=0) == ESHAPE and call(M=9) == ESHAPE
+    assert call(n_head=30) == ESHAPE            # not a multiple of n_kv
+    assert call(n_head=72, n_kv=8) == ESHAPE    # groups of 9
+    assert call(n_ctx=0) == ESHAPE
+    assert call(M=4, n_ctx=3) == ESHAPE         # a token would see no position
+    assert call(n_ctx=1025) == ESHAPE           # beyond the capacity
+    assert call(q=A + 4) == EALIGN
+    assert call(kc=A + 8) == EALIGN
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=ws - 1) == EWORKSPACE
+    assert call(ws=A + 128) == EALIGN
+    s = L.q4k_kv_store
+    ok_s = (A, A, 1, 8, 128, 0, 16, A, A, A, A, None)
+    assert s(None, *ok_s[1:]) == EINVAL
+    assert s(*ok_s[:4], 64, *ok_s[5:]) == ESHAPE
+    assert s(*ok_s[:5], 16, *ok_s[6:]) == ESHAPE          # pos0 + M > cap
+    assert s(*ok_s[:5], -1, *ok_s[6:]) == ESHAPE
+    assert s(A + 4, *ok_s[1:]) == EALIGN
+    assert s(*ok_s[:7], A + 8, *ok_s[8:]) == EALIGN
