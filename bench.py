@@ -544,6 +544,157 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
     return out
 
 
+ATTN_HEADS, ATTN_KV_HEADS, HEAD_DIM = 32, 8, 128
+
+
+def attn_bytes(n_ctx, M=1):
+    """Algorithmic bytes of one attention launch: the codes and scales of K and
+    V over the context, the queries read and the outputs written."""
+    return ATTN_KV_HEADS * n_ctx * (2 * HEAD_DIM + 8) + 2 * 4 * M * ATTN_HEADS * HEAD_DIM
+
+
+def measure_attention(torch, q4k, qi, oracle, dec, ctxs=(1024, 16384), reps=5):
+    """INT8-KV decode attention (q4k_kv_store + q4k_attn_decode), Qwen3-4B heads.
+
+    For each context: one layer's cache written by q4k_kv_store from seeded fp32
+    K/V and checked against the oracle (all 32 heads, fresh seeded query), then
+    copied to as many layer caches as fill 600 MB (more than the 256 MB
+    Infinity Cache), and a graph of one attention launch per layer cache timed
+    between two events.  Then the decode token with attention at 1024
+    positions: per layer the q|k|v GEMV, the cache store of the new k, v at
+    position 1023, attention over 1024 positions into the o GEMV (with the
+    residual add), gate|up and down."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    scale = HEAD_DIM ** -0.5
+    out = {"heads": ATTN_HEADS, "kv_heads": ATTN_KV_HEADS, "head_dim": HEAD_DIM,
+           "kv_format": "int8 codes + fp32 absmax scale per (layer, position, kv head)"}
+    ws = q4k.attn_workspace(dev, q4k.q4k_attn_workspace_bytes(1, ATTN_HEADS, ATTN_KV_HEADS))
+    wsb = ws.numel()
+    cap_stream = torch.cuda.Stream()
+
+    def caches(nl, n_ctx):
+        return (torch.empty((nl, ATTN_KV_HEADS, n_ctx, HEAD_DIM), dtype=torch.int8, device=dev),
+                torch.empty((nl, ATTN_KV_HEADS, n_ctx), dtype=torch.float32, device=dev),
+                torch.empty((nl, ATTN_KV_HEADS, n_ctx, HEAD_DIM), dtype=torch.int8, device=dev),
+                torch.empty((nl, ATTN_KV_HEADS, n_ctx), dtype=torch.float32, device=dev))
+
+    def fill(c, n_ctx, seed):
+        kc, ks, vc, vs = c
+        k, v = qi.make_kv(n_ctx, ATTN_KV_HEADS, HEAD_DIM, seed)
+        dk, dv = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        for p0 in range(0, n_ctx, 4096):
+            m = min(4096, n_ctx - p0)
+            q4k.q4k_kv_store(dk[p0:p0 + m], dv[p0:p0 + m], p0, kc[0], ks[0], vc[0], vs[0])
+        for l in range(1, kc.shape[0]):
+            kc[l].copy_(kc[0]); ks[l].copy_(ks[0]); vc[l].copy_(vc[0]); vs[l].copy_(vs[0])
+        torch.cuda.synchronize()
+        return k, v
+
+    def attn_call(c, l, n_ctx, q, o, s):
+        kc, ks, vc, vs = c
+        if L.q4k_attn_decode(q.data_ptr(), 1, ATTN_HEADS, ATTN_KV_HEADS, HEAD_DIM,
+                             kc[l].data_ptr(), ks[l].data_ptr(), vc[l].data_ptr(),
+                             vs[l].data_ptr(), n_ctx, n_ctx, scale, o.data_ptr(),
+                             ws.data_ptr(), wsb, s):
+            raise RuntimeError("q4k_attn_decode launch failed")
+
+    legs = {}
+    for n_ctx in ctxs:
+        per = attn_bytes(n_ctx)
+        nl = max(LAYERS, int(np.ceil(600e6 / per)))
+        c = caches(nl, n_ctx)
+        k, v = fill(c, n_ctx, qi.kv_seed(0))
+        q = qi.make_query(1, ATTN_HEADS, HEAD_DIM, qi.query_seed(0))
+        dq = torch.from_numpy(q).to(dev)
+        got = q4k.q4k_attn_decode(dq, c[0][0], c[1][0], c[2][0], c[3][0], n_ctx, scale)
+        torch.cuda.synchronize()
+        kq, ksq = oracle.kv_quantize(k)
+        vq, vsq = oracle.kv_quantize(v)
+        ref = oracle.attn_int8kv(q, kq.transpose(1, 0, 2), ksq.T, vq.transpose(1, 0, 2), vsq.T,
+                                 n_ctx, scale, parallel=True)
+        g64 = got.cpu().numpy().astype(np.float64)
+        err = np.abs(g64 - ref)
+        if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+            raise SystemExit("parity: attention at %d positions outside tolerance" % n_ctx)
+        qs = torch.from_numpy(qi.make_query(nl, ATTN_HEADS, HEAD_DIM, qi.query_seed(1))).to(dev)
+        os_ = torch.empty_like(qs)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            s = torch.cuda.current_stream().cuda_stream
+            for l in range(nl):
+                attn_call(c, l, n_ctx, qs[l], os_[l], s)
+        torch.cuda.synchronize()
+        g.replay()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3 / nl)
+        t = float(np.median(times))
+        legs[str(n_ctx)] = {
+            "n_ctx": n_ctx, "layer_caches": nl, "bytes_per_launch": per,
+            "us_per_launch": round(t * 1e6, 3), "us_dist": dist(np.array(times) * 1e6),
+            "GBps": round(per / t / 1e9, 1), "hbm_frac": round(per / t / 1e9 / HBM_PEAK_GBS, 4),
+            "us_per_token_36_layers": round(36 * t * 1e6, 2),
+            "spot_check": {"outputs": int(ref.size),
+                           "max_rel_err": float((err / np.maximum(np.abs(ref), 0.05)).max())}}
+        del c, qs, os_, g
+        torch.cuda.empty_cache()
+    out["attention_only"] = legs
+
+    # Decode token with attention over 1024 positions.
+    n_ctx = 1024
+    c = caches(LAYERS, n_ctx)
+    fill(c, n_ctx, qi.kv_seed(0))
+    att = torch.empty((1, ATTN_HEADS * HEAD_DIM), dtype=torch.float32, device=dev)
+    q_, k_, v_ = dec.yp[0], dec.yp[1], dec.yp[2]
+    nproj = len(dec.shapes)
+
+    def token(l, s):
+        dec.batch(4 * l, s)                                   # q | k | v
+        kc, ks, vc, vs = c
+        if L.q4k_kv_store(k_.data_ptr(), v_.data_ptr(), 1, ATTN_KV_HEADS, HEAD_DIM, n_ctx - 1,
+                          n_ctx, kc[l].data_ptr(), ks[l].data_ptr(), vc[l].data_ptr(),
+                          vs[l].data_ptr(), s):
+            raise RuntimeError("q4k_kv_store launch failed")
+        attn_call(c, l, n_ctx, q_, att, s)
+        wt, N, K = dec.weights[l * nproj + 3]                 # o, from the attention output
+        if L.q4k_quantize_gemv_residual(wt.data_ptr(), N, K, att.data_ptr(), 1,
+                                        dec.resid.data_ptr(), dec.resid.data_ptr(), s):
+            raise RuntimeError("q4k_quantize_gemv_residual launch failed")
+        dec.batch(4 * l + 2, s)                               # gate | up
+        dec.batch_residual(4 * l + 3, s)                      # down (+ residual)
+
+    g = dec.graph(token, range(LAYERS), cap_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    times = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.median(times))
+    tok_bytes = dec.bytes_fused + LAYERS * attn_bytes(n_ctx)
+    out["decode_token_with_attention"] = {
+        "n_ctx": n_ctx, "launches_per_token": 6 * LAYERS,
+        "ms_per_token": round(t * 1e3, 4), "ms_dist": dist_ms(np.array(times)),
+        "tok_per_s": round(1.0 / t, 1), "bytes_per_token": int(tok_bytes),
+        "GBps": round(tok_bytes / t / 1e9, 1),
+        "note": "per layer: q|k|v GEMV, kv store of the new k and v, attention over 1024 "
+                "positions, o GEMV on the attention output with the residual add, gate|up, "
+                "down with the residual add (norms and rotary embedding are not in scope)"}
+    del c, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_small_batch(torch, dec, oracle, steps=5):
     """Small-batch verification GEMV: M = 2, 4, 8 seeded N(0,1) activation rows
     against the 36-layer sweep's weights, through q4k_gemv and through q4k_gemm.
@@ -1141,6 +1292,7 @@ def main():
     n_launch = dec.n_batch
     small = None if args.no_extra else measure_small_batch(torch, dec, oracle)
     ceilings = None if args.no_extra else measure_ceilings(torch, q4k, dec)
+    attention = None if args.no_extra else measure_attention(torch, q4k, qi, oracle, dec)
     del g_batch, dec
     torch.cuda.empty_cache()
     prefill = None if args.no_prefill else measure_prefill(torch, q4k, qi, oracle,
@@ -1193,6 +1345,7 @@ def main():
         "parity": parity,
         "prefill_gemm": prefill,
         "small_batch_gemv": small,
+        "int8_kv_attention": attention,
         "moe_layer": moe,
         "q6k_decode_gemv": q6k,
         "decode_gemv_one_large_launch": large,

@@ -140,6 +140,7 @@ struct Round {
 
 __global__ __launch_bounds__(64 * kWaves) void attn_kernel(const AttnArgs a) {
     __shared__ float red[kWaves][4][kQV][kPartStride];   // [wave][lane row][r][...]
+    __shared__ float fac[kQV][kWaves * 4], fac_max[kQV];
     __shared__ unsigned last_flag;
     const int units = a.n_kv * a.nqb;
     const int unit = blockIdx.x % units;      // neighbouring workgroups: different units
@@ -324,34 +325,52 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(const AttnArgs a) {
     }
     __syncthreads();
 
-    // Merge the workgroup's 4 partials per wave: thread (r, dim c).
-    static_assert(kWaves * 64 == kQV * kHD, "one thread per output of the query block");
-    const int r = threadIdx.x >> 7, c = threadIdx.x & (kHD - 1);
-    float mc = -INFINITY;
+    // Merge the workgroup's partials (4 per wave).  The rescale factors
+    // 2^(m_e - max) are formed once per (query vector, partial) into LDS; then
+    // thread (r, dims c0..c0+kDims-1) sums its outputs.
+    constexpr int kE = kWaves * 4;
+    constexpr int kDims = kQV * kHD / (64 * kWaves);   // consecutive dims per thread
+    static_assert(kDims == 1 || kDims == 2, "threads per query block");
+    if (threadIdx.x < kQV * kE) {
+        const int fr = threadIdx.x / kE, fe = threadIdx.x % kE;
+        float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < kWaves * 4; ++e) mc = fmaxf(mc, red[e >> 2][e & 3][r][kHD]);
-    float o = 0.0f, lc = 0.0f;
+        for (int e = 0; e < kE; ++e) mx = fmaxf(mx, red[e >> 2][e & 3][fr][kHD]);
+        fac[fr][fe] = rescale(red[fe >> 2][fe & 3][fr][kHD], mx);
+        if (fe == 0) fac_max[fr] = mx;
+    }
+    __syncthreads();
+    const int r = threadIdx.x / (kHD / kDims), c0 = (threadIdx.x % (kHD / kDims)) * kDims;
+    const float mc = fac_max[r];
+    float o[kDims], lc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < kWaves * 4; ++e) {
+    for (int d = 0; d < kDims; ++d) o[d] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
         const float *pe = red[e >> 2][e & 3][r];
-        const float f = rescale(pe[kHD], mc);
-        o = fmaf(f, pe[c], o);
+        const float f = fac[r][e];
+#pragma unroll
+        for (int d = 0; d < kDims; ++d) o[d] = fmaf(f, pe[c0 + d], o[d]);
         lc = fmaf(f, pe[kHD + 1], lc);
     }
     const int v = qb * kQV + r;
     const bool valid = v < GM;
-    float *dst = valid ? a.out + ((int64_t)(v / a.G) * n_head + kvh * a.G + v % a.G) * kHD + c
+    float *dst = valid ? a.out + ((int64_t)(v / a.G) * n_head + kvh * a.G + v % a.G) * kHD + c0
                        : nullptr;
     if (a.n_chunks == 1) {
-        if (valid) *dst = o / lc;
+        if (valid)
+#pragma unroll
+            for (int d = 0; d < kDims; ++d) dst[d] = o[d] / lc;
         return;
     }
 
     // Partial of this chunk, through agent-coherent stores; the counter is
     // bumped once every store of the workgroup has completed.
     float *pp = a.part + (((int64_t)unit * a.n_chunks + chunk) * kQV + r) * kPartStride;
-    __hip_atomic_store(pp + c, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c == 0)
+#pragma unroll
+    for (int d = 0; d < kDims; ++d)
+        __hip_atomic_store(pp + c0 + d, o[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c0 == 0)
         __hip_atomic_store(reinterpret_cast<unsigned long long *>(pp + kHD),
                            (unsigned long long)__float_as_uint(mc) |
                                ((unsigned long long)__float_as_uint(lc) << 32),
@@ -365,32 +384,38 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(const AttnArgs a) {
     if (!last_flag) return;
 
     // The last workgroup of the unit merges the chunks in chunk order; every
-    // thread loads every chunk's (max, sum) and its dim before using any.
+    // thread loads every chunk's (max, sum) and its dims before using any.
     const float *pu = a.part + (int64_t)unit * a.n_chunks * kQV * kPartStride + r * kPartStride;
     unsigned long long ml[kMaxAttnChunks];
-    float od[kMaxAttnChunks];
+    float od[kMaxAttnChunks][kDims];
 #pragma unroll
     for (int k = 0; k < kMaxAttnChunks; ++k)
         if (k < a.n_chunks) {
             const float *pc = pu + (int64_t)k * kQV * kPartStride;
             ml[k] = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(pc + kHD),
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            od[k] = __hip_atomic_load(pc + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int d = 0; d < kDims; ++d)
+                od[k][d] = __hip_atomic_load(pc + c0 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     float mall = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kMaxAttnChunks; ++k)
         if (k < a.n_chunks) mall = fmaxf(mall, __uint_as_float((unsigned)ml[k]));
     float lsum = 0.0f;
-    o = 0.0f;
+#pragma unroll
+    for (int d = 0; d < kDims; ++d) o[d] = 0.0f;
 #pragma unroll
     for (int k = 0; k < kMaxAttnChunks; ++k)
         if (k < a.n_chunks) {
             const float f = rescale(__uint_as_float((unsigned)ml[k]), mall);
             lsum = fmaf(f, __uint_as_float((unsigned)(ml[k] >> 32)), lsum);
-            o = fmaf(f, od[k], o);
+#pragma unroll
+            for (int d = 0; d < kDims; ++d) o[d] = fmaf(f, od[k][d], o[d]);
         }
-    if (valid) *dst = o / lsum;
+    if (valid)
+#pragma unroll
+        for (int d = 0; d < kDims; ++d) dst[d] = o[d] / lsum;
     if (threadIdx.x == 0) __hip_atomic_store(a.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
