@@ -201,7 +201,7 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
                        hipStream_t stream) {
     if (gemv_mfma_preferred(N, K, M, scales, sums))
         return launch_gemv_mfma(w, N, K, codes, scales, sums, M, y, stream);
-    if (M * K <= kFusedMaxMK) {
+    if (stream_fits(M, K)) {
         const GemvProblem p = {w, nullptr, y, N};
         const stream::Prepared Q = {codes, scales, sums};
         return stream::run<false>(&p, 1, K, M, Q, stream);

@@ -58,7 +58,7 @@ int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                       float *y, void *stream) {
     if (!w || !x || !y) return Q4K_EINVAL;
     if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1 || M > 8) return Q4K_ESHAPE;
-    if (N > kMaxDim || K > kMaxDim || M * K > q4k::kFusedMaxMK) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || !q4k::stream_fits(M, K)) return Q4K_ESHAPE;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_EALIGN;
     return from_hip(q4k::launch_quantize_gemv(static_cast<const uint8_t *>(w), N, K, x, M, y,
                                               static_cast<hipStream_t>(stream)));
@@ -68,7 +68,7 @@ int q4k_quantize_gemv_residual(const void *w, int64_t N, int64_t K, const float 
                                int64_t M, const float *residual, float *y, void *stream) {
     if (!w || !x || !y || !residual) return Q4K_EINVAL;
     if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1 || M > 8) return Q4K_ESHAPE;
-    if (N > kMaxDim || K > kMaxDim || M * K > q4k::kFusedMaxMK) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || !q4k::stream_fits(M, K)) return Q4K_ESHAPE;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(residual, 4))
         return Q4K_EALIGN;
     // In place (residual == y) or disjoint: a partial overlap would read
@@ -86,7 +86,7 @@ int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t
     if (!problems) return Q4K_EINVAL;
     if (count < 1 || count > q4k::kMaxGemvBatch) return Q4K_ESHAPE;
     if (K < q4k::kQK || K % q4k::kQK != 0 || K > kMaxDim || M < 1 || M > 8 ||
-        M * K > q4k::kFusedMaxMK)
+        !q4k::stream_fits(M, K))
         return Q4K_ESHAPE;
     for (int i = 0; i < count; ++i) {
         const q4k_gemv_problem &p = problems[i];
@@ -229,7 +229,7 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes, const flo
              int64_t M, float *y, void *stream) {
     if (!w || !codes || !scales || !y) return Q4K_EINVAL;
     if (N < 1 || N > kMaxDim || K < q4k::kQK || K % q4k::kQK != 0 || K > q4k::kQ6MaxK ||
-        M < 1 || M > 8 || M * K > q4k::kFusedMaxMK)
+        M < 1 || M > 8 || !q4k::q6k_fits(M, K))
         return Q4K_ESHAPE;
     if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 4))
         return Q4K_EALIGN;
@@ -241,7 +241,7 @@ int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                       void *stream) {
     if (!w || !x || !y) return Q4K_EINVAL;
     if (N < 1 || N > kMaxDim || K < q4k::kQK || K % q4k::kQK != 0 || K > q4k::kQ6MaxK ||
-        M < 1 || M > 8 || M * K > q4k::kFusedMaxMK)
+        M < 1 || M > 8 || !q4k::q6k_fits(M, K))
         return Q4K_ESHAPE;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4K_EALIGN;
     return from_hip(q4k::launch_q6k_quantize_gemv(static_cast<const uint8_t *>(w), N, K, x, M, y,

@@ -30,6 +30,22 @@ inline int cu_count() {
     return v;
 }
 
+// LDS bytes one workgroup may allocate on the current device (cached per
+// device; 65536 if unknown).
+inline size_t lds_limit() {
+    static std::atomic<int> n[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    int v = n[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess ||
+            v <= 0)
+            v = 65536;
+        n[dev].store(v, std::memory_order_relaxed);
+    }
+    return (size_t)v;
+}
 
 // Routed-expert limits (the route grouping runs in one workgroup's LDS).
 constexpr int kMoeMaxPairs = 4096;     // T * topk
@@ -53,15 +69,17 @@ hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t
                             hipStream_t stream);
 
 // Q6_K GEMV on prepared Q8 rows or fp32 rows quantized inside (M <= 8,
-// M*K <= kFusedMaxMK, K <= kQ6MaxK).
+// K <= kQ6MaxK, the staged rows within one workgroup's LDS: q6k_fits).
 constexpr int64_t kQ6MaxK = 48 * 256;
+bool q6k_fits(int64_t M, int64_t K);
 hipError_t launch_q6k_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                            const float *scales, int64_t M, float *y, hipStream_t stream);
 hipError_t launch_q6k_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                     int64_t M, float *y, hipStream_t stream);
 
-// Fused Q8 quantization + GEMV on fp32 activations (M <= 8, M*K <= kFusedMaxMK).
-constexpr int64_t kFusedMaxMK = 32768;
+// Streaming GEMV (fused Q8 quantization or prepared rows): M <= 8 rows whose
+// Q8 codes, scales and sums fit one workgroup's LDS with the smallest row block.
+bool stream_fits(int64_t M, int64_t K);
 hipError_t launch_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                 int64_t M, float *y, hipStream_t stream);
 hipError_t launch_quantize_gemv_residual(const uint8_t *w, int64_t N, int64_t K, const float *x,

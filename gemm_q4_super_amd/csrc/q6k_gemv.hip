@@ -1,11 +1,12 @@
 // Q6_K decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T with W in Q6_K,
-// M = 1..8, M*K <= 32768, on prepared Q8 rows (q6k_gemv) or on fp32 rows that
+// M = 1..8 (the staged Q8 rows within one workgroup's LDS, e.g. M = 8 at
+// K = 9728 in the 160 KB of a gfx950 workgroup), on prepared Q8 rows (q6k_gemv) or on fp32 rows that
 // each workgroup quantizes with q4k_quantize_act's arithmetic
 // (q6k_quantize_gemv: same codes, so the two give the same bits).
 //
 // Q6_K (public GGUF layout; real Q4_K_M files keep some tensors in it, and the
-// decode kernels of genie's "Path G" -- "genie-ai-runtime ...", section 3 --
-// are Q6_K ones): 256 weights of one row in 210 bytes, ql[128] (low 4 bits of
+// decode kernels of genie's "Path G" -- "genie-ai-runtime ...", section 6,
+// "The negatives I kept" -- are Q6_K ones): 256 weights of one row in 210 bytes, ql[128] (low 4 bits of
 // the 6-bit quants), qh[64] (high 2 bits), int8 sc[16] (one per 16 weights),
 // fp16 d; w = d*sc[e/16]*(q[e] - 32).  Element e = 128h + 32t + l keeps its low
 // bits in ql[64h + 32(t%2) + l] (low nibble for t < 2, high for t >= 2) and its
@@ -293,15 +294,14 @@ hipError_t launch_m(const uint8_t *w, int64_t N, int nsb, const Act &a, float *y
             if (v >= 2) return launch_mcv<M, 2, 2>(w, N, nsb, a, y, stream);
         return launch_mcv<M, 2, 1>(w, N, nsb, a, y, stream);
     }
-    // K of 33..48 super-blocks: M * K <= 32768 keeps M <= 3 here
-    if constexpr (M <= 3) return launch_mcv<M, 3, 1>(w, N, nsb, a, y, stream);
-    return hipErrorInvalidValue;
+    // K of 33..48 super-blocks: 3 columns per wave, one row group
+    return launch_mcv<M, 3, 1>(w, N, nsb, a, y, stream);
 }
 
 hipError_t run_q6k(const uint8_t *w, int64_t N, int64_t K, const Act &a, int64_t M, float *y,
                    hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    if (K > kQ6MaxK || M * K > kFusedMaxMK) return hipErrorInvalidValue;
+    if (!q6k_fits(M, K)) return hipErrorInvalidValue;
     switch (M) {
     case 1: return launch_m<1>(w, N, nsb, a, y, stream);
     case 2: return launch_m<2>(w, N, nsb, a, y, stream);
@@ -316,6 +316,14 @@ hipError_t run_q6k(const uint8_t *w, int64_t N, int64_t K, const Act &a, int64_t
 }
 
 }  // namespace
+
+// The staged rows of every column (kQ6Stage bytes per column and row) and the
+// cross-wave sums (at most 4 row groups of 8) fit one workgroup's LDS.
+bool q6k_fits(int64_t M, int64_t K) {
+    if (M < 1 || M > 8 || K < kQK || K % kQK != 0 || K > kQ6MaxK) return false;
+    const size_t red = sizeof(float) * kQ6Waves * 8 * 4 * (size_t)M;
+    return (size_t)(K / kQK) * (size_t)M * kQ6Stage + red <= lds_limit();
+}
 
 hipError_t launch_q6k_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                            const float *scales, int64_t M, float *y, hipStream_t stream) {

@@ -1,5 +1,6 @@
 // Streaming Q4_K x Q8 GEMV for decode and small batches (M = 1..8 activation
-// rows, M*K <= 32768): y_i = Q8(x_i) * W_i^T for up to 8 products with the
+// rows whose Q8 form fits one workgroup's LDS, e.g. M = 8 at K = 9728 in the
+// 160 KB of a gfx950 workgroup): y_i = Q8(x_i) * W_i^T for up to 8 products with the
 // same K and M in one launch.  Included by qgemv.hip (fp32 activations,
 // quantized inside the kernel) and gemv.hip (prepared Q8 rows); both run the
 // same kernel body and the same partition, so they are bit-identical.
@@ -347,7 +348,7 @@ inline void consider(Plan &best, const GemvProblem *probs, int count, int nsb, i
     const int waves = (nsb + S * cpw - 1) / (S * cpw);
     if (waves > kWaves) return;
     const size_t lds = q8_bytes(M, nsb) + col_bytes(M, RB, nsb);
-    if (lds > 64 * 1024) return;
+    if (lds > lds_limit()) return;
     const int cus = cu_count();
     for (int c = 0; c < count; ++c) {
         const int64_t C = (probs[c].N + RB - 1) / RB * RB;

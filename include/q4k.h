@@ -97,8 +97,12 @@ int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
  * activations x (device, [M][K], 16-byte aligned).  Each workgroup quantizes
  * the Q8 blocks it needs with the same arithmetic as q4k_quantize_act (codes
  * bit-identical), so the result equals q4k_quantize_act followed by q4k_gemv,
- * bit for bit, with one launch instead of two.  Limits: 1 <= M <= 8 and
- * M*K <= 32768 (the Q8 blocks live in LDS); other arguments as for q4k_gemv. */
+ * bit for bit, with one launch instead of two.  Limits: 1 <= M <= 8, and the
+ * Q8 form of the M rows lives in one workgroup's LDS: M*(K/256)*328 bytes at
+ * most the device's LDS per workgroup (163840 on MI355X: K up to 15872 at
+ * M = 8, 31744 at M = 4, e.g. the 9728-wide down projection at any M), and
+ * K/256 <= 192 (M <= 4), 128 (M <= 6), 64 (M <= 8).  Other arguments as for
+ * q4k_gemv. */
 int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
                       int64_t M, float *y, void *stream);
 
@@ -277,8 +281,10 @@ size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, i
  * quant q), qh[64] (high 2 bits), int8 sc[16] (one per 16 weights), fp16 d
  * (public GGUF layout) -- and w = d*sc[e/16]*(q[e] - 32).
  *   w       device Q6_K bytes, N rows x (K/256)*210 bytes, 16-byte aligned.
- *   N >= 1, K % 256 == 0, 256 <= K <= 12288, 1 <= M <= 8, M*K <= 32768 (the
- *           Q8 rows are staged in LDS).
+ *   N >= 1, K % 256 == 0, 256 <= K <= 12288, 1 <= M <= 8, and the staged Q8
+ *           rows fit one workgroup's LDS: (K/256)*M*416 + 2048*M bytes at most
+ *           the device's LDS per workgroup (163840 on MI355X: any K up to
+ *           11264 at M = 8, e.g. the 9728-wide down projection).
  *   codes   device int8 [M][K] (16-byte aligned); scales fp32 [M][K/32]
  *           (4-byte aligned) -- as written by q4k_quantize_act (its block
  *           sums are not needed).

@@ -79,7 +79,7 @@ def test_q6k_gemv_argument_checks(L):
     assert f(A, 16, 512, A, A, 0, A, None) == ESHAPE
     assert f(A, 16, 512, A, A, 9, A, None) == ESHAPE
     assert f(A, 16, 12544, A, A, 1, A, None) == ESHAPE    # K beyond 48 super-blocks
-    assert f(A, 16, 9728, A, A, 4, A, None) == ESHAPE     # M*K beyond the LDS limit
+    assert f(A, 16, 12288, A, A, 8, A, None) == ESHAPE    # staged rows beyond any LDS
     assert f(A + 8, 16, 512, A, A, 1, A, None) == EALIGN
     assert f(A, 16, 512, A + 8, A, 1, A, None) == EALIGN
     assert f(A, 16, 512, A, A + 2, 1, A, None) == EALIGN
@@ -93,7 +93,7 @@ def test_q6k_quantize_gemv_argument_checks(L):
     assert f(A, 16, 512, A, 1, None, None) == EINVAL
     assert f(A, 16, 500, A, 1, A, None) == ESHAPE
     assert f(A, 16, 512, A, 9, A, None) == ESHAPE
-    assert f(A, 16, 9728, A, 4, A, None) == ESHAPE
+    assert f(A, 16, 12288, A, 8, A, None) == ESHAPE
     assert f(A, 0, 512, A, 1, A, None) == ESHAPE
     assert f(A + 4, 16, 512, A, 1, A, None) == EALIGN
     assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
@@ -105,7 +105,8 @@ def test_quantize_gemv_argument_checks(L):
     assert f(A, 16, 512, None, 1, A, None) == EINVAL
     assert f(A, 16, 500, A, 1, A, None) == ESHAPE
     assert f(A, 16, 512, A, 9, A, None) == ESHAPE
-    assert f(A, 16, 9728, A, 4, A, None) == ESHAPE      # M*K beyond the LDS limit
+    assert f(A, 16, 16384, A, 8, A, None) == ESHAPE     # staged rows beyond any LDS
+    assert f(A, 16, 65536, A, 1, A, None) == ESHAPE     # more columns than 16 waves take
     assert f(A, 0, 512, A, 1, A, None) == ESHAPE
     assert f(A + 4, 16, 512, A, 1, A, None) == EALIGN
     assert f(A, 16, 512, A + 4, 1, A, None) == EALIGN
@@ -119,7 +120,7 @@ def test_quantize_gemv_residual_argument_checks(L):
     assert f(A, 16, 512, A, 1, B, None, None) == EINVAL
     assert f(A, 16, 500, A, 1, B, A, None) == ESHAPE
     assert f(A, 16, 512, A, 9, B, A, None) == ESHAPE
-    assert f(A, 16, 9728, A, 4, B, A, None) == ESHAPE   # M*K beyond the LDS limit
+    assert f(A, 16, 16384, A, 8, B, A, None) == ESHAPE  # staged rows beyond any LDS
     assert f(A, 16, 512, A, 1, B + 2, A, None) == EALIGN
     assert f(A + 4, 16, 512, A, 1, B, A, None) == EALIGN
     # residual partly overlapping y (not the same buffer) is rejected
@@ -140,7 +141,7 @@ def test_quantize_gemv_batch_argument_checks(L):
     assert call([good] * 9) == ESHAPE
     assert call([good], K=500) == ESHAPE
     assert call([good], M=9) == ESHAPE
-    assert call([good], K=9728, M=4) == ESHAPE
+    assert call([good], K=16384, M=8) == ESHAPE
     assert call([good, (A, A, A, 0)]) == ESHAPE
     assert call([good, (None, A, A, 16)]) == EINVAL
     assert call([good, (A, A, None, 16)]) == EINVAL

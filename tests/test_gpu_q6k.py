@@ -39,8 +39,6 @@ def _q6k(q4k, w, N, K, x, oracle_lib, rows=None):
                                  (257, 1280), (1000, 2560), (65, 3328)])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
 def test_q6k_gemv_shapes_and_tails(q4k, oracle_lib, N, K, M):
-    if M * K > 32768:
-        pytest.skip("M*K beyond the documented limit")
     w, _ = qi.make_q6k(N, K, 500 + N + K)
     x = qi.make_act(M, K, 600 + M + K)
     x[0, :32] = 0.0                      # an all-zero activation block
@@ -96,9 +94,7 @@ def test_q6k_gemv_qwen3_4b_shapes_sampled(q4k, oracle_lib, proj):
     name, K, N = qi.QWEN3_4B_LAYER[proj]
     w = qi.make_q6k_bytes(N, K, 730 + proj)
     rows = np.unique(np.r_[0, 1, N - 1, np.random.default_rng(proj).integers(0, N, 60)])
-    for M in (1, 3):
-        if M * K > 32768:
-            continue
+    for M in (1, 3, 8):
         x = qi.make_act(M, K, 740 + proj + M)
         y, ref = _q6k(q4k, w, N, K, x, oracle_lib, rows=rows)
         assert_close(y, ref, "q6k %s M=%d" % (name, M))
@@ -120,7 +116,8 @@ def test_q6k_gemv_writes_only_its_output(q4k, oracle_lib):
 
 @pytest.mark.parametrize("N,K,M", [(1, 256, 1), (9, 768, 1), (33, 2560, 1), (100, 4096, 2),
                                    (257, 1280, 3), (65, 3328, 5), (40, 4096, 8), (2560, 9728, 3),
-                                   (4096, 2560, 1)])
+                                   (4096, 2560, 1), (2560, 9728, 4), (2560, 9728, 8),
+                                   (300, 11264, 8), (200, 12288, 7)])
 def test_q6k_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     """One launch (quantize inside) equals q4k_quantize_act followed by
     q6k_gemv bit for bit, and the oracle within tolerance."""

@@ -249,7 +249,11 @@ def test_gemv_qwen3_4b_shapes_sampled(q4k, oracle_lib, proj):
                                    (64, 32768, 1), (16, 256, 2), (17, 2560, 3), (1000, 2560, 4),
                                    (33, 1024, 6), (129, 3840, 7), (4097, 4096, 8),
                                    (2560, 4096, 8), (1024, 2560, 8), (2048, 512, 4),
-                                   (4096, 768, 3), (2049, 1280, 5), (2500, 3328, 6)])
+                                   (4096, 768, 3), (2049, 1280, 5), (2500, 3328, 6),
+                                   # the down projection's width at small batches, and the
+                                   # widest rows the LDS takes per M
+                                   (2560, 9728, 4), (2560, 9728, 8), (1000, 12288, 6),
+                                   (300, 15872, 8), (500, 31744, 4), (64, 49152, 1)])
 def test_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     """One launch (quantize inside the GEMV) equals q4k_quantize_act followed
     by q4k_gemv bit for bit, and the oracle within tolerance.  For M = 2..8 the
@@ -309,6 +313,7 @@ _BATCHES = {
     "eight_m2_t2": (768, 2, [1000, 1000, 1000, 1000, 70, 1, 33, 2]),
     "m8": (4096, 8, [300, 257]),
     "single": (9728, 1, [2560]),
+    "down_m8": (9728, 8, [2560, 1000]),
 }
 
 

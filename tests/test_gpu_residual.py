@@ -37,7 +37,8 @@ def _check_oracle(y, r, w, N, K, x, oracle_lib, rows, what):
 @pytest.mark.parametrize("N,K,M", [(1, 256, 1), (37, 512, 2), (1000, 2560, 1), (2560, 4096, 1),
                                    (2560, 9728, 1), (2560, 9728, 3), (4096, 2560, 1),
                                    (129, 3840, 7), (2049, 1280, 5), (40000, 2560, 1),
-                                   (64, 32768, 1), (17, 2560, 8), (4096, 4096, 8)])
+                                   (64, 32768, 1), (17, 2560, 8), (4096, 4096, 8),
+                                   (2560, 9728, 4), (2560, 9728, 8)])
 def test_residual_equals_gemv_plus_residual(q4k, oracle_lib, N, K, M):
     """Out of place: bits of fp32(residual + q4k_quantize_gemv), and the oracle."""
     import torch
