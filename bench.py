@@ -1002,9 +1002,9 @@ def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
               torch.empty((P, F // 32), dtype=torch.float32, device=dev),
               torch.empty((P, F // 32), dtype=torch.int32, device=dev))
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
-        ws_gu = torch.empty(q4k.q4k_moe_workspace_bytes(T, TOPK, E, F), dtype=torch.uint8,
+        ws_gu = torch.zeros(q4k.q4k_moe_workspace_bytes(T, TOPK, E, F), dtype=torch.uint8,
                             device=dev)
-        ws_dn = torch.empty(q4k.q4k_moe_workspace_bytes(T, TOPK, E, H), dtype=torch.uint8,
+        ws_dn = torch.zeros(q4k.q4k_moe_workspace_bytes(T, TOPK, E, H), dtype=torch.uint8,
                             device=dev)
 
         def layer(l, s):
@@ -1025,7 +1025,7 @@ def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
             if st:
                 raise RuntimeError("launch failed")
 
-        ws_ffn = torch.empty(q4k.q4k_moe_ffn_workspace_bytes(T, TOPK, E, H, F),
+        ws_ffn = torch.zeros(q4k.q4k_moe_ffn_workspace_bytes(T, TOPK, E, H, F),
                              dtype=torch.uint8, device=dev)
         y2 = torch.empty_like(y)
 
@@ -1043,13 +1043,16 @@ def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
                 for l in range(layers):
                     fn(l, s)
             gr.replay()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(steps):
-                gr.replay()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e-3 / (steps * layers)
+            per = []
+            for _ in range(5):   # median of 5 timings of `steps` replays
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(steps):
+                    gr.replay()
+                b.record()
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) * 1e-3 / (steps * layers))
+            return float(np.median(per))
 
         # spot check before timing: layer 0 through q4k_moe_ffn against the
         # oracle layer (codes of h may differ by one next to a rounding
@@ -1076,7 +1079,7 @@ def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
                            "distinct_experts": float(distinct),
                            "expert_MB_per_layer": round(nbytes / 1e6, 2),
                            "GBps": round(nbytes / t / 1e9, 1),
-                           "path": "q4k_moe_ffn (%d launches)" % (3 if T <= 2 else 5),
+                           "path": "q4k_moe_ffn (%d launches)" % (2 if T <= 2 else 4),
                            "six_call_chain_us_per_layer": round(t_chain * 1e6, 2),
                            "fused_equals_chain_bitwise": same, "oracle_spot_check": spot}
     del W

@@ -323,7 +323,7 @@ def q4k_moe_gemv(w, n_experts, expert_stride, N, K, ids, route_w, codes, scales,
     T, topk = ids.shape
     if workspace is None:
         nbytes = q4k_moe_workspace_bytes(T, topk, n_experts, N)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
     if y is None:
         rows = T if route_w is not None else T * topk
         y = torch.empty((rows, N), dtype=torch.float32, device=codes.device)
@@ -347,7 +347,7 @@ def q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H,
     T, topk = ids.shape
     if workspace is None:
         nbytes = q4k_moe_ffn_workspace_bytes(T, topk, n_experts, H, F)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=x.device)
     _check(lib().q4k_moe_ffn(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n_experts, stride_gate_up,

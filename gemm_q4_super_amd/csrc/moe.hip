@@ -20,9 +20,11 @@
 //  * SwiGLU(g, u) of fp32 rows, quantized in the kernel (the FFN's down),
 // all through the same quantizer and SwiGLU arithmetic as q4k_quantize_act,
 // so the fused layer's codes equal the unfused chain's bit for bit.
-// reduce_kernel (with routing weights): y[t] = sum over slots s in order
-// 0..topk-1 of route_w[t][s] * z[t*topk+s] -- fixed order, no float atomics,
-// bit-reproducible.
+// With routing weights the same launch also forms y[t] = sum over slots s in
+// order 0..topk-1 of route_w[t][s] * z[t*topk+s]: the per-slot products z go
+// to the workspace through agent-coherent stores, and the last workgroup to
+// finish a row block (a counter per row block) adds them up for that block --
+// fixed order, no float atomics, bit-reproducible, no separate launch.
 #include <algorithm>
 
 #include "q4k_device.h"
@@ -52,6 +54,16 @@ struct MoeArgs {
     const int32_t *sums;
     const float *xa, *xb;      // ACT_F32: x [.][K]; ACT_SWIGLU: g, u [P][K]
     const int32_t *ids;
+    int direct;                // one token: slot a is pair a (no grouping)
+    // Routed sum inside the launch (null cnt: none): the per-slot products go
+    // to out[0] through agent-coherent stores, and the last workgroup of each
+    // row block writes y[t][n] = sum over slots s in order of
+    // route_w[t][s] * out[0][t*topk+s][n].  cnt: one counter per row block,
+    // zero between calls.
+    const float *route_w;
+    float *y;
+    unsigned *cnt;
+    int T;
 };
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
@@ -79,6 +91,69 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total) {
     }
     *total = __shfl(x, 63, 64);
     return x - v;
+}
+
+// End of a workgroup of a launch with the routed sum inside: once every
+// per-slot product the workgroup stored has completed, it counts itself on its
+// row block's counter; the last of the row block's gridDim.y workgroups adds
+// the slots of every token in slot order (one fma per slot, in order)
+// and returns the counter to zero.  Every workgroup of the row block calls
+// this exactly once, also those whose slot has no expert.
+__device__ void routed_sum(const MoeArgs &A, const int *s_ids, int row_base, int RB) {
+    __shared__ unsigned last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(A.cnt + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
+    __syncthreads();
+    if (!last) return;
+    const int N = A.N, topk = A.topk, E = A.E;
+    const int rows = min(RB, N - row_base);
+    const int total = A.T * rows;
+    // one output per thread when they fit the workgroup, else kOut per
+    // thread at a time; a thread's loads are all in flight before it stores
+    if (total <= (int)blockDim.x) {
+        if ((int)threadIdx.x < total) {
+            const int t = threadIdx.x / rows, n = row_base + threadIdx.x % rows;
+            float v = 0.0f;
+            for (int s = 0; s < topk; ++s) {
+                const int p = t * topk + s;
+                const int e = s_ids[p];
+                const float z = __hip_atomic_load(A.out[0] + (int64_t)p * N + n,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e >= 0 && e < E) v = fmaf(A.route_w[p], z, v);
+            }
+            A.y[(int64_t)t * N + n] = v;
+        }
+    }
+    constexpr int kOut = 4;
+    for (int i0 = threadIdx.x; i0 < total && total > (int)blockDim.x; i0 += kOut * blockDim.x) {
+        int t[kOut], n[kOut];
+        float v[kOut];
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            const int i = min(i0 + k * (int)blockDim.x, total - 1);
+            t[k] = i / rows;
+            n[k] = row_base + i % rows;
+            v[k] = 0.0f;
+        }
+        for (int s = 0; s < topk; ++s) {
+#pragma unroll
+            for (int k = 0; k < kOut; ++k) {
+                const int p = t[k] * topk + s;
+                const int e = s_ids[p];
+                const float z = __hip_atomic_load(A.out[0] + (int64_t)p * N + n[k],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (e >= 0 && e < E) v[k] = fmaf(A.route_w[p], z, v[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kOut; ++k)
+            if (i0 + k * (int)blockDim.x < total) A.y[(int64_t)t[k] * N + n[k]] = v[k];
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(A.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One workgroup: the touched expert of slot a (blockIdx.y, past the first
@@ -115,16 +190,21 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
     const int lane = tid & 63, wave = tid >> 6;
     const int nw = nt >> 6;
 
-    // ---- grouping, in LDS: ids, touched-expert flags
+    // ---- grouping, in LDS: ids, touched-expert flags (a one-token call maps
+    // slot a to pair a directly: no flags, scan or pair list)
+    const bool direct = A.direct != 0;             // uniform
     for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
-    for (int e = tid; e < E; e += nt) s_flag[e] = 0;
+    if (!direct)
+        for (int e = tid; e < E; e += nt) s_flag[e] = 0;
     if (tid == 0) s_e = -1;
     __syncthreads();
-    for (int p = tid; p < P; p += nt) {
-        const int e = s_ids[p];
-        if (e >= 0 && e < E) s_flag[e] = 1;        // same value from every writer
+    if (!direct) {
+        for (int p = tid; p < P; p += nt) {
+            const int e = s_ids[p];
+            if (e >= 0 && e < E) s_flag[e] = 1;    // same value from every writer
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (A.zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
         // per-slot rows of skipped pairs are zero (this block of rows)
         for (int p = 0; p < P; ++p) {
@@ -136,9 +216,17 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
         return;
     }
     const int mi = (int)blockIdx.y >= A.slots ? 1 : 0;   // which projection
-    // slot a is the a-th smallest touched expert: each thread counts the
-    // flags of a range of experts, a block scan places the ranges
-    {
+    if (direct) {
+        if (tid == 0) {
+            const int a = (int)blockIdx.y - mi * A.slots;
+            const int ea = s_ids[a];
+            s_e = ea >= 0 && ea < E ? ea : -1;
+            s_pairs[0] = a;
+        }
+        __syncthreads();
+    } else {
+        // slot a is the a-th smallest touched expert: each thread counts the
+        // flags of a range of experts, a block scan places the ranges
         const int a = (int)blockIdx.y - mi * A.slots;
         const int per = (E + nt - 1) / nt;
         const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
@@ -161,11 +249,14 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
         __syncthreads();
     }
     const int e = s_e;
-    if (e < 0) return;                             // uniform: slot past the touched experts
+    if (e < 0) {                                   // uniform: slot past the touched experts
+        if (A.cnt) routed_sum(A, s_ids, row_base, RB);
+        return;
+    }
     // the expert's pairs in ascending order: per round of nt pairs, wave
     // ballots and the earlier waves' counts place each one
-    int cnt = 0;
-    for (int p0 = 0; p0 < P; p0 += nt) {
+    int cnt = direct ? 1 : 0;
+    for (int p0 = 0; p0 < P && !direct; p0 += nt) {
         const int p = p0 + tid;
         const bool f = p < P && s_ids[p] == e;
         const unsigned long long mask = __ballot(f);
@@ -353,28 +444,16 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
                 float t = 0.0f;
                 for (int wv = 0; wv < nw; ++wv)
                     for (int k = 0; k < S; ++k) t += red[wv][k * RB + rr][m];
-                out[(int64_t)s_pairs[c0 + m] * N + n] = t;
+                float *o = out + (int64_t)s_pairs[c0 + m] * N + n;
+                if (A.cnt)
+                    __hip_atomic_store(o, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    *o = t;
             }
         }
         __syncthreads();
     }
-}
-
-__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ z,
-                                                     const float *__restrict__ route_w,
-                                                     const int32_t *__restrict__ ids, int E,
-                                                     int T, int topk, int N,
-                                                     float *__restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)T * N) return;
-    const int t = (int)(i / N), n = (int)(i % N);
-    float v = 0.0f;
-    for (int s = 0; s < topk; ++s) {
-        const int p = t * topk + s;
-        const int e = ids[p];
-        if (e >= 0 && e < E) v = fmaf(route_w[p], z[(int64_t)p * N + n], v);
-    }
-    y[i] = v;
+    if (A.cnt) routed_sum(A, s_ids, row_base, RB);
 }
 
 // Launch shape for K = 256*nsb: column slots per wave enough that at most
@@ -417,23 +496,19 @@ hipError_t launch_kernel(const MoeArgs &A, int64_t T, int nmat, const Shape &sh,
     return hipGetLastError();
 }
 
-hipError_t launch_reduce(const float *z, const float *route_w, const int32_t *ids, int64_t E,
-                         int64_t T, int64_t topk, int64_t N, float *y, hipStream_t stream) {
-    const int64_t total = T * N;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       stream, z, route_w, ids, (int)E, (int)T, (int)topk, (int)N, y);
-    return hipGetLastError();
-}
-
 size_t f32_bytes(int64_t rows, int64_t cols) {
     return (size_t)((4 * rows * cols + 255) & ~int64_t(255));
 }
+
+// Routed-sum counters at the front of a workspace: one per row block of an
+// N-row launch (row blocks hold at least 16 rows).
+size_t counter_bytes(int64_t N) { return f32_bytes(1, (N + 15) / 16); }
 
 }  // namespace
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N) {
     (void)n_experts;
-    return f32_bytes(T * topk, N);   // per-slot products z
+    return counter_bytes(N) + f32_bytes(T * topk, N);   // counters, per-slot products z
 }
 
 hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, int64_t N,
@@ -441,7 +516,7 @@ hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, 
                            int64_t topk, const int8_t *codes, const float *scales,
                            const int32_t *sums, int act_per_slot, float *y, void *workspace,
                            hipStream_t stream) {
-    float *z = static_cast<float *>(workspace);
+    float *z = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + counter_bytes(N));
     const int P = (int)(T * topk), E = (int)n_experts;
     const Shape sh = shape(K / kQK);
     MoeArgs A = {};
@@ -461,9 +536,14 @@ hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride, 
     A.scales = scales;
     A.sums = sums;
     A.ids = ids;
-    hipError_t err = launch_kernel<ACT_Q8>(A, T, 1, sh, stream);
-    if (err != hipSuccess || !route_w) return err;
-    return launch_reduce(z, route_w, ids, n_experts, T, topk, N, y, stream);
+    A.direct = T == 1;
+    if (route_w) {
+        A.route_w = route_w;
+        A.y = y;
+        A.T = (int)T;
+        A.cnt = static_cast<unsigned *>(workspace);
+    }
+    return launch_kernel<ACT_Q8>(A, T, 1, sh, stream);
 }
 
 // Q8 rows: codes, scales, sums (each 256-byte aligned).
@@ -473,8 +553,10 @@ size_t q8_rows_bytes(int64_t rows, int64_t K) {
 
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t H, int64_t F) {
     const int64_t P = T * topk;
-    // g, u, z; Q8 of x and of h for the unfused activations of larger T
-    return 2 * f32_bytes(P, F) + f32_bytes(P, H) + q8_rows_bytes(T, H) + q8_rows_bytes(P, F);
+    // counters of the down launch; g, u, z; Q8 of x and of h for the unfused
+    // activations of larger T
+    return counter_bytes(H) + 2 * f32_bytes(P, F) + f32_bytes(P, H) + q8_rows_bytes(T, H) +
+           q8_rows_bytes(P, F);
 }
 
 hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
@@ -483,7 +565,8 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
                           int64_t topk, const float *x, float *y, void *workspace,
                           hipStream_t stream) {
     const int64_t P = T * topk;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    unsigned *cnt = static_cast<unsigned *>(workspace);
+    uint8_t *ws = static_cast<uint8_t *>(workspace) + counter_bytes(H);
     float *g = reinterpret_cast<float *>(ws);
     float *u = reinterpret_cast<float *>(ws + f32_bytes(P, F));
     float *z = reinterpret_cast<float *>(ws + 2 * f32_bytes(P, F));
@@ -518,6 +601,7 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     A.slots = (int)(P < E ? P : E);
     A.zero_skipped = 0;
     A.ids = ids;
+    A.direct = T == 1;
     hipError_t err;
     if (fuse) {
         A.xa = x;
@@ -531,9 +615,14 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
         err = launch_kernel<ACT_Q8>(A, T, 2, sh1, stream);
     }
     if (err != hipSuccess) return err;
-    // down: SwiGLU(g, u) quantized in the kernel, per-slot products z
+    // down: SwiGLU(g, u) quantized in the kernel, per-slot products z, and the
+    // routed sum by the last workgroup of each row block
     const Shape sh2 = shape(F / kQK);
     MoeArgs B = A;
+    B.route_w = route_w;
+    B.y = y;
+    B.T = (int)T;
+    B.cnt = cnt;
     B.w[0] = B.w[1] = w_down;
     B.out[0] = B.out[1] = z;
     B.stride = stride_down;
@@ -553,8 +642,7 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
         B.sums = hsu;
         err = launch_kernel<ACT_Q8>(B, T, 1, sh2, stream);
     }
-    if (err != hipSuccess) return err;
-    return launch_reduce(z, route_w, ids, n_experts, T, topk, H, y, stream);
+    return err;
 }
 
 }  // namespace q4k

@@ -214,8 +214,9 @@ int q4k_gemm_batch_noalloc(const q4k_gemm_problem *problems, int count, int64_t 
  * 16).  For token t < T and slot s < topk the expert is ids[t*topk+s].
  * Pairs are grouped by expert on the device (deterministically, in ascending
  * pair order, inside the GEMV kernel), so each touched expert's weights are
- * read once per call however many tokens chose it.  One kernel is enqueued,
- * and with routing weights a second for the slot-ordered weighted sum.
+ * read once per call however many tokens chose it.  One kernel is enqueued;
+ * with routing weights the last workgroup to finish each block of output rows
+ * also forms the slot-ordered weighted sum of that block.
  *   ids          device int32 [T][topk], expected in [0, n_experts).  They live
  *                on the device and are not checked on the host; a pair whose id
  *                is out of range is skipped on the device (its per-slot output
@@ -228,9 +229,13 @@ int q4k_gemm_batch_noalloc(const q4k_gemm_problem *problems, int count, int64_t 
  *                [T*topk][K]).
  *   codes/scales/sums as for q4k_gemv.
  *   workspace    device buffer of at least q4k_moe_workspace_bytes(T, topk,
- *                n_experts, N) bytes, 256-byte aligned; its contents on entry
- *                are ignored (it holds the per-slot products when route_w is
- *                given).  Calls sharing a workspace must not overlap.
+ *                n_experts, N) bytes, 256-byte aligned.  It starts with
+ *                counters (4 bytes per 16 rows of N, rounded up to 256 bytes)
+ *                that must be zero before the first call that uses it (e.g.
+ *                hipMemset of the whole buffer once after allocation); every
+ *                call leaves them zero.  The rest holds the per-slot products
+ *                when route_w is given.  Calls sharing a workspace must not
+ *                overlap.
  * Limits: 1 <= topk <= n_experts <= 4096, T >= 1, T*topk <= 4096. */
 int q4k_moe_gemv(const void *w_experts, int64_t n_experts,
                  int64_t expert_stride_bytes, int64_t N, int64_t K,
@@ -249,10 +254,11 @@ size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64
  * result is bit-identical to the unfused chain q4k_quantize_act(x);
  * q4k_moe_gemv(gate), (up); q4k_quantize_act(u, gate = g);
  * q4k_moe_gemv(down, route_w, act_per_slot = 1).  The gate and up products
- * share one launch; for T <= 2 the activations are quantized (and h formed)
- * inside the GEMV kernels, three launches in all; for larger T, where that
- * would repeat the work in every workgroup reading a row, the quantizer runs
- * once per row as its own launch (five in all).
+ * share one launch, and the down launch forms the routed sum itself; for
+ * T <= 2 the activations are quantized (and h formed) inside the GEMV
+ * kernels, two launches in all; for larger T, where that would repeat the
+ * work in every workgroup reading a row, the quantizer runs once per row as
+ * its own launch (four in all).
  *   w_gate, w_up  n_experts Q4_K matrices of F rows x H columns each, at
  *                 stride_gate_up bytes (>= F*(H/256)*144, multiple of 16)
  *   w_down        n_experts Q4_K matrices of H rows x F columns, at stride_down
@@ -260,9 +266,12 @@ size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64
  *                 (out-of-range ids are skipped); route_w is required
  *   x             device fp32 [T][H], 16-byte aligned; y: device fp32 [T][H]
  *   workspace     device buffer of at least q4k_moe_ffn_workspace_bytes(T,
- *                 topk, n_experts, H, F) bytes, 256-byte aligned (g, u, the
- *                 per-slot down products and Q8 rows of x and h); contents on
- *                 entry are ignored; calls sharing a workspace must not overlap.
+ *                 topk, n_experts, H, F) bytes, 256-byte aligned: counters of
+ *                 the down launch (4 bytes per 16 rows of H, rounded up to 256
+ *                 bytes; zero before the first call that uses the buffer, left
+ *                 zero by every call), then g, u, the per-slot down products
+ *                 and Q8 rows of x and h; calls sharing a workspace must not
+ *                 overlap.
  * Limits as for q4k_moe_gemv; H and F multiples of 256. */
 int q4k_moe_ffn(const void *w_gate, const void *w_up, const void *w_down, int64_t n_experts,
                 int64_t stride_gate_up, int64_t stride_down, int64_t H, int64_t F,

@@ -284,3 +284,53 @@ def test_moe_ffn_repeated_and_bad_ids_and_two_passes(q4k, oracle_lib):
     hs[~keep] = 0.0
     _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids_o, rw_o, wd, H_, F_,
                         "moe_ffn repeated/bad ids")
+
+
+def test_moe_routed_sum_in_launch_reuses_workspace(q4k, oracle_lib):
+    """The weighted sum is formed inside the down launch by the last
+    workgroup of each row block: one zero-filled workspace serves repeated
+    calls at T = 1, 16, 1 (its counters are back at zero after each), the
+    bits repeat, and q4k_moe_gemv with routing weights equals the sum of its
+    per-slot products in slot order."""
+    import torch
+    E, H, F, topk = qi.MOE_EXPERTS, qi.MOE_HIDDEN, qi.MOE_FFN, qi.MOE_TOPK
+    wg = np.concatenate([qi.make_q4k_bytes(F, H, qi.expert_seed(5, e, 0)) for e in range(E)])
+    wu = np.concatenate([qi.make_q4k_bytes(F, H, qi.expert_seed(5, e, 1)) for e in range(E)])
+    wd = np.concatenate([qi.make_q4k_bytes(H, F, qi.expert_seed(5, e, 2)) for e in range(E)])
+    dwg, dwu, dwd = to_dev(wg), to_dev(wu), to_dev(wd)
+    sgu, sd = F * (H // 256) * 144, H * (F // 256) * 144
+    nbytes = max(q4k.q4k_moe_ffn_workspace_bytes(T, topk, E, H, F) for T in (1, 16))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for T in (1, 16, 1):
+        ids, rw = qi.make_routing(T, E, topk, qi.routing_seed(50 + T))
+        x = to_dev(qi.make_act(T, H, 60 + T))
+        y = q4k.q4k_moe_ffn(dwg, dwu, dwd, E, sgu, sd, H, F, to_dev(ids), to_dev(rw), x,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        assert (ws[:256].cpu().numpy() == 0).all()
+        outs.append(y.cpu().numpy())
+        if T == 16:
+            ref = oracle_lib.moe_layer(wg, wu, wd, E, H, F, ids, rw, x.cpu().numpy(),
+                                       parallel=True)
+            assert_close(outs[-1], ref["y"], "moe_ffn T=16 shared workspace")
+    assert (outs[0].view(np.uint32) == outs[2].view(np.uint32)).all()
+    # q4k_moe_gemv: weighted sum in the launch = slot-ordered fma of its products
+    T = 4
+    ids, rw = qi.make_routing(T, E, topk, qi.routing_seed(77))
+    codes, scales, sums = oracle_lib.quantize_act(qi.make_act(T * topk, F, 78))
+    args = (dwd, E, sd, H, F, to_dev(ids))
+    z = q4k.q4k_moe_gemv(*args, None, to_dev(codes), to_dev(scales), to_dev(sums), True)
+    y = q4k.q4k_moe_gemv(*args, to_dev(rw), to_dev(codes), to_dev(scales), to_dev(sums), True)
+    torch.cuda.synchronize()
+    z, y = z.cpu().numpy(), y.cpu().numpy()
+    # v = fma(rw, z, v) per slot in order; a product of two fp32 is exact in
+    # fp64, so each step is the fp64 sum rounded once to fp32 (up to a rare
+    # double rounding: at most one unit in the last place)
+    want = np.zeros((T, H), np.float32)
+    for t in range(T):
+        for s in range(topk):
+            want[t] = (np.float64(rw[t, s]) * z[t * topk + s].astype(np.float64) +
+                       want[t].astype(np.float64)).astype(np.float32)
+    ulps = np.abs(y.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, ulps.max()
