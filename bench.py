@@ -968,6 +968,77 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
             "parity": {"rows_checked_per_shape": "24 sampled", "max_rel_err": worst}}
 
 
+def measure_q6k_gemm(torch, q4k, qi, oracle, M=512, reps=20):
+    """Q6_K prefill GEMM (q6k_gemm) on the seven Qwen3-4B projection shapes at
+    M = 512, each launch timed in a graph of `reps` launches (median of 5),
+    beside q4k_gemm on the same shapes and activations; every shape is first
+    spot-checked against the oracle on sampled rows."""
+    dev = torch.device("cuda:0")
+    L = q4k.lib()
+    ws = q4k.gemm_workspace(dev)
+    cap = torch.cuda.Stream()
+    out, tot = {}, {"q6k_us": 0.0, "q4k_us": 0.0, "flop": 0.0}
+    for p, (name, K, N) in enumerate(qi.QWEN3_4B_LAYER):
+        w6 = qi.make_q6k_bytes(N, K, qi.weight_seed(6, 0, p))
+        w4 = qi.make_q4k_bytes(N, K, qi.weight_seed(2, 0, p))
+        x = qi.make_act(M, K, qi.act_seed(60000 + p))
+        codes, scales, sums = oracle.quantize_act(x)
+        d6, d4 = torch.from_numpy(w6).to(dev), torch.from_numpy(w4).to(dev)
+        dc, dsc, dsu = (torch.from_numpy(a).to(dev) for a in (codes, scales, sums))
+        y = q4k.q6k_gemm(d6, N, K, dc, dsc)
+        torch.cuda.synchronize()
+        rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 14)])
+        ref = oracle.q6k_matvec(w6, N, K, codes, scales, rows=rows, parallel=True)
+        got = y.cpu().numpy()[:, rows].astype(np.float64)
+        if (np.abs(got - ref) > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
+            raise SystemExit("parity: q6k_gemm %s outside tolerance" % name)
+        yb = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+        def timed(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                s = torch.cuda.current_stream().cuda_stream
+                for _ in range(reps):
+                    fn(s)
+            g.replay()
+            per = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) * 1e-3 / reps)
+            return float(np.median(per))
+
+        def run6(s):
+            if L.q6k_gemm(d6.data_ptr(), N, K, dc.data_ptr(), dsc.data_ptr(), M, yb.data_ptr(),
+                          ws.data_ptr(), ws.numel(), s):
+                raise RuntimeError("q6k_gemm launch failed")
+
+        def run4(s):
+            if L.q4k_gemm(d4.data_ptr(), N, K, dc.data_ptr(), dsc.data_ptr(), dsu.data_ptr(), M,
+                          yb.data_ptr(), ws.data_ptr(), ws.numel(), s):
+                raise RuntimeError("q4k_gemm launch failed")
+
+        t6, t4 = timed(run6), timed(run4)
+        flop = 2.0 * M * N * K
+        out[name] = {"N": N, "K": K, "q6k_us": round(t6 * 1e6, 2),
+                     "q6k_TOPS": round(flop / t6 / 1e12, 1), "q4k_us": round(t4 * 1e6, 2),
+                     "q4k_TOPS": round(flop / t4 / 1e12, 1)}
+        tot["q6k_us"] += t6 * 1e6
+        tot["q4k_us"] += t4 * 1e6
+        tot["flop"] += flop
+    out["one_layer"] = {"q6k_us": round(tot["q6k_us"], 1),
+                        "q6k_TOPS": round(tot["flop"] / tot["q6k_us"] / 1e6, 1),
+                        "q4k_us": round(tot["q4k_us"], 1),
+                        "q4k_TOPS": round(tot["flop"] / tot["q4k_us"] / 1e6, 1)}
+    out["M"] = M
+    out["note"] = ("Q6_K: 4 fp16 matrix-core ops per 32-element block (two exact weight parts) "
+                   "and no min term, against Q4_K's 2 plus the 3-part min term per super-block")
+    return out
+
+
 def measure_moe(torch, q4k, qi, oracle, steps=5, layers=8, Ts=(1, 16)):
     """Routed-expert FFN layer (64 experts, hidden 2048, FFN 1024, top-8) over
     `layers` distinct seeded layers per pass (1.81 GB, past the last-level
@@ -1302,6 +1373,7 @@ def main():
                                                            args.prefill_steps)
     moe = None if args.no_extra else measure_moe(torch, q4k, qi, oracle)
     q6k = None if args.no_extra else measure_q6k(torch, q4k, qi, oracle)
+    q6k_gemm = None if args.no_extra else measure_q6k_gemm(torch, q4k, qi, oracle)
     large = None if args.no_extra else measure_large_launch(torch, q4k, qi)
     cpu, cpu_all = (None, None) if args.no_cpu else cpu_baselines(qi, oracle, args.cpu_seconds)
 
@@ -1351,6 +1423,7 @@ def main():
         "int8_kv_attention": attention,
         "moe_layer": moe,
         "q6k_decode_gemv": q6k,
+        "q6k_prefill_gemm": q6k_gemm,
         "decode_gemv_one_large_launch": large,
     }
     print(json.dumps(out))

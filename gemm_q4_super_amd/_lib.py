@@ -23,6 +23,7 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_ffn_workspace_bytes",
     "q6k_gemv",
     "q6k_quantize_gemv",
+    "q6k_gemm",
     "q4k_kv_store",
     "q4k_attn_workspace_bytes",
     "q4k_attn_decode",
@@ -88,6 +89,7 @@ def lib():
         L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
         L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+        L.q6k_gemm.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
         L.q4k_kv_store.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
         L.q4k_attn_workspace_bytes.argtypes = [_I, _I, _I]
         L.q4k_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -102,7 +104,7 @@ def lib():
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
                      "q4k_quantize_gemv_residual",
                      "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q4k_kv_store",
+                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q6k_gemm", "q4k_kv_store",
                      "q4k_attn_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -354,6 +356,20 @@ def q4k_moe_ffn(w_gate, w_up, w_down, n_experts, stride_gate_up, stride_down, H,
                              stride_down, H, F, _ptr(ids), _ptr(route_w), T, topk, _ptr(x),
                              _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)),
            "q4k_moe_ffn")
+    return y
+
+
+def q6k_gemm(w, N, K, codes, scales, y=None, workspace="auto"):
+    """Q6_K prefill GEMM: y [M, N] = Q8 rows (codes, scales) x W^T."""
+    import torch
+    for t, n in ((w, "w"), (codes, "codes"), (scales, "scales")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    wp, wb = _gemm_ws(workspace, codes.device)
+    _check(lib().q6k_gemm(_ptr(w), N, K, _ptr(codes), _ptr(scales), M, _ptr(y), wp, wb,
+                          _stream(codes)), "q6k_gemm")
     return y
 
 

@@ -89,6 +89,7 @@ constexpr int TN = 2;        // 32-row weight tiles per matrix-core wave
 constexpr int OSTR = 72;     // fp16 per operand row and step: [kh 2][s 2][lh 2][8] + 8 pad
 
 constexpr int QSTR = 80;     // bytes per int8 operand row and step: [s 2][lh 2][16] + 16 pad
+constexpr int kQ6SB = 210;   // bytes per Q6_K super-block
 
 // fp16 operands: integer-valued sc*q and codes.
 template <int WN, int WM>
@@ -110,8 +111,21 @@ struct __attribute__((aligned(16))) LdsI {
     unsigned short wm[2][3][WN][8];
     unsigned short pm[2][3][WM][8];
 };
-template <int WN, int WM, bool I8>
-using Lds = typename std::conditional<I8, LdsI<WN, WM>, LdsF<WN, WM>>::type;
+// Q6_K fp16 operands: sc*(q - 32) of a 16-weight sub-block as two exact
+// parts, 16*sc*(q_hi - 2) (q_hi the quant's top 2 bits) and sc*q_lo (its low
+// 4 bits), and the codes.  No min term.
+template <int WN, int WM>
+struct __attribute__((aligned(16))) LdsQ6 {
+    _Float16 aw[2][WN][OSTR];          // sc*q_lo of a step's two 32-blocks
+    _Float16 ah[2][WN][OSTR];          // 16*sc*(q_hi - 2)
+    _Float16 bx[2][WM][OSTR];          // codes
+    float dn[2][WN];                   // d of the super-block (by super-block parity)
+    float as[2][8][WM];                // activation block scale a[j][row]
+};
+template <int WN, int WM, bool I8, bool Q6>
+using Lds = typename std::conditional<
+    Q6, LdsQ6<WN, WM>,
+    typename std::conditional<I8, LdsI<WN, WM>, LdsF<WN, WM>>::type>::type;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -250,14 +264,15 @@ struct Walk {
     }
 };
 
-template <int WVN, int WVM, int TM, int NV, bool I8>
+template <int WVN, int WVM, int TM, int NV, bool I8, bool Q6>
 __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     const GemmSet set, const Sched sch, int nsb, const int8_t *__restrict__ codes,
     const float *__restrict__ scales, const int32_t *__restrict__ sums, int M) {
     using C = Cfg<WVN, WVM, TM, NV>;
     constexpr int WN = C::WN, WM = C::WM, P = C::P, NC = C::NC;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-    Lds<WN, WM, I8> &L = *reinterpret_cast<Lds<WN, WM, I8> *>(lds_raw);
+    Lds<WN, WM, I8, Q6> &L = *reinterpret_cast<Lds<WN, WM, I8, Q6> *>(lds_raw);
+    static_assert(!(I8 && Q6), "the Q6_K contraction is the fp16 one");
 
     const int G = sch.groups;
     const int gi = (G % NXCD == 0) ? (int)(blockIdx.x % NXCD) * (G / NXCD) + (int)(blockIdx.x / NXCD)
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     const int64_t ub = range_begin(gi, sch), ue = range_begin(gi + 1, sch);
     if (ub >= ue) return;   // the whole workgroup exits, before any barrier
     const int K = nsb * 256, nblk = nsb * 8;
-    const int64_t row_bytes = (int64_t)nsb * 144;
+    const int64_t row_bytes = (int64_t)nsb * (Q6 ? kQ6SB : 144);
     const int tid = threadIdx.x;
 
     if (tid >= 64 * NC) {
@@ -289,9 +304,20 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
         // lines within a few instructions (loaded one quarter per step, each
         // line was fetched again for every quarter); it is converted one and
         // two units later.
+        // Q6_K: a 210-byte super-block starts at an even byte, so each 16-byte
+        // field the lane needs is read as 5 dwords from the 4-byte boundary at
+        // or below it and shifted into place at conversion (every read stays
+        // inside the super-block).  Fields of lane c of a row: ql[16c + 32i]
+        // (i < 4), qh[16c + 32i] (i < 2), the 16 scales; d by a 2-byte load.
+        struct Q6Raw {
+            unsigned ql[4][5], qh[2][5], sc[5];
+            unsigned d, odd;          // d's fp16 bits; 2 if the super-block starts at 2 mod 4
+        };
         Step S[8];
         Block blk[2];
-        const bool vec_as = ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(sums)) & 15) == 0;
+        Q6Raw q6[Q6 ? 2 : 1][C::NA];
+        const bool vec_as = ((reinterpret_cast<uintptr_t>(scales) |
+                              (Q6 ? 0 : reinterpret_cast<uintptr_t>(sums))) & 15) == 0;
 
         // The unit at pw into slot k; pw then moves on (not past the last unit).
         Walk<WN, WM> pw;
@@ -305,11 +331,36 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             for (int i = 0; i < C::NA; ++i) {
                 const int e = min(p + i * P, C::CA - 1);
                 const int row = min(tl.n0 + (e >> 1), tl.N - 1);
-                const uint8_t *src = tl.w + (int64_t)row * row_bytes + (int64_t)b * 144;
-                blk[k].h[i] = *reinterpret_cast<const u32x4 *>(src);
+                if constexpr (Q6) {
+                    const uint8_t *sb = tl.w + (int64_t)row * row_bytes + (int64_t)b * kQ6SB;
+                    const unsigned odd = (unsigned)(reinterpret_cast<uintptr_t>(sb) & 2);
+                    const uint8_t *base = sb - odd;              // 4-byte aligned
+                    const int c = e & 1;
+                    // dword 4 of a field is only used when odd; otherwise dword 3 is
+                    // read again (so no read passes the super-block's last byte)
+                    auto field = [&](unsigned *r5, int o) {
+                        const unsigned *q = reinterpret_cast<const unsigned *>(base + o);
+                        r5[0] = q[0];
+                        r5[1] = q[1];
+                        r5[2] = q[2];
+                        r5[3] = q[3];
+                        r5[4] = q[odd ? 4 : 3];
+                    };
+                    Q6Raw &R = q6[Q6 ? k : 0][i];
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    S[4 * k + g].q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
+                    for (int f = 0; f < 4; ++f) field(R.ql[f], 16 * c + 32 * f);
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) field(R.qh[f], 128 + 16 * c + 32 * f);
+                    field(R.sc, 192);
+                    R.d = *reinterpret_cast<const unsigned short *>(sb + 208);
+                    R.odd = odd;
+                } else {
+                    const uint8_t *src = tl.w + (int64_t)row * row_bytes + (int64_t)b * 144;
+                    blk[k].h[i] = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        S[4 * k + g].q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
+                }
             }
 #pragma unroll
             for (int i = 0; i < C::NB; ++i) {
@@ -325,20 +376,25 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 if (vec_as) {
                     const f32x4 a0 = *reinterpret_cast<const f32x4 *>(scales + o);
                     const f32x4 a1 = *reinterpret_cast<const f32x4 *>(scales + o + 4);
-                    const i32x4 s0 = *reinterpret_cast<const i32x4 *>(sums + o);
-                    const i32x4 s1 = *reinterpret_cast<const i32x4 *>(sums + o + 4);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         blk[k].a[i][j] = a0[j];
                         blk[k].a[i][4 + j] = a1[j];
-                        blk[k].s[i][j] = s0[j];
-                        blk[k].s[i][4 + j] = s1[j];
+                    }
+                    if constexpr (!Q6) {
+                        const i32x4 s0 = *reinterpret_cast<const i32x4 *>(sums + o);
+                        const i32x4 s1 = *reinterpret_cast<const i32x4 *>(sums + o + 4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            blk[k].s[i][j] = s0[j];
+                            blk[k].s[i][4 + j] = s1[j];
+                        }
                     }
                 } else {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         blk[k].a[i][j] = scales[o + j];
-                        blk[k].s[i][j] = sums[o + j];
+                        if constexpr (!Q6) blk[k].s[i][j] = sums[o + j];
                     }
                 }
             }
@@ -357,6 +413,72 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             constexpr int F = decltype(bufc)::value;
             const Step &R = S[4 * k + g];
             const Block &B = blk[k];
+            if constexpr (Q6) {
+#pragma unroll
+            for (int i = 0; i < C::NA; ++i) {
+                const int e = p + i * P;
+                if (C::CA % P != 0 && e >= C::CA) continue;
+                const int row = e >> 1, c = e & 1;
+                const Q6Raw &W = q6[k][i];
+                const unsigned sh = W.odd;   // bytes to shift the 5-dword reads by
+                auto field = [&](const unsigned *r5) {
+                    u32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_alignbyte(r5[j + 1], r5[j], sh);
+                    return v;
+                };
+                // step g: elements 64g + 16c + j (32-block 2g) and 64g + 32 + 16c + j
+                // (block 2g + 1), j < 16: low 4 bits in ql[64h + 16c + j] and
+                // ql[64h + 32 + 16c + j] (high nibble for odd g), high 2 bits in
+                // qh[32h + 16c + j] bits 4(g%2) and 4(g%2) + 2; scales
+                // sc[4g + c] and sc[4g + 2 + c]
+                constexpr int h = g >> 1, od = g & 1;
+                const u32x4 qa = field(W.ql[2 * h]), qb = field(W.ql[2 * h + 1]);
+                const u32x4 qhv = field(W.qh[h]);
+                const u32x4 scv = field(W.sc);
+                u32x4 la, lb, ha, hb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    la[j] = (od ? qa[j] >> 4 : qa[j]) & 0x0F0F0F0Fu;
+                    lb[j] = (od ? qb[j] >> 4 : qb[j]) & 0x0F0F0F0Fu;
+                    ha[j] = (qhv[j] >> (4 * od)) & 0x03030303u;
+                    hb[j] = (qhv[j] >> (4 * od + 2)) & 0x03030303u;
+                }
+                auto sc_byte = [&](int idx) {   // int8 scale idx of the super-block
+                    return (float)(int8_t)((scv[idx >> 2] >> (8 * (idx & 3))) & 0xFFu);
+                };
+                const float sa = c ? sc_byte(4 * g + 1) : sc_byte(4 * g);
+                const float sb2 = c ? sc_byte(4 * g + 3) : sc_byte(4 * g + 2);
+                const half2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+                const half2 m1026 = {(_Float16)-1026.0f, (_Float16)-1026.0f};
+                const half2 va = {(_Float16)sa, (_Float16)sa}, vb = {(_Float16)sb2, (_Float16)sb2};
+                const half2 wa = {(_Float16)(16.0f * sa), (_Float16)(16.0f * sa)};
+                const half2 wb = {(_Float16)(16.0f * sb2), (_Float16)(16.0f * sb2)};
+                // q_lo * sc: (1024 + q_lo) - 1024 is exact, and so is the product
+                // (|sc * q_lo| <= 1920); 16 sc (q_hi - 2) likewise (a multiple of
+                // 16 of magnitude <= 4096)
+                auto lo8 = [&](unsigned v0, unsigned v1, half2 sv) {
+                    return cat4((bias_pair_lo(v0) + m1024) * sv, (bias_pair_hi(v0) + m1024) * sv,
+                                (bias_pair_lo(v1) + m1024) * sv, (bias_pair_hi(v1) + m1024) * sv);
+                };
+                auto hi8 = [&](unsigned v0, unsigned v1, half2 sv) {
+                    return cat4((bias_pair_lo(v0) + m1026) * sv, (bias_pair_hi(v0) + m1026) * sv,
+                                (bias_pair_lo(v1) + m1026) * sv, (bias_pair_hi(v1) + m1026) * sv);
+                };
+                _Float16 *dl = &L.aw[F][row][32 * c];
+                _Float16 *dh = &L.ah[F][row][32 * c];
+                *reinterpret_cast<half8 *>(dl + 0) = lo8(la.x, la.y, va);
+                *reinterpret_cast<half8 *>(dl + 8) = lo8(la.z, la.w, va);
+                *reinterpret_cast<half8 *>(dl + 16) = lo8(lb.x, lb.y, vb);
+                *reinterpret_cast<half8 *>(dl + 24) = lo8(lb.z, lb.w, vb);
+                *reinterpret_cast<half8 *>(dh + 0) = hi8(ha.x, ha.y, wa);
+                *reinterpret_cast<half8 *>(dh + 8) = hi8(ha.z, ha.w, wa);
+                *reinterpret_cast<half8 *>(dh + 16) = hi8(hb.x, hb.y, wb);
+                *reinterpret_cast<half8 *>(dh + 24) = hi8(hb.z, hb.w, wb);
+                if (g == 0 && c == 0)
+                    L.dn[Q][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)W.d);
+            }
+            } else {
 #pragma unroll
             for (int i = 0; i < C::NA; ++i) {
                 const int e = p + i * P;
@@ -436,6 +558,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                     }
                 }
             }
+            }
             const half2 m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
             for (int i = 0; i < C::NB; ++i) {
@@ -461,7 +584,13 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                 *reinterpret_cast<half8 *>(dst + 32) = conv(c1.x, c1.y);   // 16..23
                 *reinterpret_cast<half8 *>(dst + 40) = conv(c1.z, c1.w);   // 24..31
                 }
-                if (g == 0) {
+                if constexpr (Q6) {
+                    // lane s of the row: the scales of blocks 4s .. 4s+3
+                    if (g == 0)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            L.as[Q][4 * s + k][row] = s ? B.a[i][4 + k] : B.a[i][k];
+                } else if (g == 0) {
                     // lane s of the row: the scales and min-term parts of blocks 4s .. 4s+3
                     unsigned pt[3][4];
 #pragma unroll
@@ -564,6 +693,37 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                     for (int i = 0; i < 16; ++i)
                         acc[u][t][i] = fmaf((float)D[i], a[t] * w[u][i], acc[u][t][i]);
                 }
+        } else if constexpr (Q6) {
+            // 4 matrix-core ops per 32x32 tile: elements 0..15 (high part, low
+            // part), then 16..31; E = sum of sc*(q - 32)*code over the block
+            half8 AH[TN][2], AL[TN][2], B[TM][2];
+#pragma unroll
+            for (int u = 0; u < TN; ++u) {
+                const _Float16 *sl = &L.aw[F][(wn * TN + u) * 32 + lr][16 * s + 8 * lh];
+                const _Float16 *sh = &L.ah[F][(wn * TN + u) * 32 + lr][16 * s + 8 * lh];
+                AL[u][0] = *reinterpret_cast<const half8 *>(sl);
+                AL[u][1] = *reinterpret_cast<const half8 *>(sl + 32);
+                AH[u][0] = *reinterpret_cast<const half8 *>(sh);
+                AH[u][1] = *reinterpret_cast<const half8 *>(sh + 32);
+            }
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                const _Float16 *src = &L.bx[F][(wm * TM + t) * 32 + lr][16 * s + 8 * lh];
+                B[t][0] = *reinterpret_cast<const half8 *>(src);
+                B[t][1] = *reinterpret_cast<const half8 *>(src + 32);
+            }
+#pragma unroll
+            for (int u = 0; u < TN; ++u)
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    f32x16 e = __builtin_amdgcn_mfma_f32_32x32x16_f16(AH[u][0], B[t][0], zero16, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_32x32x16_f16(AL[u][0], B[t][0], e, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_32x32x16_f16(AH[u][1], B[t][1], e, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_32x32x16_f16(AL[u][1], B[t][1], e, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        usb[u][t][i] = J == 0 ? e[i] * a[t] : fmaf(e[i], a[t], usb[u][t][i]);
+                }
         } else {
             half8 A[TN][2], B[TM][2];
 #pragma unroll
@@ -613,6 +773,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[u][t][i] = fmaf(dv[i], usb[u][t][i], acc[u][t][i]);
         }
+        if constexpr (!Q6) {
 #pragma unroll
         for (int pp = 0; pp < 3; ++pp) {
             bf16x8 W[TN], X[TM];
@@ -629,6 +790,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
                     acc[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(W[u], X[t], acc[u][t], 0, 0, 0);
+        }
         }
     };
 
@@ -774,7 +936,7 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
     }
 }
 
-template <int WVN, int WVM, int TM, int NV, bool I8 = GEMM_I8>
+template <int WVN, int WVM, int TM, int NV, bool I8 = GEMM_I8, bool Q6 = false>
 hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const float *scales,
                        const int32_t *sums, int64_t M, void *ws, hipStream_t stream) {
     using C = Cfg<WVN, WVM, TM, NV>;
@@ -792,9 +954,9 @@ hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const f
         s.cnt = static_cast<int *>(ws);
         s.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kGemmCounters * 4);
     }
-    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM, NV, I8>), dim3((unsigned)s.groups), dim3(C::T),
-                       sizeof(Lds<C::WN, C::WM, I8>), stream, set, s, nsb, codes, scales, sums,
-                       (int)M);
+    hipLaunchKernelGGL((gemm_kernel<WVN, WVM, TM, NV, I8, Q6>), dim3((unsigned)s.groups),
+                       dim3(C::T), sizeof(Lds<C::WN, C::WM, I8, Q6>), stream, set, s, nsb, codes,
+                       scales, sums, (int)M);
     return hipGetLastError();
 }
 
@@ -845,10 +1007,8 @@ size_t gemm_workspace_bytes() {
     return (size_t)kGemmCounters * 4 + (size_t)2 * kGemmMaxGroups * 128 * 128 * 4;
 }
 
-hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
-                             const int8_t *codes, const float *scales, const int32_t *sums,
-                             int64_t M, void *workspace, hipStream_t stream) {
-    const int nsb = (int)(K / kQK);
+namespace {
+GemmSet make_set(const GemmProblem *probs, int count) {
     GemmSet set = {};
     set.count = count;
     set.tile0[0] = 0;
@@ -858,12 +1018,38 @@ hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
         set.N[p] = (int)probs[p].N;
         set.tile0[p + 1] = set.tile0[p] + (int)((probs[p].N + 127) / 128);   // WN = 128
     }
+    return set;
+}
+}  // namespace
+
 #ifndef GEMM_BIG
 #define GEMM_BIG 2, 2, 2, 4
 #endif
+
+hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
+                             const int8_t *codes, const float *scales, const int32_t *sums,
+                             int64_t M, void *workspace, hipStream_t stream) {
+    const int nsb = (int)(K / kQK);
+    const GemmSet set = make_set(probs, count);
     if (M > 64) return launch_tile<GEMM_BIG>(set, nsb, codes, scales, sums, M, workspace, stream);
     if (M > 32) return launch_tile<2, 2, 1, 4>(set, nsb, codes, scales, sums, M, workspace, stream);
     return launch_tile<2, 1, 1, 2>(set, nsb, codes, scales, sums, M, workspace, stream);
+}
+
+// Q6_K weights: the same tiles, units and split, the fp16 contraction.
+hipError_t launch_q6k_gemm_batch(const GemmProblem *probs, int count, int64_t K,
+                                 const int8_t *codes, const float *scales, int64_t M,
+                                 void *workspace, hipStream_t stream) {
+    const int nsb = (int)(K / kQK);
+    const GemmSet set = make_set(probs, count);
+    if (M > 64)
+        return launch_tile<2, 2, 2, 4, false, true>(set, nsb, codes, scales, nullptr, M, workspace,
+                                                    stream);
+    if (M > 32)
+        return launch_tile<2, 2, 1, 4, false, true>(set, nsb, codes, scales, nullptr, M, workspace,
+                                                    stream);
+    return launch_tile<2, 1, 1, 2, false, true>(set, nsb, codes, scales, nullptr, M, workspace,
+                                                stream);
 }
 
 hipError_t launch_gemm(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,

@@ -248,6 +248,20 @@ int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int q6k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
+             int64_t M, float *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!w || !codes || !scales || !y) return Q4K_EINVAL;
+    if (N < 1 || K < q4k::kQK || K % q4k::kQK != 0 || M < 1) return Q4K_ESHAPE;
+    if (N > kMaxDim || K > kMaxDim || M > kMaxDim) return Q4K_ESHAPE;
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 4))
+        return Q4K_EALIGN;
+    const int st = check_gemm_workspace(workspace, workspace_bytes);
+    if (st != Q4K_OK) return st;
+    const q4k::GemmProblem p = {w, y, N};
+    return from_hip(q4k::launch_q6k_gemm_batch(&p, 1, K, codes, scales, M, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int q4k_kv_store(const float *k, const float *v, int64_t M, int64_t n_kv, int64_t head_dim,
                  int64_t pos0, int64_t cap, int8_t *k_codes, float *k_scales, int8_t *v_codes,
                  float *v_scales, void *stream) {

@@ -110,6 +110,10 @@ hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
                              const int8_t *codes, const float *scales, const int32_t *sums,
                              int64_t M, void *workspace, hipStream_t stream);
 
+hipError_t launch_q6k_gemm_batch(const GemmProblem *probs, int count, int64_t K,
+                                 const int8_t *codes, const float *scales, int64_t M,
+                                 void *workspace, hipStream_t stream);
+
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64_t N);
 
 hipError_t launch_moe_gemv(const uint8_t *w, int64_t n_experts, int64_t stride,

@@ -285,7 +285,8 @@ size_t q4k_moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, i
 
 /* Q6_K decode / small-batch GEMV: y[M][N] = Q8(x)[M][K] * W^T for M = 1..8
  * with W in Q6_K, the format real Q4_K_M files keep some tensors in (and the
- * target of the decode kernels of "genie-ai-runtime ...", section 3, Path G):
+ * target of the decode kernels of "genie-ai-runtime ...", section 6, "The
+ * negatives I kept", Path G):
  * per 256 weights of a row 210 bytes -- ql[128] (low 4 bits of each 6-bit
  * quant q), qh[64] (high 2 bits), int8 sc[16] (one per 16 weights), fp16 d
  * (public GGUF layout) -- and w = d*sc[e/16]*(q[e] - 32).
@@ -310,6 +311,24 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
  * limits as for q6k_gemv. */
 int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
                       float *y, void *stream);
+
+/* Q6_K prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T with W in Q6_K (layout and
+ * weights as for q6k_gemv), the batched product of prefill ("genie-ai-runtime
+ * ...", section 3, Path B and Path E) on the Q6_K tensors of a Q4_K_M model
+ * (section 6, "The negatives I kept", Path G).  The same tiles, work split and
+ * workspace as q4k_gemm: the weights of a 16-weight sub-block enter the fp16
+ * matrix cores as two exact integer parts, 16*sc*(q_hi - 2) and sc*q_lo (q =
+ * 16 q_hi + q_lo), against the Q8 codes, so each 32-element block's sum of
+ * sc*(q - 32)*code is formed in fp32 (exactly while its partial sums stay
+ * below 2^24, i.e. for all but near-maximal scales and codes throughout a
+ * block); the block scale a and d are applied in fp32.  No sums are needed.
+ *   w        device Q6_K bytes, N rows x (K/256)*210 bytes, 16-byte aligned
+ *   codes    device int8 [M][K] (16-byte aligned); scales fp32 [M][K/32]
+ *   workspace, determinism: as for q4k_gemm.  Any M >= 1, N >= 1,
+ *   K % 256 == 0.  fp32 result within a relative error of 2e-3 (absolute
+ *   1e-4 near zero) of the exact sum. */
+int q6k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
+             int64_t M, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /* INT8 KV cache (genie-ai-runtime's Path I, section 4 "Memory-first: making
  * every byte count": one absmax scale per (layer, position, kv-head)).  One

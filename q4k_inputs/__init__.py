@@ -142,7 +142,8 @@ def make_q4k_bytes(N: int, K: int, seed: int) -> np.ndarray:
 
 # Q6_K super-block (public GGUF format; real "Q4_K_M" files keep some tensors in
 # Q6_K, and the decode kernels genie's "Path G" targets are Q6_K ones --
-# "genie-ai-runtime ...", section 3 -- but the pages do not print the layout):
+# "genie-ai-runtime ...", section 6, "The negatives I kept" -- but the pages do
+# not print the layout):
 # 256 weights of one row in 210 bytes:
 #
 #     bytes 0..127    ql   low 4 bits of the 6-bit quants

@@ -304,3 +304,22 @@ def test_attn_argument_checks(L):
     assert s(*ok_s[:5], -1, *ok_s[6:]) == ESHAPE
     assert s(A + 4, *ok_s[1:]) == EALIGN
     assert s(*ok_s[:7], A + 8, *ok_s[8:]) == EALIGN
+
+
+def test_q6k_gemm_argument_checks(L):
+    f = L.q6k_gemm
+    need = int(L.q4k_gemm_workspace_bytes())
+    ok = (A, 16, 512, A, A, 1, A, A, need, None)
+    assert f(None, *ok[1:]) == EINVAL
+    assert f(*ok[:3], None, *ok[4:]) == EINVAL
+    assert f(*ok[:4], None, *ok[5:]) == EINVAL
+    assert f(*ok[:6], None, *ok[7:]) == EINVAL
+    assert f(A, 16, 500, *ok[3:]) == ESHAPE
+    assert f(A, 0, 512, *ok[3:]) == ESHAPE
+    assert f(*ok[:5], 0, *ok[6:]) == ESHAPE
+    assert f(A + 8, *ok[1:]) == EALIGN
+    assert f(*ok[:3], A + 8, *ok[4:]) == EALIGN
+    assert f(*ok[:4], A + 2, *ok[5:]) == EALIGN
+    assert f(*ok[:7], None, 16, None) == EWORKSPACE
+    assert f(*ok[:7], A, need - 1, None) == EWORKSPACE
+    assert f(*ok[:7], A + 16, need, None) == EALIGN
