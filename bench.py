@@ -697,10 +697,12 @@ def measure_attention(torch, q4k, qi, oracle, dec, ctxs=(1024, 16384), reps=5):
 
 def measure_small_batch(torch, dec, oracle, steps=5):
     """Small-batch verification GEMV: M = 2, 4, 8 seeded N(0,1) activation rows
-    against the 36-layer sweep's weights, through q4k_gemv and through q4k_gemm.
-    Only the products are timed (the Q8 rows are prepared once).  Before
-    timing, layer 0's seven products through both paths are checked against
-    the oracle on sampled weight rows (all M activation rows)."""
+    against the 36-layer sweep's weights, through q4k_gemv (one launch per
+    product, 252) and through q4k_gemm_batch per launch group ({q,k,v}, {o},
+    {gate,up}, {down}: 144 launches; up to 8 rows it runs the same streaming
+    kernel batched).  Only the products are timed (the Q8 rows are prepared
+    once).  Before timing, layer 0's seven products through both paths are
+    checked against the oracle on sampled weight rows (all M rows)."""
     import gemm_q4_super_amd as q4k
     L = dec.L
     dev = torch.device("cuda:0")
@@ -723,7 +725,8 @@ def measure_small_batch(torch, dec, oracle, steps=5):
                 raise SystemExit("small batch: Q8 codes differ from the oracle (M=%d)" % M)
             rows = np.unique(np.r_[0, N - 1, np.random.default_rng(M * 7 + p).integers(0, N, 12)])
             ref = oracle.matvec(dec.host_w[p], N, K, rc, rs, rows=rows, parallel=True)
-            for y in (q4k.q4k_gemv(wt, N, K, c, sc, su), q4k.q4k_gemm(wt, N, K, c, sc, su)):
+            for y in (q4k.q4k_gemv(wt, N, K, c, sc, su),
+                      q4k.q4k_gemm_batch([(wt, N)], K, c, sc, su)[0]):
                 got = y.cpu().numpy()[:, rows].astype(np.float64)
                 err = np.abs(got - ref)
                 if (err > np.maximum(2e-3 * np.abs(ref), 1e-4)).any():
@@ -731,18 +734,31 @@ def measure_small_batch(torch, dec, oracle, steps=5):
                 worst = max(worst, float((err / np.maximum(np.abs(ref), 0.05)).max()))
                 checked += ref.size
         res = {"parity": {"outputs_checked": checked, "max_rel_err": worst}}
-        for path in ("gemv", "gemm"):
+        # batched launches: products of one group write their own outputs
+        yp = [torch.empty((M, N), dtype=torch.float32, device=dev) for _, _, N in dec.shapes]
+        groups = []
+        for grp in dec.groups:
+            arr = (q4k._lib.GemmProblem * len(grp))()
+            for j, i in enumerate(grp):
+                wt, N, K = dec.weights[i]
+                arr[j] = q4k._lib.GemmProblem(wt.data_ptr(), yp[i % len(dec.shapes)].data_ptr(), N)
+            groups.append((arr, len(grp), dec.weights[grp[0]][2]))
+        for path in ("gemv", "batched"):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 s = torch.cuda.current_stream().cuda_stream
-                for wt, N, K in dec.weights:
-                    c, sc, su = xs[K]
-                    a = (wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(), M,
-                         ys[N].data_ptr())
-                    st = (L.q4k_gemv(*a, s) if path == "gemv" else
-                          L.q4k_gemm(*a, gws.data_ptr(), gws.numel(), s))
-                    if st:
-                        raise RuntimeError("launch failed")
+                if path == "gemv":
+                    for wt, N, K in dec.weights:
+                        c, sc, su = xs[K]
+                        if L.q4k_gemv(wt.data_ptr(), N, K, c.data_ptr(), sc.data_ptr(),
+                                      su.data_ptr(), M, ys[N].data_ptr(), s):
+                            raise RuntimeError("launch failed")
+                else:
+                    for arr, n, K in groups:
+                        c, sc, su = xs[K]
+                        if L.q4k_gemm_batch(arr, n, K, c.data_ptr(), sc.data_ptr(), su.data_ptr(),
+                                            M, gws.data_ptr(), gws.numel(), s):
+                            raise RuntimeError("launch failed")
             g.replay()
             ts = []
             for _ in range(steps):
@@ -757,10 +773,11 @@ def measure_small_batch(torch, dec, oracle, steps=5):
             nbytes = sum(gemv_bytes(N, K, M) for _, N, K in dec.weights)
             ops = sum(2 * M * N * K for _, N, K in dec.weights)
             res[path] = {"us_per_sweep": round(t * 1e6, 1), "GBps": round(nbytes / t / 1e9, 1),
-                         "TOPS": round(ops / t / 1e12, 2), "us_dist": {
-                             k: (round(v * 1e6, 1) if k != "passes" else v)
-                             for k, v in dist(ts).items()}}
-        res["faster"] = min(("gemv", "gemm"), key=lambda k: res[k]["us_per_sweep"])
+                         "TOPS": round(ops / t / 1e12, 2),
+                         "calls": len(dec.weights) if path == "gemv" else len(groups),
+                         "us_dist": {k: (round(v * 1e6, 1) if k != "passes" else v)
+                                     for k, v in dist(ts).items()}}
+        res["faster"] = min(("gemv", "batched"), key=lambda k: res[k]["us_per_sweep"])
         out["M=%d" % M] = res
     return out
 

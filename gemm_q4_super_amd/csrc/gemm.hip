@@ -1029,6 +1029,25 @@ GemmSet make_set(const GemmProblem *probs, int count) {
 hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
                              const int8_t *codes, const float *scales, const int32_t *sums,
                              int64_t M, void *workspace, hipStream_t stream) {
+    // A few rows would leave the matrix-core tiles mostly idle: up to 8 rows
+    // run q4k_gemv's kernels (the same bits) -- each product the matrix-core
+    // GEMV prefers on its own, the others together in one streaming launch.
+    if (M <= 8 && stream_fits(M, K)) {
+        GemvProblem gp[kMaxGemmBatch];
+        int ng = 0;
+        for (int p = 0; p < count; ++p) {
+            if (gemv_mfma_preferred(probs[p].N, K, M, scales, sums)) {
+                const hipError_t e =
+                    launch_gemv_mfma(static_cast<const uint8_t *>(probs[p].w), probs[p].N, K,
+                                     codes, scales, sums, M, probs[p].y, stream);
+                if (e != hipSuccess) return e;
+            } else {
+                gp[ng++] = {probs[p].w, nullptr, probs[p].y, probs[p].N};
+            }
+        }
+        return ng ? launch_gemv_batch_prepared(gp, ng, K, codes, scales, sums, M, stream)
+                  : hipSuccess;
+    }
     const int nsb = (int)(K / kQK);
     const GemmSet set = make_set(probs, count);
     if (M > 64) return launch_tile<GEMM_BIG>(set, nsb, codes, scales, sums, M, workspace, stream);

@@ -221,4 +221,11 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
     }
 }
 
+hipError_t launch_gemv_batch_prepared(const GemvProblem *probs, int count, int64_t K,
+                                      const int8_t *codes, const float *scales,
+                                      const int32_t *sums, int64_t M, hipStream_t stream) {
+    const stream::Prepared Q = {codes, scales, sums};
+    return stream::run<false>(probs, count, K, M, Q, stream);
+}
+
 }  // namespace q4k

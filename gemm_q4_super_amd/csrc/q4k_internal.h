@@ -87,6 +87,11 @@ hipError_t launch_quantize_gemv_residual(const uint8_t *w, int64_t N, int64_t K,
                                          hipStream_t stream);
 using GemvProblem = q4k_gemv_problem;
 constexpr int kMaxGemvBatch = 8;
+// The streaming GEMV over a batch on prepared Q8 rows (M <= 8, stream_fits):
+// the kernel of q4k_gemv's streaming path, one launch.
+hipError_t launch_gemv_batch_prepared(const GemvProblem *probs, int count, int64_t K,
+                                      const int8_t *codes, const float *scales,
+                                      const int32_t *sums, int64_t M, hipStream_t stream);
 hipError_t launch_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
                                       int64_t M, hipStream_t stream);
 

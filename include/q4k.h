@@ -158,6 +158,10 @@ int q4k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t
  *                    that uses it (e.g. hipMemset once after allocation);
  *                    every call leaves them zero.  The rest holds partial
  *                    tiles.  Calls sharing a workspace must not overlap.
+ * Up to 8 rows (M <= 8, where the rows fit q4k_quantize_gemv's LDS limit)
+ * would leave the matrix-core tiles mostly idle: such calls run q4k_gemv's
+ * kernels on the prepared rows instead (no workspace used), with q4k_gemv's
+ * result bit for bit.
  * Results are deterministic: the same inputs give the same bits on every call.
  * Other arguments and the result contract as for q4k_gemv, without the
  * M <= 8 limit. */
@@ -181,7 +185,9 @@ typedef struct q4k_gemm_problem {
  * the q, k and v projections of a layer, or gate and up): for every problem
  * i, y_i = Q8(x)[M][K] * W_i^T, the same arithmetic as q4k_gemm on that
  * problem alone.  Launching them together fills the GPU where each alone
- * would not.  `problems` is a host array of `count` entries (1 <= count <= 8),
+ * would not; with M <= 8 (the verification rows of drafted tokens, "genie-ai-
+ * runtime ...", section 9) the products q4k_gemv would run on its streaming
+ * kernel go out as one launch, the others one launch each.  `problems` is a host array of `count` entries (1 <= count <= 8),
  * read during the call; outputs must not overlap.  Workspace as for q4k_gemm.
  * Limits and checks as for q4k_gemm, applied to every problem. */
 int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,

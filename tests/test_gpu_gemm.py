@@ -310,3 +310,28 @@ def test_gemm_batch_leaves_other_memory_untouched(q4k, oracle_lib):
         assert (host[off:off + gap] == -3.0).all()
         off += gap + M * N
     assert (host[off:] == -3.0).all()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_gemm_few_rows_run_the_gemv_bit_for_bit(q4k, oracle_lib, M):
+    """Up to 8 rows q4k_gemm and q4k_gemm_batch run the streaming GEMV: the
+    same bits as q4k_gemv, the batch (q|k|v of one layer, one launch) the same
+    as the products one by one, and the oracle within tolerance."""
+    import torch
+    K = 2560
+    shapes = [4096, 1024, 1024]
+    ws = [qi.make_q4k_bytes(N, K, 3000 + N + M) for N in shapes]
+    x = qi.make_act(M, K, 3100 + M)
+    codes, scales, sums = oracle_lib.quantize_act(x)
+    dc, dsc, dsu = to_dev(codes), to_dev(scales), to_dev(sums)
+    dws = [to_dev(w) for w in ws]
+    ys = q4k.q4k_gemm_batch([(w, N) for w, N in zip(dws, shapes)], K, dc, dsc, dsu)
+    for w, dw, N, yb in zip(ws, dws, shapes, ys):
+        y1 = q4k.q4k_gemm(dw, N, K, dc, dsc, dsu)
+        y2 = q4k.q4k_gemv(dw, N, K, dc, dsc, dsu)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+        assert torch.equal(yb.view(torch.int32), y2.view(torch.int32))
+        rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N).integers(0, N, 40)])
+        ref = oracle_lib.matvec(w, N, K, codes, scales, rows=rows)
+        assert_close(y1.cpu().numpy()[:, rows], ref, "gemm M=%d N=%d" % (M, N))
