@@ -29,7 +29,8 @@ sweep, single-threaded and on all cores (OpenMP over output rows).  Beside
 them, outside the timed region: the practical decode ceilings (a plain
 16-byte stream read of each launch group's bytes and an empty kernel), the
 prefill GEMM (M = 512, 20 steps, with the shader clock sampled during the
-steps for a measured-clock peak), the small-batch GEMV (M = 2, 4, 8), the
+steps for a measured-clock peak, and how far fp16 matrix-core ops and fp32
+vector fmas of one SIMD overlap), the small-batch GEMV (M = 2, 4, 8), the
 routed-expert layer (T = 1, 16) and the Q6_K decode GEMV over the same
 projection shapes -- each checked against the oracle before it is timed --
 and the oracle's own rate on each of those workloads.
@@ -538,9 +539,46 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
                         "mean_launch_us": round(gemm_s / pre.units * 1e6, 2),
                         "timing": "median over %d steps of HIP events around the %d GEMM "
                                   "launches of a step" % (steps, pre.units)},
-           "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity}
+           "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity,
+           "matrix_vector_coissue": measure_coissue(torch, q4k)}
     del pre
     torch.cuda.empty_cache()
+    return out
+
+
+def measure_coissue(torch, q4k, iters=16384, reps=5):
+    """Whether fp16 matrix-core ops and fp32 vector fmas from two waves of one
+    SIMD overlap (q4k_ceiling_mfma_valu, one workgroup per CU): the time of
+    the matrix-core waves alone, the vector waves alone (vrep rounds of 32
+    fmas per 4 matrix ops) and both together; overlap = (alone sum - both) /
+    the shorter alone time (1: fully concurrent, 0: one after the other)."""
+    L = q4k.lib()
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(grid, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def timed(vrep, what):
+        if L.q4k_ceiling_mfma_valu(grid, iters, vrep, what, sink.data_ptr(), s):
+            raise RuntimeError("q4k_ceiling_mfma_valu failed")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            L.q4k_ceiling_mfma_valu(grid, iters, vrep, what, sink.data_ptr(), s)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    mfma_ops = grid * 4 * iters * 4 * 32 * 32 * 16 * 2
+    out = {"grid": grid, "matrix_op": "v_mfma_f32_32x32x16_f16", "iters": iters}
+    t_m = timed(1, 1)
+    out["matrix_alone_us"] = round(t_m * 1e6, 1)
+    out["matrix_alone_TFLOPS"] = round(mfma_ops / t_m / 1e12, 1)
+    for vrep in (1, 2):
+        t_v = timed(vrep, 2)
+        t_b = timed(vrep, 3)
+        out["vrep_%d" % vrep] = {"vector_alone_us": round(t_v * 1e6, 1),
+                                 "both_us": round(t_b * 1e6, 1),
+                                 "overlap": round((t_m + t_v - t_b) / min(t_m, t_v), 3)}
     return out
 
 

@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "q4k_attn_decode",
     "q4k_ceiling_stream_read",
     "q4k_ceiling_empty",
+    "q4k_ceiling_mfma_valu",
     "q4k_status_string",
 )
 
@@ -99,6 +100,8 @@ def lib():
         L.q4k_ceiling_stream_read.restype = ctypes.c_int
         L.q4k_ceiling_empty.argtypes = [_I, _P]
         L.q4k_ceiling_empty.restype = ctypes.c_int
+        L.q4k_ceiling_mfma_valu.argtypes = [_I, _I, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.q4k_ceiling_mfma_valu.restype = ctypes.c_int
         L.q4k_status_string.argtypes = [ctypes.c_int]
         L.q4k_status_string.restype = ctypes.c_char_p
         for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",

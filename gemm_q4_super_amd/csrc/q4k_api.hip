@@ -316,6 +316,17 @@ int q4k_ceiling_empty(int64_t grid, void *stream) {
     return from_hip(q4k::launch_empty(grid, static_cast<hipStream_t>(stream)));
 }
 
+int q4k_ceiling_mfma_valu(int64_t grid, int64_t iters, int vrep, int what, float *sink,
+                          void *stream) {
+    if (!sink) return Q4K_EINVAL;
+    if (grid < 1 || grid > (int64_t(1) << 20) || iters < 1 || iters > (int64_t(1) << 24) ||
+        vrep < 0 || vrep > 64 || what < 1 || what > 3)
+        return Q4K_ESHAPE;
+    if (!aligned(sink, 4)) return Q4K_EALIGN;
+    return from_hip(q4k::launch_mfma_valu(grid, iters, vrep, what, sink,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char *q4k_status_string(int status) {
     switch (status) {
     case Q4K_OK: return "ok";

@@ -159,5 +159,7 @@ hipError_t launch_attn(const float *q, int64_t M, int64_t n_head, int64_t n_kv, 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
                               hipStream_t stream);
 hipError_t launch_empty(int64_t grid, hipStream_t stream);
+hipError_t launch_mfma_valu(int64_t grid, int64_t iters, int vrep, int what, float *sink,
+                            hipStream_t stream);
 
 }  // namespace q4k

@@ -393,10 +393,21 @@ int q4k_attn_decode(const float *q, int64_t M, int64_t n_head, int64_t n_kv, int
  *   >= grid words): the bytes of a launch moved with no arithmetic.
  * q4k_ceiling_empty: `grid` workgroups of an empty kernel: the cost of a
  *   kernel boundary alone.
+ * q4k_ceiling_mfma_valu: `grid` workgroups of 8 waves.  With bit 0 of `what`
+ *   set, waves 0-3 (one per SIMD) issue `iters` x 4 v_mfma_f32_32x32x16_f16
+ *   in four independent accumulator chains; with bit 1 set, waves 4-7 (one
+ *   per SIMD, beside them) issue `iters` x `vrep` x 32 fp32 fmas in sixteen
+ *   independent chains.  Timing what = 1, 2 and 3 shows how far the two
+ *   kinds of work overlap on one SIMD -- the question that bounds the prefill
+ *   GEMM, whose fp32 epilogue follows its matrix-core ops.  One float per
+ *   workgroup goes to `sink` (device, >= grid floats).  1 <= iters <= 2^24,
+ *   0 <= vrep <= 64, 1 <= what <= 3.
  * 1 <= grid <= 2^20. */
 int q4k_ceiling_stream_read(const void *buf, int64_t bytes, int64_t grid, unsigned *sink,
                             void *stream);
 int q4k_ceiling_empty(int64_t grid, void *stream);
+int q4k_ceiling_mfma_valu(int64_t grid, int64_t iters, int vrep, int what, float *sink,
+                          void *stream);
 
 /* Static description of a status code. */
 const char *q4k_status_string(int status);

@@ -194,6 +194,13 @@ def test_ceiling_argument_checks(L):
     assert L.q4k_ceiling_stream_read(A, 1024, 0, A, None) == ESHAPE
     assert L.q4k_ceiling_stream_read(A + 4, 1024, 1, A, None) == EALIGN
     assert L.q4k_ceiling_empty(0, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 16, 1, 3, None, None) == EINVAL
+    assert L.q4k_ceiling_mfma_valu(0, 16, 1, 3, A, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 0, 1, 3, A, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 16, 65, 3, A, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 16, 1, 0, A, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 16, 1, 4, A, None) == ESHAPE
+    assert L.q4k_ceiling_mfma_valu(1, 16, 1, 3, A + 2, None) == EALIGN
 
 
 def test_quantize_argument_checks(L):
