@@ -299,11 +299,12 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             int s[C::NB][8];
         };
         // Two units' worth of raw data: register set 4k + g holds quarter g of
-        // the unit in slot k.  A unit is loaded in one burst, so the two lanes
-        // of a row read its 144 weight bytes and 256 code bytes as whole cache
-        // lines within a few instructions (loaded one quarter per step, each
-        // line was fetched again for every quarter); it is converted one and
-        // two units later.
+        // the unit in slot k.  A unit's weight bytes (the two lanes of a row
+        // read its 144 bytes) and its activation bytes (256 codes per row,
+        // block scales and sums) are each loaded in one burst, so every cache
+        // line is read within a few instructions (loaded one quarter per step,
+        // each line was fetched again for every quarter); it is converted one
+        // and two units later.
         // Q6_K: a 210-byte super-block starts at an even byte, so each 16-byte
         // field the lane needs is read as 5 dwords from the 4-byte boundary at
         // or below it and shifted into place at conversion (every read stays
@@ -319,11 +320,13 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
         const bool vec_as = ((reinterpret_cast<uintptr_t>(scales) |
                               (Q6 ? 0 : reinterpret_cast<uintptr_t>(sums))) & 15) == 0;
 
-        // The unit at pw into slot k; pw then moves on (not past the last unit).
+        // The unit at pw into slot k, in two parts: its weight bytes
+        // (load_w), then its activation bytes (load_a), after which pw moves
+        // on (not past the last unit).
         Walk<WN, WM> pw;
         int64_t pu = ub;
         pw.start(set, ub, nsb, sch.tiles_m);
-        auto load_unit = [&](auto kc) {
+        auto load_w = [&](auto kc) {
             constexpr int k = decltype(kc)::value;
             const Tile &tl = pw.tl;
             const int b = pw.b;
@@ -362,6 +365,11 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                         S[4 * k + g].q[i] = *reinterpret_cast<const u32x4 *>(src + 16 + 32 * g + 16 * (e & 1));
                 }
             }
+        };
+        auto load_a = [&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const Tile &tl = pw.tl;
+            const int b = pw.b;
 #pragma unroll
             for (int i = 0; i < C::NB; ++i) {
                 const int e = min(p + i * P, C::CB - 1);
@@ -612,15 +620,21 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             }
         };
 
-        // Per step: load the step two ahead into the register set the current
-        // step used, convert the next step into the other LDS buffer, barrier.
+        // Per step: convert the next step into the other LDS buffer, barrier.
         // Units alternate between slots 0 and 1.  Per unit: convert quarters
         // 1..3 of it and quarter 0 of the next unit, one per step (the
-        // matrix-core waves read the LDS buffer a step later); once its last
-        // quarter is converted, its slot is reloaded with the unit two ahead.
+        // matrix-core waves read the LDS buffer a step later).  Once its last
+        // quarter is converted, the slot's weight registers are reloaded with
+        // the unit two ahead, and its activation registers a step later, at
+        // the step where the matrix-core waves end a super-block: issuing the
+        // whole reload at once made that one step of four the converting
+        // waves' slowest while the matrix-core waves' slowest came a step
+        // later (the 36-layer M = 512 step: 244 -> 230 us per layer).
         __builtin_amdgcn_s_setprio(2);   // conversion feeds the next step: issue it first
-        load_unit(IC<0>{});
-        load_unit(IC<1>{});
+        load_w(IC<0>{});
+        load_a(IC<0>{});
+        load_w(IC<1>{});
+        load_a(IC<1>{});
         convert(IC<0>{}, IC<0>{}, IC<0>{}, 0);
         __syncthreads();
 #pragma unroll 1
@@ -630,9 +644,10 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             convert(IC<0>{}, IC<2>{}, IC<0>{}, 0);
             __syncthreads();
             convert(IC<0>{}, IC<3>{}, IC<1>{}, 0);
-            load_unit(IC<0>{});
+            load_w(IC<0>{});
             __syncthreads();
             convert(IC<1>{}, IC<0>{}, IC<0>{}, 1);
+            load_a(IC<0>{});
             __syncthreads();
             if (u + 1 >= ue) break;
             convert(IC<1>{}, IC<1>{}, IC<1>{}, 1);
@@ -640,9 +655,10 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
             convert(IC<1>{}, IC<2>{}, IC<0>{}, 1);
             __syncthreads();
             convert(IC<1>{}, IC<3>{}, IC<1>{}, 1);
-            load_unit(IC<1>{});
+            load_w(IC<1>{});
             __syncthreads();
             convert(IC<0>{}, IC<0>{}, IC<0>{}, 0);
+            load_a(IC<1>{});
             __syncthreads();
         }
         return;
