@@ -77,6 +77,7 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -545,24 +546,19 @@ __global__ __launch_bounds__(64 * (WVN * WVM + NV), 1) void gemm_kernel(
                     if (g == 0) L.dn[Q][row] = half_lo(h.x);
                 }
                 if (g == 0) {
+                    // lane c of the row: the three parts of -dmin*mn_j for j = 4c .. 4c+3
                     const float dmin = half_hi(h.x);
-                    unsigned pt[3][8];
-                    split3(-dmin * (float)scale6<0>(h, true), pt[0][0], pt[1][0], pt[2][0]);
-                    split3(-dmin * (float)scale6<1>(h, true), pt[0][1], pt[1][1], pt[2][1]);
-                    split3(-dmin * (float)scale6<2>(h, true), pt[0][2], pt[1][2], pt[2][2]);
-                    split3(-dmin * (float)scale6<3>(h, true), pt[0][3], pt[1][3], pt[2][3]);
-                    split3(-dmin * (float)scale6<4>(h, true), pt[0][4], pt[1][4], pt[2][4]);
-                    split3(-dmin * (float)scale6<5>(h, true), pt[0][5], pt[1][5], pt[2][5]);
-                    split3(-dmin * (float)scale6<6>(h, true), pt[0][6], pt[1][6], pt[2][6]);
-                    split3(-dmin * (float)scale6<7>(h, true), pt[0][7], pt[1][7], pt[2][7]);
-                    // lane c = 0 stores hi and mid, lane c = 1 stores lo
+                    const unsigned m4[4] = {c ? scale6<4>(h, true) : scale6<0>(h, true),
+                                            c ? scale6<5>(h, true) : scale6<1>(h, true),
+                                            c ? scale6<6>(h, true) : scale6<2>(h, true),
+                                            c ? scale6<7>(h, true) : scale6<3>(h, true)};
+                    unsigned pt[3][4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) split3(-dmin * (float)m4[k], pt[0][k], pt[1][k], pt[2][k]);
 #pragma unroll
                     for (int part = 0; part < 3; ++part) {
-                        if ((part < 2) != (c == 0)) continue;
-                        u32x4 pv;
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) pv[k] = pt[part][2 * k] | (pt[part][2 * k + 1] << 16);
-                        *reinterpret_cast<u32x4 *>(&L.wm[Q][part][row][0]) = pv;
+                        const u32x2 pv = {pt[part][0] | (pt[part][1] << 16), pt[part][2] | (pt[part][3] << 16)};
+                        *reinterpret_cast<u32x2 *>(&L.wm[Q][part][row][4 * c]) = pv;
                     }
                 }
             }
