@@ -28,6 +28,7 @@ roofline (algorithmic bytes per launch / mean launch duration, against
 sweep, single-threaded and on all cores (OpenMP over output rows).  Beside
 them, outside the timed region: the practical decode ceilings (a plain
 16-byte stream read of each launch group's bytes and an empty kernel), the
+same sweep at one GPU's share of an 8-way row shard, the
 prefill GEMM (M = 512, 20 steps, with the shader clock sampled during the
 steps for a measured-clock peak, and how far fp16 matrix-core ops and fp32
 vector fmas of one SIMD overlap), the small-batch GEMV (M = 2, 4, 8), the
@@ -872,6 +873,76 @@ def measure_ceilings(torch, q4k, dec, reps=5):
     return {"stream_read_per_launch_group": out, "empty_kernel_us_per_launch": empty}
 
 
+def measure_shard(torch, q4k, dec, G=8, steps=20):
+    """The decode sweep at one GPU's share of a G-way row shard (each GPU owns
+    N/G complete Q4_K rows of every projection: q 2560->512, k and v ->128,
+    o 4096->320, gate and up ->1216, down 9728->320 at G = 8): the first N/G
+    rows of each of the sweep's 252 matrices (a prefix of its row-major
+    bytes), the same activations and the same four batched launches per
+    layer.  Checked first: every shard output equals the full launch's output
+    for that row, bit for bit (a row's sum does not depend on the launch
+    shape).  The shard's 36 layers (255 MB) about fill the 256 MB last-level
+    cache, as they would on each of G GPUs."""
+    L = q4k.lib()
+    dev = torch.device("cuda:0")
+    ys = [torch.empty((1, N // G), dtype=torch.float32, device=dev) for _, _, N in dec.shapes]
+    batches, nbytes = [], 0
+    for grp in dec.groups:
+        arr = (q4k._lib.GemvProblem * len(grp))()
+        for j, i in enumerate(grp):
+            wt, N, K = dec.weights[i]
+            arr[j] = q4k._lib.GemvProblem(wt.data_ptr(), dec.acts[i].data_ptr(),
+                                          ys[i % len(dec.shapes)].data_ptr(), N // G)
+            nbytes += fused_bytes(N // G, K)
+        batches.append((arr, len(grp), dec.weights[grp[0]][2]))
+
+    def launch(g, s):
+        arr, n, K = batches[g]
+        if L.q4k_quantize_gemv_batch(arr, n, K, 1, s):
+            raise RuntimeError("q4k_quantize_gemv_batch launch failed")
+
+    # layer 0: shard outputs against the full launches' first N/G outputs
+    s = torch.cuda.current_stream().cuda_stream
+    for g in range(4):
+        dec.batch(g, s)
+        launch(g, s)
+    torch.cuda.synchronize()
+    for p, (name, K, N) in enumerate(dec.shapes):
+        if not torch.equal(ys[p], dec.yp[p][:, :N // G]):
+            raise SystemExit("shard: %s differs from the full launch's rows" % name)
+    cap = torch.cuda.Stream()
+    g_all = dec.graph(launch, range(len(batches)), cap)
+    g_all.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g_all.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = float(np.median(times))
+    per_group = {}
+    for gi, (gname, members) in enumerate((("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)),
+                                           ("down", (6,)))):
+        g = dec.graph(launch, range(gi, len(batches), 4), cap)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per_group[gname] = {"N": [dec.shapes[m][2] // G for m in members],
+                            "us": round(a.elapsed_time(b) * 1e-3 / LAYERS * 1e6, 3)}
+    return {"shards": G, "workload": "first N/%d rows of every projection of the 36-layer decode "
+                                     "sweep, batch 1, fused Q8, 4 batched launches per layer" % G,
+            "bytes_per_token": nbytes, "us_per_token": round(t * 1e6, 1),
+            "us_dist": dist(np.array(times) * 1e6), "GBps": round(nbytes / t / 1e9, 1),
+            "launches_per_token": len(batches), "per_group": per_group,
+            "check": "every shard output bit-identical to the full launch's (layer 0)"}
+
+
 def q6k_bytes(N, K, M=1):
     """Algorithmic bytes of one Q6_K GEMV: weights once (210 B per 256), the
     Q8 codes and scales it reads, the fp32 output."""
@@ -1421,6 +1492,7 @@ def main():
     n_launch = dec.n_batch
     small = None if args.no_extra else measure_small_batch(torch, dec, oracle)
     ceilings = None if args.no_extra else measure_ceilings(torch, q4k, dec)
+    shard = None if args.no_extra else measure_shard(torch, q4k, dec)
     attention = None if args.no_extra else measure_attention(torch, q4k, qi, oracle, dec)
     del g_batch, dec
     torch.cuda.empty_cache()
@@ -1472,6 +1544,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baselines": cpu_all,
         "decode_ceilings": ceilings,
+        "decode_one_gpu_share_of_8": shard,
         "parity": parity,
         "prefill_gemm": prefill,
         "small_batch_gemv": small,
