@@ -174,6 +174,8 @@ def parse():
     ap.add_argument("--prefill-group", choices=sorted(PREFILL_GROUPS),
                     help="only run 3 launches of one prefill launch group (for profiler "
                          "counter passes) and exit")
+    ap.add_argument("--gemm-int8", action="store_true",
+                    help="with --prefill-group: the GEMM's int8 contraction")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (known bytes, "
                          "to scale the HBM traffic counters of a profiler run) and exit")
@@ -201,9 +203,11 @@ def copy_calibration(torch):
 PREFILL_GROUPS = {"qkv": (0, 1, 2), "o": (3,), "gate_up": (4, 5), "down": (6,)}
 
 
-def prefill_group(torch, q4k, qi, name, launches=3):
+def prefill_group(torch, q4k, qi, name, launches=3, int8=False):
     """Only `launches` launches of one prefill launch group (layer 0's weights,
-    M = 512), for profiler counter passes; prints one line and exits."""
+    M = 512), for profiler counter passes; prints one line and exits.  int8:
+    the GEMM's int8 contraction (libq4k_gemm_int8.so)."""
+    L = q4k.lib_gemm_int8() if int8 else None
     dev = torch.device("cuda:0")
     idx = PREFILL_GROUPS[name]
     K = qi.QWEN3_4B_LAYER[idx[0]][1]
@@ -214,12 +218,13 @@ def prefill_group(torch, q4k, qi, name, launches=3):
     c, sc, su = q4k.q4k_quantize_act(x)
     for _ in range(launches):
         if len(probs) > 1:
-            q4k.q4k_gemm_batch(probs, K, c, sc, su)
+            q4k.q4k_gemm_batch(probs, K, c, sc, su, library=L)
         else:
-            q4k.q4k_gemm(probs[0][0], probs[0][1], K, c, sc, su)
+            q4k.q4k_gemm(probs[0][0], probs[0][1], K, c, sc, su, library=L)
     torch.cuda.synchronize()
     print(json.dumps({"prefill_group": {"name": name, "N": [N for _, N in probs], "K": K,
-                                        "M": PREFILL_M, "launches": launches}}))
+                                        "M": PREFILL_M, "launches": launches,
+                                        "contraction": "int8" if int8 else "fp16"}}))
 
 
 class Decode:
@@ -431,10 +436,11 @@ class Prefill:
                                  sc.data_ptr(), su.data_ptr(), PREFILL_M, *self.ws_args, s):
             raise RuntimeError("q4k_gemm_batch launch failed")
 
-    def parity(self, oracle):
+    def parity(self, oracle, library=None):
         """Layer 0: every projection through q4k_gemm and through the batched
         launches of the headline path, 8 sampled weight rows x all 512
-        activation rows each, against the oracle."""
+        activation rows each, against the oracle (library: the GEMM's int8
+        contraction instead of the default)."""
         torch, q4k = self.torch, self.q4k
         max_rel, checked = 0.0, 0
         batched = {}
@@ -442,13 +448,13 @@ class Prefill:
             K = self.shapes[idx[0]][1]
             c, sc, su = q4k.q4k_quantize_act(self.act_of[idx[0]])
             ys = q4k.q4k_gemm_batch([(self.weights[p][0], self.shapes[p][2]) for p in idx],
-                                    K, c, sc, su)
+                                    K, c, sc, su, library=library)
             batched.update(zip(idx, ys))
         for p, (name, K, N) in enumerate(self.shapes):
             wt = self.weights[p][0]
             src = self.act_of[p] if p not in (1, 2, 5) else self.act_of[{1: 0, 2: 0, 5: 4}[p]]
             c, sc, su = q4k.q4k_quantize_act(src)
-            y = q4k.q4k_gemm(wt, N, K, c, sc, su)
+            y = q4k.q4k_gemm(wt, N, K, c, sc, su, library=library)
             torch.cuda.synchronize()
             rc, rs, _ = oracle.quantize_act(src.cpu().numpy())
             rows = np.unique(np.r_[0, N - 1, np.random.default_rng(p).integers(0, N, 6)])
@@ -461,6 +467,35 @@ class Prefill:
                 max_rel = max(max_rel, float((err / np.maximum(np.abs(ref), 0.05)).max()))
                 checked += ref.size
         return {"outputs_checked": checked, "max_rel_err": max_rel}
+
+
+def prefill_int8(torch, q4k, pre, oracle, g_q, cap, steps):
+    """The same 36-layer prefill step with the GEMM's int8 contraction
+    (libq4k_gemm_int8.so: v_mfma_i32_32x32x32_i8, exact int32 sub-block dots,
+    three fp32 vector ops per output and sub-block), checked against the oracle
+    first, timed as the default."""
+    pre.L = q4k.lib_gemm_int8()
+    try:
+        parity = pre.parity(oracle, library=pre.L)
+        g8 = Decode.graph(pre, pre.gemm_unit, range(pre.units), cap)
+        g_q.replay()
+        g8.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g8.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+    finally:
+        pre.L = q4k.lib()
+    t = float(np.median(times))
+    tops = pre.ops / t / 1e12
+    return {"gemm_ms_per_step": round(t * 1e3, 3), "gemm_ms_per_step_dist": dist_ms(times),
+            "TOPS": round(tops, 1), "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "parity": parity}
 
 
 def measure_prefill(torch, q4k, qi, oracle, steps):
@@ -541,6 +576,7 @@ def measure_prefill(torch, q4k, qi, oracle, steps):
                         "timing": "median over %d steps of HIP events around the %d GEMM "
                                   "launches of a step" % (steps, pre.units)},
            "per_group": per_group, "single_call_per_shape": per_shape, "parity": parity,
+           "int8_contraction": prefill_int8(torch, q4k, pre, oracle, g_q, cap, steps),
            "matrix_vector_coissue": measure_coissue(torch, q4k)}
     del pre
     torch.cuda.empty_cache()
@@ -1403,7 +1439,7 @@ def main():
     import gemm_q4_super_amd as q4k
     import q4k_inputs as qi
     if args.prefill_group:
-        prefill_group(torch, q4k, qi, args.prefill_group)
+        prefill_group(torch, q4k, qi, args.prefill_group, int8=args.gemm_int8)
         return
     import oracle
 

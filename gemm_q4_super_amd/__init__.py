@@ -15,6 +15,7 @@ Functions carry the C names:
     q4k_gemm(w, N, K, codes, scales, sums, workspace="auto") -> y [M, N]
     q4k_gemm_batch([(w, N), ...], K, codes, scales, sums, workspace="auto")
                                                      -> [y, ...] (<= 8 products, one launch)
+        (both take library=lib_gemm_int8() for the GEMM's int8 contraction)
     gemm_workspace(device)                           -> the zero-filled GEMM workspace reused
                                                         by workspace="auto"
     q4k_moe_gemv(w, n_experts, stride, N, K, ids, route_w, codes, scales, sums,
@@ -34,6 +35,7 @@ from ._lib import (  # noqa: F401
     attn_workspace,
     gemm_workspace,
     lib,
+    lib_gemm_int8,
     lib_path,
     q4k_gemm,
     q4k_gemm_batch,

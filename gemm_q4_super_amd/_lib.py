@@ -6,6 +6,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libq4k.so")
+lib_gemm_int8_path = os.path.join(_HERE, "libq4k_gemm_int8.so")
 
 EXPORTED_SYMBOLS = (
     "q4k_quantize_act",
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
 _P = ctypes.c_void_p
 _I = ctypes.c_int64
 _lib = None
+_lib_int8 = None
 
 
 class GemvProblem(ctypes.Structure):
@@ -54,64 +56,81 @@ class Q4KError(RuntimeError):
         super().__init__("%s failed: %s (%d)" % (what, q4k_status_string(status), status))
 
 
+def _load(path):
+    try:
+        import torch  # noqa: F401  -- load torch's HIP runtime first (same soname)
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise RuntimeError("%s not built: run `python -m gemm_q4_super_amd.build` "
+                           "(or __graft_entry__.build())" % os.path.basename(path))
+    return _declare(ctypes.CDLL(path))
+
+
 def lib():
     """The loaded library (raises if libq4k.so has not been built)."""
     global _lib
     if _lib is None:
-        try:
-            import torch  # noqa: F401  -- load torch's HIP runtime first (same soname)
-        except ImportError:
-            pass
-        if not os.path.exists(lib_path):
-            raise RuntimeError("libq4k.so not built: run `python -m gemm_q4_super_amd.build` "
-                               "(or __graft_entry__.build())")
-        L = ctypes.CDLL(lib_path)
-        L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
-        L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
-        L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
-        L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
-                                     _I, _P, ctypes.c_size_t, _P]
-        L.q4k_gemm_batch_noalloc.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P,
-                                             _P, _P, _I, _P]
-        L.q4k_gemm_batch_noalloc.restype = ctypes.c_int
-        L.q4k_gemm_workspace_bytes.argtypes = []
-        L.q4k_gemm_workspace_bytes.restype = ctypes.c_size_t
-        L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
-        L.q4k_quantize_gemv_residual.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P]
-        L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
-                                              _I, _P]
-        L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
-                                   ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
-        L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
-        L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
-        L.q4k_moe_ffn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
-                                  ctypes.c_size_t, _P]
-        L.q4k_moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
-        L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
-        L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
-        L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
-        L.q6k_gemm.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
-        L.q4k_kv_store.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
-        L.q4k_attn_workspace_bytes.argtypes = [_I, _I, _I]
-        L.q4k_attn_workspace_bytes.restype = ctypes.c_size_t
-        L.q4k_attn_decode.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
-                                      ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
-        L.q4k_ceiling_stream_read.argtypes = [_P, _I, _I, _P, _P]
-        L.q4k_ceiling_stream_read.restype = ctypes.c_int
-        L.q4k_ceiling_empty.argtypes = [_I, _P]
-        L.q4k_ceiling_empty.restype = ctypes.c_int
-        L.q4k_ceiling_mfma_valu.argtypes = [_I, _I, ctypes.c_int, ctypes.c_int, _P, _P]
-        L.q4k_ceiling_mfma_valu.restype = ctypes.c_int
-        L.q4k_status_string.argtypes = [ctypes.c_int]
-        L.q4k_status_string.restype = ctypes.c_char_p
-        for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
-                     "q4k_quantize_gemv_residual",
-                     "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                     "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q6k_gemm", "q4k_kv_store",
-                     "q4k_attn_decode"):
-            getattr(L, name).restype = ctypes.c_int
-        _lib = L
+        _lib = _load(lib_path)
     return _lib
+
+
+def lib_gemm_int8():
+    """The same library with the prefill GEMM's int8 contraction
+    (libq4k_gemm_int8.so; raises if it has not been built)."""
+    global _lib_int8
+    if _lib_int8 is None:
+        _lib_int8 = _load(lib_gemm_int8_path)
+    return _lib_int8
+
+
+def _declare(L):
+    """Argument and result types of every exported call."""
+    L.q4k_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
+    L.q4k_gemv.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P]
+    L.q4k_gemm.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
+    L.q4k_gemm_batch.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P, _P, _P,
+                                 _I, _P, ctypes.c_size_t, _P]
+    L.q4k_gemm_batch_noalloc.argtypes = [ctypes.POINTER(GemmProblem), ctypes.c_int, _I, _P,
+                                         _P, _P, _I, _P]
+    L.q4k_gemm_batch_noalloc.restype = ctypes.c_int
+    L.q4k_gemm_workspace_bytes.argtypes = []
+    L.q4k_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.q4k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+    L.q4k_quantize_gemv_residual.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P]
+    L.q4k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I,
+                                          _I, _P]
+    L.q4k_moe_gemv.argtypes = [_P, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
+                               ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+    L.q4k_moe_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    L.q4k_moe_workspace_bytes.restype = ctypes.c_size_t
+    L.q4k_moe_ffn.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P,
+                              ctypes.c_size_t, _P]
+    L.q4k_moe_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+    L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+    L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
+    L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+    L.q6k_gemm.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
+    L.q4k_kv_store.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+    L.q4k_attn_workspace_bytes.argtypes = [_I, _I, _I]
+    L.q4k_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.q4k_attn_decode.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
+                                  ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+    L.q4k_ceiling_stream_read.argtypes = [_P, _I, _I, _P, _P]
+    L.q4k_ceiling_stream_read.restype = ctypes.c_int
+    L.q4k_ceiling_empty.argtypes = [_I, _P]
+    L.q4k_ceiling_empty.restype = ctypes.c_int
+    L.q4k_ceiling_mfma_valu.argtypes = [_I, _I, ctypes.c_int, ctypes.c_int, _P, _P]
+    L.q4k_ceiling_mfma_valu.restype = ctypes.c_int
+    L.q4k_status_string.argtypes = [ctypes.c_int]
+    L.q4k_status_string.restype = ctypes.c_char_p
+    for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
+                 "q4k_quantize_gemv_residual",
+                 "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
+                 "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q6k_gemm", "q4k_kv_store",
+                 "q4k_attn_decode"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
 
 
 def q4k_status_string(status: int) -> str:
@@ -278,7 +297,7 @@ def _gemm_ws(workspace, device):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def q4k_gemm(w, N, K, codes, scales, sums, y=None, workspace="auto"):
+def q4k_gemm(w, N, K, codes, scales, sums, y=None, workspace="auto", library=None):
     import torch
     for t, n in ((w, "w"), (codes, "codes"), (scales, "scales"), (sums, "sums")):
         _dev(t, n)
@@ -286,16 +305,17 @@ def q4k_gemm(w, N, K, codes, scales, sums, y=None, workspace="auto"):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     wp, wb = _gemm_ws(workspace, codes.device)
-    _check(lib().q4k_gemm(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(sums), M, _ptr(y),
-                          wp, wb, _stream(codes)), "q4k_gemm")
+    _check((library or lib()).q4k_gemm(_ptr(w), N, K, _ptr(codes), _ptr(scales), _ptr(sums), M,
+                                       _ptr(y), wp, wb, _stream(codes)), "q4k_gemm")
     return y
 
 
-def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None, workspace="auto"):
+def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None, workspace="auto", library=None):
     """Several prefill GEMMs against the same Q8 rows in one launch.
 
     `problems` is a sequence of (w, N); returns the list of outputs y_i [M, N_i]
-    (or fills `ys`)."""
+    (or fills `ys`).  `library` (for q4k_gemm too): lib_gemm_int8() runs the
+    int8 contraction; default lib()."""
     import torch
     problems = list(problems)
     if not problems:
@@ -310,8 +330,9 @@ def q4k_gemm_batch(problems, K, codes, scales, sums, ys=None, workspace="auto"):
         _dev(w, "w")
         arr[i] = GemmProblem(_ptr(w), _ptr(y), N)
     wp, wb = _gemm_ws(workspace, codes.device)
-    _check(lib().q4k_gemm_batch(arr, len(problems), K, _ptr(codes), _ptr(scales), _ptr(sums), M,
-                                wp, wb, _stream(codes)), "q4k_gemm_batch")
+    _check((library or lib()).q4k_gemm_batch(arr, len(problems), K, _ptr(codes), _ptr(scales),
+                                             _ptr(sums), M, wp, wb, _stream(codes)),
+           "q4k_gemm_batch")
     return ys
 
 

@@ -3,7 +3,11 @@
     python -m gemm_q4_super_amd.build
 
 Each csrc/*.hip is compiled to an object under _build/ in parallel, then
-linked into gemm_q4_super_amd/libq4k.so next to this file.
+linked into gemm_q4_super_amd/libq4k.so next to this file.  A second library,
+libq4k_gemm_int8.so, is the same objects with the prefill GEMM compiled for
+its int8 contraction (v_mfma_i32_32x32x32_i8 on the quants and codes) instead
+of the default fp16 one: the comparison the default was chosen by, kept built
+and tested.
 """
 from __future__ import annotations
 
@@ -40,39 +44,43 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I" + os.path.join(ROOT, "include")]
 
-
-# Q4K_GEMM_INT8=1 builds the prefill GEMM's int8 contraction instead of the
-# default fp16 one (same results to fp32 rounding; kept for comparison).
-if os.environ.get("Q4K_GEMM_INT8") == "1":
-    COMMON.append("-DGEMM_I8=true")
+LIB_GEMM_INT8 = os.path.join(HERE, "libq4k_gemm_int8.so")
 
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+def _compile(src: str, suffix: str = "", defs=()) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + suffix + ".o")
+    cmd = [hipcc()] + COMMON + list(defs) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    gemm_src = os.path.join(CSRC, "gemm.hip")
+    jobs = [(src, "", ()) for src in srcs] + [(gemm_src, "_int8", ("-DGEMM_I8=true",))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    base, int8_gemm = objs[:-1], objs[-1]
+    _link(base, LIB)
+    _link([o for o in base if os.path.basename(o) != "gemm.o"] + [int8_gemm], LIB_GEMM_INT8)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", LIB_GEMM_INT8)
     return LIB
 
 

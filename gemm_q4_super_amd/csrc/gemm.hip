@@ -67,7 +67,8 @@
 // acc += D * (a * d*sc)) instead of the fp16 one on integer-valued operands.
 // Both are parity-tested; on the 512-token prefill the int8 one measured
 // 1.27x slower (three vector ops per output and sub-block against one), so
-// fp16 is the default.  Build with Q4K_GEMM_INT8=1 for the int8 path.
+// fp16 is the default.  The build links the int8 form into a second library
+// (libq4k_gemm_int8.so) beside the default one.
 #ifndef GEMM_I8
 #define GEMM_I8 false
 #endif

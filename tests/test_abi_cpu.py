@@ -35,6 +35,21 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_int8_gemm_library_exports_the_same_calls():
+    """libq4k_gemm_int8.so (the GEMM's int8 contraction) is the same library
+    apart from the GEMM object: same entry points, same host checks."""
+    L8 = q4k.lib_gemm_int8()
+    for name in _declared():
+        assert hasattr(L8, name), name
+    P = q4k._lib.GemmProblem
+    arr = (P * 1)(P(A, A, 16))
+    need = L8.q4k_gemm_workspace_bytes()
+    assert need == q4k.lib().q4k_gemm_workspace_bytes()
+    assert L8.q4k_gemm(None, 16, 512, A, A, A, 16, A, None, 0, None) == EINVAL
+    assert L8.q4k_gemm_batch(arr, 1, 500, A, A, A, 16, None, 0, None) == ESHAPE
+    assert L8.q4k_gemm_batch(arr, 1, 512, A, A, A, 16, A, need - 1, None) == EWORKSPACE
+
+
 def test_status_strings(L):
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert q4k.q4k_status_string(st) != "unknown status"
