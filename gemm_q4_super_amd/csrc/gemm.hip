@@ -66,7 +66,7 @@
 // quants and codes, exact int32 sub-block dots, fp32 epilogue
 // acc += D * (a * d*sc)) instead of the fp16 one on integer-valued operands.
 // Both are parity-tested; on the 512-token prefill the int8 one measured
-// 1.27x slower (three vector ops per output and sub-block against one), so
+// about 1.3x slower (three vector ops per output and sub-block against one), so
 // fp16 is the default.  The build links the int8 form into a second library
 // (libq4k_gemm_int8.so) beside the default one.
 #ifndef GEMM_I8
