@@ -420,7 +420,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(const AttnArgs a) {
 }
 
 // Chunking: about kAttnTargetGroups workgroups in all, chunks a multiple of
-// one wave round per wave, at most kMaxAttnChunks per unit.
+// one wave round per wave, at most kMaxAttnChunks per unit, and at least
+// n_ctx/8 positions up to 256: the last workgroup's chunk-ordered merge grows
+// with the chunk count, so a short context is better cut into fewer, longer
+// chunks (Qwen3-4B heads, one token: 2048 positions 14.9 -> 12.7 us, 4096
+// 16.3 -> 14.3 us, 1024 11.8 -> 11.4 us; unchanged from 8192 on).
 struct AttnPlan {
     int nqb, units, chunk, n_chunks;
 };
@@ -433,7 +437,8 @@ AttnPlan plan_attn(int64_t M, int64_t n_head, int64_t n_kv, int64_t n_ctx) {
     const int64_t step = (int64_t)kWaves * 8;   // a chunk gives every wave whole passes
     int64_t want = std::max<int64_t>(1, std::min<int64_t>(kMaxAttnChunks, kAttnTargetGroups / p.units));
     int64_t chunk = (n_ctx + want - 1) / want;
-    chunk = std::max<int64_t>(step, (chunk + step - 1) / step * step);
+    const int64_t lo = std::min<int64_t>(256, (n_ctx / 8 + step - 1) / step * step);
+    chunk = std::max<int64_t>(std::max<int64_t>(step, lo), (chunk + step - 1) / step * step);
     p.chunk = (int)chunk;
     p.n_chunks = (int)((n_ctx + chunk - 1) / chunk);
     return p;
