@@ -114,6 +114,9 @@ CASES = [
     (6, 2, 1, 200, 200, 1.0),       # groups of 3: a partly filled query block
     (64, 8, 8, 2000, 2000, 1.0),    # groups of 8, 64 query vectors per kv head
     (32, 8, 1, 16384, 16384, 1.0),  # the long-context decode
+    (32, 8, 1, 2048, 2048, 1.0),    # short contexts: 8 to 16 chunks of 256 positions
+    (32, 8, 1, 3000, 3072, 2.0),
+    (32, 8, 2, 4096, 4096, 1.0),
 ]
 
 

@@ -342,6 +342,32 @@ def test_quantize_gemv_batch_bit_identical_to_single(q4k, oracle_lib, name):
         assert_close(a if rows is None else a[:, rows], ref, "batch %s problem %d" % (name, i))
 
 
+@pytest.mark.parametrize("group", ["qkv", "o", "gate_up", "down"])
+def test_quantize_gemv_batch_row_shard_bit_identical(q4k, oracle_lib, group):
+    """One GPU's share of an 8-way row shard of a decode launch group: the
+    first N/8 rows of each matrix (a prefix of its bytes) give, row for row,
+    the same bits as the full launch (a row's sum does not depend on the
+    launch shape), and the oracle within tolerance."""
+    import torch
+    idx = {"qkv": (0, 1, 2), "o": (3,), "gate_up": (4, 5), "down": (6,)}[group]
+    K = qi.QWEN3_4B_LAYER[idx[0]][1]
+    Ns = [qi.QWEN3_4B_LAYER[p][2] for p in idx]
+    ws = [qi.make_q4k_bytes(N, K, qi.weight_seed(1, 5, p)) for N, p in zip(Ns, idx)]
+    xs = [qi.make_act(1, K, qi.act_seed(500 + p)) for p in idx]
+    wd = [to_dev(w) for w in ws]
+    xd = [to_dev(x) for x in xs]
+    full = q4k.q4k_quantize_gemv_batch([(w, N, x) for w, N, x in zip(wd, Ns, xd)], K)
+    shard = q4k.q4k_quantize_gemv_batch([(w, N // 8, x) for w, N, x in zip(wd, Ns, xd)], K)
+    torch.cuda.synchronize()
+    for i, N in enumerate(Ns):
+        a, b = shard[i].cpu().numpy(), full[i].cpu().numpy()[:, :N // 8]
+        assert (a.view(np.uint32) == b.view(np.uint32)).all(), "%s problem %d" % (group, i)
+        rows = np.unique(np.r_[0, N // 8 - 1, np.random.default_rng(N).integers(0, N // 8, 24)])
+        rc, rs, _ = oracle_lib.quantize_act(xs[i])
+        ref = oracle_lib.matvec(ws[i], N, K, rc, rs, rows=rows)
+        assert_close(a[:, rows], ref, "shard %s problem %d" % (group, i))
+
+
 def test_quantize_gemv_batch_leaves_other_memory_untouched(q4k):
     """Outputs are written only inside each [M, N_i] block: guard words around
     every output survive."""
