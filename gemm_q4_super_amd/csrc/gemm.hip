@@ -961,9 +961,15 @@ hipError_t launch_tile(const GemmSet &set, int nsb, const int8_t *codes, const f
     s.groups = (int)tiles;
     const int64_t cus = std::min<int64_t>(cu_count(), kGemmMaxGroups);
     // Split tiles across workgroups only where whole tiles would leave CUs idle
-    // in the last round, and only where the counters fit the workspace.
+    // in the last round, and only where the counters fit the workspace.  The
+    // units are cut into one equal range per CU, except where cutting every
+    // tile into the same whole number of parts still keeps at least 90 % of
+    // the CUs busy (80 tiles: 3 parts on 240 workgroups): then no range
+    // straddles two tiles and each tile has the fewest parts to add (the
+    // 36-layer M = 512 step: {down} 56.7 -> 54.8 us, {o} 31.7 -> 31.3).
     if (ws && tiles % cus != 0 && tiles * C::NC <= kGemmCounters && s.units >= cus) {
-        s.groups = (int)cus;
+        const int64_t whole = tiles < cus ? tiles * (cus / tiles) : 0;
+        s.groups = (int)(10 * whole >= 9 * cus ? whole : cus);
         s.cnt = static_cast<int *>(ws);
         s.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kGemmCounters * 4);
     }
