@@ -25,6 +25,12 @@
 // to the workspace through agent-coherent stores, and the last workgroup to
 // finish a row block (a counter per row block) adds them up for that block --
 // fixed order, no float atomics, bit-reproducible, no separate launch.
+//
+// One-token layers take a shorter path with the same bits: the gate|up launch
+// holds the same rows of both projections in each workgroup and writes
+// Q8(SwiGLU(g, u)) itself (ACT_F32_H8), and moe_down_sum_kernel gives each
+// workgroup a few output rows and all of the token's slots, summing them in
+// slot order inside the workgroup -- no per-slot products or counters.
 #include <algorithm>
 
 #include "q4k_device.h"
@@ -33,7 +39,7 @@
 namespace q4k {
 namespace {
 
-constexpr int kMoeWaves = 4;         // waves per workgroup, at most
+constexpr int kMoeWaves = 4;         // waves per workgroup, at most (8 for ACT_F32_H8)
 constexpr int kMoeV = 8;             // row groups per lane
 constexpr int kMoeMC = 4;            // pairs per pass over a weight block
 constexpr int kMoeMC2MaxT = 8;       // up to this many tokens, 2 pairs per pass (fewer
@@ -41,8 +47,13 @@ constexpr int kMoeMC2MaxT = 8;       // up to this many tokens, 2 pairs per pass
 constexpr int kStageBytes = 256 + 64;   // one staged column: codes, 8 scales, 8 sums
 constexpr int kStageSlots = 2;          // column slots per wave, at most (the staged columns)
 constexpr int kFuseMaxT = 2;            // tokens up to which the FFN quantizes in its GEMVs
+constexpr int kDownSumSlots = 8;        // slots of a one-token layer whose down launch sums them in
+                                        // each workgroup
 
-enum { ACT_Q8 = 0, ACT_F32 = 1, ACT_SWIGLU = 2 };
+// ACT_F32_H8: fp32 rows quantized in the kernel, as ACT_F32, in a launch whose
+// workgroups each hold the same rows of both projections (gate in the first
+// half of the block, up in the second) and write Q8(SwiGLU(g, u)) of them.
+enum { ACT_Q8 = 0, ACT_F32 = 1, ACT_SWIGLU = 2, ACT_F32_H8 = 3 };
 
 struct MoeArgs {
     const uint8_t *w[2];       // expert matrices (w[1]: second projection of a shared launch)
@@ -64,6 +75,10 @@ struct MoeArgs {
     float *y;
     unsigned *cnt;
     int T;
+    // ACT_F32_H8: Q8 rows of h = SwiGLU(g, u), one per pair [P][N]
+    int8_t *hc;
+    float *hs;
+    int32_t *hsu;
 };
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
@@ -174,17 +189,22 @@ __device__ void routed_sum(const MoeArgs &A, const int *s_ids, int row_base, int
 // With zero_skipped, the last row of workgroups (blockIdx.y == gridDim.y - 1)
 // writes zeros to the rows of pairs whose id is out of range instead.
 template <int V, int MC, int MODE>
-__global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
+__global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(const MoeArgs A) {
     extern __shared__ __attribute__((aligned(16))) int lds_m[];
     const int P = A.P, E = A.E, N = A.N, nsb = A.nsb, lg_rg = A.lg_rg;
     int *s_ids = lds_m;                      // [P rounded up to 4]
     int *s_flag = s_ids + ((P + 3) & ~3);    // [E] expert touched
     int *s_pairs = s_flag + E;               // [P] this slot's pairs, ascending
-    __shared__ float red[kMoeWaves][8 * V][MC];
-    __shared__ int s_wt[kMoeWaves];
+    constexpr bool H8 = MODE == ACT_F32_H8;
+    constexpr int NWMAX = H8 ? 2 * kMoeWaves : kMoeWaves;
+    __shared__ float red[NWMAX][8 * V][MC];
+    __shared__ int s_wt[NWMAX];
     __shared__ int s_e;
+    static_assert(!H8 || MC == 1, "one pair per workgroup when h is formed");
+    __shared__ float hrow[H8 ? 8 * V : 1];         // H8: g then u of the block's rows
     const int RG = 1 << lg_rg, S = 8 >> lg_rg, RB = RG * V;
-    const int row_base = (int)blockIdx.x * RB;
+    const int RBr = H8 ? RB / 2 : RB;              // rows of each projection
+    const int row_base = (int)blockIdx.x * RBr;
     if (row_base >= N) return;                     // uniform per workgroup
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -210,7 +230,7 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
         for (int p = 0; p < P; ++p) {
             const int e = s_ids[p];
             if (e >= 0 && e < E) continue;
-            for (int n = row_base + tid; n < min(N, row_base + RB); n += nt)
+            for (int n = row_base + tid; n < min(N, row_base + RBr); n += nt)
                 A.out[0][(int64_t)p * N + n] = 0.0f;
         }
         return;
@@ -281,6 +301,9 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
     // the block's first row in 64 bits, 32-bit offsets within it
     const uint8_t *__restrict__ wb =
         A.w[mi] + (int64_t)e * A.stride + (int64_t)row_base * row_bytes;
+    // H8: row groups V/2.. are the same rows of the second projection
+    const uint8_t *__restrict__ wb_up =
+        H8 ? A.w[1] + (int64_t)e * A.stride + (int64_t)row_base * row_bytes : wb;
     const int span = nw * S;                       // columns per pass
     const int npass = (nsb + span - 1) / span;
     // this wave's activation stage: [S][MC] columns of codes, scales, sums
@@ -358,10 +381,13 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
             u32x4 qw[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const unsigned rr = (unsigned)(min(row_base + v * RG + r, N - 1) - row_base);
+                const bool up = H8 && v >= V / 2;      // compile-time per v
+                const int vv = up ? v - V / 2 : v;
+                const uint8_t *__restrict__ wv = up ? wb_up : wb;
+                const unsigned rr = (unsigned)(min(row_base + vv * RG + r, N - 1) - row_base);
                 const unsigned o = rr * row_bytes + (unsigned)bc * 144u;
-                hd[v] = *reinterpret_cast<const unsigned *>(wb + (o + 4u * (lane & 3)));
-                qw[v] = load_weights16(wb + (o + 16u + 16u * L.l));
+                hd[v] = *reinterpret_cast<const unsigned *>(wv + (o + 4u * (lane & 3)));
+                qw[v] = load_weights16(wv + (o + 16u + 16u * L.l));
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (MODE == ACT_Q8) {
@@ -439,21 +465,168 @@ __global__ __launch_bounds__(256) void moe_kernel(const MoeArgs A) {
         __syncthreads();
         for (int i = threadIdx.x; i < RB * MC; i += blockDim.x) {
             const int rr = i / MC, m = i % MC;
-            const int n = row_base + rr;
+            const int n = row_base + (H8 ? rr % RBr : rr);
             if (m < mc && n < N) {
                 float t = 0.0f;
                 for (int wv = 0; wv < nw; ++wv)
                     for (int k = 0; k < S; ++k) t += red[wv][k * RB + rr][m];
-                float *o = out + (int64_t)s_pairs[c0 + m] * N + n;
-                if (A.cnt)
-                    __hip_atomic_store(o, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else
-                    *o = t;
+                if constexpr (H8) {
+                    hrow[rr] = t;
+                } else {
+                    float *o = out + (int64_t)s_pairs[c0 + m] * N + n;
+                    if (A.cnt)
+                        __hip_atomic_store(o, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *o = t;
+                }
             }
         }
         __syncthreads();
+        if constexpr (H8) {
+            // h = SwiGLU(g, u) of the block's rows, quantized in blocks of 32
+            // (8 lanes x 4 values each, the quantizer's own layout): the same
+            // codes the down launch would form from g and u
+            if (wave == 0) {
+                // one value per lane (the fp64 exp is the long part), then the
+                // quantizer's 8 lanes x 4 values per block
+                for (int j = lane; j < RBr; j += 64) hrow[j] = swiglu1(hrow[j], hrow[RBr + j]);
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+                const int nb = RBr / 32;
+                const int bq = min(lane >> 3, nb - 1), q4 = lane & 7;
+                const int j = 32 * bq + 4 * q4;
+                const f32x4 h4 = {hrow[j], hrow[j + 1], hrow[j + 2], hrow[j + 3]};
+                const Q8Lane q = quantize_block8(h4);
+                if ((lane >> 3) < nb) {
+                    const int pr = s_pairs[c0];
+                    *reinterpret_cast<unsigned *>(A.hc + (int64_t)pr * N + row_base + j) = q.codes;
+                    if (q4 == 0) {
+                        const int64_t so = (int64_t)pr * (N / 32) + row_base / 32 + bq;
+                        A.hs[so] = q.d;
+                        A.hsu[so] = q.sum;
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
     if (A.cnt) routed_sum(A, s_ids, row_base, RB);
+}
+
+// Down projection of a one-token layer with the routed sum in the workgroup:
+// a workgroup takes RG = 8 rows of the output and every slot of the token
+// (each slot's expert weights for those rows), so no workgroup waits for
+// another.  Its waves are nwc column waves (one column of a pass each) times
+// PM/PH slot sets of PH slots (the slots' weights in registers at once).  The
+// lane layout, the staging of the prepared Q8 rows of h and the order of every
+// sum are those of moe_kernel for the same K (S = 1: K <= 1024): a slot's
+// product z is the same float, and y[n] = sum over slots s in order of
+// route_w[s] * z[s][n] (slots whose id is out of range skipped) the same as
+// the last workgroup of a row block forms it there.
+template <int PM, int PH>
+__global__ __launch_bounds__(512) void moe_down_sum_kernel(const MoeArgs A) {
+    static_assert(PM % PH == 0 && PH % 4 == 0 && PH <= 8, "slot sets of 4 or 8");
+    constexpr int kSets = PM / PH;
+    __shared__ float red[kMoeWaves][8][PM];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kMoeWaves * kSets][PH][kStageBytes];
+    const int P = A.P, E = A.E, N = A.N, nsb = A.nsb;
+    const int row_base = (int)blockIdx.x * 8;
+    if (row_base >= N) return;                     // uniform per workgroup
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwc = ((int)blockDim.x >> 6) / kSets;  // column waves
+    const int set = wave / nwc, wc = wave % nwc;
+    const int p0 = set * PH;                       // the wave's first slot
+    const int r = lane >> 3;                       // row of the lane group
+    const LaneMap L(lane & 7);
+    const ScaleBits SB(lane & 7);
+    const int K = nsb * 256, nblk = nsb * 8;
+    const unsigned row_bytes = (unsigned)nsb * 144u;
+    const unsigned rr = (unsigned)min(row_base + r, N - 1);
+    // the slots' experts (scalar loads); an out-of-range id reads expert 0 and
+    // is left out of the sum; slots past P repeat slot P-1's addresses (cache
+    // hits) and are left out too
+    int ex[PH];
+#pragma unroll
+    for (int p = 0; p < PH; ++p) {
+        const int e = A.ids[min(p0 + p, P - 1)];
+        ex[p] = e >= 0 && e < E ? e : 0;
+    }
+    float acc[PH];
+#pragma unroll
+    for (int p = 0; p < PH; ++p) acc[p] = 0.0f;
+    const int npass = (nsb + nwc - 1) / nwc;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int b = pass * nwc + wc;             // the wave's column
+        const bool live = b < nsb;
+        const int bc = min(b, nsb - 1);
+        // prepared Q8 rows of the slots: codes as 16 lanes x 16 bytes per slot
+        // (slots p0 + 4i + lane/16), scales and sums as 8 lanes x 4 bytes
+        // (slot p0 + lane/8)
+        i32x4 qc[PH / 4];
+#pragma unroll
+        for (int i = 0; i < PH / 4; ++i) {
+            const int k = min(p0 + (lane >> 4) + 4 * i, P - 1);
+            qc[i] = *reinterpret_cast<const i32x4 *>(A.codes + (int64_t)k * K + 256 * bc +
+                                                     16 * (lane & 15));
+        }
+        const int ks = min(p0 + (lane >> 3), P - 1);
+        const int64_t so = (int64_t)ks * nblk + 8 * bc + (lane & 7);
+        const float qa = A.scales[so];
+        const int qs = A.sums[so];
+        __builtin_amdgcn_sched_barrier(0);
+        unsigned hd[PH];
+        u32x4 qw[PH];
+#pragma unroll
+        for (int p = 0; p < PH; ++p) {
+            const uint8_t *__restrict__ wp = A.w[0] + (int64_t)ex[p] * A.stride;
+            const int64_t o = (int64_t)rr * row_bytes + (int64_t)bc * 144;
+            hd[p] = *reinterpret_cast<const unsigned *>(wp + o + 4 * (lane & 3));
+            qw[p] = load_weights16(wp + o + 16 + 16 * L.l);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < PH / 4; ++i)
+            *reinterpret_cast<i32x4 *>(&stage[wave][(lane >> 4) + 4 * i][16 * (lane & 15)]) = qc[i];
+        if ((lane >> 3) < PH) {
+            reinterpret_cast<float *>(&stage[wave][lane >> 3][256])[lane & 7] = qa;
+            reinterpret_cast<float *>(&stage[wave][lane >> 3][288])[lane & 7] = (float)qs;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): the stage is written
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < PH; ++p) {
+            float ds, dm;
+            decode_scale_bits(SB, quad_gather(hd[p]), ds, dm);
+            const uint8_t *st = &stage[wave][p][0];
+            const i32x4 cA = *reinterpret_cast<const i32x4 *>(st + L.offA);
+            const i32x4 cB = *reinterpret_cast<const i32x4 *>(st + L.offB);
+            const float a = reinterpret_cast<const float *>(st + 256)[L.l];
+            const float sm = reinterpret_cast<const float *>(st + 288)[L.l];
+            int qlo[4], qhi[4];
+            unpack_nibbles(qw[p], qlo, qhi);
+            const int D = subblock_dot(L, qlo, qhi, cA, cB);
+            const float t = a * fmaf(ds, (float)D, -(dm * sm));
+            acc[p] += live ? t : 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // the next pass rewrites the stage
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int p = 0; p < PH; ++p) {
+        const float t = group8_sum(acc[p]);
+        if (L.l == 0) red[wc][r][p0 + p] = t;
+    }
+    __syncthreads();
+    if (tid < 8 && row_base + tid < N) {
+        float v = 0.0f;
+        for (int p = 0; p < P; ++p) {
+            const int e = A.ids[p];
+            float z = 0.0f;
+            for (int c = 0; c < nwc; ++c) z += red[c][tid][p];
+            if (e >= 0 && e < E) v = fmaf(A.route_w[p], z, v);
+        }
+        A.y[row_base + tid] = v;
+    }
 }
 
 // Launch shape for K = 256*nsb: column slots per wave enough that at most
@@ -487,12 +660,19 @@ hipError_t launch_kernel(const MoeArgs &A, int64_t T, int nmat, const Shape &sh,
         hipLaunchKernelGGL(kern, grid, dim3(64 * sh.nw),
                            moe_lds_bytes(A.P, A.E, sh.nw, sh.S, MC), stream, A);
     };
-    if (T == 1)
-        go(moe_kernel<kMoeV, 1, MODE>, 1);
-    else if (T <= kMoeMC2MaxT)
-        go(moe_kernel<kMoeV, 2, MODE>, 2);
-    else
-        go(moe_kernel<kMoeV, kMoeMC, MODE>, kMoeMC);
+    if constexpr (MODE == ACT_F32_H8) {
+        // one token: a workgroup holds RB/2 rows of both projections
+        const dim3 g8((unsigned)((A.N + sh.RB / 2 - 1) / (sh.RB / 2)), (unsigned)A.slots);
+        hipLaunchKernelGGL((moe_kernel<kMoeV, 1, MODE>), g8, dim3(64 * sh.nw),
+                           moe_lds_bytes(A.P, A.E, sh.nw, sh.S, 1), stream, A);
+    } else {
+        if (T == 1)
+            go(moe_kernel<kMoeV, 1, MODE>, 1);
+        else if (T <= kMoeMC2MaxT)
+            go(moe_kernel<kMoeV, 2, MODE>, 2);
+        else
+            go(moe_kernel<kMoeV, kMoeMC, MODE>, kMoeMC);
+    }
     return hipGetLastError();
 }
 
@@ -579,12 +759,68 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     float *hs = reinterpret_cast<float *>(hq + f32_bytes(P, F / 4));
     int32_t *hsu = reinterpret_cast<int32_t *>(hq + f32_bytes(P, F / 4) + f32_bytes(P, F / 32));
     const int E = (int)n_experts;
+    const Shape sh1 = shape(H / kQK), sh2 = shape(F / kQK);
+    if (T == 1 && topk <= kDownSumSlots && sh2.lg_rg == 3) {
+        // One token: the gate|up launch forms Q8(h) itself (each workgroup
+        // holds the same rows of both projections), and the down launch sums
+        // the slots inside each workgroup -- no per-slot products, counters
+        // or waits between workgroups.  Same bits as the launches below.
+        MoeArgs A = {};
+        A.w[0] = w_gate;
+        A.w[1] = w_up;
+        A.out[0] = g;
+        A.out[1] = u;
+        A.stride = stride_gu;
+        A.N = (int)F;
+        A.nsb = (int)(H / kQK);
+        A.topk = (int)topk;
+        A.P = (int)P;
+        A.E = E;
+        A.slots = (int)(P < E ? P : E);
+        A.ids = ids;
+        A.direct = 1;
+        A.xa = x;
+        A.hc = hc;
+        A.hs = hs;
+        A.hsu = hsu;
+        // RG = 8 rows per lane group and one column per wave, as many waves as
+        // sh1 covers columns per pass: a lane adds the same columns in the same
+        // order as under sh1, so g and u are the gate|up launch's own bits
+        Shape sh8;
+        sh8.lg_rg = 3;
+        sh8.S = 1;
+        sh8.nw = sh1.nw * sh1.S;
+        sh8.RB = 8 * kMoeV;
+        A.lg_rg = sh8.lg_rg;
+        hipError_t err = launch_kernel<ACT_F32_H8>(A, T, 1, sh8, stream);
+        if (err != hipSuccess) return err;
+        MoeArgs B = {};
+        B.w[0] = w_down;
+        B.stride = stride_down;
+        B.N = (int)H;
+        B.nsb = (int)(F / kQK);
+        B.P = (int)P;
+        B.E = E;
+        B.ids = ids;
+        B.codes = hc;
+        B.scales = hs;
+        B.sums = hsu;
+        B.route_w = route_w;
+        B.y = y;
+        // up to 4 slots: one set of waves; up to 8: two sets of 4 slots
+        if (topk <= 4)
+            hipLaunchKernelGGL((moe_down_sum_kernel<4, 4>), dim3((unsigned)((H + 7) / 8)),
+                               dim3(64 * sh2.nw), 0, stream, B);
+        else
+            hipLaunchKernelGGL((moe_down_sum_kernel<kDownSumSlots, 4>),
+                               dim3((unsigned)((H + 7) / 8)), dim3(2 * 64 * sh2.nw), 0, stream, B);
+        return hipGetLastError();
+    }
     // In-kernel activations quantize a token's row once per workgroup that
     // reads it (row blocks x experts); past a few tokens that repetition costs
     // more than the launches a separate quantizer needs.  Same codes either way.
     const bool fuse = T <= kFuseMaxT;
     // gate and up in one launch
-    const Shape sh1 = shape(H / kQK);
     MoeArgs A = {};
     A.w[0] = w_gate;
     A.w[1] = w_up;
@@ -617,7 +853,6 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     if (err != hipSuccess) return err;
     // down: SwiGLU(g, u) quantized in the kernel, per-slot products z, and the
     // routed sum by the last workgroup of each row block
-    const Shape sh2 = shape(F / kQK);
     MoeArgs B = A;
     B.route_w = route_w;
     B.y = y;

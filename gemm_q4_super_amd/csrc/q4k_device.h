@@ -148,13 +148,14 @@ __device__ __forceinline__ Q8Lane quantize_block8(f32x4 v) {
 // SwiGLU of four values, h = silu(g) * u = g / (1 + e^-g) * u, evaluated in
 // fp64 from the fp32 g, u and rounded to fp32 once (the expert FFN's
 // nonlinearity; the same arithmetic wherever h is formed).
+__device__ __forceinline__ float swiglu1(float g, float u) {
+    const double gd = (double)g;
+    return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+}
 __device__ __forceinline__ f32x4 swiglu4(f32x4 g, f32x4 u) {
     f32x4 h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double gd = (double)g[i];
-        h[i] = (float)(gd / (1.0 + exp(-gd)) * (double)u[i]);
-    }
+    for (int i = 0; i < 4; ++i) h[i] = swiglu1(g[i], u[i]);
     return h;
 }
 

@@ -286,6 +286,46 @@ def test_moe_ffn_repeated_and_bad_ids_and_two_passes(q4k, oracle_lib):
                         "moe_ffn repeated/bad ids")
 
 
+@pytest.mark.parametrize("topk,F_,bad", [(1, 512, None), (3, 1024, 1), (6, 512, 4), (8, 1024, 7)])
+def test_moe_ffn_one_token(q4k, oracle_lib, topk, F_, bad):
+    """One token: gate|up forms Q8(h) in its workgroups and the down launch
+    sums the slots inside each workgroup (4- and 8-slot forms, 2 and 4 waves,
+    gate|up over several passes at H = 3072, an out-of-range id): equal to the
+    chain bit for bit and close to the oracle."""
+    import torch
+    n_exp, H_ = 9, 3072
+    wg = np.concatenate([qi.make_q4k_bytes(F_, H_, 2300 + e) for e in range(n_exp)])
+    wu = np.concatenate([qi.make_q4k_bytes(F_, H_, 2400 + e) for e in range(n_exp)])
+    wd = np.concatenate([qi.make_q4k_bytes(H_, F_, 2500 + e) for e in range(n_exp)])
+    ids = np.random.default_rng(topk).permutation(n_exp)[:topk].astype(np.int32)[None, :]
+    if bad is not None:
+        ids[0, bad % topk] = n_exp + 3
+    rw = np.random.default_rng(10 + topk).standard_normal((1, topk)).astype(np.float32)
+    x = to_dev(qi.make_act(1, H_, 92 + topk))
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
+    y1b = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
+    g, u, hc, hs, y2 = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
+    torch.cuda.synchronize()
+    y1, y1b = y1.cpu().numpy(), y1b.cpu().numpy()
+    assert np.isfinite(y1).all()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    assert (y1.view(np.uint32) == y1b.view(np.uint32)).all()
+    keep = ((ids >= 0) & (ids < n_exp)).ravel()
+    ids_o = np.where(keep[None, :], ids, 0).astype(np.int32)
+    rw_o = np.where(keep[None, :], rw, 0).astype(np.float32)
+    ref = oracle_lib.moe_layer(wg, wu, wd, n_exp, H_, F_, ids_o, rw_o, x.cpu().numpy())
+    for k in ("g", "u", "h", "hc", "hs"):
+        ref[k] = np.where(keep[:, None], ref[k], 0).astype(ref[k].dtype)
+    g[~keep] = 0.0
+    u[~keep] = 0.0
+    hc[~keep] = 0
+    hs[~keep] = 0.0
+    _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids_o, rw_o, wd, H_, F_,
+                        "moe_ffn one token topk=%d F=%d" % (topk, F_))
+
+
 def test_moe_routed_sum_in_launch_reuses_workspace(q4k, oracle_lib):
     """The weighted sum is formed inside the down launch by the last
     workgroup of each row block: one zero-filled workspace serves repeated
