@@ -26,11 +26,13 @@
 // finish a row block (a counter per row block) adds them up for that block --
 // fixed order, no float atomics, bit-reproducible, no separate launch.
 //
-// One-token layers take a shorter path with the same bits: the gate|up launch
-// holds the same rows of both projections in each workgroup and writes
-// Q8(SwiGLU(g, u)) itself (ACT_F32_H8), and moe_down_sum_kernel gives each
-// workgroup a few output rows and all of the token's slots, summing them in
-// slot order inside the workgroup -- no per-slot products or counters.
+// Layers of up to 256 pairs take shorter paths with the same bits: for one or
+// two tokens the gate|up launch holds the same rows of both projections in
+// each workgroup and writes Q8(SwiGLU(g, u)) itself (ACT_F32_H8), and the
+// down launch (moe_down_sum_kernel for one token, moe_down_rows_kernel for
+// more) gives each workgroup a few output rows and every pair, summing the
+// slots in slot order inside the workgroup -- no per-slot products or
+// counters.
 #include <algorithm>
 
 #include "q4k_device.h"
@@ -49,6 +51,9 @@ constexpr int kStageSlots = 2;          // column slots per wave, at most (the s
 constexpr int kFuseMaxT = 2;            // tokens up to which the FFN quantizes in its GEMVs
 constexpr int kDownSumSlots = 8;        // slots of a one-token layer whose down launch sums them in
                                         // each workgroup
+constexpr int kRowsMaxPairs = 256;      // pairs up to which the down launch takes every pair per
+                                        // row block (moe_down_rows_kernel)
+constexpr int kRowsChunk = 8;           // experts whose weights a lane holds at once there
 
 // ACT_F32_H8: fp32 rows quantized in the kernel, as ACT_F32, in a launch whose
 // workgroups each hold the same rows of both projections (gate in the first
@@ -629,6 +634,164 @@ __global__ __launch_bounds__(512) void moe_down_sum_kernel(const MoeArgs A) {
     }
 }
 
+// Down projection with the routed sum in the workgroup, for several tokens
+// (P <= kRowsMaxPairs pairs, K <= 1024 so that a pass is one column per
+// wave): a workgroup takes RG = 8 output rows, sorts the valid pairs by
+// expert once (a count per expert, a scan, cursors), and takes them XB at a
+// time: each pair's expert weights for the wave's column of the 8 rows and
+// its prepared Q8 row of h, all requested together, then the dots.  Its waves
+// are nwc column waves times sets of them that take alternate chunks, so
+// several chunks' loads are in flight.  The per-pair products stay in LDS and
+// the routed sum is formed from them in slot order: no per-slot products in
+// memory, no counters.  Lane layout and the order of every sum are those of
+// moe_kernel for the same K, so the bits equal the chain's.
+template <int XB>
+__global__ __launch_bounds__(1024) void moe_down_rows_kernel(const MoeArgs A) {
+    extern __shared__ __attribute__((aligned(16))) int lds_r[];
+    __shared__ int s_wt[16];
+    __shared__ int s_tot[1];
+    const int P = A.P, E = A.E, N = A.N, nsb = A.nsb, topk = A.topk;
+    const int row_base = (int)blockIdx.x * 8;
+    if (row_base >= N) return;                     // uniform per workgroup
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    const int nwc = nsb;                           // column waves (one pass)
+    const int sets = (nt >> 6) / nwc, set = wave / nwc, wc = wave % nwc;
+    int *s_ids = lds_r;                            // [P rounded up to 4]
+    int *cnt = s_ids + ((P + 3) & ~3);             // [E] pairs per expert, then cursor
+    int *sorted = cnt + E;                         // [P] valid pairs by expert
+    float *red = reinterpret_cast<float *>(
+        reinterpret_cast<uint8_t *>(lds_r) + align16(sizeof(int) * (((P + 3) & ~3) + (size_t)E + P)));
+    uint8_t *stage = reinterpret_cast<uint8_t *>(red) + align16(sizeof(float) * (size_t)nwc * 8 * P) +
+                     (size_t)wave * XB * kStageBytes;
+
+    // ---- grouping: a count per expert, a scan of the counts over expert
+    // ranges, then each valid pair placed at its expert's cursor
+    for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
+    for (int e = tid; e < E; e += nt) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += nt) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    {
+        const int per = (E + nt - 1) / nt;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        int c = 0;
+        for (int e = e0; e < e1; ++e) c += cnt[e];
+        int wtot;
+        const int ex = wave_exclusive_scan(c, &wtot);
+        if (lane == 0) s_wt[wave] = wtot;
+        __syncthreads();
+        int bc = ex;
+        for (int k = 0; k < wave; ++k) bc += s_wt[k];
+        for (int e = e0; e < e1; ++e) {
+            const int n = cnt[e];
+            cnt[e] = bc;                           // cursor of the expert's pairs
+            bc += n;
+        }
+        if (tid == nt - 1) s_tot[0] = bc;          // valid pairs
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += nt) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) sorted[atomicAdd(&cnt[e], 1)] = p;   // order within an expert is free
+    }
+    __syncthreads();
+
+    const int r = lane >> 3;                       // row of the lane group
+    const LaneMap L(lane & 7);
+    const ScaleBits SB(lane & 7);
+    const int K = nsb * 256, nblk = nsb * 8;
+    const unsigned row_bytes = (unsigned)nsb * 144u;
+    // the lane's row and column within an expert's matrix
+    const unsigned lo = (unsigned)min(row_base + r, N - 1) * row_bytes + (unsigned)wc * 144u;
+    // Chunks of XB consecutive pairs in expert order, every load of a chunk
+    // issued together: each pair's expert rows (pairs of one expert sit side
+    // by side, so the repeats hit in cache), then its Q8 rows of h for the
+    // wave's column -- one wait per chunk, and the wave sets' chunks in
+    // flight side by side.
+    const int nv = s_tot[0];
+    const int nchunks = (nv + XB - 1) / XB;
+    static_assert(XB == 8, "two code loads and one scale load per lane");
+    for (int c = set; c < nchunks; c += sets) {
+        const int q0 = c * XB;
+        unsigned hd[XB];
+        u32x4 qw[XB];
+#pragma unroll
+        for (int k = 0; k < XB; ++k) {
+            const int e = s_ids[sorted[min(q0 + k, nv - 1)]];
+            const uint8_t *__restrict__ wp = A.w[0] + (int64_t)e * A.stride;
+            hd[k] = *reinterpret_cast<const unsigned *>(wp + (lo + 4u * (lane & 3)));
+            qw[k] = load_weights16(wp + (lo + 16u + 16u * L.l));
+        }
+        // codes as 16 lanes x 16 bytes per pair (pairs 4i + lane/16), scales
+        // and sums as 8 lanes x 4 bytes (pair lane/8)
+        i32x4 cv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pc = sorted[min(q0 + (lane >> 4) + 4 * i, nv - 1)];
+            cv[i] = *reinterpret_cast<const i32x4 *>(A.codes + (int64_t)pc * K + 256 * wc + 16 * (lane & 15));
+        }
+        const int ps = sorted[min(q0 + (lane >> 3), nv - 1)];
+        const int64_t so = (int64_t)ps * nblk + 8 * wc + (lane & 7);
+        const float qa = A.scales[so];
+        const int qs = A.sums[so];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<i32x4 *>(stage + (size_t)((lane >> 4) + 4 * i) * kStageBytes + 16 * (lane & 15)) = cv[i];
+        reinterpret_cast<float *>(stage + (size_t)(lane >> 3) * kStageBytes + 256)[lane & 7] = qa;
+        reinterpret_cast<float *>(stage + (size_t)(lane >> 3) * kStageBytes + 288)[lane & 7] = (float)qs;
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): the stage is written
+        __builtin_amdgcn_wave_barrier();
+        const int nq = min(XB, nv - q0);
+#pragma unroll
+        for (int k = 0; k < XB; ++k) {
+            if (k >= nq) break;                    // uniform
+            float ds, dm;
+            decode_scale_bits(SB, quad_gather(hd[k]), ds, dm);
+            int qlo[4], qhi[4];
+            unpack_nibbles(qw[k], qlo, qhi);
+            const uint8_t *sj = stage + (size_t)k * kStageBytes;
+            const i32x4 cA = *reinterpret_cast<const i32x4 *>(sj + L.offA);
+            const i32x4 cB = *reinterpret_cast<const i32x4 *>(sj + L.offB);
+            const float a = reinterpret_cast<const float *>(sj + 256)[L.l];
+            const float sm = reinterpret_cast<const float *>(sj + 288)[L.l];
+            const int D = subblock_dot(L, qlo, qhi, cA, cB);
+            float acc = 0.0f;
+            acc += a * fmaf(ds, (float)D, -(dm * sm));
+            const float t = group8_sum(acc);
+            if (L.l == 0) red[((size_t)wc * 8 + r) * P + sorted[q0 + k]] = t;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // the stage is rewritten next
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    // y[t][n] = sum over slots s in order of route_w * z, z the column terms in order
+    const int T = P / topk;
+    for (int i = tid; i < T * 8; i += nt) {
+        const int t = i >> 3, rw = i & 7, n = row_base + rw;
+        if (n >= N) continue;
+        float v = 0.0f;
+        for (int sl = 0; sl < topk; ++sl) {
+            const int p = t * topk + sl;
+            const int e = s_ids[p];
+            if (e >= 0 && e < E) {
+                float z = 0.0f;
+                for (int cc = 0; cc < nwc; ++cc) z += red[((size_t)cc * 8 + rw) * P + p];
+                v = fmaf(A.route_w[p], z, v);
+            }
+        }
+        A.y[(int64_t)t * N + n] = v;
+    }
+}
+
+// Dynamic LDS of moe_down_rows_kernel.
+size_t rows_lds_bytes(int P, int E, int nwc, int nw) {
+    return align16(sizeof(int) * (((size_t)(P + 3) & ~size_t(3)) + (size_t)E + P)) +
+           align16(sizeof(float) * (size_t)nwc * 8 * P) + (size_t)nw * kRowsChunk * kStageBytes;
+}
+
 // Launch shape for K = 256*nsb: column slots per wave enough that at most
 // kMoeWaves waves cover K in one pass (S = kStageSlots at most; wider K takes
 // several passes).  The shape depends on K alone -- not on the activation
@@ -760,11 +923,13 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     int32_t *hsu = reinterpret_cast<int32_t *>(hq + f32_bytes(P, F / 4) + f32_bytes(P, F / 32));
     const int E = (int)n_experts;
     const Shape sh1 = shape(H / kQK), sh2 = shape(F / kQK);
-    if (T == 1 && topk <= kDownSumSlots && sh2.lg_rg == 3) {
-        // One token: the gate|up launch forms Q8(h) itself (each workgroup
-        // holds the same rows of both projections), and the down launch sums
-        // the slots inside each workgroup -- no per-slot products, counters
-        // or waits between workgroups.  Same bits as the launches below.
+    // gate|up forming Q8(h) itself: each workgroup holds the same rows of both
+    // projections for one pair (slot a = pair a, a token's repeated expert
+    // computed twice with the same bits); RG = 8 rows per lane group and one
+    // column per wave, as many waves as sh1 covers columns per pass, so a lane
+    // adds the same columns in the same order as under sh1 and g, u keep the
+    // gate|up launch's own bits
+    auto gate_up_h8 = [&]() {
         MoeArgs A = {};
         A.w[0] = w_gate;
         A.w[1] = w_up;
@@ -776,44 +941,87 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
         A.topk = (int)topk;
         A.P = (int)P;
         A.E = E;
-        A.slots = (int)(P < E ? P : E);
+        A.slots = (int)P;
         A.ids = ids;
         A.direct = 1;
         A.xa = x;
         A.hc = hc;
         A.hs = hs;
         A.hsu = hsu;
-        // RG = 8 rows per lane group and one column per wave, as many waves as
-        // sh1 covers columns per pass: a lane adds the same columns in the same
-        // order as under sh1, so g and u are the gate|up launch's own bits
         Shape sh8;
         sh8.lg_rg = 3;
         sh8.S = 1;
         sh8.nw = sh1.nw * sh1.S;
         sh8.RB = 8 * kMoeV;
         A.lg_rg = sh8.lg_rg;
-        hipError_t err = launch_kernel<ACT_F32_H8>(A, T, 1, sh8, stream);
+        return launch_kernel<ACT_F32_H8>(A, T, 1, sh8, stream);
+    };
+    // down on the prepared Q8(h) with the routed sum inside each workgroup
+    MoeArgs B = {};
+    B.w[0] = w_down;
+    B.stride = stride_down;
+    B.N = (int)H;
+    B.nsb = (int)(F / kQK);
+    B.topk = (int)topk;
+    B.P = (int)P;
+    B.E = E;
+    B.ids = ids;
+    B.codes = hc;
+    B.scales = hs;
+    B.sums = hsu;
+    B.act_per_slot = 1;
+    B.route_w = route_w;
+    B.y = y;
+    B.T = (int)T;
+    const dim3 down_grid((unsigned)((H + 7) / 8));
+    if (T == 1 && topk <= kDownSumSlots && sh2.lg_rg == 3) {
+        // One token: no grouping at all; the down workgroups hold every slot's
+        // weights at once.  Same bits as the launches below.
+        hipError_t err = gate_up_h8();
         if (err != hipSuccess) return err;
-        MoeArgs B = {};
-        B.w[0] = w_down;
-        B.stride = stride_down;
-        B.N = (int)H;
-        B.nsb = (int)(F / kQK);
-        B.P = (int)P;
-        B.E = E;
-        B.ids = ids;
-        B.codes = hc;
-        B.scales = hs;
-        B.sums = hsu;
-        B.route_w = route_w;
-        B.y = y;
         // up to 4 slots: one set of waves; up to 8: two sets of 4 slots
         if (topk <= 4)
-            hipLaunchKernelGGL((moe_down_sum_kernel<4, 4>), dim3((unsigned)((H + 7) / 8)),
-                               dim3(64 * sh2.nw), 0, stream, B);
+            hipLaunchKernelGGL((moe_down_sum_kernel<4, 4>), down_grid, dim3(64 * sh2.nw), 0, stream, B);
         else
-            hipLaunchKernelGGL((moe_down_sum_kernel<kDownSumSlots, 4>),
-                               dim3((unsigned)((H + 7) / 8)), dim3(2 * 64 * sh2.nw), 0, stream, B);
+            hipLaunchKernelGGL((moe_down_sum_kernel<kDownSumSlots, 4>), down_grid,
+                               dim3(2 * 64 * sh2.nw), 0, stream, B);
+        return hipGetLastError();
+    }
+    if (T > 1 && P <= kRowsMaxPairs && sh2.lg_rg == 3) {
+        // A few tokens: Q8(h) from the gate|up launch (two tokens) or the
+        // quantizer (more), then one down launch over every pair per row
+        // block that sums the slots in the workgroup.  Same bits.
+        hipError_t err;
+        if (T <= kFuseMaxT) {
+            err = gate_up_h8();
+        } else {
+            err = launch_quantize(x, T, H, nullptr, xc, xs, xsu, stream);
+            if (err != hipSuccess) return err;
+            MoeArgs A = {};
+            A.w[0] = w_gate;
+            A.w[1] = w_up;
+            A.out[0] = g;
+            A.out[1] = u;
+            A.stride = stride_gu;
+            A.N = (int)F;
+            A.nsb = (int)(H / kQK);
+            A.lg_rg = sh1.lg_rg;
+            A.topk = (int)topk;
+            A.P = (int)P;
+            A.E = E;
+            A.slots = (int)(P < E ? P : E);
+            A.ids = ids;
+            A.codes = xc;
+            A.scales = xs;
+            A.sums = xsu;
+            err = launch_kernel<ACT_Q8>(A, T, 2, sh1, stream);
+            if (err != hipSuccess) return err;
+            err = launch_quantize(u, P, F, g, hc, hs, hsu, stream);
+        }
+        if (err != hipSuccess) return err;
+        const int nwc = sh2.nw, nw = nwc * (16 / nwc);
+        hipLaunchKernelGGL((moe_down_rows_kernel<kRowsChunk>), down_grid, dim3(64 * nw),
+                           rows_lds_bytes((int)P, E, nwc, nw), stream, B);
         return hipGetLastError();
     }
     // In-kernel activations quantize a token's row once per workgroup that
@@ -853,7 +1061,7 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     if (err != hipSuccess) return err;
     // down: SwiGLU(g, u) quantized in the kernel, per-slot products z, and the
     // routed sum by the last workgroup of each row block
-    MoeArgs B = A;
+    B = A;
     B.route_w = route_w;
     B.y = y;
     B.T = (int)T;

@@ -262,9 +262,10 @@ size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64
  * q4k_moe_gemv(down, route_w, act_per_slot = 1).  The gate and up products
  * share one launch, and the down launch forms the routed sum itself; for
  * T <= 2 the activations are quantized (and h formed) inside the GEMV
- * kernels, two launches in all (for one token the gate|up launch writes Q8(h)
- * and each down workgroup sums all of the token's slots itself, with the same
- * bits); for larger T, where that would repeat the
+ * kernels, two launches in all (for F <= 1024 the gate|up launch writes
+ * Q8(h)); for F <= 1024 and up to 256 pairs each down workgroup sums the
+ * slots of its rows itself, with the same bits; for larger T, where that
+ * would repeat the
  * work in every workgroup reading a row, the quantizer runs once per row as
  * its own launch (four in all).
  *   w_gate, w_up  n_experts Q4_K matrices of F rows x H columns each, at

@@ -326,6 +326,35 @@ def test_moe_ffn_one_token(q4k, oracle_lib, topk, F_, bad):
                         "moe_ffn one token topk=%d F=%d" % (topk, F_))
 
 
+@pytest.mark.parametrize("T,topk,F_", [(2, 4, 512), (3, 8, 1024), (1, 8, 2048), (40, 8, 512),
+                                       (32, 8, 1024)])
+def test_moe_ffn_launch_forms(q4k, oracle_lib, T, topk, F_):
+    """Every form q4k_moe_ffn picks: two tokens (Q8(h) from the gate|up launch,
+    the row-block down launch), three (the quantizer, then the row-block down
+    launch), one token on a wide FFN and more than 256 pairs (the grouped
+    launches with the routed sum by the last workgroup), and exactly 256
+    pairs (the row-block down launch at its limit): equal to the chain
+    bit for bit and close to the oracle."""
+    import torch
+    n_exp, H_ = 12, 512
+    wg = np.concatenate([qi.make_q4k_bytes(F_, H_, 3300 + e) for e in range(n_exp)])
+    wu = np.concatenate([qi.make_q4k_bytes(F_, H_, 3400 + e) for e in range(n_exp)])
+    wd = np.concatenate([qi.make_q4k_bytes(H_, F_, 3500 + e) for e in range(n_exp)])
+    ids, rw = qi.make_routing(T, n_exp, topk, 900 + T)
+    x = to_dev(qi.make_act(T, H_, 93 + T))
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
+    g, u, hc, hs, y2 = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
+    torch.cuda.synchronize()
+    y1 = y1.cpu().numpy()
+    assert np.isfinite(y1).all()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    ref = oracle_lib.moe_layer(wg, wu, wd, n_exp, H_, F_, ids, rw, x.cpu().numpy(), parallel=True)
+    _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids, rw, wd, H_, F_,
+                        "moe_ffn T=%d topk=%d F=%d" % (T, topk, F_))
+
+
 def test_moe_routed_sum_in_launch_reuses_workspace(q4k, oracle_lib):
     """The weighted sum is formed inside the down launch by the last
     workgroup of each row block: one zero-filled workspace serves repeated
