@@ -774,8 +774,9 @@ def measure_small_batch(torch, dec, oracle, steps=5):
     """Small-batch verification GEMV: M = 2, 4, 8 seeded N(0,1) activation rows
     against the 36-layer sweep's weights, through q4k_gemv (one launch per
     product, 252) and through q4k_gemm_batch per launch group ({q,k,v}, {o},
-    {gate,up}, {down}: 144 launches; up to 8 rows it runs the same streaming
-    kernel batched).  Only the products are timed (the Q8 rows are prepared
+    {gate,up}, {down}: 144 launches; up to 8 rows it runs one of q4k_gemv's
+    kernels over the whole group -- streaming at M = 2, the matrix-core GEMV
+    from M = 3 where the group's rows favour it).  Only the products are timed (the Q8 rows are prepared
     once).  Before timing, layer 0's seven products through both paths are
     checked against the oracle on sampled weight rows (all M rows)."""
     import gemm_q4_super_amd as q4k

@@ -1049,23 +1049,19 @@ hipError_t launch_gemm_batch(const GemmProblem *probs, int count, int64_t K,
                              const int8_t *codes, const float *scales, const int32_t *sums,
                              int64_t M, void *workspace, hipStream_t stream) {
     // A few rows would leave the matrix-core tiles mostly idle: up to 8 rows
-    // run q4k_gemv's kernels (the same bits) -- each product the matrix-core
-    // GEMV prefers on its own, the others together in one streaming launch.
+    // run q4k_gemv's kernels (the same bits), all products in one launch --
+    // the matrix-core GEMV where it is preferred for the launch's rows, else
+    // the streaming one.
     if (M <= 8 && stream_fits(M, K)) {
         GemvProblem gp[kMaxGemmBatch];
-        int ng = 0;
+        int64_t rows = 0;
         for (int p = 0; p < count; ++p) {
-            if (gemv_mfma_preferred(probs[p].N, K, M, scales, sums)) {
-                const hipError_t e =
-                    launch_gemv_mfma(static_cast<const uint8_t *>(probs[p].w), probs[p].N, K,
-                                     codes, scales, sums, M, probs[p].y, stream);
-                if (e != hipSuccess) return e;
-            } else {
-                gp[ng++] = {probs[p].w, nullptr, probs[p].y, probs[p].N};
-            }
+            gp[p] = {probs[p].w, nullptr, probs[p].y, probs[p].N};
+            rows += probs[p].N;
         }
-        return ng ? launch_gemv_batch_prepared(gp, ng, K, codes, scales, sums, M, stream)
-                  : hipSuccess;
+        if (gemv_mfma_preferred(rows, K, M, scales, sums))
+            return launch_gemv_mfma_batch(gp, count, K, codes, scales, sums, M, stream);
+        return launch_gemv_batch_prepared(gp, count, K, codes, scales, sums, M, stream);
     }
     const int nsb = (int)(K / kQK);
     const GemmSet set = make_set(probs, count);

@@ -27,6 +27,12 @@
 // column order.  Same values, operations and order as the streaming GEMV, so
 // both paths give the same bits.
 //
+// A launch takes up to kMaxGemvBatch products with the same K and M (a
+// launch group such as q|k|v): workgroups are dealt out over the products'
+// tiles in order, each finding its product from its tile index (the first
+// product's arguments lead the argument block, preloaded into registers); a
+// one-product launch has its own entry kernel with no table.
+//
 // Workgroup: one 16-row tile and all K/256 columns; wave w owns columns
 // [w CPW, (w + 1) CPW).  A wave stages its columns' Q8 codes, scales and sums
 // in LDS (loads issued before its weight loads; no workgroup barrier before
@@ -50,10 +56,23 @@ __host__ __device__ constexpr size_t mfma_lds_bytes(int M, int nsb) {
     return (size_t)nsb * (col_stride(M) + 2 * 256 + 16 * 64);
 }
 
+// Products 1.. of one launch: weights, outputs, rows, and the first tile of
+// each (tile0[count] = all tiles; entry 0 unused, product 0 travels in the
+// leading kernel arguments).
+struct MfmaSet {
+    const uint8_t *w[kMaxGemvBatch];
+    float *y[kMaxGemvBatch];
+    int N[kMaxGemvBatch];
+    int tile0[kMaxGemvBatch + 1];
+    int count;
+};
+
+// One workgroup: the 16-row tile of rows row_base.. of one product.
 template <int CPW>
-__global__ __launch_bounds__(1024) void gemv_mfma_kernel(
-    const uint8_t *__restrict__ w, float *__restrict__ y, const int8_t *__restrict__ codes,
-    const float *__restrict__ scales, const int32_t *__restrict__ sums, int N, int nsb, int M) {
+__device__ __forceinline__ void gemv_mfma_tile(
+    const uint8_t *__restrict__ w, float *__restrict__ y, const int N, const int row_base,
+    const int8_t *__restrict__ codes, const float *__restrict__ scales,
+    const int32_t *__restrict__ sums, int nsb, int M) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
@@ -63,7 +82,6 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
     const int q = lane >> 4;           // k-group
     const bool Yh = q >= 2;            // this lane's sub-blocks: 7-t (Y) or t (X)
     const int K = nsb * 256, nblk = nsb * 8;
-    const int row_base = (int)blockIdx.x * 16;
     const int cs = col_stride(M);
     uint8_t *lcodes = lds;
     float *la = reinterpret_cast<float *>(lds + (size_t)nsb * cs);   // [nsb][8 j][8 m]
@@ -232,15 +250,43 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(
     }
 }
 
+// One product per launch.
 template <int CPW>
-hipError_t launch_cpw(const uint8_t *w, int64_t N, int nsb, const int8_t *codes,
-                      const float *scales, const int32_t *sums, int M, float *y,
-                      hipStream_t stream) {
+__global__ __launch_bounds__(1024) void gemv_mfma_kernel(
+    const uint8_t *__restrict__ w, float *__restrict__ y, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const int32_t *__restrict__ sums, int N, int nsb, int M) {
+    gemv_mfma_tile<CPW>(w, y, N, (int)blockIdx.x * 16, codes, scales, sums, nsb, M);
+}
+
+// Several products per launch: the first one's arguments lead (preloaded into
+// registers), the others come from the table.
+template <int CPW>
+__global__ __launch_bounds__(1024) void gemv_mfma_batch_kernel(
+    const uint8_t *w0, float *y0, int N0, int tiles0, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const int32_t *__restrict__ sums, int nsb, int M,
+    const MfmaSet set) {
+    if ((int)blockIdx.x < tiles0) {                // uniform
+        gemv_mfma_tile<CPW>(w0, y0, N0, (int)blockIdx.x * 16, codes, scales, sums, nsb, M);
+        return;
+    }
+    int pi = 1;
+    while (pi + 1 < set.count && (int)blockIdx.x >= set.tile0[pi + 1]) ++pi;
+    gemv_mfma_tile<CPW>(set.w[pi], set.y[pi], set.N[pi], ((int)blockIdx.x - set.tile0[pi]) * 16,
+                        codes, scales, sums, nsb, M);
+}
+
+template <int CPW>
+hipError_t launch_cpw(const MfmaSet &set, int nsb, const int8_t *codes, const float *scales,
+                      const int32_t *sums, int M, hipStream_t stream) {
     const int waves = (nsb + CPW - 1) / CPW;
-    const int tiles = (int)((N + 15) / 16);
-    hipLaunchKernelGGL((gemv_mfma_kernel<CPW>), dim3(tiles), dim3(64 * waves),
-                       mfma_lds_bytes(M, nsb), stream, w, y, codes, scales, sums, (int)N, nsb,
-                       M);
+    if (set.count == 1)
+        hipLaunchKernelGGL((gemv_mfma_kernel<CPW>), dim3(set.tile0[1]), dim3(64 * waves),
+                           mfma_lds_bytes(M, nsb), stream, set.w[0], set.y[0], codes, scales, sums,
+                           set.N[0], nsb, M);
+    else
+        hipLaunchKernelGGL((gemv_mfma_batch_kernel<CPW>), dim3(set.tile0[set.count]), dim3(64 * waves),
+                           mfma_lds_bytes(M, nsb), stream, set.w[0], set.y[0], set.N[0], set.tile0[1],
+                           codes, scales, sums, nsb, M, set);
     return hipGetLastError();
 }
 
@@ -259,25 +305,42 @@ bool gemv_mfma_fits(int64_t K, int64_t M, const void *scales, const void *sums) 
 // leaves most CUs idle, and the streaming GEMV keeps up until M = 5 (N = 1024,
 // M = 3: 3.45 against 3.77 us); at M = 2 the streaming GEMV's lighter vector
 // work wins.
+// N: the rows of the launch (all its products').
 bool gemv_mfma_preferred(int64_t N, int64_t K, int64_t M, const void *scales, const void *sums) {
     if (!gemv_mfma_fits(K, M, scales, sums)) return false;
     return M >= 3 && (N >= 2048 || M >= 5);
 }
 
-hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
-                            const float *scales, const int32_t *sums, int64_t M, float *y,
-                            hipStream_t stream) {
+hipError_t launch_gemv_mfma_batch(const GemvProblem *probs, int count, int64_t K,
+                                  const int8_t *codes, const float *scales, const int32_t *sums,
+                                  int64_t M, hipStream_t stream) {
+    if (count < 1 || count > kMaxGemvBatch) return hipErrorInvalidValue;
+    MfmaSet set = {};
+    set.count = count;
+    for (int p = 0; p < count; ++p) {
+        set.w[p] = static_cast<const uint8_t *>(probs[p].w);
+        set.y[p] = probs[p].y;
+        set.N[p] = (int)probs[p].N;
+        set.tile0[p + 1] = set.tile0[p] + (int)((probs[p].N + 15) / 16);
+    }
     const int nsb = (int)(K / kQK);
     // columns per wave: the fewest that keep the workgroup within 8 waves, and
     // at most 3 (up to 16 waves): past 24 columns more waves issue the loads
     // sooner (2560 x 9728: 10.1 us at 13 waves against 11.3 at 8)
     const int cpw = std::min((nsb + 7) / 8, kMaxCpw);
     switch (cpw) {
-    case 1: return launch_cpw<1>(w, N, nsb, codes, scales, sums, (int)M, y, stream);
-    case 2: return launch_cpw<2>(w, N, nsb, codes, scales, sums, (int)M, y, stream);
-    case 3: return launch_cpw<3>(w, N, nsb, codes, scales, sums, (int)M, y, stream);
+    case 1: return launch_cpw<1>(set, nsb, codes, scales, sums, (int)M, stream);
+    case 2: return launch_cpw<2>(set, nsb, codes, scales, sums, (int)M, stream);
+    case 3: return launch_cpw<3>(set, nsb, codes, scales, sums, (int)M, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
+                            const float *scales, const int32_t *sums, int64_t M, float *y,
+                            hipStream_t stream) {
+    const GemvProblem p = {w, nullptr, y, N};
+    return launch_gemv_mfma_batch(&p, 1, K, codes, scales, sums, M, stream);
 }
 
 }  // namespace q4k

@@ -63,6 +63,7 @@ hipError_t launch_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *cod
 // LDS holds the rows and scales / sums are 16-byte aligned; the same bits as
 // the streaming GEMV.
 bool gemv_mfma_fits(int64_t K, int64_t M, const void *scales, const void *sums);
+// N: the rows of the launch (all its products').
 bool gemv_mfma_preferred(int64_t N, int64_t K, int64_t M, const void *scales, const void *sums);
 hipError_t launch_gemv_mfma(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                             const float *scales, const int32_t *sums, int64_t M, float *y,
@@ -86,6 +87,11 @@ hipError_t launch_quantize_gemv_residual(const uint8_t *w, int64_t N, int64_t K,
                                          int64_t M, const float *residual, float *y,
                                          hipStream_t stream);
 using GemvProblem = q4k_gemv_problem;
+// Matrix-core GEMV over up to kMaxGemvBatch products with the same K and rows,
+// one launch (the same bits as one launch per product).
+hipError_t launch_gemv_mfma_batch(const GemvProblem *probs, int count, int64_t K,
+                                  const int8_t *codes, const float *scales, const int32_t *sums,
+                                  int64_t M, hipStream_t stream);
 constexpr int kMaxGemvBatch = 8;
 // The streaming GEMV over a batch on prepared Q8 rows (M <= 8, stream_fits):
 // the kernel of q4k_gemv's streaming path, one launch.

@@ -186,8 +186,10 @@ typedef struct q4k_gemm_problem {
  * i, y_i = Q8(x)[M][K] * W_i^T, the same arithmetic as q4k_gemm on that
  * problem alone.  Launching them together fills the GPU where each alone
  * would not; with M <= 8 (the verification rows of drafted tokens, "genie-ai-
- * runtime ...", section 9) the products q4k_gemv would run on its streaming
- * kernel go out as one launch, the others one launch each.  `problems` is a host array of `count` entries (1 <= count <= 8),
+ * runtime ...", section 9) all products go out as one launch of one of
+ * q4k_gemv's kernels (the matrix-core GEMV where the launch's rows favour it,
+ * else the streaming one; either gives q4k_gemv's bits).  `problems` is a host
+ * array of `count` entries (1 <= count <= 8),
  * read during the call; outputs must not overlap.  Workspace as for q4k_gemm.
  * Limits and checks as for q4k_gemm, applied to every problem. */
 int q4k_gemm_batch(const q4k_gemm_problem *problems, int count, int64_t K,

@@ -259,6 +259,11 @@ _GEMM_BATCHES = {
     "ragged_m129": (129, 768, [1000, 33, 1, 257]),
     "eight_m40": (40, 512, [100, 200, 300, 1, 64, 65, 127, 128]),
     "m7_pair": (7, 1024, [513, 1023]),
+    # up to 8 rows: the matrix-core GEMV over all products in one launch
+    # where the launch's rows favour it (products found by tile index)
+    "qkv_m4": (4, 2560, [4096, 1024, 1024]),
+    "eight_m3": (3, 512, [100, 200, 300, 1, 64, 65, 127, 2048]),
+    "eight_m8": (8, 768, [16, 17, 1, 300, 33, 48, 1000, 5]),
 }
 
 
