@@ -1025,7 +1025,9 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
     """Q6_K decode GEMV (q6k_gemv, prepared Q8 rows, M = 1) over the 36-layer
     sweep's projection shapes with distinct seeded Q6_K matrices (2.98 GB):
     one graph of the 252 launches, replayed once untimed and `steps` times
-    timed, plus a per-shape breakdown and a sampled check against the oracle."""
+    timed, plus a per-shape breakdown and a sampled check against the oracle;
+    beside it the sweep with the quantizer inside, per product (252 launches)
+    and batched per launch group (144, q6k_quantize_gemv_batch)."""
     L = q4k.lib()
     dev = torch.device("cuda:0")
     shapes = qi.QWEN3_4B_LAYER
@@ -1077,6 +1079,34 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
                     raise RuntimeError("q6k_quantize_gemv launch failed")
     tf = timed(gf, steps)
     fbytes = LAYERS * sum(N * K // 256 * 210 + 4 * K + 4 * N for _, K, N in shapes)
+    # ... and batched per launch group like the Q4_K headline ({q,k,v}, {o},
+    # {gate,up}, {down}: 144 launches, q6k_quantize_gemv_batch), checked bit for
+    # bit against q6k_quantize_gemv on layer 0 first
+    P = q4k._lib.GemvProblem
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
+    yb = [torch.empty((1, N), dtype=torch.float32, device=dev) for _, _, N in shapes]
+    def group_array(l, grp):
+        return (P * len(grp))(*[P(ws[p][l].data_ptr(), xs[shapes[p][1]].data_ptr(),
+                                  yb[p].data_ptr(), shapes[p][2]) for p in grp])
+    barrs = [[(group_array(l, grp), len(grp), shapes[grp[0]][1]) for grp in groups]
+             for l in range(LAYERS)]
+    s0 = torch.cuda.current_stream().cuda_stream
+    for arr, n, K in barrs[0]:
+        if L.q6k_quantize_gemv_batch(arr, n, K, 1, s0):
+            raise RuntimeError("q6k_quantize_gemv_batch launch failed")
+    for p, (name, K, N) in enumerate(shapes):
+        y1 = q4k.q6k_quantize_gemv(ws[p][0], N, K, xs[K])
+        torch.cuda.synchronize()
+        if not torch.equal(y1, yb[p]):
+            raise RuntimeError("q6k_quantize_gemv_batch differs from q6k_quantize_gemv on %s" % name)
+    gb = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gb, stream=cap):
+        s = torch.cuda.current_stream().cuda_stream
+        for l in range(LAYERS):
+            for arr, n, K in barrs[l]:
+                if L.q6k_quantize_gemv_batch(arr, n, K, 1, s):
+                    raise RuntimeError("q6k_quantize_gemv_batch launch failed")
+    tb = timed(gb, steps)
     per = {}
     for p, (name, K, N) in enumerate(shapes):
         d = timed(graph([p]), steps) / LAYERS
@@ -1125,6 +1155,11 @@ def measure_q6k(torch, q4k, qi, oracle, steps=5):
             "mean_launch_us": round(t / (LAYERS * len(shapes)) * 1e6, 3),
             "fused_quantizer_sweep": {"us_per_sweep": round(tf * 1e6, 1),
                                       "GBps": round(fbytes / tf / 1e9, 1)},
+            "fused_batched_sweep": {"launches": LAYERS * len(groups),
+                                    "us_per_sweep": round(tb * 1e6, 1),
+                                    "GBps": round(fbytes / tb / 1e9, 1),
+                                    "hbm_frac": round(fbytes / tb / 1e9 / HBM_PEAK_GBS, 4),
+                                    "bit_identical_to_single_calls": True},
             "per_shape": per,
             "output_head_151936x2560": {"us": round(th * 1e6, 2), "GBps": round(hb / th / 1e9, 1),
                                         "hbm_frac": round(hb / th / 1e9 / HBM_PEAK_GBS, 4)},

@@ -24,6 +24,8 @@ Functions carry the C names:
                 ids, route_w, x, workspace=None)     -> y [T, H]  (whole expert FFN layer)
     q6k_gemv(w, N, K, codes, scales)                 -> y [M, N]   (Q6_K weights, M <= 8)
     q6k_quantize_gemv(w, N, K, x)                    -> y [M, N]   (Q6_K, fp32 x, one launch)
+    q6k_gemv_batch([(w, N)...], K, codes, scales)    -> [y_i]      (Q6_K, one launch)
+    q6k_quantize_gemv_batch([(w, N, x)...], K)       -> [y_i]      (Q6_K, fp32 x, one launch)
     q6k_gemm(w, N, K, codes, scales, workspace="auto") -> y [M, N] (Q6_K prefill GEMM)
     q4k_kv_store(k, v, pos0, k_codes, k_scales, v_codes, v_scales)
                                                      (INT8 KV cache entries of M positions)
@@ -54,6 +56,8 @@ from ._lib import (  # noqa: F401
     q4k_status_string,
     q6k_gemm,
     q6k_gemv,
+    q6k_gemv_batch,
     q6k_quantize_gemv,
+    q6k_quantize_gemv_batch,
     EXPORTED_SYMBOLS,
 )

@@ -24,6 +24,8 @@ EXPORTED_SYMBOLS = (
     "q4k_moe_ffn_workspace_bytes",
     "q6k_gemv",
     "q6k_quantize_gemv",
+    "q6k_gemv_batch",
+    "q6k_quantize_gemv_batch",
     "q6k_gemm",
     "q4k_kv_store",
     "q4k_attn_workspace_bytes",
@@ -110,6 +112,9 @@ def _declare(L):
     L.q4k_moe_ffn_workspace_bytes.restype = ctypes.c_size_t
     L.q6k_gemv.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P]
     L.q6k_quantize_gemv.argtypes = [_P, _I, _I, _P, _I, _P, _P]
+    L.q6k_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I, _P, _P, _I, _P]
+    L.q6k_quantize_gemv_batch.argtypes = [ctypes.POINTER(GemvProblem), ctypes.c_int, _I, _I,
+                                          _P]
     L.q6k_gemm.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, ctypes.c_size_t, _P]
     L.q4k_kv_store.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.q4k_attn_workspace_bytes.argtypes = [_I, _I, _I]
@@ -127,7 +132,8 @@ def _declare(L):
     for name in ("q4k_quantize_act", "q4k_gemv", "q4k_quantize_gemv",
                  "q4k_quantize_gemv_residual",
                  "q4k_quantize_gemv_batch", "q4k_gemm", "q4k_gemm_batch", "q4k_moe_gemv",
-                 "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q6k_gemm", "q4k_kv_store",
+                 "q4k_moe_ffn", "q6k_gemv", "q6k_quantize_gemv", "q6k_gemv_batch",
+                 "q6k_quantize_gemv_batch", "q6k_gemm", "q4k_kv_store",
                  "q4k_attn_decode"):
         getattr(L, name).restype = ctypes.c_int
     return L
@@ -215,6 +221,50 @@ def q6k_quantize_gemv(w, N, K, x, y=None):
     _check(lib().q6k_quantize_gemv(_ptr(w), N, K, _ptr(x), M, _ptr(y), _stream(x)),
            "q6k_quantize_gemv")
     return y
+
+
+def q6k_gemv_batch(problems, K, codes, scales, ys=None):
+    """Several Q6_K GEMVs on the same prepared Q8 rows in one launch.
+
+    `problems` is a sequence of (w, N); returns the list of outputs y_i [M, N_i]
+    (or fills `ys`)."""
+    import torch
+    problems = list(problems)
+    if not problems:
+        raise ValueError("q6k_gemv_batch: empty batch")
+    _dev(codes, "codes"); _dev(scales, "scales")
+    M = codes.shape[0]
+    if ys is None:
+        ys = [torch.empty((M, N), dtype=torch.float32, device=codes.device) for _, N in problems]
+    arr = (GemvProblem * len(problems))()
+    for i, ((w, N), y) in enumerate(zip(problems, ys)):
+        _dev(w, "w")
+        arr[i] = GemvProblem(_ptr(w), None, _ptr(y), N)
+    _check(lib().q6k_gemv_batch(arr, len(problems), K, _ptr(codes), _ptr(scales), M,
+                                _stream(codes)), "q6k_gemv_batch")
+    return ys
+
+
+def q6k_quantize_gemv_batch(problems, K, ys=None):
+    """Several Q6_K quantize-and-GEMV products with the same K and M in one
+    launch.  `problems` is a sequence of (w, N, x) with fp32 x [M, K]; returns
+    the list of outputs y_i [M, N_i] (or fills `ys`)."""
+    import torch
+    problems = list(problems)
+    if not problems:
+        raise ValueError("q6k_quantize_gemv_batch: empty batch")
+    M = problems[0][2].shape[0]
+    if ys is None:
+        ys = [torch.empty((M, N), dtype=torch.float32, device=x.device) for _, N, x in problems]
+    arr = (GemvProblem * len(problems))()
+    for i, ((w, N, x), y) in enumerate(zip(problems, ys)):
+        _dev(w, "w"); _dev(x, "x")
+        if x.shape[0] != M:
+            raise ValueError("q6k_quantize_gemv_batch: every x must have the same M")
+        arr[i] = GemvProblem(_ptr(w), _ptr(x), _ptr(y), N)
+    _check(lib().q6k_quantize_gemv_batch(arr, len(problems), K, M, _stream(problems[0][2])),
+           "q6k_quantize_gemv_batch")
+    return ys
 
 
 def q4k_quantize_gemv(w, N, K, x, y=None):

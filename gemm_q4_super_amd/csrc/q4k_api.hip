@@ -248,6 +248,41 @@ int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int q6k_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K, const int8_t *codes,
+                   const float *scales, int64_t M, void *stream) {
+    if (!problems || !codes || !scales) return Q4K_EINVAL;
+    if (count < 1 || count > q4k::kMaxGemvBatch) return Q4K_ESHAPE;
+    if (K < q4k::kQK || K % q4k::kQK != 0 || K > q4k::kQ6MaxK || M < 1 || M > 8 ||
+        !q4k::q6k_fits(M, K))
+        return Q4K_ESHAPE;
+    if (!aligned(codes, 16) || !aligned(scales, 4)) return Q4K_EALIGN;
+    for (int i = 0; i < count; ++i) {
+        const q4k_gemv_problem &p = problems[i];
+        if (!p.w || !p.y) return Q4K_EINVAL;
+        if (p.N < 1 || p.N > kMaxDim) return Q4K_ESHAPE;
+        if (!aligned(p.w, 16) || !aligned(p.y, 4)) return Q4K_EALIGN;
+    }
+    return from_hip(q4k::launch_q6k_gemv_batch(problems, count, K, codes, scales, M,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int q6k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K, int64_t M,
+                            void *stream) {
+    if (!problems) return Q4K_EINVAL;
+    if (count < 1 || count > q4k::kMaxGemvBatch) return Q4K_ESHAPE;
+    if (K < q4k::kQK || K % q4k::kQK != 0 || K > q4k::kQ6MaxK || M < 1 || M > 8 ||
+        !q4k::q6k_fits(M, K))
+        return Q4K_ESHAPE;
+    for (int i = 0; i < count; ++i) {
+        const q4k_gemv_problem &p = problems[i];
+        if (!p.w || !p.x || !p.y) return Q4K_EINVAL;
+        if (p.N < 1 || p.N > kMaxDim) return Q4K_ESHAPE;
+        if (!aligned(p.w, 16) || !aligned(p.x, 16) || !aligned(p.y, 4)) return Q4K_EALIGN;
+    }
+    return from_hip(q4k::launch_q6k_quantize_gemv_batch(problems, count, K, M,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 int q6k_gemm(const void *w, int64_t N, int64_t K, const int8_t *codes, const float *scales,
              int64_t M, float *y, void *workspace, size_t workspace_bytes, void *stream) {
     if (!w || !codes || !scales || !y) return Q4K_EINVAL;

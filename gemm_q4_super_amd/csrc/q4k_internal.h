@@ -87,6 +87,13 @@ hipError_t launch_quantize_gemv_residual(const uint8_t *w, int64_t N, int64_t K,
                                          int64_t M, const float *residual, float *y,
                                          hipStream_t stream);
 using GemvProblem = q4k_gemv_problem;
+// Q6_K GEMV over up to kMaxGemvBatch products (Q6_K weights in w), one launch:
+// shared prepared Q8 rows, or fp32 rows per product (x) quantized inside.
+hipError_t launch_q6k_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                 const int8_t *codes, const float *scales, int64_t M,
+                                 hipStream_t stream);
+hipError_t launch_q6k_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                          int64_t M, hipStream_t stream);
 // Matrix-core GEMV over up to kMaxGemvBatch products with the same K and rows,
 // one launch (the same bits as one launch per product).
 hipError_t launch_gemv_mfma_batch(const GemvProblem *probs, int count, int64_t K,

@@ -54,10 +54,12 @@ __device__ __forceinline__ u32x4 load12(const uint8_t *p) {   // 4-byte aligned
     return r;
 }
 
+// One workgroup: rows row_base .. row_base + 8V - 1 of one product.
 template <int M, int CPW, int V, bool FUSED>
-__global__ __launch_bounds__(1024) void q6k_gemv_kernel(
+__device__ __forceinline__ void q6k_rows(
     const uint8_t *__restrict__ w, float *__restrict__ y, const int8_t *__restrict__ codes,
-    const float *__restrict__ scales, const float *__restrict__ x, int N, int nsb) {
+    const float *__restrict__ scales, const float *__restrict__ x, const int N, const int nsb,
+    const int row_base) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float red[kQ6Waves][8 * V][M];
 
@@ -67,7 +69,6 @@ __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     const int g = lane >> 3;              // row of the 8-row set
     const int h = (lane >> 2) & 1, u = lane & 3;
     const int K = nsb * 256, nblk = nsb * 8;
-    const int row_base = (int)blockIdx.x * 8 * V;
     const int wcol0 = wave * CPW;
     const int ncols = min(CPW, nsb - wcol0);   // >= 1 (the host sizes the workgroup)
 
@@ -250,67 +251,132 @@ __global__ __launch_bounds__(1024) void q6k_gemv_kernel(
     }
 }
 
-// Activation of a call: prepared Q8 rows (codes, scales) or fp32 rows x.
+// One product per launch.
+template <int M, int CPW, int V, bool FUSED>
+__global__ __launch_bounds__(1024) void q6k_gemv_kernel(
+    const uint8_t *__restrict__ w, float *__restrict__ y, const int8_t *__restrict__ codes,
+    const float *__restrict__ scales, const float *__restrict__ x, int N, int nsb) {
+    q6k_rows<M, CPW, V, FUSED>(w, y, codes, scales, x, N, nsb, (int)blockIdx.x * 8 * V);
+}
+
+// Products 1.. of a launch of several (product 0 travels in the leading
+// kernel arguments, preloaded into registers): weights, fp32 rows (fused
+// launches), outputs, rows, first workgroup of each (block0[count] = all).
+struct Q6Set {
+    const uint8_t *w[kMaxGemvBatch];
+    const float *x[kMaxGemvBatch];
+    float *y[kMaxGemvBatch];
+    int N[kMaxGemvBatch];
+    int block0[kMaxGemvBatch + 1];
+    int count;
+};
+
+// Several products with the same K and M per launch: workgroups are dealt out
+// over the products' row blocks in order, each finding its product from its
+// block index.  Per row the same work as a one-product launch.
+template <int M, int CPW, int V, bool FUSED>
+__global__ __launch_bounds__(1024) void q6k_gemv_batch_kernel(
+    const uint8_t *w0, float *y0, const float *x0, int N0, int blocks0,
+    const int8_t *__restrict__ codes, const float *__restrict__ scales, int nsb, const Q6Set set) {
+    if ((int)blockIdx.x < blocks0) {               // uniform
+        q6k_rows<M, CPW, V, FUSED>(w0, y0, codes, scales, x0, N0, nsb, (int)blockIdx.x * 8 * V);
+        return;
+    }
+    int pi = 1;
+    while (pi + 1 < set.count && (int)blockIdx.x >= set.block0[pi + 1]) ++pi;
+    q6k_rows<M, CPW, V, FUSED>(set.w[pi], set.y[pi], codes, scales, set.x[pi], set.N[pi], nsb,
+                               ((int)blockIdx.x - set.block0[pi]) * 8 * V);
+}
+
+// Activation of a call: prepared Q8 rows (codes, scales) shared by its
+// products, or fp32 rows per product (GemvProblem::x).
 struct Act {
     const int8_t *codes;
     const float *scales;
-    const float *x;
+    bool fused;
 };
 
 template <int M, int CPW, int V>
-hipError_t launch_mcv(const uint8_t *w, int64_t N, int nsb, const Act &a, float *y,
+hipError_t launch_mcv(const GemvProblem *probs, int count, int nsb, const Act &a,
                       hipStream_t stream) {
     const int waves = (nsb + CPW - 1) / CPW;
-    const int blocks = (int)((N + 8 * V - 1) / (8 * V));
     const size_t lds = (size_t)nsb * M * kQ6Stage;
-    if (a.x)
-        hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, true>), dim3(blocks), dim3(64 * waves),
-                           lds, stream, w, y, nullptr, nullptr, a.x, (int)N, nsb);
+    const int rb = 8 * V;
+    if (count == 1) {
+        const GemvProblem &p = probs[0];
+        const int blocks = (int)((p.N + rb - 1) / rb);
+        if (a.fused)
+            hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, true>), dim3(blocks), dim3(64 * waves),
+                               lds, stream, static_cast<const uint8_t *>(p.w), p.y, nullptr,
+                               nullptr, p.x, (int)p.N, nsb);
+        else
+            hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, false>), dim3(blocks), dim3(64 * waves),
+                               lds, stream, static_cast<const uint8_t *>(p.w), p.y, a.codes,
+                               a.scales, nullptr, (int)p.N, nsb);
+        return hipGetLastError();
+    }
+    Q6Set set = {};
+    set.count = count;
+    for (int i = 0; i < count; ++i) {
+        set.w[i] = static_cast<const uint8_t *>(probs[i].w);
+        set.x[i] = probs[i].x;
+        set.y[i] = probs[i].y;
+        set.N[i] = (int)probs[i].N;
+        set.block0[i + 1] = set.block0[i] + (int)((probs[i].N + rb - 1) / rb);
+    }
+    if (a.fused)
+        hipLaunchKernelGGL((q6k_gemv_batch_kernel<M, CPW, V, true>), dim3(set.block0[count]),
+                           dim3(64 * waves), lds, stream, set.w[0], set.y[0], set.x[0], set.N[0],
+                           set.block0[1], nullptr, nullptr, nsb, set);
     else
-        hipLaunchKernelGGL((q6k_gemv_kernel<M, CPW, V, false>), dim3(blocks), dim3(64 * waves),
-                           lds, stream, w, y, a.codes, a.scales, nullptr, (int)N, nsb);
+        hipLaunchKernelGGL((q6k_gemv_batch_kernel<M, CPW, V, false>), dim3(set.block0[count]),
+                           dim3(64 * waves), lds, stream, set.w[0], set.y[0], nullptr, set.N[0],
+                           set.block0[1], a.codes, a.scales, nsb, set);
     return hipGetLastError();
 }
 
 // Launch shape: columns per wave so that at most 16 waves cover K; rows per
-// workgroup (8 V) so that the workgroups come near one or two per CU; at most 4
-// super-blocks per lane in flight (V * CPW <= 4), 2 past M = 4 (registers).
+// workgroup (8 V) so that the workgroups (of all the launch's rows) come near
+// one or two per CU; at most 4 super-blocks per lane in flight (V * CPW <= 4),
+// 2 past M = 4 (registers).  A row's arithmetic does not depend on V.
 template <int M>
-hipError_t launch_m(const uint8_t *w, int64_t N, int nsb, const Act &a, float *y,
+hipError_t launch_m(const GemvProblem *probs, int count, int nsb, const Act &a,
                     hipStream_t stream) {
     constexpr int kUnits = M <= 4 ? 4 : 2;
     const int cpw = (nsb + kQ6Waves - 1) / kQ6Waves;
-    const int64_t rows_per_cu = (N + cu_count() - 1) / cu_count();
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) rows += probs[i].N;
+    const int64_t rows_per_cu = (rows + cu_count() - 1) / cu_count();
     const int v = (int)std::max<int64_t>(
         1, std::min<int64_t>(kUnits / cpw, std::max<int64_t>(1, rows_per_cu / 8)));
     if (cpw == 1) {
         if constexpr (kUnits >= 4)
-            if (v >= 4) return launch_mcv<M, 1, 4>(w, N, nsb, a, y, stream);
-        if (v >= 2) return launch_mcv<M, 1, 2>(w, N, nsb, a, y, stream);
-        return launch_mcv<M, 1, 1>(w, N, nsb, a, y, stream);
+            if (v >= 4) return launch_mcv<M, 1, 4>(probs, count, nsb, a, stream);
+        if (v >= 2) return launch_mcv<M, 1, 2>(probs, count, nsb, a, stream);
+        return launch_mcv<M, 1, 1>(probs, count, nsb, a, stream);
     }
     if (cpw == 2) {
         if constexpr (kUnits >= 4)
-            if (v >= 2) return launch_mcv<M, 2, 2>(w, N, nsb, a, y, stream);
-        return launch_mcv<M, 2, 1>(w, N, nsb, a, y, stream);
+            if (v >= 2) return launch_mcv<M, 2, 2>(probs, count, nsb, a, stream);
+        return launch_mcv<M, 2, 1>(probs, count, nsb, a, stream);
     }
     // K of 33..48 super-blocks: 3 columns per wave, one row group
-    return launch_mcv<M, 3, 1>(w, N, nsb, a, y, stream);
+    return launch_mcv<M, 3, 1>(probs, count, nsb, a, stream);
 }
 
-hipError_t run_q6k(const uint8_t *w, int64_t N, int64_t K, const Act &a, int64_t M, float *y,
+hipError_t run_q6k(const GemvProblem *probs, int count, int64_t K, const Act &a, int64_t M,
                    hipStream_t stream) {
     const int nsb = (int)(K / kQK);
-    if (!q6k_fits(M, K)) return hipErrorInvalidValue;
+    if (!q6k_fits(M, K) || count < 1 || count > kMaxGemvBatch) return hipErrorInvalidValue;
     switch (M) {
-    case 1: return launch_m<1>(w, N, nsb, a, y, stream);
-    case 2: return launch_m<2>(w, N, nsb, a, y, stream);
-    case 3: return launch_m<3>(w, N, nsb, a, y, stream);
-    case 4: return launch_m<4>(w, N, nsb, a, y, stream);
-    case 5: return launch_m<5>(w, N, nsb, a, y, stream);
-    case 6: return launch_m<6>(w, N, nsb, a, y, stream);
-    case 7: return launch_m<7>(w, N, nsb, a, y, stream);
-    case 8: return launch_m<8>(w, N, nsb, a, y, stream);
+    case 1: return launch_m<1>(probs, count, nsb, a, stream);
+    case 2: return launch_m<2>(probs, count, nsb, a, stream);
+    case 3: return launch_m<3>(probs, count, nsb, a, stream);
+    case 4: return launch_m<4>(probs, count, nsb, a, stream);
+    case 5: return launch_m<5>(probs, count, nsb, a, stream);
+    case 6: return launch_m<6>(probs, count, nsb, a, stream);
+    case 7: return launch_m<7>(probs, count, nsb, a, stream);
+    case 8: return launch_m<8>(probs, count, nsb, a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -327,12 +393,25 @@ bool q6k_fits(int64_t M, int64_t K) {
 
 hipError_t launch_q6k_gemv(const uint8_t *w, int64_t N, int64_t K, const int8_t *codes,
                            const float *scales, int64_t M, float *y, hipStream_t stream) {
-    return run_q6k(w, N, K, Act{codes, scales, nullptr}, M, y, stream);
+    const GemvProblem p = {w, nullptr, y, N};
+    return run_q6k(&p, 1, K, Act{codes, scales, false}, M, stream);
 }
 
 hipError_t launch_q6k_quantize_gemv(const uint8_t *w, int64_t N, int64_t K, const float *x,
                                     int64_t M, float *y, hipStream_t stream) {
-    return run_q6k(w, N, K, Act{nullptr, nullptr, x}, M, y, stream);
+    const GemvProblem p = {w, x, y, N};
+    return run_q6k(&p, 1, K, Act{nullptr, nullptr, true}, M, stream);
+}
+
+hipError_t launch_q6k_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                 const int8_t *codes, const float *scales, int64_t M,
+                                 hipStream_t stream) {
+    return run_q6k(probs, count, K, Act{codes, scales, false}, M, stream);
+}
+
+hipError_t launch_q6k_quantize_gemv_batch(const GemvProblem *probs, int count, int64_t K,
+                                          int64_t M, hipStream_t stream) {
+    return run_q6k(probs, count, K, Act{nullptr, nullptr, true}, M, stream);
 }
 
 }  // namespace q4k

@@ -106,7 +106,6 @@ int q4k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
 int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
                       int64_t M, float *y, void *stream);
 
-/* One product of a batch for q4k_quantize_gemv_batch. */
 /* Quantize-and-GEMV with the residual add in its last step:
  * y[M][N] = residual[M][N] + Q8(x)[M][K] * W^T.  The decode step adds the
  * output of the attention-output and down projections to the residual stream;
@@ -121,6 +120,8 @@ int q4k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x,
 int q4k_quantize_gemv_residual(const void *w, int64_t N, int64_t K, const float *x,
                                int64_t M, const float *residual, float *y, void *stream);
 
+/* One product of a batch for q4k_quantize_gemv_batch (and, with Q6_K
+ * weights, q6k_gemv_batch and q6k_quantize_gemv_batch). */
 typedef struct q4k_gemv_problem {
     const void *w;     /* device Q4_K weights, N rows x (K/256)*144 bytes, 16-byte aligned */
     const float *x;    /* device fp32 activations [M][K], 16-byte aligned                */
@@ -322,6 +323,26 @@ int q6k_gemv(const void *w, int64_t N, int64_t K, const int8_t *codes,
  * limits as for q6k_gemv. */
 int q6k_quantize_gemv(const void *w, int64_t N, int64_t K, const float *x, int64_t M,
                       float *y, void *stream);
+
+/* Several Q6_K GEMVs with the same K and M on the same prepared Q8 rows in
+ * one launch (the launch groups of a decode step, e.g. q|k|v or gate|up, on a
+ * model whose tensors are Q6_K): for every problem i, y_i = Q8(x)[M][K] *
+ * W_i^T, each bit-identical to q6k_gemv on that problem alone.  `problems` is
+ * a host array of `count` entries (1 <= count <= 8), read during the call:
+ * w the problem's Q6_K weights (N rows x (K/256)*210 bytes, 16-byte aligned),
+ * y its output [M][N]; x is not read.  codes and scales as for q6k_gemv.
+ * Outputs must not overlap.  Limits and checks as for q6k_gemv, applied to
+ * every problem. */
+int q6k_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K, const int8_t *codes,
+                   const float *scales, int64_t M, void *stream);
+
+/* q6k_quantize_gemv for several problems with the same K and M in one launch,
+ * each with its own fp32 rows x_i [M][K] (16-byte aligned), each output
+ * bit-identical to q6k_quantize_gemv on that problem alone.  `problems` as
+ * for q6k_gemv_batch, x read; other arguments, limits and checks as for
+ * q6k_quantize_gemv, applied to every problem. */
+int q6k_quantize_gemv_batch(const q4k_gemv_problem *problems, int count, int64_t K, int64_t M,
+                            void *stream);
 
 /* Q6_K prefill GEMM: y[M][N] = Q8(x)[M][K] * W^T with W in Q6_K (layout and
  * weights as for q6k_gemv), the batched product of prefill ("genie-ai-runtime

@@ -165,6 +165,45 @@ def test_quantize_gemv_batch_argument_checks(L):
     assert call([good, (A, A, A + 2, 16)]) == EALIGN
 
 
+def test_q6k_gemv_batch_argument_checks(L):
+    f, g = L.q6k_gemv_batch, L.q6k_quantize_gemv_batch
+    P = q4k._lib.GemvProblem
+
+    def arr(probs):
+        return (P * max(len(probs), 1))(*[P(*p) for p in probs])
+
+    def call(probs, K=512, M=1, codes=A, scales=A):
+        return f(arr(probs), len(probs), K, codes, scales, M, None)
+
+    def callq(probs, K=512, M=1):
+        return g(arr(probs), len(probs), K, M, None)
+    good = (A, A, A, 16)
+    assert f(None, 1, 512, A, A, 1, None) == EINVAL
+    assert call([good], codes=None) == EINVAL
+    assert call([good], scales=None) == EINVAL
+    assert call([]) == ESHAPE
+    assert call([good] * 9) == ESHAPE
+    assert call([good], K=500) == ESHAPE
+    assert call([good], M=9) == ESHAPE
+    assert call([good], K=12544) == ESHAPE              # K beyond 48 super-blocks
+    assert call([good], K=12288, M=8) == ESHAPE         # staged rows beyond any LDS
+    assert call([good, (A, A, A, 0)]) == ESHAPE
+    assert call([good, (None, A, A, 16)]) == EINVAL
+    assert call([good, (A, A, None, 16)]) == EINVAL
+    assert call([good], codes=A + 8) == EALIGN
+    assert call([good], scales=A + 2) == EALIGN
+    assert call([good, (A + 4, A, A, 16)]) == EALIGN
+    assert call([good, (A, A, A + 2, 16)]) == EALIGN
+    assert g(None, 1, 512, 1, None) == EINVAL
+    assert callq([]) == ESHAPE
+    assert callq([good] * 9) == ESHAPE
+    assert callq([good], K=500) == ESHAPE
+    assert callq([good], M=9) == ESHAPE
+    assert callq([good], K=12288, M=8) == ESHAPE
+    assert callq([good, (A, None, A, 16)]) == EINVAL
+    assert callq([good, (A, A + 4, A, 16)]) == EALIGN
+
+
 def test_gemm_batch_argument_checks(L):
     f = L.q4k_gemm_batch
     P = q4k._lib.GemmProblem

@@ -136,3 +136,38 @@ def test_q6k_quantize_gemv_bit_identical_to_two_step(q4k, oracle_lib, N, K, M):
     rc, rs, _ = oracle_lib.quantize_act(x)
     ref = oracle_lib.q6k_matvec(w, N, K, rc, rs, rows=rows)
     assert_close(y1 if rows is None else y1[:, rows], ref, "q6k_quantize_gemv N=%d K=%d M=%d" % (N, K, M))
+
+
+_Q6_BATCHES = {
+    # name: (K, [N_i]) -- the decode launch groups, and eight ragged products
+    "qkv": (2560, [4096, 1024, 1024]),
+    "gate_up": (2560, [9728, 9728]),
+    "eight_ragged": (768, [1, 7, 33, 100, 257, 8, 9, 1000]),
+}
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("name", sorted(_Q6_BATCHES))
+def test_q6k_gemv_batch_bit_identical_to_single(q4k, oracle_lib, name, M):
+    """q6k_gemv_batch (one launch, shared prepared rows) equals q6k_gemv on
+    each product bit for bit; q6k_quantize_gemv_batch (each product its own
+    fp32 rows) equals q6k_quantize_gemv likewise; sampled rows within the
+    tolerance of the oracle."""
+    import torch
+    K, Ns = _Q6_BATCHES[name]
+    ws = [to_dev(qi.make_q6k_bytes(N, K, 5100 + 31 * i + N)) for i, N in enumerate(Ns)]
+    x = qi.make_act(M, K, 5200 + M + K)
+    codes, scales, _ = oracle_lib.quantize_act(x)
+    dc, ds = to_dev(codes), to_dev(scales)
+    ys = q4k.q6k_gemv_batch(list(zip(ws, Ns)), K, dc, ds)
+    singles = [q4k.q6k_gemv(w, N, K, dc, ds) for w, N in zip(ws, Ns)]
+    xs = [to_dev(qi.make_act(M, K, 5300 + 7 * i + M)) for i in range(len(Ns))]
+    yq = q4k.q6k_quantize_gemv_batch([(w, N, xi) for w, N, xi in zip(ws, Ns, xs)], K)
+    sq = [q4k.q6k_quantize_gemv(w, N, K, xi) for w, N, xi in zip(ws, Ns, xs)]
+    torch.cuda.synchronize()
+    for i, (w, N) in enumerate(zip(ws, Ns)):
+        assert torch.equal(ys[i].view(torch.int32), singles[i].view(torch.int32)), "%s %d" % (name, i)
+        assert torch.equal(yq[i].view(torch.int32), sq[i].view(torch.int32)), "%s fused %d" % (name, i)
+        rows = np.unique(np.r_[0, N - 1, np.random.default_rng(N + i).integers(0, N, 12)])
+        ref = oracle_lib.q6k_matvec(w.cpu().numpy(), N, K, codes, scales, rows=rows)
+        assert_close(ys[i].cpu().numpy()[:, rows], ref, "q6k_gemv_batch %s product %d" % (name, i))
