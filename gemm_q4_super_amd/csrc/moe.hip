@@ -71,6 +71,10 @@ struct MoeArgs {
     const float *xa, *xb;      // ACT_F32: x [.][K]; ACT_SWIGLU: g, u [P][K]
     const int32_t *ids;
     int direct;                // one token: slot a is pair a (no grouping)
+    // the grouping made once for the call (moe_quantize_group_kernel), or
+    // null: slot a's expert tab_e[a] (-1 past the touched ones) and its pairs
+    // tab_p[tab_s[a] .. tab_s[a + 1])
+    const int *tab_e, *tab_s, *tab_p;
     // Routed sum inside the launch (null cnt: none): the per-slot products go
     // to out[0] through agent-coherent stores, and the last workgroup of each
     // row block writes y[t][n] = sum over slots s in order of
@@ -215,87 +219,99 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
     const int lane = tid & 63, wave = tid >> 6;
     const int nw = nt >> 6;
 
-    // ---- grouping, in LDS: ids, touched-expert flags (a one-token call maps
-    // slot a to pair a directly: no flags, scan or pair list)
-    const bool direct = A.direct != 0;             // uniform
-    for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
-    if (!direct)
-        for (int e = tid; e < E; e += nt) s_flag[e] = 0;
-    if (tid == 0) s_e = -1;
-    __syncthreads();
-    if (!direct) {
-        for (int p = tid; p < P; p += nt) {
-            const int e = s_ids[p];
-            if (e >= 0 && e < E) s_flag[e] = 1;    // same value from every writer
-        }
-        __syncthreads();
-    }
-    if (A.zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
-        // per-slot rows of skipped pairs are zero (this block of rows)
-        for (int p = 0; p < P; ++p) {
-            const int e = s_ids[p];
-            if (e >= 0 && e < E) continue;
-            for (int n = row_base + tid; n < min(N, row_base + RBr); n += nt)
-                A.out[0][(int64_t)p * N + n] = 0.0f;
-        }
-        return;
-    }
-    const int mi = (int)blockIdx.y >= A.slots ? 1 : 0;   // which projection
-    if (direct) {
-        if (tid == 0) {
-            const int a = (int)blockIdx.y - mi * A.slots;
-            const int ea = s_ids[a];
-            s_e = ea >= 0 && ea < E ? ea : -1;
-            s_pairs[0] = a;
-        }
+    int mi, e, cnt;
+    if (A.tab_e) {                                 // uniform: the call's grouping table
+        mi = (int)blockIdx.y >= A.slots ? 1 : 0;
+        const int a = (int)blockIdx.y - mi * A.slots;
+        e = A.tab_e[a];
+        if (e < 0) return;                         // slot past the touched experts
+        const int q0 = A.tab_s[a];
+        cnt = A.tab_s[a + 1] - q0;
+        for (int p = tid; p < cnt; p += nt) s_pairs[p] = A.tab_p[q0 + p];
         __syncthreads();
     } else {
-        // slot a is the a-th smallest touched expert: each thread counts the
-        // flags of a range of experts, a block scan places the ranges
-        const int a = (int)blockIdx.y - mi * A.slots;
-        const int per = (E + nt - 1) / nt;
-        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-        int c = 0;
-        for (int e = e0; e < e1; ++e) c += s_flag[e];
-        int wtot;
-        const int ex = wave_exclusive_scan(c, &wtot);
-        if (lane == 0) s_wt[wave] = wtot;
+        // ---- grouping, in LDS: ids, touched-expert flags (a one-token call maps
+        // slot a to pair a directly: no flags, scan or pair list)
+        const bool direct = A.direct != 0;             // uniform
+        for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
+        if (!direct)
+            for (int e = tid; e < E; e += nt) s_flag[e] = 0;
+        if (tid == 0) s_e = -1;
         __syncthreads();
-        int base = ex;
-        for (int k = 0; k < wave; ++k) base += s_wt[k];
-        if (a >= base && a < base + c) {
-            int k = a - base;
-            for (int e = e0; e < e1; ++e)
-                if (s_flag[e] && k-- == 0) {
-                    s_e = e;
-                    break;
-                }
+        if (!direct) {
+            for (int p = tid; p < P; p += nt) {
+                const int e = s_ids[p];
+                if (e >= 0 && e < E) s_flag[e] = 1;    // same value from every writer
+            }
+            __syncthreads();
+        }
+        if (A.zero_skipped && (int)blockIdx.y == (int)gridDim.y - 1) {
+            // per-slot rows of skipped pairs are zero (this block of rows)
+            for (int p = 0; p < P; ++p) {
+                const int e = s_ids[p];
+                if (e >= 0 && e < E) continue;
+                for (int n = row_base + tid; n < min(N, row_base + RBr); n += nt)
+                    A.out[0][(int64_t)p * N + n] = 0.0f;
+            }
+            return;
+        }
+        mi = (int)blockIdx.y >= A.slots ? 1 : 0;         // which projection
+        if (direct) {
+            if (tid == 0) {
+                const int a = (int)blockIdx.y - mi * A.slots;
+                const int ea = s_ids[a];
+                s_e = ea >= 0 && ea < E ? ea : -1;
+                s_pairs[0] = a;
+            }
+            __syncthreads();
+        } else {
+            // slot a is the a-th smallest touched expert: each thread counts the
+            // flags of a range of experts, a block scan places the ranges
+            const int a = (int)blockIdx.y - mi * A.slots;
+            const int per = (E + nt - 1) / nt;
+            const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+            int c = 0;
+            for (int e = e0; e < e1; ++e) c += s_flag[e];
+            int wtot;
+            const int ex = wave_exclusive_scan(c, &wtot);
+            if (lane == 0) s_wt[wave] = wtot;
+            __syncthreads();
+            int base = ex;
+            for (int k = 0; k < wave; ++k) base += s_wt[k];
+            if (a >= base && a < base + c) {
+                int k = a - base;
+                for (int e = e0; e < e1; ++e)
+                    if (s_flag[e] && k-- == 0) {
+                        s_e = e;
+                        break;
+                    }
+            }
+            __syncthreads();
+        }
+        e = s_e;
+        if (e < 0) {                                   // uniform: slot past the touched experts
+            if (A.cnt) routed_sum(A, s_ids, row_base, RB);
+            return;
+        }
+        // the expert's pairs in ascending order: per round of nt pairs, wave
+        // ballots and the earlier waves' counts place each one
+        cnt = direct ? 1 : 0;
+        for (int p0 = 0; p0 < P && !direct; p0 += nt) {
+            const int p = p0 + tid;
+            const bool f = p < P && s_ids[p] == e;
+            const unsigned long long mask = __ballot(f);
+            const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0));
+            __syncthreads();                           // s_wt free again
+            if (lane == 0) s_wt[wave] = __popcll(mask);
+            __syncthreads();
+            int base = cnt;
+            for (int k = 0; k < wave; ++k) base += s_wt[k];
+            if (f) s_pairs[base + below] = p;
+            for (int k = 0; k < nw; ++k) cnt += s_wt[k];
         }
         __syncthreads();
     }
-    const int e = s_e;
-    if (e < 0) {                                   // uniform: slot past the touched experts
-        if (A.cnt) routed_sum(A, s_ids, row_base, RB);
-        return;
-    }
-    // the expert's pairs in ascending order: per round of nt pairs, wave
-    // ballots and the earlier waves' counts place each one
-    int cnt = direct ? 1 : 0;
-    for (int p0 = 0; p0 < P && !direct; p0 += nt) {
-        const int p = p0 + tid;
-        const bool f = p < P && s_ids[p] == e;
-        const unsigned long long mask = __ballot(f);
-        const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0));
-        __syncthreads();                           // s_wt free again
-        if (lane == 0) s_wt[wave] = __popcll(mask);
-        __syncthreads();
-        int base = cnt;
-        for (int k = 0; k < wave; ++k) base += s_wt[k];
-        if (f) s_pairs[base + below] = p;
-        for (int k = 0; k < nw; ++k) cnt += s_wt[k];
-    }
-    __syncthreads();
 
     const int g = lane >> 3, r = g & (RG - 1), sl = g >> lg_rg;
     const LaneMap L(lane & 7);
@@ -792,6 +808,85 @@ size_t rows_lds_bytes(int P, int E, int nwc, int nw) {
            align16(sizeof(float) * (size_t)nwc * 8 * P) + (size_t)nw * kRowsChunk * kStageBytes;
 }
 
+// The tokens' Q8 rows (workgroups 0 .. qgrid-1: q4k_quantize_act's mapping
+// and arithmetic, 8 lanes per 32-value block, so the same codes) and, in the
+// last workgroup, the call's pair grouping for the gate|up launch: slot a is
+// the a-th smallest touched expert (tab_e[a], -1 for the slots past them) and
+// its pairs are tab_p[tab_s[a] .. tab_s[a + 1]) -- made once here instead of
+// in every workgroup of that launch.  The order of an expert's pairs is free
+// (each pair's products are independent of it).
+__global__ __launch_bounds__(256) void moe_quantize_group_kernel(
+    const float *__restrict__ x, int64_t nblocks, int8_t *__restrict__ codes,
+    float *__restrict__ scales, int32_t *__restrict__ sums, const int32_t *__restrict__ ids,
+    int P, int E, int slots, int *tab_e, int *tab_s, int *tab_p) {
+    extern __shared__ __attribute__((aligned(16))) int lds_g[];
+    __shared__ int s_wt[4];
+    __shared__ int s_tot[2];
+    if ((int)blockIdx.x + 1 < (int)gridDim.x) {
+        const int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+        const int sub = threadIdx.x & 7;
+        if (blk >= nblocks) return;                // whole 8-lane groups
+        const int64_t off = blk * 32 + sub * 4;
+        const Q8Lane q = quantize_block8(*reinterpret_cast<const f32x4 *>(x + off));
+        *reinterpret_cast<unsigned *>(codes + off) = q.codes;
+        if (sub == 0) {
+            scales[blk] = q.d;
+            sums[blk] = q.sum;
+        }
+        return;
+    }
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+    int *s_ids = lds_g;                            // [P]
+    int *cnt = s_ids + P;                          // [E] pairs per expert, then cursor
+    for (int p = tid; p < P; p += nt) s_ids[p] = ids[p];
+    for (int e = tid; e < E; e += nt) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += nt) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    {
+        // one scan of (pairs, touched) over expert ranges: each touched expert's
+        // slot and first pair
+        const int per = (E + nt - 1) / nt;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        int c = 0, f = 0;
+        for (int e = e0; e < e1; ++e) {
+            c += cnt[e];
+            f += cnt[e] > 0;
+        }
+        int wtot;
+        const int ex = wave_exclusive_scan((c << 16) | f, &wtot);   // c, f <= 4096
+        if (lane == 0) s_wt[wave] = wtot;
+        __syncthreads();
+        int base = ex;
+        for (int k = 0; k < wave; ++k) base += s_wt[k];
+        int bc = base >> 16, bf = base & 0xFFFF;
+        for (int e = e0; e < e1; ++e) {
+            const int n = cnt[e];
+            if (n > 0) {
+                tab_e[bf] = e;
+                tab_s[bf] = bc;
+                ++bf;
+            }
+            cnt[e] = bc;
+            bc += n;
+        }
+        if (tid == nt - 1) {
+            s_tot[0] = bf;
+            s_tot[1] = bc;
+        }
+    }
+    __syncthreads();
+    for (int a = s_tot[0] + tid; a < slots; a += nt) tab_e[a] = -1;
+    for (int a = s_tot[0] + tid; a <= slots; a += nt) tab_s[a] = s_tot[1];
+    for (int p = tid; p < P; p += nt) {
+        const int e = s_ids[p];
+        if (e >= 0 && e < E) tab_p[atomicAdd(&cnt[e], 1)] = p;
+    }
+}
+
 // Launch shape for K = 256*nsb: column slots per wave enough that at most
 // kMoeWaves waves cover K in one pass (S = kStageSlots at most; wider K takes
 // several passes).  The shape depends on K alone -- not on the activation
@@ -897,9 +992,9 @@ size_t q8_rows_bytes(int64_t rows, int64_t K) {
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t topk, int64_t H, int64_t F) {
     const int64_t P = T * topk;
     // counters of the down launch; g, u, z; Q8 of x and of h for the unfused
-    // activations of larger T
+    // activations of larger T; the pair grouping (3P + 1 ints)
     return counter_bytes(H) + 2 * f32_bytes(P, F) + f32_bytes(P, H) + q8_rows_bytes(T, H) +
-           q8_rows_bytes(P, F);
+           q8_rows_bytes(P, F) + f32_bytes(1, 3 * P + 1);
 }
 
 hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint8_t *w_down,
@@ -921,6 +1016,7 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
     int8_t *hc = reinterpret_cast<int8_t *>(hq);
     float *hs = reinterpret_cast<float *>(hq + f32_bytes(P, F / 4));
     int32_t *hsu = reinterpret_cast<int32_t *>(hq + f32_bytes(P, F / 4) + f32_bytes(P, F / 32));
+    int *tab = reinterpret_cast<int *>(hq + q8_rows_bytes(P, F));   // [P] e, [P + 1] s, [P] p
     const int E = (int)n_experts;
     const Shape sh1 = shape(H / kQK), sh2 = shape(F / kQK);
     // gate|up forming Q8(h) itself: each workgroup holds the same rows of both
@@ -995,9 +1091,19 @@ hipError_t launch_moe_ffn(const uint8_t *w_gate, const uint8_t *w_up, const uint
         if (T <= kFuseMaxT) {
             err = gate_up_h8();
         } else {
-            err = launch_quantize(x, T, H, nullptr, xc, xs, xsu, stream);
+            // x's Q8 rows and the pair grouping in one launch
+            const int slots = (int)(P < E ? P : E);
+            const int64_t nblocks = T * (H / kQB);
+            const int qgrid = (int)((nblocks + 31) / 32);
+            hipLaunchKernelGGL(moe_quantize_group_kernel, dim3(qgrid + 1), dim3(256),
+                               sizeof(int) * (size_t)(P + E), stream, x, nblocks, xc, xs, xsu,
+                               ids, (int)P, E, slots, tab, tab + P, tab + 2 * P + 1);
+            err = hipGetLastError();
             if (err != hipSuccess) return err;
             MoeArgs A = {};
+            A.tab_e = tab;
+            A.tab_s = tab + P;
+            A.tab_p = tab + 2 * P + 1;
             A.w[0] = w_gate;
             A.w[1] = w_up;
             A.out[0] = g;

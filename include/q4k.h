@@ -281,9 +281,9 @@ size_t q4k_moe_workspace_bytes(int64_t T, int64_t topk, int64_t n_experts, int64
  *                 topk, n_experts, H, F) bytes, 256-byte aligned: counters of
  *                 the down launch (4 bytes per 16 rows of H, rounded up to 256
  *                 bytes; zero before the first call that uses the buffer, left
- *                 zero by every call), then g, u, the per-slot down products
- *                 and Q8 rows of x and h; calls sharing a workspace must not
- *                 overlap.
+ *                 zero by every call), then g, u, the per-slot down products,
+ *                 Q8 rows of x and h and the pair grouping; calls sharing a
+ *                 workspace must not overlap.
  * Limits as for q4k_moe_gemv; H and F multiples of 256. */
 int q4k_moe_ffn(const void *w_gate, const void *w_up, const void *w_down, int64_t n_experts,
                 int64_t stride_gate_up, int64_t stride_down, int64_t H, int64_t F,
