@@ -8,7 +8,9 @@
 // per-slot rows of skipped pairs).  Every workgroup groups the pairs itself
 // from ids[T][topk] (at most 4096 ids, in LDS): slot a is the a-th smallest
 // touched expert, and its pairs are taken in ascending pair order --
-// deterministic, no tables in memory and no separate grouping launch.  It then
+// deterministic, no tables in memory and no separate grouping launch (the
+// routed-expert layer above two tokens instead reads a table that its
+// quantizer launch makes once, moe_quantize_group_kernel).  It then
 // computes one block of that expert's rows for all of its pairs (the decode
 // GEMV's lane layout, every load in flight before the arithmetic), MC pairs
 // per pass with the weights in registers, so every touched expert's weights
