@@ -355,6 +355,30 @@ def test_moe_ffn_launch_forms(q4k, oracle_lib, T, topk, F_):
                         "moe_ffn T=%d topk=%d F=%d" % (T, topk, F_))
 
 
+def test_moe_ffn_many_experts(q4k, oracle_lib):
+    """2048 small experts (H = F = 256: one column per row) at 256 pairs: the
+    once-per-call grouping and the row-block down launch scan more experts
+    than threads; equal to the chain bit for bit and close to the oracle."""
+    import torch
+    n_exp, H_, F_, T, topk = 2048, 256, 256, 32, 8
+    wg = qi.make_q4k_bytes(n_exp * F_, H_, 4100)
+    wu = qi.make_q4k_bytes(n_exp * F_, H_, 4101)
+    wd = qi.make_q4k_bytes(n_exp * H_, F_, 4102)
+    ids, rw = qi.make_routing(T, n_exp, topk, 4103)
+    ids[5, 3] = ids[5, 2]                      # a token routing twice to one expert
+    x = to_dev(qi.make_act(T, H_, 4104))
+    dwg, dwu, dwd, dids, drw = to_dev(wg), to_dev(wu), to_dev(wd), to_dev(ids), to_dev(rw)
+    sgu, sd = F_ * (H_ // 256) * 144, H_ * (F_ // 256) * 144
+    y1 = q4k.q4k_moe_ffn(dwg, dwu, dwd, n_exp, sgu, sd, H_, F_, dids, drw, x)
+    g, u, hc, hs, y2 = _chain_parts(q4k, dwg, dwu, dwd, dids, drw, x, n_exp, H_, F_)
+    torch.cuda.synchronize()
+    y1 = y1.cpu().numpy()
+    assert np.isfinite(y1).all()
+    assert (y1.view(np.uint32) == y2.view(np.uint32)).all()
+    ref = oracle_lib.moe_layer(wg, wu, wd, n_exp, H_, F_, ids, rw, x.cpu().numpy(), parallel=True)
+    _assert_layer_close(oracle_lib, ref, g, u, hc, hs, y1, ids, rw, wd, H_, F_, "moe_ffn 2048 experts")
+
+
 def test_moe_routed_sum_in_launch_reuses_workspace(q4k, oracle_lib):
     """The weighted sum is formed inside the down launch by the last
     workgroup of each row block: one zero-filled workspace serves repeated
