@@ -222,6 +222,7 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
     const int nw = nt >> 6;
 
     int mi, e, cnt;
+    int pair_a = -1;                               // the slot's one pair (direct calls), else -1
     if (A.tab_e) {                                 // uniform: the call's grouping table
         mi = (int)blockIdx.y >= A.slots ? 1 : 0;
         const int a = (int)blockIdx.y - mi * A.slots;
@@ -231,6 +232,14 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
         cnt = A.tab_s[a + 1] - q0;
         for (int p = tid; p < cnt; p += nt) s_pairs[p] = A.tab_p[q0 + p];
         __syncthreads();
+    } else if (A.direct && !A.zero_skipped && !A.cnt) {
+        // one pair per slot, nothing else to do per call: the slot's id read
+        // by every thread, no staging of the ids and no barrier
+        mi = (int)blockIdx.y >= A.slots ? 1 : 0;
+        pair_a = (int)blockIdx.y - mi * A.slots;
+        e = A.ids[pair_a];
+        if (e < 0 || e >= E) return;               // uniform: the pair belongs to no expert
+        cnt = 1;
     } else {
         // ---- grouping, in LDS: ids, touched-expert flags (a one-token call maps
         // slot a to pair a directly: no flags, scan or pair list)
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
         int arow[MC];
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
-            const int pr = s_pairs[c0 + min(m, mc - 1)];
+            const int pr = pair_a >= 0 ? pair_a : s_pairs[c0 + min(m, mc - 1)];
             arow[m] = A.act_per_slot ? pr : pr / A.topk;
         }
         float acc[V][MC];
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
             int qs = 0;
             if constexpr (MODE == ACT_Q8) {
                 auto row_of = [&](int mm) {   // arow[mm] for a per-lane mm (from LDS)
-                    const int pr = s_pairs[c0 + min(mm, mc - 1)];
+                    const int pr = pair_a >= 0 ? pair_a : s_pairs[c0 + min(mm, mc - 1)];
                     return A.act_per_slot ? pr : pr / A.topk;
                 };
 #pragma unroll
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
                 if constexpr (H8) {
                     hrow[rr] = t;
                 } else {
-                    float *o = out + (int64_t)s_pairs[c0 + m] * N + n;
+                    float *o = out + (int64_t)(pair_a >= 0 ? pair_a : s_pairs[c0 + m]) * N + n;
                     if (A.cnt)
                         __hip_atomic_store(o, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     else
@@ -521,7 +530,7 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
                 const f32x4 h4 = {hrow[j], hrow[j + 1], hrow[j + 2], hrow[j + 3]};
                 const Q8Lane q = quantize_block8(h4);
                 if ((lane >> 3) < nb) {
-                    const int pr = s_pairs[c0];
+                    const int pr = pair_a >= 0 ? pair_a : s_pairs[c0];
                     *reinterpret_cast<unsigned *>(A.hc + (int64_t)pr * N + row_base + j) = q.codes;
                     if (q4 == 0) {
                         const int64_t so = (int64_t)pr * (N / 32) + row_base / 32 + bq;
@@ -573,6 +582,16 @@ __global__ __launch_bounds__(512) void moe_down_sum_kernel(const MoeArgs A) {
     for (int p = 0; p < PH; ++p) {
         const int e = A.ids[min(p0 + p, P - 1)];
         ex[p] = e >= 0 && e < E ? e : 0;
+    }
+    // every slot's id and routing weight for the final sum, requested now
+    // rather than after the barrier (slots past P repeat slot P-1 and are
+    // not added)
+    int eid[PM];
+    float rw[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        eid[p] = A.ids[min(p, P - 1)];
+        rw[p] = A.route_w[min(p, P - 1)];
     }
     float acc[PH];
 #pragma unroll
@@ -642,11 +661,12 @@ __global__ __launch_bounds__(512) void moe_down_sum_kernel(const MoeArgs A) {
     __syncthreads();
     if (tid < 8 && row_base + tid < N) {
         float v = 0.0f;
-        for (int p = 0; p < P; ++p) {
-            const int e = A.ids[p];
+#pragma unroll
+        for (int p = 0; p < PM; ++p) {
+            if (p >= P) break;                     // uniform
             float z = 0.0f;
             for (int c = 0; c < nwc; ++c) z += red[c][tid][p];
-            if (e >= 0 && e < E) v = fmaf(A.route_w[p], z, v);
+            if (eid[p] >= 0 && eid[p] < E) v = fmaf(rw[p], z, v);
         }
         A.y[row_base + tid] = v;
     }
@@ -677,14 +697,18 @@ __global__ __launch_bounds__(1024) void moe_down_rows_kernel(const MoeArgs A) {
     int *s_ids = lds_r;                            // [P rounded up to 4]
     int *cnt = s_ids + ((P + 3) & ~3);             // [E] pairs per expert, then cursor
     int *sorted = cnt + E;                         // [P] valid pairs by expert
+    float *s_rw = reinterpret_cast<float *>(sorted + P);   // [P] routing weights
     float *red = reinterpret_cast<float *>(
-        reinterpret_cast<uint8_t *>(lds_r) + align16(sizeof(int) * (((P + 3) & ~3) + (size_t)E + P)));
+        reinterpret_cast<uint8_t *>(lds_r) + align16(sizeof(int) * (((P + 3) & ~3) + (size_t)E + 2 * P)));
     uint8_t *stage = reinterpret_cast<uint8_t *>(red) + align16(sizeof(float) * (size_t)nwc * 8 * P) +
                      (size_t)wave * XB * kStageBytes;
 
     // ---- grouping: a count per expert, a scan of the counts over expert
     // ranges, then each valid pair placed at its expert's cursor
-    for (int p = tid; p < P; p += nt) s_ids[p] = A.ids[p];
+    for (int p = tid; p < P; p += nt) {
+        s_ids[p] = A.ids[p];
+        s_rw[p] = A.route_w[p];                    // for the routed sum at the end
+    }
     for (int e = tid; e < E; e += nt) cnt[e] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += nt) {
@@ -797,7 +821,7 @@ __global__ __launch_bounds__(1024) void moe_down_rows_kernel(const MoeArgs A) {
             if (e >= 0 && e < E) {
                 float z = 0.0f;
                 for (int cc = 0; cc < nwc; ++cc) z += red[((size_t)cc * 8 + rw) * P + p];
-                v = fmaf(A.route_w[p], z, v);
+                v = fmaf(s_rw[p], z, v);
             }
         }
         A.y[(int64_t)t * N + n] = v;
@@ -806,7 +830,7 @@ __global__ __launch_bounds__(1024) void moe_down_rows_kernel(const MoeArgs A) {
 
 // Dynamic LDS of moe_down_rows_kernel.
 size_t rows_lds_bytes(int P, int E, int nwc, int nw) {
-    return align16(sizeof(int) * (((size_t)(P + 3) & ~size_t(3)) + (size_t)E + P)) +
+    return align16(sizeof(int) * (((size_t)(P + 3) & ~size_t(3)) + (size_t)E + 2 * (size_t)P)) +
            align16(sizeof(float) * (size_t)nwc * 8 * P) + (size_t)nw * kRowsChunk * kStageBytes;
 }
 
