@@ -500,8 +500,18 @@ __global__ __launch_bounds__(MODE == ACT_F32_H8 ? 512 : 256) void moe_kernel(con
             const int n = row_base + (H8 ? rr % RBr : rr);
             if (m < mc && n < N) {
                 float t = 0.0f;
-                for (int wv = 0; wv < nw; ++wv)
-                    for (int k = 0; k < S; ++k) t += red[wv][k * RB + rr][m];
+                if (S == 1) {                          // uniform
+                    // every wave's term requested before the first add (rows of
+                    // waves past nw are read and not added)
+                    float tw[NWMAX];
+#pragma unroll
+                    for (int wv = 0; wv < NWMAX; ++wv) tw[wv] = red[wv][rr][m];
+#pragma unroll
+                    for (int wv = 0; wv < NWMAX; ++wv) t = wv < nw ? t + tw[wv] : t;
+                } else {
+                    for (int wv = 0; wv < nw; ++wv)
+                        for (int k = 0; k < S; ++k) t += red[wv][k * RB + rr][m];
+                }
                 if constexpr (H8) {
                     hrow[rr] = t;
                 } else {
@@ -660,13 +670,21 @@ __global__ __launch_bounds__(512) void moe_down_sum_kernel(const MoeArgs A) {
     }
     __syncthreads();
     if (tid < 8 && row_base + tid < N) {
+        // every slot's column terms requested before the first add; terms of
+        // waves past nwc and slots past P are read and not added (selects, so
+        // no read waits behind a branch)
+        float zr[PM][kMoeWaves];
+#pragma unroll
+        for (int p = 0; p < PM; ++p)
+#pragma unroll
+            for (int c = 0; c < kMoeWaves; ++c) zr[p][c] = red[c][tid][p];
         float v = 0.0f;
 #pragma unroll
         for (int p = 0; p < PM; ++p) {
-            if (p >= P) break;                     // uniform
             float z = 0.0f;
-            for (int c = 0; c < nwc; ++c) z += red[c][tid][p];
-            if (eid[p] >= 0 && eid[p] < E) v = fmaf(rw[p], z, v);
+#pragma unroll
+            for (int c = 0; c < kMoeWaves; ++c) z = c < nwc ? z + zr[p][c] : z;
+            v = p < P && eid[p] >= 0 && eid[p] < E ? fmaf(rw[p], z, v) : v;
         }
         A.y[row_base + tid] = v;
     }
@@ -815,13 +833,27 @@ __global__ __launch_bounds__(1024) void moe_down_rows_kernel(const MoeArgs A) {
         const int t = i >> 3, rw = i & 7, n = row_base + rw;
         if (n >= N) continue;
         float v = 0.0f;
-        for (int sl = 0; sl < topk; ++sl) {
-            const int p = t * topk + sl;
-            const int e = s_ids[p];
-            if (e >= 0 && e < E) {
+        // 8 slots at a time, every read of them requested before the first add
+        // (slots past topk repeat the last slot and column waves past nwc the
+        // last wave; neither is added)
+        for (int s0 = 0; s0 < topk; s0 += 8) {
+            int ee[8];
+            float ww[8], zr[8][kMoeWaves];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int p = t * topk + min(s0 + j, topk - 1);
+                ee[j] = s_ids[p];
+                ww[j] = s_rw[p];
+#pragma unroll
+                for (int cc = 0; cc < kMoeWaves; ++cc)
+                    zr[j][cc] = red[((size_t)min(cc, nwc - 1) * 8 + rw) * P + p];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
                 float z = 0.0f;
-                for (int cc = 0; cc < nwc; ++cc) z += red[((size_t)cc * 8 + rw) * P + p];
-                v = fmaf(s_rw[p], z, v);
+#pragma unroll
+                for (int cc = 0; cc < kMoeWaves; ++cc) z = cc < nwc ? z + zr[j][cc] : z;
+                v = s0 + j < topk && ee[j] >= 0 && ee[j] < E ? fmaf(ww[j], z, v) : v;
             }
         }
         A.y[(int64_t)t * N + n] = v;
