@@ -138,17 +138,28 @@ __device__ void routed_sum(const MoeArgs &A, const int *s_ids, int row_base, int
     const int rows = min(RB, N - row_base);
     const int total = A.T * rows;
     // one output per thread when they fit the workgroup, else kOut per
-    // thread at a time; a thread's loads are all in flight before it stores
+    // thread at a time; the slots are taken kSlotStep at a time with every
+    // load of a step issued before its first fma (slots past topk repeat the
+    // last slot and are not added: selects, so no load waits behind a branch)
+    constexpr int kSlotStep = 8;
     if (total <= (int)blockDim.x) {
         if ((int)threadIdx.x < total) {
             const int t = threadIdx.x / rows, n = row_base + threadIdx.x % rows;
             float v = 0.0f;
-            for (int s = 0; s < topk; ++s) {
-                const int p = t * topk + s;
-                const int e = s_ids[p];
-                const float z = __hip_atomic_load(A.out[0] + (int64_t)p * N + n,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (e >= 0 && e < E) v = fmaf(A.route_w[p], z, v);
+            for (int s0 = 0; s0 < topk; s0 += kSlotStep) {
+                int ee[kSlotStep];
+                float zz[kSlotStep], ww[kSlotStep];
+#pragma unroll
+                for (int j = 0; j < kSlotStep; ++j) {
+                    const int p = t * topk + min(s0 + j, topk - 1);
+                    ee[j] = s_ids[p];
+                    zz[j] = __hip_atomic_load(A.out[0] + (int64_t)p * N + n, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    ww[j] = A.route_w[p];
+                }
+#pragma unroll
+                for (int j = 0; j < kSlotStep; ++j)
+                    v = s0 + j < topk && ee[j] >= 0 && ee[j] < E ? fmaf(ww[j], zz[j], v) : v;
             }
             A.y[(int64_t)t * N + n] = v;
         }
@@ -164,15 +175,25 @@ __device__ void routed_sum(const MoeArgs &A, const int *s_ids, int row_base, int
             n[k] = row_base + i % rows;
             v[k] = 0.0f;
         }
-        for (int s = 0; s < topk; ++s) {
+        for (int s0 = 0; s0 < topk; s0 += kSlotStep) {
+            int ee[kOut][kSlotStep];
+            float zz[kOut][kSlotStep], ww[kOut][kSlotStep];
 #pragma unroll
-            for (int k = 0; k < kOut; ++k) {
-                const int p = t[k] * topk + s;
-                const int e = s_ids[p];
-                const float z = __hip_atomic_load(A.out[0] + (int64_t)p * N + n[k],
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (e >= 0 && e < E) v[k] = fmaf(A.route_w[p], z, v[k]);
-            }
+            for (int k = 0; k < kOut; ++k)
+#pragma unroll
+                for (int j = 0; j < kSlotStep; ++j) {
+                    const int p = t[k] * topk + min(s0 + j, topk - 1);
+                    ee[k][j] = s_ids[p];
+                    zz[k][j] = __hip_atomic_load(A.out[0] + (int64_t)p * N + n[k], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    ww[k][j] = A.route_w[p];
+                }
+#pragma unroll
+            for (int k = 0; k < kOut; ++k)
+#pragma unroll
+                for (int j = 0; j < kSlotStep; ++j)
+                    v[k] = s0 + j < topk && ee[k][j] >= 0 && ee[k][j] < E
+                               ? fmaf(ww[k][j], zz[k][j], v[k]) : v[k];
         }
 #pragma unroll
         for (int k = 0; k < kOut; ++k)
