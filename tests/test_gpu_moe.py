@@ -327,14 +327,17 @@ def test_moe_ffn_one_token(q4k, oracle_lib, topk, F_, bad):
 
 
 @pytest.mark.parametrize("T,topk,F_", [(2, 4, 512), (3, 8, 1024), (1, 8, 2048), (40, 8, 512),
-                                       (32, 8, 1024)])
+                                       (32, 8, 1024), (3, 12, 512), (1, 10, 512)])
 def test_moe_ffn_launch_forms(q4k, oracle_lib, T, topk, F_):
     """Every form q4k_moe_ffn picks: two tokens (Q8(h) from the gate|up launch,
     the row-block down launch), three (the quantizer, then the row-block down
     launch), one token on a wide FFN and more than 256 pairs (the grouped
     launches with the routed sum by the last workgroup), and exactly 256
-    pairs (the row-block down launch at its limit): equal to the chain
-    bit for bit and close to the oracle."""
+    pairs (the row-block down launch at its limit); and more than 8 slots per
+    token (the slot sums take 8 slots per step: a second, partial step), in
+    the row-block down launch (T = 3) and, one token past the one-token
+    down launch's 8 slots, in the routed sum by the last workgroup: equal to
+    the chain bit for bit and close to the oracle."""
     import torch
     n_exp, H_ = 12, 512
     wg = np.concatenate([qi.make_q4k_bytes(F_, H_, 3300 + e) for e in range(n_exp)])
